@@ -1,0 +1,199 @@
+/*
+ * spec_verify.h -- C ABI of libspec_verify.so, the verify step of speculative
+ * decoding on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *  [SD]     "Fast Inference from Transformers via Speculative Decoding",
+ *           Pith review page (pith.science, arXiv 2211.17192).
+ *  [Falcon] "Falcon: Faster and Parallel Inference of Large Language Models
+ *           through Enhanced Semi-Autoregressive Drafting and Custom-Designed
+ *           Decoding Tree", Pith review page (pith.science, arXiv 2412.12639).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named *logits, tokens, uniforms, temperature, parents, out_* and
+ *    workspace are DEVICE pointers owned by the caller. The library never
+ *    allocates, frees or retains them past the call.
+ *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *    stream). Every call only enqueues work on it and returns; outputs are
+ *    valid once the stream reaches that point. No call synchronises.
+ *  - Strides are in ELEMENTS of the logits' dtype. Every logits row must start
+ *    on a 16-byte boundary: base pointer, row stride and sequence stride times
+ *    the element size must all be multiples of 16 bytes (a sequence stride of 0
+ *    is allowed and makes every sequence share one block of rows). The kernels
+ *    may read the rest of the 16-byte block that holds a row's last element;
+ *    those bytes are ignored.
+ *  - Return value: SV_OK, or a negative sv_status. Argument errors are found
+ *    on the host before any HIP call, so nothing is enqueued when a call fails
+ *    that way. Data-dependent problems (bad token, NaN row, ...) do not fail
+ *    the call: the affected sequence reports -1 (see each call).
+ *  - Workspace: device memory of at least the size the matching *_workspace_bytes
+ *    function returns, 256-byte aligned, zero-filled before its first use and
+ *    again before it is used for a call of another kind or another (B, gamma
+ *    or N, V) (sv_workspace_clear does that). Every call that runs to
+ *    completion leaves its counters at zero, so later calls of the same kind
+ *    and shape on the same stream can reuse it as it is. Calls that overlap in
+ *    time must not share a workspace.
+ *  - No C++ exception crosses this interface. The library holds no global
+ *    mutable state apart from the thread-local last HIP error.
+ *  - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_NULL = -1,      /* a required pointer is NULL */
+  SV_ERR_SHAPE = -2,     /* B, gamma, V or N out of range, stride < V, size overflow */
+  SV_ERR_DTYPE = -3,     /* dtype is not SV_F32 or SV_BF16 */
+  SV_ERR_ALIGN = -4,     /* a logits row does not start on a 16-byte boundary; a
+                            4-byte array is not 4-byte aligned; workspace not 256-byte aligned */
+  SV_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
+  SV_ERR_HIP = -6,       /* a HIP launch failed; sv_last_hip_error() gives the hipError_t */
+  SV_ERR_ARG = -7        /* any other invalid argument (e.g. an unknown stage) */
+} sv_status;
+
+/* Limits checked on the host. */
+#define SV_MAX_GAMMA 64
+#define SV_MAX_TREE_NODES 1024
+#define SV_MAX_VOCAB (1 << 30)
+#define SV_MAX_BATCH (1 << 24)
+
+/* Workspace sizes in bytes (valid for either logits dtype). 0 for shapes
+ * outside the limits above. */
+size_t sv_sample_workspace_bytes(int B, int gamma, int V);
+size_t sv_tree_workspace_bytes(int B, int N, int V);
+
+/* Zero-fill `bytes` of device memory at `workspace` on `stream` with a small
+ * kernel (no memset node, so it is safe inside captured graphs). */
+int sv_workspace_clear(void* workspace, size_t bytes, void* stream);
+
+/* Optional per-position diagnostics of spec_verify_sample; any member may be
+ * NULL (not written). Values are fp32 roundings of fp64 results. */
+typedef struct {
+  float* p_x;        /* [B][gamma]: p_i(x_i), target probability of draft token i */
+  float* q_x;        /* [B][gamma]: q_i(x_i), draft probability of draft token i */
+  float* resid_mass; /* [B]: mass of the distribution the final token was drawn from,
+                        before renormalisation: 1 - alpha_n after a rejection at n
+                        (alpha_n = sum_v min(p_n,v, q_n,v)), about 1 for the bonus row */
+} sv_sample_diag;
+
+/*
+ * spec_verify_sample -- speculative sampling verification of B sequences.
+ *
+ * Defines: [SD] "The pith" and "What carries the argument" (score gamma drafted
+ * tokens in one parallel target pass, keep the longest accepted prefix, emit
+ * several tokens per target call); [SD] "Desk Editor's Note" and "Referee
+ * Report" (Summary, Significance) (a rejection-sampling correction whose
+ * accept probability comes from the target conditional); [SD] abstract, "Core
+ * claim" and "Circularity Check" (the output distribution is exactly the
+ * target's). For sequence b with temperature T:
+ *   p_i = softmax(target row i / T), q_i = softmax(draft row i / T);
+ *   accept x_i iff u[b][i] < p_i(x_i) / q_i(x_i), for i = 0, 1, ... until the
+ *   first rejection n (n = gamma if all are accepted);
+ *   after a rejection draw y from max(0, p_n - q_n) renormalised, otherwise
+ *   from p_gamma (the bonus row), by inverse CDF in token-id order at
+ *   u[b][gamma] (the smallest v whose running mass exceeds u * total);
+ *   out_tokens[b] = x_0 .. x_{n-1}, y, then -1; out_num_accepted[b] = n.
+ *
+ * target_logits : logical [B][gamma+1][V], dtype target_dtype; row i (i < gamma)
+ *                 holds the target's next-token logits after the drafts
+ *                 x_0..x_{i-1}; row gamma is the bonus row.
+ * draft_logits  : logical [B][gamma][V], dtype draft_dtype; row i is the
+ *                 distribution x_i was drawn from.
+ * draft_tokens  : [B][gamma] int32, contiguous.
+ * uniforms      : [B][gamma+1] float, contiguous, each in [0, 1): u[b][i]
+ *                 for the accept test of position i, u[b][gamma] for the draw.
+ * temperature   : [B] float, each finite, positive and normal (>= 2^-126).
+ * out_num_accepted : [B] int32: n in [0, gamma], or -1 for an invalid sequence.
+ * out_tokens    : [B][gamma+1] int32 (all -1 for an invalid sequence).
+ * diag          : may be NULL.
+ *
+ * A sequence is invalid (-1) when its temperature is not usable, or when a
+ * position the method reaches (accept tests 0..n, the draw at n or gamma) has a
+ * token outside [0, V), a draft token whose draft logit is -inf, a uniform
+ * outside [0, 1), or a target/draft row with NaN, +inf or no finite value.
+ * Rows after the first rejection are not consulted.
+ */
+int spec_verify_sample(const void* target_logits, int target_dtype, int64_t target_seq_stride,
+                       int64_t target_row_stride, const void* draft_logits, int draft_dtype,
+                       int64_t draft_seq_stride, int64_t draft_row_stride, const int32_t* draft_tokens,
+                       const float* uniforms, const float* temperature, int B, int gamma, int V,
+                       int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_sample_stage -- the two halves of spec_verify_sample, for callers
+ * that want to time or overlap them. Same arguments and meaning as
+ * spec_verify_sample; `stage` selects:
+ *   1: row statistics of every target and draft row, accept tests and first
+ *      rejection (results stay in the workspace);
+ *   2: the residual / bonus draw and every output.
+ * Stage 2 must follow stage 1 on the same stream with the same arguments and
+ * workspace. spec_verify_sample is stage 1 then stage 2.
+ */
+int spec_verify_sample_stage(int stage, const void* target_logits, int target_dtype,
+                             int64_t target_seq_stride, int64_t target_row_stride, const void* draft_logits,
+                             int draft_dtype, int64_t draft_seq_stride, int64_t draft_row_stride,
+                             const int32_t* draft_tokens, const float* uniforms, const float* temperature,
+                             int B, int gamma, int V, int32_t* out_num_accepted, int32_t* out_tokens,
+                             const sv_sample_diag* diag, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * spec_verify_greedy_tree -- greedy verification of B draft trees.
+ *
+ * Defines: [Falcon] "What carries the argument" (the drafter proposes a tree of
+ * candidate branches that the target verifies in one parallel pass) and
+ * [Falcon] "Assumptions & free parameters" with Figure 4 (greedy decoding,
+ * temperature 0; the result equals vanilla autoregressive decoding). For tree b:
+ *   g_j = argmax_v logits[b][j][v] (lowest v on ties; -0 equals +0);
+ *   node 0 (the root) is accepted; node j >= 1 is accepted iff its parent is
+ *   accepted and tokens[b][j] == g_{parents[b][j]};
+ *   d = the accepted node of largest depth (lowest node id on ties);
+ *   out_accept_len[b] = depth(d); out_path[b] = node ids root .. d, then -1;
+ *   out_bonus[b] = g_d.
+ *
+ * target_logits : logical [B][N][V]; row j holds the target's next-token
+ *                 logits after node j.
+ * parents       : [B][N] int32, contiguous; parents[b][0] = -1 and
+ *                 0 <= parents[b][j] < j.
+ * tokens        : [B][N] int32, contiguous; tokens[b][0] (the root) is unused,
+ *                 tokens[b][j] in [0, V) for j >= 1.
+ * out_accept_len: [B] int32: depth of d, or -1 for an invalid tree.
+ * out_path      : [B][N] int32.
+ * out_bonus     : [B] int32.
+ * out_argmax    : [B][N] int32 per-node argmax (-1 for a row with NaN or
+ *                 +inf); may be NULL.
+ *
+ * A tree is invalid (-1 everywhere) if its parent array breaks the rule above,
+ * a non-root token is outside [0, V), or any of its rows holds NaN or +inf.
+ * A row of -inf only has argmax 0.
+ */
+int spec_verify_greedy_tree(const void* target_logits, int dtype, int64_t seq_stride, int64_t row_stride,
+                            const int32_t* parents, const int32_t* tokens, int B, int N, int V,
+                            int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus,
+                            int32_t* out_argmax, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text of a status code (static storage). */
+const char* sv_status_string(int status);
+
+/* hipError_t of the last failed HIP call made by this thread inside the library (0 = none). */
+int sv_last_hip_error(void);
+
+/* Library version string. */
+const char* sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

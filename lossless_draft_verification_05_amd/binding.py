@@ -1,0 +1,260 @@
+"""ctypes binding of libspec_verify.so.
+
+Argument marshalling only: every step of the verify path runs in the HIP
+kernels behind the C ABI declared in include/spec_verify.h. PyTorch supplies
+device memory and the current stream; nothing here computes on the data.
+There is no fallback: if the shared library is missing, ``load`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspec_verify.so")
+
+SV_F32, SV_BF16 = 0, 1
+SV_OK = 0
+_ARG_ERRORS = {-1, -2, -3, -4, -5, -7}
+
+_lib = None
+
+# Every symbol the header declares, with its ctypes signature.
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "sv_sample_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "sv_tree_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "sv_workspace_clear": (_i32, [_vp, _sz, _vp]),
+    "spec_verify_sample": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32,
+                                  _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample_stage": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32,
+                                        _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_greedy_tree": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                       _sz, _vp]),
+    "sv_status_string": (ctypes.c_char_p, [_i32]),
+    "sv_last_hip_error": (_i32, []),
+    "sv_version": (ctypes.c_char_p, []),
+}
+
+
+class SampleDiag(ctypes.Structure):
+    _fields_ = [("p_x", ctypes.c_void_p), ("q_x", ctypes.c_void_p), ("resid_mass", ctypes.c_void_p)]
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m lossless_draft_verification_05_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return load().sv_status_string(st).decode()
+
+
+def _check(st: int, what: str):
+    if st == SV_OK:
+        return
+    msg = f"{what}: {status_string(st)} (status {st})"
+    if st in _ARG_ERRORS:
+        raise ValueError(msg)
+    raise RuntimeError(f"{msg}; hipError {load().sv_last_hip_error()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise ValueError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _logits3(t: torch.Tensor, name: str, rows: int):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 3:
+        raise ValueError(f"{name} must be a 3-d CUDA tensor")
+    if t.shape[1] != rows:
+        raise ValueError(f"{name} must have {rows} rows per sequence, got {t.shape[1]}")
+    if t.stride(2) != 1 and t.shape[2] > 1:
+        raise ValueError(f"{name} rows must be contiguous (last stride 1)")
+    return t.stride(0), t.stride(1)
+
+
+class Workspace:
+    """Zero-initialised device workspace, grown on demand and reused.
+
+    Each completed call leaves the counters it used at zero, so calls of the
+    same kind and shape ordered on one stream can share it. The counters sit at
+    shape-dependent offsets, so the buffer is cleared (on the call's stream)
+    whenever the kind or shape of the call changes. Calls that may run at the
+    same time need separate Workspace objects.
+    """
+
+    def __init__(self):
+        self.buf = None
+        self.key = None
+
+    def get(self, nbytes: int, device, key, stream=None) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self.key = key
+        elif key != self.key:
+            sv_workspace_clear(self.buf, stream)
+            self.key = key
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws, nbytes, device, key, stream):
+    """A Workspace object (default: one per device) or a caller-managed uint8 tensor."""
+    if ws is None:
+        ws = _default_ws.setdefault(device, Workspace())
+    buf = ws.get(nbytes, device, key, stream) if isinstance(ws, Workspace) else ws
+    if buf.numel() < nbytes:
+        raise ValueError(f"workspace has {buf.numel()} bytes, needs {nbytes}")
+    return buf
+
+
+def sv_sample_workspace_bytes(B: int, gamma: int, V: int) -> int:
+    return int(load().sv_sample_workspace_bytes(B, gamma, V))
+
+
+def sv_tree_workspace_bytes(B: int, N: int, V: int) -> int:
+    return int(load().sv_tree_workspace_bytes(B, N, V))
+
+
+def sv_workspace_clear(buf: torch.Tensor, stream=None):
+    _check(load().sv_workspace_clear(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream)),
+           "sv_workspace_clear")
+
+
+def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_num_accepted, out_tokens, diag,
+                 workspace, stream):
+    lib = load()
+    B, G1, V = target.shape
+    G = G1 - 1
+    ts, tr = _logits3(target, "target", G + 1)
+    ds, dr = _logits3(draft, "draft", G)
+    if draft.shape[0] != B or draft.shape[2] != V:
+        raise ValueError("draft must be [B][gamma][V] matching target")
+    dev = target.device
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, G))
+    _need(uniforms, "uniforms", torch.float32, (B, G + 1))
+    _need(temperature, "temperature", torch.float32, (B,))
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    _need(out_num_accepted, "out_num_accepted", torch.int32, (B,))
+    _need(out_tokens, "out_tokens", torch.int32, (B, G + 1))
+    d = None
+    dptr = None
+    if diag:
+        d = {"p_x": torch.empty((B, G), dtype=torch.float32, device=dev),
+             "q_x": torch.empty((B, G), dtype=torch.float32, device=dev),
+             "resid_mass": torch.empty(B, dtype=torch.float32, device=dev)}
+        dptr = SampleDiag(d["p_x"].data_ptr(), d["q_x"].data_ptr(), d["resid_mass"].data_ptr())
+    nbytes = sv_sample_workspace_bytes(B, G, V)
+    if nbytes == 0:
+        raise ValueError(f"shape B={B} gamma={G} V={V} out of range")
+    ws = _workspace(workspace, nbytes, dev, ("sample", B, G, V), stream)
+    args = (_ptr(target), _dtype_code(target), ts, tr, _ptr(draft), _dtype_code(draft), ds, dr, _ptr(draft_tokens),
+            _ptr(uniforms), _ptr(temperature), B, G, V, _ptr(out_num_accepted), _ptr(out_tokens),
+            ctypes.byref(dptr) if dptr is not None else None, _ptr(ws), ws.numel(), _stream(stream))
+    if stage is None:
+        st = lib.spec_verify_sample(*args)
+        _check(st, "spec_verify_sample")
+    else:
+        st = lib.spec_verify_sample_stage(stage, *args)
+        _check(st, f"spec_verify_sample_stage({stage})")
+    return out_num_accepted, out_tokens, d
+
+
+def spec_verify_sample(target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
+                       out_tokens=None, diag=False, workspace=None, stream=None):
+    """Speculative-sampling verify of B sequences on the GPU (see include/spec_verify.h).
+
+    target [B][gamma+1][V] and draft [B][gamma][V] are bf16 or fp32 CUDA tensors
+    whose rows are contiguous and 16-byte aligned (a stride-0 batch dimension
+    is allowed); draft_tokens int32 [B][gamma]; uniforms fp32 [B][gamma+1];
+    temperature fp32 [B]. Returns (num_accepted [B], tokens [B][gamma+1], diag
+    dict or None). Work is enqueued on ``stream`` (default: current stream).
+    """
+    return _sample_call(None, target, draft, draft_tokens, uniforms, temperature, out_num_accepted, out_tokens,
+                        diag, workspace, stream)
+
+
+def spec_verify_sample_stage(stage, target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
+                             out_tokens=None, diag=False, workspace=None, stream=None):
+    """Stage 1 (row statistics, accept tests) or 2 (draw, outputs) of spec_verify_sample."""
+    return _sample_call(int(stage), target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
+                        out_tokens, diag, workspace, stream)
+
+
+def spec_verify_greedy_tree(logits, parents, tokens, *, out_accept_len=None, out_path=None, out_bonus=None,
+                            out_argmax=None, want_argmax=True, workspace=None, stream=None):
+    """Greedy decoding-tree verify of B trees (see include/spec_verify.h).
+
+    logits [B][N][V] bf16/fp32 (rows contiguous, 16-byte aligned); parents and
+    tokens int32 [B][N]. Returns (accept_len [B], path [B][N], bonus [B],
+    argmax [B][N] or None).
+    """
+    lib = load()
+    B, N, V = logits.shape
+    s0, s1 = _logits3(logits, "logits", N)
+    dev = logits.device
+    _need(parents, "parents", torch.int32, (B, N))
+    _need(tokens, "tokens", torch.int32, (B, N))
+    if out_accept_len is None:
+        out_accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_path is None:
+        out_path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if out_bonus is None:
+        out_bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_argmax is None and want_argmax:
+        out_argmax = torch.empty((B, N), dtype=torch.int32, device=dev)
+    nbytes = sv_tree_workspace_bytes(B, N, V)
+    if nbytes == 0:
+        raise ValueError(f"shape B={B} N={N} V={V} out of range")
+    ws = _workspace(workspace, nbytes, dev, ("tree", B, N, V), stream)
+    st = lib.spec_verify_greedy_tree(_ptr(logits), _dtype_code(logits), s0, s1, _ptr(parents), _ptr(tokens), B, N, V,
+                                     _ptr(out_accept_len), _ptr(out_path), _ptr(out_bonus), _ptr(out_argmax), _ptr(ws),
+                                     ws.numel(), _stream(stream))
+    _check(st, "spec_verify_greedy_tree")
+    return out_accept_len, out_path, out_bonus, out_argmax
+
+
+def version() -> str:
+    return load().sv_version().decode()

@@ -1,0 +1,268 @@
+// sv_api.hip -- the C ABI of libspec_verify: argument checks on the host, work
+// decomposition, workspace layout and kernel launches. Every argument error is
+// returned before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/spec_verify.h"
+#include "sv_plan.hpp"
+
+namespace sv {
+hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stage, hipStream_t stream);
+hipError_t launch_tree(const TreeLaunch& A, int dt, hipStream_t stream);
+
+static thread_local int g_last_hip_error = 0;
+
+static int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SV_OK;
+  g_last_hip_error = (int)e;
+  return SV_ERR_HIP;
+}
+
+static inline int esz_of(int dt) { return dt == SV_BF16 ? 2 : 4; }
+static inline bool dtype_ok(int dt) { return dt == SV_F32 || dt == SV_BF16; }
+static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Largest byte offset touched by a [B][rows][V] view, or -1 on overflow.
+static int64_t extent_bytes(int64_t B, int64_t rows, int64_t V, int64_t seq_stride, int64_t row_stride, int esz) {
+  const int64_t lim = INT64_MAX / 8;
+  if (seq_stride > lim / (B > 0 ? B : 1) || row_stride > lim / (rows > 0 ? rows : 1)) return -1;
+  int64_t e = (B - 1) * seq_stride + (rows - 1) * row_stride + V;
+  if (e > lim / esz) return -1;
+  return e * esz;
+}
+
+static int check_rows(const void* base, int dt, int64_t seq_stride, int64_t row_stride, int64_t B, int64_t rows,
+                      int64_t V) {
+  if (!dtype_ok(dt)) return SV_ERR_DTYPE;
+  if (row_stride < V || seq_stride < 0) return SV_ERR_SHAPE;
+  const int esz = esz_of(dt);
+  if (extent_bytes(B, rows, V, seq_stride, row_stride, esz) < 0) return SV_ERR_SHAPE;
+  if (!aligned(base, 16) || (row_stride * esz) % 16 != 0 || (seq_stride * esz) % 16 != 0) return SV_ERR_ALIGN;
+  return SV_OK;
+}
+
+struct SampleArgs {
+  const void* tgt;
+  int tdt;
+  int64_t tss, trs;
+  const void* dft;
+  int ddt;
+  int64_t dss, drs;
+  const int32_t* tokens;
+  const float* uniforms;
+  const float* temps;
+  int B, gamma, V;
+  int32_t* out_n;
+  int32_t* out_tok;
+  const sv_sample_diag* diag;
+  void* ws;
+  size_t ws_bytes;
+};
+
+static int validate_sample(const SampleArgs& a) {
+  if (!a.tgt || !a.dft || !a.tokens || !a.uniforms || !a.temps || !a.out_n || !a.out_tok) return SV_ERR_NULL;
+  if (!dtype_ok(a.tdt) || !dtype_ok(a.ddt)) return SV_ERR_DTYPE;
+  if (a.B < 1 || a.B > SV_MAX_BATCH || a.gamma < 1 || a.gamma > SV_MAX_GAMMA || a.V < 1 || a.V > SV_MAX_VOCAB)
+    return SV_ERR_SHAPE;
+  int st = check_rows(a.tgt, a.tdt, a.tss, a.trs, a.B, a.gamma + 1, a.V);
+  if (st) return st;
+  st = check_rows(a.dft, a.ddt, a.dss, a.drs, a.B, a.gamma, a.V);
+  if (st) return st;
+  if (!aligned(a.tokens, 4) || !aligned(a.uniforms, 4) || !aligned(a.temps, 4) || !aligned(a.out_n, 4) ||
+      !aligned(a.out_tok, 4))
+    return SV_ERR_ALIGN;
+  if (a.diag && ((a.diag->p_x && !aligned(a.diag->p_x, 4)) || (a.diag->q_x && !aligned(a.diag->q_x, 4)) ||
+                 (a.diag->resid_mass && !aligned(a.diag->resid_mass, 4))))
+    return SV_ERR_ALIGN;
+  if (!a.ws) return SV_ERR_WORKSPACE;
+  if (!aligned(a.ws, 256)) return SV_ERR_ALIGN;
+  if (a.ws_bytes < (size_t)sample_layout(a.B, a.gamma, a.V).total) return SV_ERR_WORKSPACE;
+  return SV_OK;
+}
+
+static SampleLaunch plan_sample(const SampleArgs& a) {
+  SampleLaunch L;
+  memset(&L, 0, sizeof(L));
+  const int et = esz_of(a.tdt), ed = esz_of(a.ddt);
+  L.tgt = (const char*)a.tgt;
+  L.t_seq_b = a.tss * et;
+  L.t_row_b = a.trs * et;
+  L.dft = (const char*)a.dft;
+  L.d_seq_b = a.dss * ed;
+  L.d_row_b = a.drs * ed;
+  L.tokens = a.tokens;
+  L.uniforms = a.uniforms;
+  L.temps = a.temps;
+  L.B = a.B;
+  L.gamma = a.gamma;
+  L.V = a.V;
+  L.out_n = a.out_n;
+  L.out_tok = a.out_tok;
+  if (a.diag) {
+    L.diag_px = a.diag->p_x;
+    L.diag_qx = a.diag->q_x;
+    L.diag_mass = a.diag->resid_mass;
+  }
+  const int64_t G = a.gamma, V = a.V, B = a.B;
+  const int64_t total = B * ((G + 1) * V * et + G * V * ed);
+  const int64_t cb = chunk_bytes_for(total);
+  split_row(V, et, cb, &L.nct, &L.cut);
+  split_row(V, ed, cb, &L.ncd, &L.cud);
+  L.per_seq = (int)((G + 1) * L.nct + G * L.ncd);
+  // draw pass: chunks of whole 4-step groups, enough workgroups to cover the GPU
+  L.ns2 = (int)draw_steps(V);
+  const int64_t max_chunks = max_draw_chunks(V);
+  int64_t nc2 = clamp64(ceil_div(2048, B), 1, max_chunks);
+  int64_t spc2 = round_up(ceil_div(L.ns2, nc2), kWaves);
+  L.spc2 = (int)spc2;
+  L.nc2 = (int)ceil_div(L.ns2, spc2);
+  const SampleLayout lay = sample_layout(B, G, V);
+  char* ws = (char*)a.ws;
+  L.part = (RowPartial*)(ws + lay.off_part);
+  L.plan = (SeqPlan*)(ws + lay.off_plan);
+  L.steptot = (double*)(ws + lay.off_step);
+  L.chunktot = (double*)(ws + lay.off_chunk);
+  L.cnt1 = (unsigned*)(ws + lay.off_cnt1);
+  L.cnt2 = (unsigned*)(ws + lay.off_cnt2);
+  return L;
+}
+
+static int run_sample(int stage_mask, const SampleArgs& a, hipStream_t stream) {
+  int st = validate_sample(a);
+  if (st) return st;
+  const SampleLaunch L = plan_sample(a);
+  // grid sizes fit a 32-bit dimension by construction of the limits; check anyway
+  if ((int64_t)L.B * L.per_seq > 0x7fffffffLL || (int64_t)L.B * L.nc2 > 0x7fffffffLL) return SV_ERR_SHAPE;
+  if (stage_mask & 1) {
+    st = hip_status(launch_sample_stage(L, a.tdt, a.ddt, 1, stream));
+    if (st) return st;
+  }
+  if (stage_mask & 2) {
+    st = hip_status(launch_sample_stage(L, a.tdt, a.ddt, 2, stream));
+    if (st) return st;
+  }
+  return SV_OK;
+}
+
+__global__ void sv_fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+size_t sv_sample_workspace_bytes(int B, int gamma, int V) {
+  if (B < 1 || B > SV_MAX_BATCH || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
+  return (size_t)sample_layout(B, gamma, V).total;
+}
+
+size_t sv_tree_workspace_bytes(int B, int N, int V) {
+  if (B < 1 || B > SV_MAX_BATCH || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB) return 0;
+  return (size_t)tree_layout(B, N, V).total;
+}
+
+int sv_workspace_clear(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return SV_ERR_NULL;
+  if (!aligned(workspace, 16)) return SV_ERR_ALIGN;
+  if (bytes == 0) return SV_OK;
+  const size_t n16 = bytes / 16, ntail = bytes % 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(sv_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (uint4*)workspace, n16, (unsigned char*)workspace + n16 * 16, ntail);
+  return hip_status(hipGetLastError());
+}
+
+int spec_verify_sample_stage(int stage, const void* target_logits, int target_dtype, int64_t target_seq_stride,
+                             int64_t target_row_stride, const void* draft_logits, int draft_dtype,
+                             int64_t draft_seq_stride, int64_t draft_row_stride, const int32_t* draft_tokens,
+                             const float* uniforms, const float* temperature, int B, int gamma, int V,
+                             int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage != 1 && stage != 2) return SV_ERR_ARG;
+  SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
+               draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
+               out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
+  return run_sample(stage == 1 ? 1 : 2, a, (hipStream_t)stream);
+}
+
+int spec_verify_sample(const void* target_logits, int target_dtype, int64_t target_seq_stride,
+                       int64_t target_row_stride, const void* draft_logits, int draft_dtype, int64_t draft_seq_stride,
+                       int64_t draft_row_stride, const int32_t* draft_tokens, const float* uniforms,
+                       const float* temperature, int B, int gamma, int V, int32_t* out_num_accepted,
+                       int32_t* out_tokens, const sv_sample_diag* diag, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
+               draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
+               out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
+  return run_sample(3, a, (hipStream_t)stream);
+}
+
+int spec_verify_greedy_tree(const void* target_logits, int dtype, int64_t seq_stride, int64_t row_stride,
+                            const int32_t* parents, const int32_t* tokens, int B, int N, int V,
+                            int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus, int32_t* out_argmax,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!target_logits || !parents || !tokens || !out_accept_len || !out_path || !out_bonus) return SV_ERR_NULL;
+  if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+  if (B < 1 || B > SV_MAX_BATCH || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB) return SV_ERR_SHAPE;
+  int st = check_rows(target_logits, dtype, seq_stride, row_stride, B, N, V);
+  if (st) return st;
+  if (!aligned(parents, 4) || !aligned(tokens, 4) || !aligned(out_accept_len, 4) || !aligned(out_path, 4) ||
+      !aligned(out_bonus, 4) || (out_argmax && !aligned(out_argmax, 4)))
+    return SV_ERR_ALIGN;
+  if (!workspace) return SV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return SV_ERR_ALIGN;
+  const TreeLayout lay = tree_layout(B, N, V);
+  if (workspace_bytes < (size_t)lay.total) return SV_ERR_WORKSPACE;
+
+  TreeLaunch L;
+  memset(&L, 0, sizeof(L));
+  const int esz = esz_of(dtype);
+  L.logits = (const char*)target_logits;
+  L.seq_b = seq_stride * esz;
+  L.row_b = row_stride * esz;
+  L.parents = parents;
+  L.tokens = tokens;
+  L.B = B;
+  L.N = N;
+  L.V = V;
+  const int64_t total = (int64_t)B * N * V * esz;
+  split_row(V, esz, chunk_bytes_for(total), &L.nch, &L.cu);
+  L.out_len = out_accept_len;
+  L.out_path = out_path;
+  L.out_bonus = out_bonus;
+  L.out_argmax = out_argmax;
+  L.part = (ArgPartial*)((char*)workspace + lay.off_part);
+  L.cnt = (unsigned*)((char*)workspace + lay.off_cnt);
+  if ((int64_t)B * N * L.nch > 0x7fffffffLL) return SV_ERR_SHAPE;
+  return hip_status(launch_tree(L, dtype, (hipStream_t)stream));
+}
+
+const char* sv_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "a required pointer is NULL";
+    case SV_ERR_SHAPE: return "shape out of range (B, gamma, N, V, strides or size overflow)";
+    case SV_ERR_DTYPE: return "unknown dtype (use SV_F32 or SV_BF16)";
+    case SV_ERR_ALIGN: return "misaligned pointer or stride (rows need 16-byte alignment)";
+    case SV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SV_ERR_HIP: return "HIP launch failed (see sv_last_hip_error)";
+    case SV_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int sv_last_hip_error(void) { return g_last_hip_error; }
+
+const char* sv_version(void) { return "spec_verify 0.1.0 (gfx950)"; }
+
+}  // extern "C"

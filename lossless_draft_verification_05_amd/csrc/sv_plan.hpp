@@ -1,0 +1,170 @@
+// sv_plan.hpp -- launch descriptors, workspace records and work decomposition
+// shared by the host library and the kernels of libspec_verify.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;  // one workgroup = 4 wave64
+constexpr int kWaves = 4;
+constexpr int kWave = 64;
+constexpr int kU1 = 4;                          // 16-byte units per lane per iteration (stats, argmax)
+constexpr int kU2 = 4;                          // 8-token octets per lane per residual step
+constexpr int kStepOctets = kWave * kU2;        // 256 octets = 2048 tokens per residual step (one wave)
+constexpr int kStepTokens = kStepOctets * 8;
+constexpr int64_t kMinChunkBytes = 16 << 10;    // stats / argmax work unit bounds
+constexpr int64_t kMaxChunkBytes = 256 << 10;
+constexpr int64_t kTargetWGs = 4096;            // ~16 workgroups per CU on 256 CUs
+constexpr int kLog2MaxNodes = 10;               // 1024 tree nodes
+
+enum : int { kModeResidual = 0, kModeBonus = 1 };
+
+// Partial statistics of one chunk of one logits row (stats pass).
+// s = sum over the chunk of exp2((x - m_ref) * kl); m_true = max x.
+struct RowPartial {
+  float m_ref;
+  float m_true;
+  double s;
+};
+
+// What the stats pass hands to the draw pass, per sequence.
+struct SeqPlan {
+  int valid;   // 0: the sequence is invalid (all outputs -1)
+  int n;       // accepted drafts
+  int mode;    // kModeResidual (row n pair) or kModeBonus (target row n == gamma)
+  float kl;    // log2(e) / T, fp32
+  float mp;    // reference (max) of target row n, logit units
+  float mq;    // reference (max) of draft row n
+  float kap_hi;  // kappa = Sp / Sq as a float pair (hi + lo)
+  float kap_lo;
+  double sp;   // sum_v exp2((x_v - mp) * kl) over target row n
+  double sq;   // same for draft row n
+};
+
+// Partial argmax of one chunk of one row (tree pass).
+struct ArgPartial {
+  float best;
+  int idx;
+  int bad;  // NaN seen
+  int pad;
+};
+
+struct SampleLaunch {
+  const char* tgt;
+  int64_t t_seq_b, t_row_b;  // strides in bytes
+  const char* dft;
+  int64_t d_seq_b, d_row_b;
+  const int32_t* tokens;
+  const float* uniforms;
+  const float* temps;
+  int B, gamma, V;
+  int32_t* out_n;
+  int32_t* out_tok;
+  float* diag_px;
+  float* diag_qx;
+  float* diag_mass;
+  // stats pass decomposition
+  int nct, ncd;  // chunks per target row / per draft row
+  int cut, cud;  // 16-byte units per chunk (multiples of 256)
+  int per_seq;   // (gamma + 1) * nct + gamma * ncd
+  // draw pass decomposition
+  int ns2;   // residual steps per row
+  int spc2;  // steps per draw-pass chunk
+  int nc2;   // draw-pass chunks per sequence
+  // workspace
+  RowPartial* part;  // [B][per_seq]
+  SeqPlan* plan;     // [B]
+  double* steptot;   // [B][ns2]
+  double* chunktot;  // [B][nc2]
+  unsigned* cnt1;    // [B]
+  unsigned* cnt2;    // [B]
+};
+
+struct TreeLaunch {
+  const char* logits;
+  int64_t seq_b, row_b;
+  const int32_t* parents;
+  const int32_t* tokens;
+  int B, N, V;
+  int nch;  // chunks per row
+  int cu;   // 16-byte units per chunk (multiple of 256)
+  int32_t* out_len;
+  int32_t* out_path;
+  int32_t* out_bonus;
+  int32_t* out_argmax;
+  ArgPartial* part;  // [B][N][nch]
+  unsigned* cnt;     // [B]
+};
+
+// ---------------------------------------------------------------------------
+// host-side decomposition helpers (pure integer arithmetic)
+// ---------------------------------------------------------------------------
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Bytes of work per stats/argmax workgroup for a call that streams total_bytes.
+inline int64_t chunk_bytes_for(int64_t total_bytes) {
+  int64_t c = clamp64(total_bytes / kTargetWGs, kMinChunkBytes, kMaxChunkBytes);
+  return round_up(c, (int64_t)kThreads * 16);
+}
+
+// Split a row of V elements of esz bytes into nch chunks of cu 16-byte units.
+inline void split_row(int64_t V, int esz, int64_t chunk_bytes, int* nch, int* cu) {
+  int64_t nu = ceil_div(V * esz, 16);
+  int64_t per = chunk_bytes / 16;
+  int64_t n = ceil_div(nu, per);
+  int64_t c = round_up(ceil_div(nu, n), kThreads);
+  *nch = (int)ceil_div(nu, c);
+  *cu = (int)c;
+}
+
+// Upper bound of chunks per row for any dtype (used to size the workspace).
+inline int64_t max_chunks_per_row(int64_t V) { return ceil_div(V * 4, kMinChunkBytes); }
+
+inline int64_t align256(int64_t x) { return round_up(x, 256); }
+
+struct SampleLayout {
+  int64_t off_part, off_plan, off_step, off_chunk, off_cnt1, off_cnt2, total;
+};
+
+inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
+inline int64_t max_draw_chunks(int64_t V) { return ceil_div(draw_steps(V), kWaves); }
+
+inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
+  SampleLayout L;
+  int64_t o = 0;
+  L.off_part = o;
+  o += align256(B * (2 * gamma + 1) * max_chunks_per_row(V) * (int64_t)sizeof(RowPartial));
+  L.off_plan = o;
+  o += align256(B * (int64_t)sizeof(SeqPlan));
+  L.off_step = o;
+  o += align256(B * draw_steps(V) * 8);
+  L.off_chunk = o;
+  o += align256(B * max_draw_chunks(V) * 8);
+  L.off_cnt1 = o;
+  o += align256(B * 4);
+  L.off_cnt2 = o;
+  o += align256(B * 4);
+  L.total = o;
+  return L;
+}
+
+struct TreeLayout {
+  int64_t off_part, off_cnt, total;
+};
+
+inline TreeLayout tree_layout(int64_t B, int64_t N, int64_t V) {
+  TreeLayout L;
+  int64_t o = 0;
+  L.off_part = o;
+  o += align256(B * N * max_chunks_per_row(V) * (int64_t)sizeof(ArgPartial));
+  L.off_cnt = o;
+  o += align256(B * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace sv

@@ -1,0 +1,257 @@
+// sv_tree.hip -- greedy decoding-tree verify on gfx950.
+//
+// Method ("Falcon: ... Custom-Designed Decoding Tree", Pith review: "What
+// carries the argument" -- the target checks all candidate branches of the
+// draft tree in one pass; "Assumptions & free parameters" and Figure 4 --
+// greedy decoding must reproduce vanilla autoregressive output): node j is
+// accepted iff its parent is accepted and its token is the argmax of the
+// parent's target row; the result is the deepest accepted node d (lowest id on
+// ties), its root path and the bonus token argmax(row d).
+//
+// One kernel: a workgroup per (sequence, node row, chunk) streams 16-byte units
+// and keeps a per-lane (max, first index) pair; the last workgroup of a
+// sequence (atomic arrival counter) merges the row partials and resolves the
+// tree in LDS by pointer jumping over the parent array (log2 N rounds), which
+// also leaves a binary-lifting table for writing the accepted path in parallel.
+#include "sv_device.hpp"
+
+namespace sv {
+
+struct ArgState {
+  float best;
+  int idx;
+  bool nan;
+};
+
+template <int DT, int NU>
+__device__ __forceinline__ void argmax_units(ArgState& st, const Unit<DT> (&un)[NU], const int64_t (&u)[NU]) {
+  constexpr int E = Unit<DT>::kEpu;
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
+    bool nan = false;
+#pragma unroll
+    for (int k = 0; k < E; k += 2) nan |= __builtin_isunordered(un[j].x[k], un[j].x[k + 1]);
+    st.nan |= nan;
+    const float gm = unit_max(un[j]);
+    if (gm > st.best) {  // strict: earlier (lower) indices win ties inside a lane
+      int kk = E - 1;
+#pragma unroll
+      for (int k = E - 1; k >= 0; --k)
+        if (un[j].x[k] == gm) kk = k;
+      st.best = gm;
+      st.idx = (int)(u[j] * E + kk);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int V, int64_t w_begin, int64_t w_end,
+                                              ArgState& st) {
+  constexpr int E = Unit<DT>::kEpu;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t nu_row = ((int64_t)V + E - 1) / E;
+  const bool ragged = (V % E) != 0;
+  int64_t full_end = w_end;
+  if (ragged && full_end > nu_row - 1) full_end = nu_row - 1;
+  int64_t base = w_begin;
+  for (; base + (int64_t)kWave * kU1 <= full_end; base += (int64_t)kWave * kU1) {
+    uint4 w[kU1];
+    int64_t u[kU1];
+#pragma unroll
+    for (int j = 0; j < kU1; ++j) {
+      u[j] = base + lane + kWave * j;
+      w[j] = load16(row + u[j] * 16);
+    }
+    Unit<DT> un[kU1];
+#pragma unroll
+    for (int j = 0; j < kU1; ++j) un[j].unpack(w[j]);
+    argmax_units<DT, kU1>(st, un, u);
+  }
+#pragma unroll
+  for (int j = 0; j < kU1; ++j) {
+    int64_t uu[1] = {base + lane + kWave * j};
+    if (uu[0] < w_end) {
+      Unit<DT> un[1];
+      un[0].unpack(load16(row + uu[0] * 16));
+      if (ragged && uu[0] == nu_row - 1) mask_tail(un[0], uu[0], V);
+      argmax_units<DT, 1>(st, un, uu);
+    }
+  }
+}
+
+__device__ __forceinline__ float ld_f32_agent(const float* p) {
+  return __uint_as_float(
+      __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ int ld_i32_agent(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
+  __shared__ float sh_v[kWaves];
+  __shared__ int sh_i[kWaves];
+  __shared__ int sh_n[kWaves];
+  __shared__ int sh_last;
+  __shared__ int s_ok;
+  __shared__ int s_key[kWaves];
+  // Resolve arrays, sized by N at launch (tree_lds_bytes):
+  //   s_g[N] int | s_up[(kLog2MaxNodes+1) * N] short | s_D[2 * N] short | s_A[2 * N] uchar
+  extern __shared__ __align__(16) char s_dyn[];
+  const int NN = A.N;
+  int* s_g = reinterpret_cast<int*>(s_dyn);
+  short* s_upb = reinterpret_cast<short*>(s_g + NN);
+  short* s_Db = s_upb + (kLog2MaxNodes + 1) * NN;
+  unsigned char* s_Ab = reinterpret_cast<unsigned char*>(s_Db + 2 * NN);
+#define s_up(k, i) s_upb[(k) * NN + (i)]
+#define s_D(k, i) s_Db[(k) * NN + (i)]
+#define s_A(k, i) s_Ab[(k) * NN + (i)]
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
+  const int per_seq = A.N * A.nch;
+  const int b = blockIdx.x / per_seq;
+  const int r = blockIdx.x % per_seq;
+  const int j = r / A.nch, c = r % A.nch;
+
+  ArgState st{-INFINITY, INT_MAX, false};
+  {
+    const char* row = A.logits + (int64_t)b * A.seq_b + (int64_t)j * A.row_b;
+    const int64_t nu = ((int64_t)A.V * Unit<DT>::kEsz + 15) / 16;
+    const int64_t q = A.cu / kWaves;
+    int64_t u0 = (int64_t)c * A.cu + (int64_t)w * q, u1 = u0 + q;
+    if (u1 > nu) u1 = nu;
+    if (u0 < u1) stream_argmax<DT>(row, A.V, u0, u1, st);
+  }
+  float bv = st.best;
+  int bi = st.idx;
+  wave_argmax(bv, bi);
+  const int nn = wave_or((int)st.nan);
+  if (lane == 0) {
+    sh_v[w] = bv;
+    sh_i[w] = bi;
+    sh_n[w] = nn;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float v = sh_v[0];
+    int i = sh_i[0];
+    for (int k = 1; k < kWaves; ++k) arg_combine(v, i, sh_v[k], sh_i[k]);
+    ArgPartial p;
+    p.best = v;
+    p.idx = i;
+    p.bad = sh_n[0] | sh_n[1] | sh_n[2] | sh_n[3];
+    p.pad = 0;
+    A.part[blockIdx.x] = p;
+    fence_release();
+    const unsigned old = atomic_arrive(&A.cnt[b]);
+    sh_last = (old == (unsigned)per_seq - 1u);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  fence_acquire();
+
+  // ---- last workgroup of tree b ----
+  const int N = A.N;
+  if (tid == 0) s_ok = 1;
+  __syncthreads();
+  const ArgPartial* P = A.part + (int64_t)b * per_seq;
+  for (int jj = tid; jj < N; jj += kThreads) {
+    float v = -INFINITY;
+    int i = INT_MAX, bad = 0;
+    for (int cc = 0; cc < A.nch; ++cc) {
+      const ArgPartial* q = P + (int64_t)jj * A.nch + cc;
+      arg_combine(v, i, ld_f32_agent(&q->best), ld_i32_agent(&q->idx));
+      bad |= ld_i32_agent(&q->bad);
+    }
+    if (v == INFINITY) bad = 1;  // +inf makes the row unusable
+    if (v == -INFINITY) i = 0;   // a row of -inf only: first index
+    s_g[jj] = i;
+    if (bad) s_ok = 0;
+    if (A.out_argmax) A.out_argmax[(int64_t)b * N + jj] = bad ? -1 : i;
+    const int pj = A.parents[(int64_t)b * N + jj];
+    const int tk = A.tokens[(int64_t)b * N + jj];
+    const bool node_ok = (jj == 0) ? (pj == -1) : (pj >= 0 && pj < jj && tk >= 0 && tk < A.V);
+    if (!node_ok) s_ok = 0;
+    s_up(0, jj) = (short)((jj == 0) ? -1 : pj);
+  }
+  __syncthreads();
+  int32_t* opath = A.out_path + (int64_t)b * N;
+  if (!s_ok) {
+    for (int t = tid; t < N; t += kThreads) opath[t] = -1;
+    if (tid == 0) {
+      A.out_len[b] = -1;
+      A.out_bonus[b] = -1;
+      atomic_reset(&A.cnt[b]);
+    }
+    return;
+  }
+  for (int jj = tid; jj < N; jj += kThreads) {
+    const int tk = A.tokens[(int64_t)b * N + jj];
+    s_A(0, jj) = (jj == 0) ? 1 : (unsigned char)(tk == s_g[s_up(0, jj)]);
+    s_D(0, jj) = (jj == 0) ? 0 : 1;
+  }
+  __syncthreads();
+  int rounds = 0;
+  while ((1 << rounds) < N) ++rounds;
+  for (int k = 0; k < rounds; ++k) {
+    const int cur = k & 1, nxt = cur ^ 1;
+    for (int jj = tid; jj < N; jj += kThreads) {
+      const int p = s_up(k, jj);
+      if (p >= 0) {
+        s_A(nxt, jj) = s_A(cur, jj) & s_A(cur, p);
+        s_D(nxt, jj) = (short)(s_D(cur, jj) + s_D(cur, p));
+        s_up(k + 1, jj) = s_up(k, p);
+      } else {
+        s_A(nxt, jj) = s_A(cur, jj);
+        s_D(nxt, jj) = s_D(cur, jj);
+        s_up(k + 1, jj) = -1;
+      }
+    }
+    __syncthreads();
+  }
+  const int fin = rounds & 1;
+  // deepest accepted node, lowest id on ties: key = depth * 2048 + (2047 - id)
+  int key = -1;
+  for (int jj = tid; jj < N; jj += kThreads)
+    if (s_A(fin, jj)) key = max(key, ((int)s_D(fin, jj) << 11) | (2047 - jj));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, kWave));
+  if (lane == 0) s_key[w] = key;
+  __syncthreads();
+  key = max(max(s_key[0], s_key[1]), max(s_key[2], s_key[3]));
+  const int d = 2047 - (key & 2047);
+  const int depth = key >> 11;
+  for (int t = tid; t < N; t += kThreads) {
+    int node = -1;
+    if (t <= depth) {
+      node = d;
+      const int dist = depth - t;
+      for (int k = 0; k < rounds && node >= 0; ++k)
+        if ((dist >> k) & 1) node = s_up(k, node);
+    }
+    opath[t] = node;
+  }
+  if (tid == 0) {
+    A.out_len[b] = depth;
+    A.out_bonus[b] = s_g[d];
+    atomic_reset(&A.cnt[b]);
+  }
+#undef s_up
+#undef s_D
+#undef s_A
+}
+
+size_t tree_lds_bytes(int N) {
+  return (size_t)N * 4 + (size_t)(kLog2MaxNodes + 1) * N * 2 + (size_t)2 * N * 2 + (size_t)2 * N + 16;
+}
+
+hipError_t launch_tree(const TreeLaunch& A, int dt, hipStream_t stream) {
+  const int64_t grid = (int64_t)A.B * A.N * A.nch;
+  if (dt == 1)
+    hipLaunchKernelGGL((sv_tree_kernel<1>), dim3((unsigned)grid), dim3(kThreads), tree_lds_bytes(A.N), stream, A);
+  else
+    hipLaunchKernelGGL((sv_tree_kernel<0>), dim3((unsigned)grid), dim3(kThreads), tree_lds_bytes(A.N), stream, A);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -431,3 +431,33 @@ def make_tree_inputs(cid: int = 4, seed: int = 0, B: int | None = None, N: int |
 
     _pmap(one, range(B))
     return TreeInputs(cfg, seed, logits, parents, tokens, planted)
+
+
+def make_custom_sample(B: int, gamma: int, V: int, target_dtype: str = "bf16", draft_dtype: str = "bf16",
+                       T=1.0, noise_sd: float = 0.8, target_sd: float = 2.0, seed: int = 0,
+                       cid: int = 100) -> SampleInputs:
+    """Generic sampling inputs: target N(0, target_sd), draft = rounded target +
+    N(0, noise_sd), drafts x ~ q (Gumbel-max), exact u24 uniforms. ``T`` is a
+    float or an array of B temperatures."""
+    temps = np.broadcast_to(np.asarray(T, dtype=np.float32), (B,)).copy()
+    cfg = SampleConfig(cid, "custom", B, gamma, V, target_dtype, draft_dtype, target_sd, float(temps[0]))
+    tgt = np.empty((B, gamma + 1, V), dtype=np.uint16 if target_dtype == "bf16" else np.float32)
+    dft = np.empty((B, gamma, V), dtype=np.uint16 if draft_dtype == "bf16" else np.float32)
+    tokens = np.empty((B, gamma), dtype=np.int32)
+
+    def one(b):
+        t32 = target_rows(cfg, seed, b, gamma + 1)
+        tq = _to_dtype(t32, target_dtype)
+        tgt[b] = tq
+        tr = decode(tq, target_dtype)[:gamma]
+        z = gen(seed, cid, S_DRAFT, b).standard_normal(tr.shape, dtype=np.float32)
+        dq = _to_dtype(tr + z * np.float32(noise_sd), draft_dtype)
+        dft[b] = dq
+        dr = decode(dq, draft_dtype).astype(np.float64)
+        g = gen(seed, cid, S_DRAFTTOK, b)
+        for i in range(gamma):
+            tokens[b, i] = gumbel_max_draw(g, dr[i], float(temps[b]))
+
+    _pmap(one, range(B))
+    u = uniforms_u24(gen(seed, cid, S_UNIFORM), (B, gamma + 1))
+    return SampleInputs(cfg, seed, tgt, dft, tokens, u, temps, np.zeros(B, np.int8), {"shared_logits": False})

@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lossless_draft_verification_05_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_\w+|spec_verify_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libspec_verify.so is not built (run python -m lossless_draft_verification_05_amd.build)")
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.SIGNATURES), set(names) ^ set(binding.SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert b"spec_verify" in lib.sv_version()
+    for st in range(-7, 1):
+        assert lib.sv_status_string(st)
+    assert lib.sv_status_string(-99) == b"unknown status"
+    assert lib.sv_last_hip_error() == 0
+
+
+def test_workspace_sizes(lib):
+    assert lib.sv_sample_workspace_bytes(0, 4, 32) == 0
+    assert lib.sv_sample_workspace_bytes(1, 65, 32) == 0
+    assert lib.sv_sample_workspace_bytes(1, 4, 0) == 0
+    assert lib.sv_tree_workspace_bytes(1, 1025, 32) == 0
+    a = lib.sv_sample_workspace_bytes(64, 4, 32000)
+    b = lib.sv_sample_workspace_bytes(128, 4, 32000)
+    c = lib.sv_sample_workspace_bytes(64, 4, 64000)
+    assert 0 < a < b and a < c and a % 256 == 0
+    assert lib.sv_tree_workspace_bytes(32, 60, 32000) > 0
+
+
+# Fake device addresses: never dereferenced, because every case below fails validation.
+A = 0x7F0000000000
+
+
+def sample_args(**over):
+    a = dict(target=A, tdt=1, tss=5 * 64, trs=64, draft=A + 0x100000, ddt=1, dss=4 * 64, drs=64, tokens=A + 0x200000,
+             uniforms=A + 0x300000, temps=A + 0x400000, B=4, G=4, V=64, out_n=A + 0x500000, out_tok=A + 0x600000,
+             diag=None, ws=A + 0x700000, wsb=1 << 30, stream=None)
+    a.update(over)
+    return a
+
+
+def call_sample(lib, stage=None, **over):
+    a = sample_args(**over)
+    args = [a["target"], a["tdt"], a["tss"], a["trs"], a["draft"], a["ddt"], a["dss"], a["drs"], a["tokens"],
+            a["uniforms"], a["temps"], a["B"], a["G"], a["V"], a["out_n"], a["out_tok"], a["diag"], a["ws"], a["wsb"],
+            a["stream"]]
+    if stage is None:
+        return lib.spec_verify_sample(*args)
+    return lib.spec_verify_sample_stage(stage, *args)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(target=None), -1), (dict(draft=None), -1), (dict(tokens=None), -1), (dict(uniforms=None), -1),
+    (dict(temps=None), -1), (dict(out_n=None), -1), (dict(out_tok=None), -1),
+    (dict(tdt=2), -3), (dict(ddt=-1), -3),
+    (dict(B=0), -2), (dict(G=0), -2), (dict(G=65), -2), (dict(V=0), -2), (dict(V=(1 << 30) + 1), -2),
+    (dict(trs=63), -2), (dict(drs=10), -2), (dict(tss=-8), -2),
+    (dict(target=A + 2), -4), (dict(trs=68), -4), (dict(tss=5 * 64 + 4), -4), (dict(ddt=0, drs=66), -4),
+    (dict(tokens=A + 2), -4), (dict(out_tok=A + 1), -4),
+    (dict(ws=None), -5), (dict(wsb=100), -5), (dict(ws=A + 0x700010), -4),
+    (dict(tss=1 << 60), -2),
+])
+def test_sample_argument_errors(lib, over, want):
+    assert call_sample(lib, **over) == want
+    assert call_sample(lib, stage=1, **over) == want
+
+
+def test_unknown_stage(lib):
+    assert call_sample(lib, stage=3) == -7
+    assert call_sample(lib, stage=0) == -7
+
+
+def call_tree(lib, **over):
+    a = dict(logits=A, dt=1, ss=60 * 64, rs=64, parents=A + 0x100000, tokens=A + 0x200000, B=2, N=60, V=64,
+             ol=A + 0x300000, op=A + 0x400000, ob=A + 0x500000, oa=None, ws=A + 0x600000, wsb=1 << 30, stream=None)
+    a.update(over)
+    return lib.spec_verify_greedy_tree(a["logits"], a["dt"], a["ss"], a["rs"], a["parents"], a["tokens"], a["B"],
+                                       a["N"], a["V"], a["ol"], a["op"], a["ob"], a["oa"], a["ws"], a["wsb"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(logits=None), -1), (dict(parents=None), -1), (dict(tokens=None), -1), (dict(ol=None), -1),
+    (dict(op=None), -1), (dict(ob=None), -1), (dict(dt=5), -3), (dict(N=0), -2), (dict(N=1025), -2),
+    (dict(B=0), -2), (dict(rs=32), -2), (dict(logits=A + 8), -4), (dict(rs=68), -4), (dict(oa=A + 2), -4),
+    (dict(ws=None), -5), (dict(wsb=16), -5),
+])
+def test_tree_argument_errors(lib, over, want):
+    assert call_tree(lib, **over) == want
+
+
+def test_clear_argument_errors(lib):
+    assert lib.sv_workspace_clear(None, 16, None) == -1
+    assert lib.sv_workspace_clear(A + 4, 16, None) == -4
+    assert lib.sv_workspace_clear(A, 0, None) == 0  # nothing to do: no HIP call
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        binding_mod = __import__("lossless_draft_verification_05_amd.binding", fromlist=["load"])
+        saved = binding_mod._lib
+        try:
+            binding_mod._lib = None
+            binding_mod.load(str(tmp_path / "missing.so"))
+        finally:
+            binding_mod._lib = saved

@@ -1,0 +1,96 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element on small
+multi-tile cases and on sampled sequences of the five full-size workloads (in
+the launch configuration the benchmark times)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _assert_tally(t, name, max_flag_frac=0.01):
+    H.log(f"[{name}] {t.summary()}")
+    assert not t.fail, t.fail[:5]
+    assert t.flagged <= max(2, max_flag_frac * t.checked), t.summary()
+
+
+@pytest.mark.parametrize("tdt,ddt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("V,pad", [(5000, None), (4099, 8), (20000, None)])
+def test_small_multitile(gpu, tdt, ddt, V, pad):
+    H.log(f"small multitile tdt={tdt} ddt={ddt} V={V} pad={pad}")
+    inp = synth.make_custom_sample(6, 3, V, tdt, ddt, T=[0.5, 0.9, 1.0, 1.3, 2.0, 0.7], noise_sd=0.8, seed=V)
+    out = H.run_sample(gpu, H.sample_tensors(inp, pad_to=pad))
+    _assert_tally(H.check_sample(inp, out), f"small {tdt}/{ddt} V={V}")
+
+
+def test_config1_tiny(gpu):
+    H.log("config 1: B=1 x 10^4 trials, gamma=4, V=32, fp32, shared logits (stride 0)")
+    inp = synth.make_sample_inputs(1, seed=0)
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    _assert_tally(H.check_sample(inp, out), "config1")
+
+
+def test_config2(gpu):
+    H.log("config 2: B=64 gamma=4 V=32000 bf16")
+    inp = synth.make_sample_inputs(2, seed=0)
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    _assert_tally(H.check_sample(inp, out), "config2")
+
+
+def test_config3_sampled(gpu):
+    H.log("config 3: B=256 gamma=8 V=128256 bf16 T=0.7 (48 sequences checked)")
+    inp = synth.make_sample_inputs(3, seed=0)
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    seqs = sorted(set(np.random.default_rng(3).choice(inp.B, 46, replace=False).tolist()) | {0, inp.B - 1})
+    _assert_tally(H.check_sample(inp, out, seqs), "config3")
+    assert (out["n"] >= 0).all()
+
+
+def test_config5_sampled(gpu):
+    H.log("config 5: B=512 gamma=5 V=256000 bf16 target / fp32 draft, per-row T (48 sequences checked)")
+    inp = synth.make_sample_inputs(5, seed=0)
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    rng = np.random.default_rng(5)
+    seqs = []
+    for cls in (0, 1, 2):
+        idx = np.flatnonzero(inp.row_class == cls)
+        seqs += rng.choice(idx, 16, replace=False).tolist()
+    _assert_tally(H.check_sample(inp, out, sorted(seqs)), "config5")
+    # class properties on every sequence: identical rows accept all drafts, disjoint rows reject at once
+    assert (out["n"][inp.row_class == 2] == inp.gamma).all()
+    assert (out["n"][inp.row_class == 1] == 0).mean() > 0.99
+
+
+def test_config4_tree(gpu):
+    H.log("config 4: 32 trees x 60 nodes, V=32000 bf16")
+    ti = synth.make_tree_inputs(4, seed=0)
+    out = H.run_tree(gpu, H.tree_tensors(ti))
+    fails = H.check_tree(ti.logits, "bf16", ti.parents, ti.tokens, out)
+    H.log(f"[config4] trees={ti.parents.shape[0]} mismatches={len(fails)} mean_len={out['len'].mean():.2f}")
+    assert not fails, fails[:3]
+
+
+def test_tree_fp32_and_multichunk(gpu):
+    H.log("tree fp32, V=300000 (several chunks per row), B=3 N=17")
+    ti = synth.make_tree_inputs(4, seed=7, B=3, N=17, V=300000, dtype="f32")
+    out = H.run_tree(gpu, H.tree_tensors(ti))
+    fails = H.check_tree(ti.logits, "f32", ti.parents, ti.tokens, out)
+    assert not fails, fails[:3]
+
+
+def test_repeat_calls_are_bit_identical(gpu):
+    H.log("determinism: config 2 twice, tree twice")
+    inp = synth.make_sample_inputs(2, seed=1)
+    tens = H.sample_tensors(inp)
+    a = H.run_sample(gpu, tens)
+    b = H.run_sample(gpu, tens)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    ti = synth.make_tree_inputs(4, seed=1)
+    tt = H.tree_tensors(ti)
+    x, y = H.run_tree(gpu, tt), H.run_tree(gpu, tt)
+    for k in x:
+        assert np.array_equal(x[k], y[k]), k
