@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
+
+A step is one pass of the whole hot path over one batch: spec_verify_sample
+(row statistics + accept tests + first rejection, then the residual/bonus draw)
+for the sampling workloads, spec_verify_greedy_tree for the tree workload.
+Inputs are seeded synthetic logits already resident in HBM. Prints ONE JSON
+line on stdout; progress goes to stderr.
+
+Workloads (the five input configurations): c1 tiny sampling (B=10^4 trials,
+gamma=4, V=32, fp32), c2 7B-class vocab (B=64, gamma=4, V=32000, bf16), c3
+large vocab (B=256, gamma=8, V=128256, bf16, T=0.7), c4 greedy tree (B=32,
+N=60, V=32000, bf16), c5 stress (B=512, gamma=5, V=256000, bf16 target, fp32
+draft, per-row T in [0.3, 1.5]). The default is c5, the largest single-GPU one.
+
+--calibrate-copy runs a plain 1 GiB device-to-device copy instead (used to
+scale the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 runs).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBPS = float(os.environ.get("SV_PEAK_HBM_GBPS", "8000"))
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+CSRC = os.path.join(ROOT, "lossless_draft_verification_05_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, as it stands, on a bounded sample
+# ----------------------------------------------------------------------------
+_CPU_DATA = None
+
+
+def _oracle_seq(b):
+    from oracle import spec_verify_oracle as O
+
+    inp, tdt, ddt = _CPU_DATA
+    lb = 0 if inp.target.shape[0] != inp.tokens.shape[0] else b
+    r = O.verify_sample_sequence(O.widen(inp.target[lb], tdt), O.widen(inp.draft[lb], ddt), inp.tokens[b],
+                                 inp.uniforms[b].astype(np.float64), float(inp.temperature[b]))
+    return r.n
+
+
+def _oracle_tree(b):
+    from oracle import spec_verify_oracle as O
+
+    ti = _CPU_DATA
+    return O.verify_tree_sequence(O.widen(ti.logits[b], ti.dtype), ti.parents[b], ti.tokens[b]).accept_len
+
+
+def cpu_baseline(inp, tree: bool, budget_s: float = 15.0):
+    """Time the oracle over the first S sequences in a pool of worker processes
+    (fork, before the GPU is touched). S is sized from a one-sequence probe so
+    the timed part takes about ``budget_s`` seconds."""
+    import multiprocessing as mp
+
+    global _CPU_DATA
+    _CPU_DATA = inp if tree else (inp, inp.cfg.target_dtype, inp.cfg.draft_dtype)
+    fn = _oracle_tree if tree else _oracle_seq
+    B = inp.parents.shape[0] if tree else inp.tokens.shape[0]
+    fn(0)  # warm (imports, first-touch)
+    t0 = time.perf_counter()
+    fn(0)
+    t_one = max(time.perf_counter() - t0, 1e-5)
+    workers = max(1, min(16, os.cpu_count() or 1))
+    # cycle over the batch (b mod B) when the whole batch takes less than the budget
+    S = int(min(50 * B, max(workers, budget_s * workers / t_one)))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        t0 = time.perf_counter()
+        pool.map(fn, [i % B for i in range(S)], chunksize=max(1, S // (4 * workers)))
+        dt = time.perf_counter() - t0
+    units = S * ((inp.parents.shape[1] - 1) if tree else inp.tokens.shape[1])
+    _CPU_DATA = None
+    return {"value": units / dt, "unit": "nodes/s" if tree else "positions/s", "cores": workers, "kind": "oracle",
+            "sample": f"{S} {'trees' if tree else 'sequences'} (index mod {B}) of the same inputs, numpy fp64, "
+                      f"{workers} worker processes, {dt:.1f} s"}
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes
+# ----------------------------------------------------------------------------
+def esz(dt):
+    return 2 if dt == "bf16" else 4
+
+
+def sample_bytes(cfg, B, G, V, n_acc=None):
+    """(stats-kernel bytes, residual-kernel bytes) the method must move per call.
+
+    The stats kernel reads every target and draft logit once (plus tokens,
+    uniforms and temperatures, counted with it). The residual kernel reads the
+    one row the draw needs again -- target and draft row n after a rejection,
+    target row gamma after full acceptance -- and the outputs are written."""
+    bt, bd = esz(cfg.target_dtype), esz(cfg.draft_dtype)
+    s1 = B * ((G + 1) * V * bt + G * V * bd) + B * (G * 4 + (G + 1) * 4 + 4)
+    if n_acc is None:
+        s2 = None
+    else:
+        rej = int((n_acc < G).sum())
+        s2 = rej * V * (bt + bd) + (B - rej) * V * bt + B * (G + 2) * 4
+    return s1, s2
+
+
+# ----------------------------------------------------------------------------
+def traffic_from_profiles(workload: str, sha: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def run_copy_calibration():
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the verify step shards by sequence "
+                                   "with no exchange (see DESIGN.md), and no multi-GPU figure is produced",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.calibrate_copy:
+        run_copy_calibration()
+        return
+
+    cid = WORKLOADS[args.workload]
+    tree = cid == 4
+    log(f"[bench] building inputs for {args.workload} (seed {args.seed})")
+    t0 = time.perf_counter()
+    inp = synth.make_tree_inputs(4, seed=args.seed) if tree else synth.make_sample_inputs(cid, seed=args.seed)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a bounded sample")
+        cpu = cpu_baseline(inp, tree)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    import torch
+
+    from lossless_draft_verification_05_amd import binding
+
+    binding.load()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a.astype(np.float32, copy=False)).to(dev)
+
+    # copies so that workloads smaller than the 256 MB Infinity Cache are not
+    # served from it across steps
+    if tree:
+        per_copy = inp.logits.nbytes
+    else:
+        per_copy = inp.target.nbytes + inp.draft.nbytes
+    R = int(min(64, max(1, -(-(512 << 20) // per_copy)))) if per_copy < (512 << 20) else 1
+    log(f"[bench] uploading {R} input cop{'y' if R == 1 else 'ies'} of {per_copy / 1e6:.1f} MB")
+    sha = kernel_source_sha()
+    if tree:
+        L = up(inp.logits, inp.dtype)
+        copies = [L] + [L.clone() for _ in range(R - 1)]
+        par = torch.from_numpy(inp.parents).to(dev)
+        tok = torch.from_numpy(inp.tokens).to(dev)
+        B, N, V = inp.logits.shape
+        ws = binding.Workspace()
+        outs = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev))
+
+        def tree_stage(stage, c):
+            return lambda: binding.spec_verify_greedy_tree_stage(stage, copies[c], par, tok, out_accept_len=outs[0],
+                                                                 out_path=outs[1], out_bonus=outs[2],
+                                                                 out_argmax=outs[3], workspace=ws)
+
+        def stages(c):
+            return [tree_stage(1, c), tree_stage(2, c)]
+        units = B * (N - 1)
+        unit = "nodes/s"
+        s1_bytes = B * N * V * esz(inp.dtype) + 2 * B * N * 4
+        cfg_desc = {"workload": f"{args.workload}: greedy decoding-tree verification", "B": B, "N": N, "V": V,
+                    "logits_dtype": inp.dtype, "seed": args.seed}
+        kernel_names = ["sv_argmax_kernel", "sv_tree_kernel"]
+    else:
+        cfg = inp.cfg
+        t0_ = up(inp.target, cfg.target_dtype)
+        d0_ = up(inp.draft, cfg.draft_dtype)
+        B = inp.tokens.shape[0]
+        tcopies = [t0_] + [t0_.clone() for _ in range(R - 1)]
+        dcopies = [d0_] + [d0_.clone() for _ in range(R - 1)]
+        if t0_.shape[0] != B:  # shared logits (c1): stride-0 batch dimension
+            tcopies = [t.expand(B, *t.shape[1:]) for t in tcopies]
+            dcopies = [d.expand(B, *d.shape[1:]) for d in dcopies]
+        tokens = torch.from_numpy(inp.tokens).to(dev)
+        uni = torch.from_numpy(inp.uniforms).to(dev)
+        temps = torch.from_numpy(inp.temperature).to(dev)
+        G, V = inp.tokens.shape[1], inp.target.shape[-1]
+        ws = binding.Workspace()
+        out_n = torch.empty(B, dtype=torch.int32, device=dev)
+        out_t = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+
+        def stage_call(stage, c):
+            return lambda: binding.spec_verify_sample_stage(stage, tcopies[c], dcopies[c], tokens, uni, temps,
+                                                            out_num_accepted=out_n, out_tokens=out_t, workspace=ws)
+
+        def stages(c):
+            return [stage_call(k, c) for k in (1, 2, 3, 4)]
+        units = B * G
+        unit = "positions/s"
+        s1_bytes, _ = sample_bytes(cfg, B, G, V)
+        tdesc = cfg.temperature if not isinstance(cfg.temperature, tuple) else f"U[{cfg.temperature[1]}, {cfg.temperature[2]}] per row"
+        cfg_desc = {"workload": f"{args.workload}: {cfg.name}", "B": B, "gamma": G, "V": V,
+                    "target_dtype": cfg.target_dtype, "draft_dtype": cfg.draft_dtype, "temperature": tdesc,
+                    "seed": args.seed}
+        kernel_names = ["sv_stats_kernel", "sv_accept_kernel", "sv_resid_kernel", "sv_draw_kernel"]
+
+    torch.cuda.synchronize()
+    for k in range(args.warmup):
+        for f in stages(k % R):
+            f()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+    ns = len(stages(0))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        fs = stages(k % R)
+        e = evs[k]
+        e[0].record()
+        for i, f in enumerate(fs):
+            f()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = [float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                for i in range(ns)]
+    log(f"[bench] {ms_per_step:.4f} ms/step; kernel event means (ms): {stage_ms}")
+
+    detail = {"kernels": {n: {"mean_us": round(m * 1e3, 3)} for n, m in zip(kernel_names, stage_ms)},
+              "input_copies": R, "kernel_source_sha": sha}
+    if tree:
+        lens = outs[0].cpu().numpy()
+        detail["mean_accept_len"] = float(lens[lens >= 0].mean())
+        detail["invalid"] = int((lens < 0).sum())
+        step_bytes = s1_bytes
+    else:
+        n_acc = out_n.cpu().numpy()
+        _, s2_bytes = sample_bytes(inp.cfg, B, G, V, n_acc)
+        step_bytes = s1_bytes + s2_bytes
+        valid = n_acc >= 0
+        detail["mean_accepted"] = float(n_acc[valid].mean())
+        detail["mean_tokens_per_verify"] = float(n_acc[valid].mean() + 1)
+        detail["invalid"] = int((~valid).sum())
+        detail["kernels"]["sv_resid_kernel"]["alg_bytes"] = int(s2_bytes)
+        detail["kernels"]["sv_resid_kernel"]["gbps"] = round(s2_bytes / (stage_ms[2] * 1e-3) / 1e9, 1)
+    detail["kernels"][kernel_names[0]]["alg_bytes"] = int(s1_bytes)
+    detail["kernels"][kernel_names[0]]["gbps"] = round(s1_bytes / (stage_ms[0] * 1e-3) / 1e9, 1)
+    detail["step_alg_bytes"] = int(step_bytes)
+    detail["step_gbps"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)
+    detail["step_frac_of_peak"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
+
+    achieved = s1_bytes / (stage_ms[0] * 1e-3) / 1e9
+    line = {
+        "metric": "verified draft positions/sec + achieved HBM GB/s (% peak), spec_verify at 1 GPU",
+        "value": units / (ms_per_step * 1e-3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded logits standing in for target/draft model outputs",
+        "config": cfg_desc,
+        "roofline": {"bound": "hbm", "kernel": kernel_names[0], "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_from_profiles(args.workload, sha)},
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

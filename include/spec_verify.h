@@ -27,12 +27,8 @@
  *    that way. Data-dependent problems (bad token, NaN row, ...) do not fail
  *    the call: the affected sequence reports -1 (see each call).
  *  - Workspace: device memory of at least the size the matching *_workspace_bytes
- *    function returns, 256-byte aligned, zero-filled before its first use and
- *    again before it is used for a call of another kind or another (B, gamma
- *    or N, V) (sv_workspace_clear does that). Every call that runs to
- *    completion leaves its counters at zero, so later calls of the same kind
- *    and shape on the same stream can reuse it as it is. Calls that overlap in
- *    time must not share a workspace.
+ *    function returns, 256-byte aligned. It needs no initialisation and holds
+ *    nothing between calls. Calls that overlap in time must not share one.
  *  - No C++ exception crosses this interface. The library holds no global
  *    mutable state apart from the thread-local last HIP error.
  *  - Results are deterministic: the same inputs give the same bits.
@@ -71,10 +67,6 @@ typedef enum {
  * outside the limits above. */
 size_t sv_sample_workspace_bytes(int B, int gamma, int V);
 size_t sv_tree_workspace_bytes(int B, int N, int V);
-
-/* Zero-fill `bytes` of device memory at `workspace` on `stream` with a small
- * kernel (no memset node, so it is safe inside captured graphs). */
-int sv_workspace_clear(void* workspace, size_t bytes, void* stream);
 
 /* Optional per-position diagnostics of spec_verify_sample; any member may be
  * NULL (not written). Values are fp32 roundings of fp64 results. */
@@ -131,14 +123,19 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * spec_verify_sample_stage -- the two halves of spec_verify_sample, for callers
- * that want to time or overlap them. Same arguments and meaning as
+ * spec_verify_sample_stage -- one of the four kernels of spec_verify_sample,
+ * for callers that want to time or overlap them. Same arguments and meaning as
  * spec_verify_sample; `stage` selects:
- *   1: row statistics of every target and draft row, accept tests and first
- *      rejection (results stay in the workspace);
- *   2: the residual / bonus draw and every output.
- * Stage 2 must follow stage 1 on the same stream with the same arguments and
- * workspace. spec_verify_sample is stage 1 then stage 2.
+ *   1: row statistics: streams every target and draft row once (max and
+ *      tempered sum-exp per row chunk, into the workspace);
+ *   2: accept tests: merges the statistics, computes p_i(x_i)/q_i(x_i), the
+ *      accept decisions and the first rejection (plan in the workspace,
+ *      diag->p_x / q_x written);
+ *   3: residual / bonus masses: streams the one row (pair) each sequence draws
+ *      from, writing per-step masses into the workspace;
+ *   4: draw: inverse CDF at u[b][gamma] and every output.
+ * Stages must run in order 1, 2, 3, 4 on one stream with the same arguments and
+ * workspace. spec_verify_sample enqueues all four.
  */
 int spec_verify_sample_stage(int stage, const void* target_logits, int target_dtype,
                              int64_t target_seq_stride, int64_t target_row_stride, const void* draft_logits,
@@ -182,6 +179,18 @@ int spec_verify_greedy_tree(const void* target_logits, int dtype, int64_t seq_st
                             const int32_t* parents, const int32_t* tokens, int B, int N, int V,
                             int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus,
                             int32_t* out_argmax, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_greedy_tree_stage -- one of the two kernels of
+ * spec_verify_greedy_tree (same arguments): stage 1 streams every row and
+ * leaves per-row argmax partials in the workspace; stage 2 merges them,
+ * resolves each tree and writes every output. Stage 2 must follow stage 1 on
+ * the same stream with the same arguments and workspace.
+ */
+int spec_verify_greedy_tree_stage(int stage, const void* target_logits, int dtype, int64_t seq_stride,
+                                  int64_t row_stride, const int32_t* parents, const int32_t* tokens, int B, int N,
+                                  int V, int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus,
+                                  int32_t* out_argmax, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Text of a status code (static storage). */
 const char* sv_status_string(int status);

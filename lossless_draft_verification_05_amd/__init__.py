@@ -10,7 +10,8 @@ call does, and fails loudly if the library is missing.
 
 def __getattr__(name):
     if name in ("spec_verify_sample", "spec_verify_sample_stage", "spec_verify_greedy_tree",
-                "sv_sample_workspace_bytes", "sv_tree_workspace_bytes", "sv_workspace_clear", "Workspace"):
+                "spec_verify_greedy_tree_stage",
+                "sv_sample_workspace_bytes", "sv_tree_workspace_bytes", "Workspace"):
         from . import binding
 
         return getattr(binding, name)

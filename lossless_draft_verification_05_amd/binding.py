@@ -26,13 +26,14 @@ _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_s
 SIGNATURES = {
     "sv_sample_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "sv_tree_workspace_bytes": (_sz, [_i32, _i32, _i32]),
-    "sv_workspace_clear": (_i32, [_vp, _sz, _vp]),
     "spec_verify_sample": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32,
                                   _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sample_stage": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32,
                                         _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy_tree": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                        _sz, _vp]),
+    "spec_verify_greedy_tree_stage": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
+                                             _vp, _vp, _sz, _vp]),
     "sv_status_string": (ctypes.c_char_p, [_i32]),
     "sv_last_hip_error": (_i32, []),
     "sv_version": (ctypes.c_char_p, []),
@@ -111,37 +112,29 @@ def _logits3(t: torch.Tensor, name: str, rows: int):
 
 
 class Workspace:
-    """Zero-initialised device workspace, grown on demand and reused.
+    """Device workspace grown on demand and reused by calls on one stream.
 
-    Each completed call leaves the counters it used at zero, so calls of the
-    same kind and shape ordered on one stream can share it. The counters sit at
-    shape-dependent offsets, so the buffer is cleared (on the call's stream)
-    whenever the kind or shape of the call changes. Calls that may run at the
-    same time need separate Workspace objects.
+    The kernels keep nothing in it between calls and need it uninitialised;
+    calls that may run at the same time need separate Workspace objects.
     """
 
     def __init__(self):
         self.buf = None
-        self.key = None
 
-    def get(self, nbytes: int, device, key, stream=None) -> torch.Tensor:
+    def get(self, nbytes: int, device) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-            self.key = key
-        elif key != self.key:
-            sv_workspace_clear(self.buf, stream)
-            self.key = key
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         return self.buf
 
 
 _default_ws = {}
 
 
-def _workspace(ws, nbytes, device, key, stream):
+def _workspace(ws, nbytes, device):
     """A Workspace object (default: one per device) or a caller-managed uint8 tensor."""
     if ws is None:
         ws = _default_ws.setdefault(device, Workspace())
-    buf = ws.get(nbytes, device, key, stream) if isinstance(ws, Workspace) else ws
+    buf = ws.get(nbytes, device) if isinstance(ws, Workspace) else ws
     if buf.numel() < nbytes:
         raise ValueError(f"workspace has {buf.numel()} bytes, needs {nbytes}")
     return buf
@@ -153,11 +146,6 @@ def sv_sample_workspace_bytes(B: int, gamma: int, V: int) -> int:
 
 def sv_tree_workspace_bytes(B: int, N: int, V: int) -> int:
     return int(load().sv_tree_workspace_bytes(B, N, V))
-
-
-def sv_workspace_clear(buf: torch.Tensor, stream=None):
-    _check(load().sv_workspace_clear(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream)),
-           "sv_workspace_clear")
 
 
 def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_num_accepted, out_tokens, diag,
@@ -189,7 +177,7 @@ def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_
     nbytes = sv_sample_workspace_bytes(B, G, V)
     if nbytes == 0:
         raise ValueError(f"shape B={B} gamma={G} V={V} out of range")
-    ws = _workspace(workspace, nbytes, dev, ("sample", B, G, V), stream)
+    ws = _workspace(workspace, nbytes, dev)
     args = (_ptr(target), _dtype_code(target), ts, tr, _ptr(draft), _dtype_code(draft), ds, dr, _ptr(draft_tokens),
             _ptr(uniforms), _ptr(temperature), B, G, V, _ptr(out_num_accepted), _ptr(out_tokens),
             ctypes.byref(dptr) if dptr is not None else None, _ptr(ws), ws.numel(), _stream(stream))
@@ -218,19 +206,13 @@ def spec_verify_sample(target, draft, draft_tokens, uniforms, temperature, *, ou
 
 def spec_verify_sample_stage(stage, target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
                              out_tokens=None, diag=False, workspace=None, stream=None):
-    """Stage 1 (row statistics, accept tests) or 2 (draw, outputs) of spec_verify_sample."""
+    """One stage of spec_verify_sample: 1 row statistics, 2 accept tests, 3 residual/bonus masses, 4 draw."""
     return _sample_call(int(stage), target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
                         out_tokens, diag, workspace, stream)
 
 
-def spec_verify_greedy_tree(logits, parents, tokens, *, out_accept_len=None, out_path=None, out_bonus=None,
-                            out_argmax=None, want_argmax=True, workspace=None, stream=None):
-    """Greedy decoding-tree verify of B trees (see include/spec_verify.h).
-
-    logits [B][N][V] bf16/fp32 (rows contiguous, 16-byte aligned); parents and
-    tokens int32 [B][N]. Returns (accept_len [B], path [B][N], bonus [B],
-    argmax [B][N] or None).
-    """
+def _tree_call(stage, logits, parents, tokens, out_accept_len, out_path, out_bonus, out_argmax, want_argmax,
+               workspace, stream):
     lib = load()
     B, N, V = logits.shape
     s0, s1 = _logits3(logits, "logits", N)
@@ -248,12 +230,33 @@ def spec_verify_greedy_tree(logits, parents, tokens, *, out_accept_len=None, out
     nbytes = sv_tree_workspace_bytes(B, N, V)
     if nbytes == 0:
         raise ValueError(f"shape B={B} N={N} V={V} out of range")
-    ws = _workspace(workspace, nbytes, dev, ("tree", B, N, V), stream)
-    st = lib.spec_verify_greedy_tree(_ptr(logits), _dtype_code(logits), s0, s1, _ptr(parents), _ptr(tokens), B, N, V,
-                                     _ptr(out_accept_len), _ptr(out_path), _ptr(out_bonus), _ptr(out_argmax), _ptr(ws),
-                                     ws.numel(), _stream(stream))
-    _check(st, "spec_verify_greedy_tree")
+    ws = _workspace(workspace, nbytes, dev)
+    args = (_ptr(logits), _dtype_code(logits), s0, s1, _ptr(parents), _ptr(tokens), B, N, V, _ptr(out_accept_len),
+            _ptr(out_path), _ptr(out_bonus), _ptr(out_argmax), _ptr(ws), ws.numel(), _stream(stream))
+    if stage is None:
+        _check(lib.spec_verify_greedy_tree(*args), "spec_verify_greedy_tree")
+    else:
+        _check(lib.spec_verify_greedy_tree_stage(stage, *args), f"spec_verify_greedy_tree_stage({stage})")
     return out_accept_len, out_path, out_bonus, out_argmax
+
+
+def spec_verify_greedy_tree(logits, parents, tokens, *, out_accept_len=None, out_path=None, out_bonus=None,
+                            out_argmax=None, want_argmax=True, workspace=None, stream=None):
+    """Greedy decoding-tree verify of B trees (see include/spec_verify.h).
+
+    logits [B][N][V] bf16/fp32 (rows contiguous, 16-byte aligned); parents and
+    tokens int32 [B][N]. Returns (accept_len [B], path [B][N], bonus [B],
+    argmax [B][N] or None).
+    """
+    return _tree_call(None, logits, parents, tokens, out_accept_len, out_path, out_bonus, out_argmax, want_argmax,
+                      workspace, stream)
+
+
+def spec_verify_greedy_tree_stage(stage, logits, parents, tokens, *, out_accept_len=None, out_path=None,
+                                  out_bonus=None, out_argmax=None, want_argmax=True, workspace=None, stream=None):
+    """One stage of spec_verify_greedy_tree: 1 per-row argmax, 2 tree resolve and outputs."""
+    return _tree_call(int(stage), logits, parents, tokens, out_accept_len, out_path, out_bonus, out_argmax,
+                      want_argmax, workspace, stream)
 
 
 def version() -> str:

@@ -11,7 +11,7 @@
 
 namespace sv {
 hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stage, hipStream_t stream);
-hipError_t launch_tree(const TreeLaunch& A, int dt, hipStream_t stream);
+hipError_t launch_tree(const TreeLaunch& A, int dt, int stage, hipStream_t stream);
 
 static thread_local int g_last_hip_error = 0;
 
@@ -125,32 +125,21 @@ static SampleLaunch plan_sample(const SampleArgs& a) {
   L.plan = (SeqPlan*)(ws + lay.off_plan);
   L.steptot = (double*)(ws + lay.off_step);
   L.chunktot = (double*)(ws + lay.off_chunk);
-  L.cnt1 = (unsigned*)(ws + lay.off_cnt1);
-  L.cnt2 = (unsigned*)(ws + lay.off_cnt2);
   return L;
 }
 
-static int run_sample(int stage_mask, const SampleArgs& a, hipStream_t stream) {
+// stages 1..4 = stats, accept, resid, draw; first..last inclusive
+static int run_sample(int first, int last, const SampleArgs& a, hipStream_t stream) {
   int st = validate_sample(a);
   if (st) return st;
   const SampleLaunch L = plan_sample(a);
   // grid sizes fit a 32-bit dimension by construction of the limits; check anyway
   if ((int64_t)L.B * L.per_seq > 0x7fffffffLL || (int64_t)L.B * L.nc2 > 0x7fffffffLL) return SV_ERR_SHAPE;
-  if (stage_mask & 1) {
-    st = hip_status(launch_sample_stage(L, a.tdt, a.ddt, 1, stream));
-    if (st) return st;
-  }
-  if (stage_mask & 2) {
-    st = hip_status(launch_sample_stage(L, a.tdt, a.ddt, 2, stream));
+  for (int s = first; s <= last; ++s) {
+    st = hip_status(launch_sample_stage(L, a.tdt, a.ddt, s, stream));
     if (st) return st;
   }
   return SV_OK;
-}
-
-__global__ void sv_fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
-  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
 }
 
 }  // namespace sv
@@ -169,30 +158,17 @@ size_t sv_tree_workspace_bytes(int B, int N, int V) {
   return (size_t)tree_layout(B, N, V).total;
 }
 
-int sv_workspace_clear(void* workspace, size_t bytes, void* stream) {
-  if (!workspace) return SV_ERR_NULL;
-  if (!aligned(workspace, 16)) return SV_ERR_ALIGN;
-  if (bytes == 0) return SV_OK;
-  const size_t n16 = bytes / 16, ntail = bytes % 16;
-  size_t blocks = (n16 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(sv_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                     (uint4*)workspace, n16, (unsigned char*)workspace + n16 * 16, ntail);
-  return hip_status(hipGetLastError());
-}
-
 int spec_verify_sample_stage(int stage, const void* target_logits, int target_dtype, int64_t target_seq_stride,
                              int64_t target_row_stride, const void* draft_logits, int draft_dtype,
                              int64_t draft_seq_stride, int64_t draft_row_stride, const int32_t* draft_tokens,
                              const float* uniforms, const float* temperature, int B, int gamma, int V,
                              int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (stage != 1 && stage != 2) return SV_ERR_ARG;
+  if (stage < 1 || stage > 4) return SV_ERR_ARG;
   SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
-  return run_sample(stage == 1 ? 1 : 2, a, (hipStream_t)stream);
+  return run_sample(stage, stage, a, (hipStream_t)stream);
 }
 
 int spec_verify_sample(const void* target_logits, int target_dtype, int64_t target_seq_stride,
@@ -204,13 +180,13 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
   SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
-  return run_sample(3, a, (hipStream_t)stream);
+  return run_sample(1, 4, a, (hipStream_t)stream);
 }
 
-int spec_verify_greedy_tree(const void* target_logits, int dtype, int64_t seq_stride, int64_t row_stride,
-                            const int32_t* parents, const int32_t* tokens, int B, int N, int V,
-                            int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus, int32_t* out_argmax,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+static int run_tree(int first, int last, const void* target_logits, int dtype, int64_t seq_stride,
+                    int64_t row_stride, const int32_t* parents, const int32_t* tokens, int B, int N, int V,
+                    int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus, int32_t* out_argmax,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!target_logits || !parents || !tokens || !out_accept_len || !out_path || !out_bonus) return SV_ERR_NULL;
   if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
   if (B < 1 || B > SV_MAX_BATCH || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB) return SV_ERR_SHAPE;
@@ -242,10 +218,32 @@ int spec_verify_greedy_tree(const void* target_logits, int dtype, int64_t seq_st
   L.out_bonus = out_bonus;
   L.out_argmax = out_argmax;
   L.part = (ArgPartial*)((char*)workspace + lay.off_part);
-  L.cnt = (unsigned*)((char*)workspace + lay.off_cnt);
   if ((int64_t)B * N * L.nch > 0x7fffffffLL) return SV_ERR_SHAPE;
-  return hip_status(launch_tree(L, dtype, (hipStream_t)stream));
+  for (int s = first; s <= last; ++s) {
+    st = hip_status(launch_tree(L, dtype, s, (hipStream_t)stream));
+    if (st) return st;
+  }
+  return SV_OK;
 }
+
+int spec_verify_greedy_tree(const void* target_logits, int dtype, int64_t seq_stride, int64_t row_stride,
+                            const int32_t* parents, const int32_t* tokens, int B, int N, int V,
+                            int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus, int32_t* out_argmax,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return run_tree(1, 2, target_logits, dtype, seq_stride, row_stride, parents, tokens, B, N, V, out_accept_len,
+                  out_path, out_bonus, out_argmax, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_greedy_tree_stage(int stage, const void* target_logits, int dtype, int64_t seq_stride,
+                                  int64_t row_stride, const int32_t* parents, const int32_t* tokens, int B, int N,
+                                  int V, int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus,
+                                  int32_t* out_argmax, void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < 1 || stage > 2) return SV_ERR_ARG;
+  return run_tree(stage, stage, target_logits, dtype, seq_stride, row_stride, parents, tokens, B, N, V,
+                  out_accept_len, out_path, out_bonus, out_argmax, workspace, workspace_bytes, stream);
+}
+
+
 
 const char* sv_status_string(int status) {
   switch (status) {

@@ -1,5 +1,5 @@
-// sv_device.hpp -- gfx950 device helpers: 16-byte row units, wave64 reductions,
-// agent-scope release/acquire for the last-arriving-workgroup pattern.
+// sv_device.hpp -- gfx950 device helpers: 16-byte row units and wave64
+// reductions shared by the verify kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -117,20 +117,6 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
     if (lane >= o) v += t;
   }
   return v;
-}
-
-// ---------------------------------------------------------------------------
-// agent-scope ordering for "last workgroup to arrive does the merge"
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
-__device__ __forceinline__ unsigned atomic_arrive(unsigned* c) {
-  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void atomic_reset(unsigned* c) {
-  __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Temperature usable iff finite, positive and a normal binary32.

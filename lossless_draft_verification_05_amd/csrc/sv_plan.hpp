@@ -29,7 +29,7 @@ struct RowPartial {
   double s;
 };
 
-// What the stats pass hands to the draw pass, per sequence.
+// What the accept kernel hands to the residual and draw kernels, per sequence.
 struct SeqPlan {
   int valid;   // 0: the sequence is invalid (all outputs -1)
   int n;       // accepted drafts
@@ -78,8 +78,6 @@ struct SampleLaunch {
   SeqPlan* plan;     // [B]
   double* steptot;   // [B][ns2]
   double* chunktot;  // [B][nc2]
-  unsigned* cnt1;    // [B]
-  unsigned* cnt2;    // [B]
 };
 
 struct TreeLaunch {
@@ -95,7 +93,6 @@ struct TreeLaunch {
   int32_t* out_bonus;
   int32_t* out_argmax;
   ArgPartial* part;  // [B][N][nch]
-  unsigned* cnt;     // [B]
 };
 
 // ---------------------------------------------------------------------------
@@ -127,7 +124,7 @@ inline int64_t max_chunks_per_row(int64_t V) { return ceil_div(V * 4, kMinChunkB
 inline int64_t align256(int64_t x) { return round_up(x, 256); }
 
 struct SampleLayout {
-  int64_t off_part, off_plan, off_step, off_chunk, off_cnt1, off_cnt2, total;
+  int64_t off_part, off_plan, off_step, off_chunk, total;
 };
 
 inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
@@ -144,16 +141,12 @@ inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
   o += align256(B * draw_steps(V) * 8);
   L.off_chunk = o;
   o += align256(B * max_draw_chunks(V) * 8);
-  L.off_cnt1 = o;
-  o += align256(B * 4);
-  L.off_cnt2 = o;
-  o += align256(B * 4);
   L.total = o;
   return L;
 }
 
 struct TreeLayout {
-  int64_t off_part, off_cnt, total;
+  int64_t off_part, total;
 };
 
 inline TreeLayout tree_layout(int64_t B, int64_t N, int64_t V) {
@@ -161,8 +154,6 @@ inline TreeLayout tree_layout(int64_t B, int64_t N, int64_t V) {
   int64_t o = 0;
   L.off_part = o;
   o += align256(B * N * max_chunks_per_row(V) * (int64_t)sizeof(ArgPartial));
-  L.off_cnt = o;
-  o += align256(B * 4);
   L.total = o;
   return L;
 }

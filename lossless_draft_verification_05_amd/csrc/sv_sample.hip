@@ -8,18 +8,23 @@
 // max(0, p_n - q_n), or after full acceptance draw from p_gamma; the draw is an
 // inverse CDF in token order at u_gamma.
 //
-// Two kernels, each a flat grid of 256-thread workgroups:
-//  stats : one workgroup per (row, chunk) of every target and draft row. Each
-//          wave streams 16-byte units with coalesced loads and keeps a per-lane
-//          tempered sum-exp against a lazily moved reference; partials go to
-//          the workspace. The last workgroup to finish a sequence (atomic
-//          arrival counter) merges them, gathers p(x), q(x), runs the accept
-//          tests and the first-rejection scan (one ballot) and writes a plan.
-//  draw  : one workgroup per (sequence, chunk) of the one row pair the draw
-//          needs (residual) or the bonus row. Each wave produces exact per-step
-//          masses (2048 tokens per step); the last workgroup of a sequence
-//          walks chunk totals -> step totals -> one rescanned step to the token
-//          whose running mass first exceeds u * total, and writes the outputs.
+// Four kernels, each a flat grid of 256-thread workgroups, ordered on the
+// caller's stream (kernel boundaries are the only synchronisation: a
+// per-workgroup agent-scope release would write back the L2 of its XCD, which
+// serialises across the device and costs more than the streaming itself):
+//  stats  : one workgroup per (row, chunk) of every target and draft row. Each
+//           wave streams 16-byte units with coalesced loads and keeps a per-lane
+//           tempered sum-exp against a lazily moved reference; one partial per
+//           workgroup goes to the workspace.
+//  accept : one workgroup per sequence merges its partials, gathers p(x), q(x),
+//           runs the accept tests and the first-rejection scan (one ballot) and
+//           writes a plan for the draw.
+//  resid  : one workgroup per (sequence, chunk) of the one row pair the draw
+//           needs (residual) or the bonus row; each wave writes exact masses of
+//           2048-token steps and the workgroup a chunk total.
+//  draw   : one workgroup per sequence walks chunk totals -> step totals -> one
+//           rescanned step to the token whose running mass first exceeds
+//           u * total, and writes the outputs.
 #include "sv_device.hpp"
 
 namespace sv {
@@ -94,16 +99,6 @@ __device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int 
   }
 }
 
-// Loads that read data other workgroups wrote during this kernel.
-__device__ __forceinline__ double ld_shared_f64(const double* p) {
-  uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __longlong_as_double((long long)v);
-}
-__device__ __forceinline__ float ld_shared_f32(const float* p) {
-  uint32_t v = __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __uint_as_float(v);
-}
-
 template <int DT>
 __device__ __forceinline__ float load_elem(const char* row, int v) {
   if constexpr (DT == 1) {
@@ -121,18 +116,13 @@ template <int TD, int DD>
 __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
   __shared__ float sh_m[kWaves], sh_mt[kWaves];
   __shared__ double sh_s[kWaves];
-  __shared__ int sh_last;
-  __shared__ float rM[kMaxRows];
-  __shared__ double rS[kMaxRows];
-  __shared__ int rV[kMaxRows];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
   const int64_t wg = blockIdx.x;
   const int b = (int)(wg / A.per_seq);
   const int r = (int)(wg % A.per_seq);
   const float T = A.temps[b];
-  const bool tv = temp_ok(T);
-  const float kl = tv ? log2e_over(T) : 1.0f;
+  const float kl = temp_ok(T) ? log2e_over(T) : 1.0f;
   const int G = A.gamma;
   const int tchunks = (G + 1) * A.nct;
 
@@ -176,15 +166,27 @@ __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
     rp.m_true = fmaxf(fmaxf(sh_mt[0], sh_mt[1]), fmaxf(sh_mt[2], sh_mt[3]));
     rp.s = sb;
     A.part[wg] = rp;
-    fence_release();
-    const unsigned old = atomic_arrive(&A.cnt1[b]);
-    sh_last = (old == (unsigned)A.per_seq - 1u);
   }
-  __syncthreads();
-  if (!sh_last) return;
-  fence_acquire();
+}
 
-  // ---- last workgroup of sequence b: merge every row of the sequence ----
+// ---------------------------------------------------------------------------
+// accept kernel: one workgroup per sequence
+// ---------------------------------------------------------------------------
+template <int TD, int DD>
+__global__ __launch_bounds__(kThreads) void sv_accept_kernel(SampleLaunch A) {
+  __shared__ float rM[kMaxRows];
+  __shared__ double rS[kMaxRows];
+  __shared__ int rV[kMaxRows];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
+  const int b = blockIdx.x;
+  const float T = A.temps[b];
+  const bool tv = temp_ok(T);
+  const float kl = tv ? log2e_over(T) : 1.0f;
+  const int G = A.gamma;
+  const int tchunks = (G + 1) * A.nct;
+
+  // merge the chunk partials of every row, in chunk order
   const int nrows = 2 * G + 1;
   for (int t = tid; t < nrows; t += kThreads) {
     int nch, base;
@@ -198,74 +200,71 @@ __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
     const RowPartial* P = A.part + (int64_t)b * A.per_seq + base;
     float Mr = -FLT_MAX, mtr = -INFINITY;
     for (int c = 0; c < nch; ++c) {
-      Mr = fmaxf(Mr, ld_shared_f32(&P[c].m_ref));
-      mtr = fmaxf(mtr, ld_shared_f32(&P[c].m_true));
+      Mr = fmaxf(Mr, P[c].m_ref);
+      mtr = fmaxf(mtr, P[c].m_true);
     }
     double S = 0.0;
-    for (int c = 0; c < nch; ++c)
-      S += ld_shared_f64(&P[c].s) * exp2(((double)ld_shared_f32(&P[c].m_ref) - (double)Mr) * (double)kl);
+    for (int c = 0; c < nch; ++c) S += P[c].s * exp2(((double)P[c].m_ref - (double)Mr) * (double)kl);
     const double St = S * exp2(((double)Mr - (double)mtr) * (double)kl);
     rM[t] = mtr;
     rS[t] = St;
     rV[t] = tv && __builtin_isfinite(St) && St > 0.0 && __builtin_isfinite(mtr);
   }
   __syncthreads();
+  if (w != 0) return;
 
-  if (w == 0) {
-    int code = 1;  // 1 accepted, 0 rejected, 2 invalid
-    if (lane < G) {
-      const int i = lane;
-      const int xi = A.tokens[(int64_t)b * G + i];
-      const float ui = A.uniforms[(int64_t)b * (G + 1) + i];
-      bool ok = tv && rV[i] && rV[G + 1 + i] && xi >= 0 && xi < A.V && ui >= 0.0f && ui < 1.0f;
-      float pxo = __builtin_nanf(""), qxo = __builtin_nanf("");
+  int code = 1;  // 1 accepted, 0 rejected, 2 invalid
+  if (lane < G) {
+    const int i = lane;
+    const int xi = A.tokens[(int64_t)b * G + i];
+    const float ui = A.uniforms[(int64_t)b * (G + 1) + i];
+    bool ok = tv && rV[i] && rV[G + 1 + i] && xi >= 0 && xi < A.V && ui >= 0.0f && ui < 1.0f;
+    float pxo = __builtin_nanf(""), qxo = __builtin_nanf("");
+    if (ok) {
+      const float lt = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)i * A.t_row_b, xi);
+      const float ld = load_elem<DD>(A.dft + (int64_t)b * A.d_seq_b + (int64_t)i * A.d_row_b, xi);
+      if (ld == -INFINITY) ok = false;
       if (ok) {
-        const float lt = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)i * A.t_row_b, xi);
-        const float ld = load_elem<DD>(A.dft + (int64_t)b * A.d_seq_b + (int64_t)i * A.d_row_b, xi);
-        if (ld == -INFINITY) ok = false;
-        if (ok) {
-          const double lp2 = ((double)lt - (double)rM[i]) * (double)kl;
-          const double lq2 = ((double)ld - (double)rM[G + 1 + i]) * (double)kl;
-          const double Sp = rS[i], Sq = rS[G + 1 + i];
-          const double rho = exp2(lp2 - lq2) * (Sq / Sp);
-          pxo = (float)(exp2(lp2) / Sp);
-          qxo = (float)(exp2(lq2) / Sq);
-          code = ((double)ui < rho) ? 1 : 0;
-        }
+        const double lp2 = ((double)lt - (double)rM[i]) * (double)kl;
+        const double lq2 = ((double)ld - (double)rM[G + 1 + i]) * (double)kl;
+        const double Sp = rS[i], Sq = rS[G + 1 + i];
+        const double rho = exp2(lp2 - lq2) * (Sq / Sp);
+        pxo = (float)(exp2(lp2) / Sp);
+        qxo = (float)(exp2(lq2) / Sq);
+        code = ((double)ui < rho) ? 1 : 0;
       }
-      if (!ok) code = 2;
-      if (A.diag_px) A.diag_px[(int64_t)b * G + i] = pxo;
-      if (A.diag_qx) A.diag_qx[(int64_t)b * G + i] = qxo;
     }
-    const unsigned long long stop = __ballot(code != 1);
-    const int n = stop ? (__ffsll((long long)stop) - 1) : G;
-    const int code_n = __shfl(code, n < G ? n : 0, kWave);
-    if (lane == 0) {
-      const float ug = A.uniforms[(int64_t)b * (G + 1) + G];
-      bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f;
-      if (n == G) valid = valid && rV[G];
-      SeqPlan P;
-      P.valid = valid;
-      P.n = n;
-      P.mode = (n == G) ? kModeBonus : kModeResidual;
-      P.kl = kl;
-      P.mp = rM[n];
-      P.sp = rS[n];
-      if (n < G) {
-        P.mq = rM[G + 1 + n];
-        P.sq = rS[G + 1 + n];
-        const double kap = P.sp / P.sq;
-        P.kap_hi = (float)kap;
-        P.kap_lo = (float)(kap - (double)P.kap_hi);
-      } else {
-        P.mq = 0.0f;
-        P.sq = 1.0;
-        P.kap_hi = 0.0f;
-        P.kap_lo = 0.0f;
-      }
-      A.plan[b] = P;
-      atomic_reset(&A.cnt1[b]);
+    if (!ok) code = 2;
+    if (A.diag_px) A.diag_px[(int64_t)b * G + i] = pxo;
+    if (A.diag_qx) A.diag_qx[(int64_t)b * G + i] = qxo;
+  }
+  const unsigned long long stop = __ballot(code != 1);
+  const int n = stop ? (__ffsll((long long)stop) - 1) : G;
+  const int code_n = __shfl(code, n < G ? n : 0, kWave);
+  if (lane == 0) {
+    const float ug = A.uniforms[(int64_t)b * (G + 1) + G];
+    bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f;
+    if (n == G) valid = valid && rV[G];
+    SeqPlan P;
+    P.valid = valid;
+    P.n = n;
+    P.mode = (n == G) ? kModeBonus : kModeResidual;
+    P.kl = kl;
+    P.mp = rM[n];
+    P.sp = rS[n];
+    if (n < G) {
+      P.mq = rM[G + 1 + n];
+      P.sq = rS[G + 1 + n];
+      const double kap = P.sp / P.sq;
+      P.kap_hi = (float)kap;
+      P.kap_lo = (float)(kap - (double)P.kap_hi);
+    } else {
+      P.mq = 0.0f;
+      P.sq = 1.0;
+      P.kap_hi = 0.0f;
+      P.kap_lo = 0.0f;
     }
+    A.plan[b] = P;
   }
 }
 
@@ -371,7 +370,7 @@ __device__ int wave_find(const double* arr, int len, double t, double& acc, int 
   double last_acc = acc;
   for (int base = 0; base < len; base += kWave) {
     const int i = base + lane;
-    const double v = (i < len) ? ld_shared_f64(arr + i) : 0.0;
+    const double v = (i < len) ? arr[i] : 0.0;
     const double incl = wave_incl_scan(v, lane);
     double excl = __shfl_up(incl, 1, kWave);
     if (lane == 0) excl = 0.0;
@@ -394,28 +393,23 @@ __device__ int wave_find(const double* arr, int len, double t, double& acc, int 
 }
 
 template <int TD, int DD>
-__global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
+__global__ __launch_bounds__(kThreads) void sv_resid_kernel(SampleLaunch A) {
   __shared__ double sh_w[kWaves];
-  __shared__ int sh_last;
-  __shared__ double sh_total;
-  __shared__ int sh_y;
-
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
   const int b = blockIdx.x / A.nc2;
   const int c = blockIdx.x % A.nc2;
   const SeqPlan P = A.plan[b];
   if (P.valid) draw_chunk<TD, DD>(A, b, P, c, P.mode, sh_w);
-  if (lane == 0) fence_release();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = atomic_arrive(&A.cnt2[b]);
-    sh_last = (old == (unsigned)A.nc2 - 1u);
-  }
-  __syncthreads();
-  if (!sh_last) return;
-  fence_acquire();
+}
 
-  // ---- last workgroup of sequence b ----
+template <int TD, int DD>
+__global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
+  __shared__ double sh_w[kWaves];
+  __shared__ double sh_total;
+  __shared__ int sh_y;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
+  const int b = blockIdx.x;
+  const SeqPlan P = A.plan[b];
   const int G = A.gamma;
   int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
   if (!P.valid) {
@@ -423,7 +417,6 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
     if (tid == 0) {
       A.out_n[b] = -1;
       if (A.diag_mass) A.diag_mass[b] = __builtin_nanf("");
-      atomic_reset(&A.cnt2[b]);
     }
     return;
   }
@@ -431,21 +424,21 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
   const double* stot = A.steptot + (int64_t)b * A.ns2;
   if (tid == 0) {
     double tot = 0.0;
-    for (int k = 0; k < A.nc2; ++k) tot += ld_shared_f64(ctot + k);
+    for (int k = 0; k < A.nc2; ++k) tot += ctot[k];
     sh_total = tot;
   }
   __syncthreads();
   int mode = P.mode;
   if (!(sh_total > 0.0) && mode == kModeResidual) {
     // Nothing left after the rejection (p_n == q_n up to rounding): draw from p_n.
+    // Rare slow path: this workgroup recomputes every chunk of target row n.
     mode = kModeBonus;
     for (int k = 0; k < A.nc2; ++k) draw_chunk<TD, DD>(A, b, P, k, mode, sh_w);
-    if (lane == 0) fence_release();
-    __syncthreads();
-    fence_acquire();
+    // draw_chunk ends with a workgroup barrier: every step and chunk mass this
+    // workgroup wrote is visible to all of its waves
     if (tid == 0) {
       double tot = 0.0;
-      for (int k = 0; k < A.nc2; ++k) tot += ld_shared_f64(ctot + k);
+      for (int k = 0; k < A.nc2; ++k) tot += ctot[k];
       sh_total = tot;
     }
     __syncthreads();
@@ -523,7 +516,6 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
   if (tid == 0) {
     A.out_n[b] = n;
     if (A.diag_mass) A.diag_mass[b] = (float)(total / P.sp);
-    atomic_reset(&A.cnt2[b]);
   }
 }
 
@@ -532,12 +524,21 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
 // ---------------------------------------------------------------------------
 template <int TD, int DD>
 static hipError_t launch_pair(const SampleLaunch& A, int stage, hipStream_t stream) {
-  if (stage == 1) {
-    const int64_t grid = (int64_t)A.B * A.per_seq;
-    hipLaunchKernelGGL((sv_stats_kernel<TD, DD>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A);
-  } else {
-    const int64_t grid = (int64_t)A.B * A.nc2;
-    hipLaunchKernelGGL((sv_draw_kernel<TD, DD>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A);
+  switch (stage) {
+    case 1:
+      hipLaunchKernelGGL((sv_stats_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.per_seq)), dim3(kThreads), 0,
+                         stream, A);
+      break;
+    case 2:
+      hipLaunchKernelGGL((sv_accept_kernel<TD, DD>), dim3((unsigned)A.B), dim3(kThreads), 0, stream, A);
+      break;
+    case 3:
+      hipLaunchKernelGGL((sv_resid_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.nc2)), dim3(kThreads), 0,
+                         stream, A);
+      break;
+    default:
+      hipLaunchKernelGGL((sv_draw_kernel<TD, DD>), dim3((unsigned)A.B), dim3(kThreads), 0, stream, A);
+      break;
   }
   return hipGetLastError();
 }

@@ -8,11 +8,14 @@
 // parent's target row; the result is the deepest accepted node d (lowest id on
 // ties), its root path and the bonus token argmax(row d).
 //
-// One kernel: a workgroup per (sequence, node row, chunk) streams 16-byte units
-// and keeps a per-lane (max, first index) pair; the last workgroup of a
-// sequence (atomic arrival counter) merges the row partials and resolves the
-// tree in LDS by pointer jumping over the parent array (log2 N rounds), which
-// also leaves a binary-lifting table for writing the accepted path in parallel.
+// Two kernels on the caller's stream (the launch boundary is the only
+// synchronisation; see the sampling kernels for why no intra-kernel handoff):
+//  argmax : a workgroup per (sequence, node row, chunk) streams 16-byte units
+//           and keeps a per-lane (max, first index) pair; one partial each.
+//  tree   : a workgroup per tree merges the row partials and resolves the tree
+//           in LDS by pointer jumping over the parent array (log2 N rounds),
+//           which also leaves a binary-lifting table for writing the accepted
+//           path in parallel.
 #include "sv_device.hpp"
 
 namespace sv {
@@ -79,34 +82,11 @@ __device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int 
   }
 }
 
-__device__ __forceinline__ float ld_f32_agent(const float* p) {
-  return __uint_as_float(
-      __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ int ld_i32_agent(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int DT>
-__global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
+__global__ __launch_bounds__(kThreads) void sv_argmax_kernel(TreeLaunch A) {
   __shared__ float sh_v[kWaves];
   __shared__ int sh_i[kWaves];
   __shared__ int sh_n[kWaves];
-  __shared__ int sh_last;
-  __shared__ int s_ok;
-  __shared__ int s_key[kWaves];
-  // Resolve arrays, sized by N at launch (tree_lds_bytes):
-  //   s_g[N] int | s_up[(kLog2MaxNodes+1) * N] short | s_D[2 * N] short | s_A[2 * N] uchar
-  extern __shared__ __align__(16) char s_dyn[];
-  const int NN = A.N;
-  int* s_g = reinterpret_cast<int*>(s_dyn);
-  short* s_upb = reinterpret_cast<short*>(s_g + NN);
-  short* s_Db = s_upb + (kLog2MaxNodes + 1) * NN;
-  unsigned char* s_Ab = reinterpret_cast<unsigned char*>(s_Db + 2 * NN);
-#define s_up(k, i) s_upb[(k) * NN + (i)]
-#define s_D(k, i) s_Db[(k) * NN + (i)]
-#define s_A(k, i) s_Ab[(k) * NN + (i)]
-
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
   const int per_seq = A.N * A.nch;
   const int b = blockIdx.x / per_seq;
@@ -142,15 +122,27 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
     p.bad = sh_n[0] | sh_n[1] | sh_n[2] | sh_n[3];
     p.pad = 0;
     A.part[blockIdx.x] = p;
-    fence_release();
-    const unsigned old = atomic_arrive(&A.cnt[b]);
-    sh_last = (old == (unsigned)per_seq - 1u);
   }
-  __syncthreads();
-  if (!sh_last) return;
-  fence_acquire();
+}
 
-  // ---- last workgroup of tree b ----
+template <int DT>
+__global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
+  __shared__ int s_ok;
+  __shared__ int s_key[kWaves];
+  // Resolve arrays, sized by N at launch (tree_lds_bytes):
+  //   s_g[N] int | s_up[(kLog2MaxNodes+1) * N] short | s_D[2 * N] short | s_A[2 * N] uchar
+  extern __shared__ __align__(16) char s_dyn[];
+  const int NN = A.N;
+  int* s_g = reinterpret_cast<int*>(s_dyn);
+  short* s_upb = reinterpret_cast<short*>(s_g + NN);
+  short* s_Db = s_upb + (kLog2MaxNodes + 1) * NN;
+  unsigned char* s_Ab = reinterpret_cast<unsigned char*>(s_Db + 2 * NN);
+#define s_up(k, i) s_upb[(k) * NN + (i)]
+#define s_D(k, i) s_Db[(k) * NN + (i)]
+#define s_A(k, i) s_Ab[(k) * NN + (i)]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
+  const int per_seq = A.N * A.nch;
+  const int b = blockIdx.x;
   const int N = A.N;
   if (tid == 0) s_ok = 1;
   __syncthreads();
@@ -160,8 +152,8 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
     int i = INT_MAX, bad = 0;
     for (int cc = 0; cc < A.nch; ++cc) {
       const ArgPartial* q = P + (int64_t)jj * A.nch + cc;
-      arg_combine(v, i, ld_f32_agent(&q->best), ld_i32_agent(&q->idx));
-      bad |= ld_i32_agent(&q->bad);
+      arg_combine(v, i, q->best, q->idx);
+      bad |= q->bad;
     }
     if (v == INFINITY) bad = 1;  // +inf makes the row unusable
     if (v == -INFINITY) i = 0;   // a row of -inf only: first index
@@ -181,7 +173,6 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
     if (tid == 0) {
       A.out_len[b] = -1;
       A.out_bonus[b] = -1;
-      atomic_reset(&A.cnt[b]);
     }
     return;
   }
@@ -234,7 +225,6 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
   if (tid == 0) {
     A.out_len[b] = depth;
     A.out_bonus[b] = s_g[d];
-    atomic_reset(&A.cnt[b]);
   }
 #undef s_up
 #undef s_D
@@ -245,12 +235,20 @@ size_t tree_lds_bytes(int N) {
   return (size_t)N * 4 + (size_t)(kLog2MaxNodes + 1) * N * 2 + (size_t)2 * N * 2 + (size_t)2 * N + 16;
 }
 
-hipError_t launch_tree(const TreeLaunch& A, int dt, hipStream_t stream) {
+// stage 1: per-row argmax partials; stage 2: per-tree resolve
+hipError_t launch_tree(const TreeLaunch& A, int dt, int stage, hipStream_t stream) {
   const int64_t grid = (int64_t)A.B * A.N * A.nch;
-  if (dt == 1)
-    hipLaunchKernelGGL((sv_tree_kernel<1>), dim3((unsigned)grid), dim3(kThreads), tree_lds_bytes(A.N), stream, A);
-  else
-    hipLaunchKernelGGL((sv_tree_kernel<0>), dim3((unsigned)grid), dim3(kThreads), tree_lds_bytes(A.N), stream, A);
+  if (stage == 1) {
+    if (dt == 1)
+      hipLaunchKernelGGL((sv_argmax_kernel<1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A);
+    else
+      hipLaunchKernelGGL((sv_argmax_kernel<0>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A);
+  } else {
+    if (dt == 1)
+      hipLaunchKernelGGL((sv_tree_kernel<1>), dim3((unsigned)A.B), dim3(kThreads), tree_lds_bytes(A.N), stream, A);
+    else
+      hipLaunchKernelGGL((sv_tree_kernel<0>), dim3((unsigned)A.B), dim3(kThreads), tree_lds_bytes(A.N), stream, A);
+  }
   return hipGetLastError();
 }
 

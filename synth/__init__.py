@@ -346,6 +346,7 @@ class TreeInputs:
     parents: np.ndarray  # [B][N] int32, parents[b][0] = -1, parents[b][j] < j
     tokens: np.ndarray  # [B][N] int32
     planted: np.ndarray  # [B][N] int8: 1 = an edge to a child was planted in row j
+    dtype: str = "bf16"  # storage dtype of ``logits``
 
 
 def tree_shape(g: np.random.Generator, N: int, block: int = 2, max_depth: int = 6,
@@ -430,7 +431,7 @@ def make_tree_inputs(cid: int = 4, seed: int = 0, B: int | None = None, N: int |
         tokens[b] = tok
 
     _pmap(one, range(B))
-    return TreeInputs(cfg, seed, logits, parents, tokens, planted)
+    return TreeInputs(cfg, seed, logits, parents, tokens, planted, dtype)
 
 
 def make_custom_sample(B: int, gamma: int, V: int, target_dtype: str = "bf16", draft_dtype: str = "bf16",

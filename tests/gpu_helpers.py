@@ -177,7 +177,7 @@ def check_sample(inp, gpu, seqs=None, tally=None):
 # tree
 # ---------------------------------------------------------------------------
 def tree_tensors(ti, device="cuda", dtype=None):
-    dt = dtype or ti.cfg.dtype
+    dt = dtype or ti.dtype
     return dict(logits=dev_logits(ti.logits, dt, device), parents=torch.from_numpy(ti.parents).to(device),
                 tokens=torch.from_numpy(ti.tokens).to(device))
 

@@ -1,0 +1,287 @@
+"""GPU edge cases against the oracle: ragged and tiny vocabularies, extreme
+gamma and temperature, masks, signed zeros, invalid inputs, strided rows,
+workspace reuse across shapes, the staged entry point, and tree corner cases."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import spec_verify_oracle as O
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, out, name, allow_flags=2):
+    t = H.check_sample(inp, out)
+    H.log(f"[{name}] {t.summary()}")
+    assert not t.fail, t.fail[:5]
+    assert t.flagged <= allow_flags
+    return t
+
+
+@pytest.mark.parametrize("V", [1, 7, 8, 9, 31, 33, 4097, 128257])
+@pytest.mark.parametrize("tdt,ddt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+def test_vocab_sizes(gpu, V, tdt, ddt):
+    H.log(f"vocab V={V} {tdt}/{ddt}")
+    inp = synth.make_custom_sample(5, 3, V, tdt, ddt, T=[0.6, 1.0, 1.0, 1.5, 0.9], seed=V + 1)
+    out = H.run_sample(gpu, H.sample_tensors(inp, pad_to=8))
+    _check(inp, out, f"V={V}")
+    if V == 1:
+        assert (out["n"] == 3).all() and (out["tokens"] == 0).all()
+
+
+@pytest.mark.parametrize("G", [1, 16, 64])
+def test_gamma_extremes(gpu, G):
+    H.log(f"gamma={G}")
+    inp = synth.make_custom_sample(4, G, 3000, "bf16", "bf16", T=1.0, noise_sd=0.3, seed=G)
+    _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), f"gamma={G}")
+
+
+@pytest.mark.parametrize("T", [0.05, 10.0, 1e-30])
+def test_temperature_extremes(gpu, T):
+    H.log(f"T={T}")
+    inp = synth.make_custom_sample(6, 4, 2048, "bf16", "f32", T=T, noise_sd=0.5, seed=11)
+    _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), f"T={T}")
+
+
+def test_batch_of_one(gpu):
+    inp = synth.make_custom_sample(1, 5, 50000, "f32", "bf16", T=0.8, seed=3)
+    _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), "B=1")
+
+
+def _custom(B=6, G=4, V=1024, tdt="f32", ddt="f32", seed=0):
+    return synth.make_custom_sample(B, G, V, tdt, ddt, T=1.0, seed=seed)
+
+
+def test_masks_and_signed_zero(gpu):
+    inp = _custom(8, 4, 1000, "bf16", "bf16", seed=2)
+    g = np.random.default_rng(2)
+    ninf = synth.f32_to_bf16_bits(np.array([-np.inf], np.float32))[0]
+    mz = synth.f32_to_bf16_bits(np.array([-0.0], np.float32))[0]
+    for arr in (inp.target, inp.draft):
+        m = g.random(arr.shape) < 0.3
+        arr[m] = ninf
+        arr[g.random(arr.shape) < 0.05] = mz
+        arr[g.random(arr.shape) < 0.05] = 0
+    # keep every draft token drawable
+    for b in range(inp.B):
+        for i in range(inp.gamma):
+            inp.draft[b, i, inp.tokens[b, i]] = 0
+    _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), "masks")
+
+
+def test_identical_and_disjoint_rows(gpu):
+    inp = _custom(8, 5, 3000, "bf16", "bf16", seed=4)
+    inp.draft[:4] = inp.target[:4, :5]  # identical: rho == 1, accept all
+    ninf = synth.f32_to_bf16_bits(np.array([-np.inf], np.float32))[0]
+    for b in range(4, 8):  # disjoint supports at position 0
+        t = inp.target[b, 0].copy()
+        inp.target[b, 0, 1500:] = ninf
+        inp.draft[b, 0, :1500] = ninf
+        inp.tokens[b, 0] = 1500 + (b * 37) % 1500
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    _check(inp, out, "identical/disjoint")
+    assert (out["n"][:4] == 5).all() and (out["n"][4:] == 0).all()
+    assert (out["tokens"][4:, 0] < 1500).all()
+
+
+def test_invalid_inputs(gpu):
+    inp = _custom(12, 4, 512, "f32", "f32", seed=5)
+    T = inp.temperature
+    T[0], T[1], T[2], T[3], T[4] = 0.0, -1.0, np.nan, np.inf, 1e-40
+    inp.tokens[5, 0] = 512  # out of range at a consumed position
+    inp.tokens[6, 0] = -1
+    inp.target[7, 0, 17] = np.nan
+    inp.draft[8, 0, 3] = np.inf
+    inp.target[9, 0, :] = -np.inf
+    inp.uniforms[10, 0] = 1.0
+    inp.uniforms[11, 4] = -0.5
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    _check(inp, out, "invalid")
+    assert (out["n"] == -1).all() and (out["tokens"] == -1).all()
+
+
+def test_unconsulted_positions_are_ignored(gpu):
+    """Rows, tokens and uniforms after the first rejection do not matter."""
+    inp = _custom(4, 5, 700, "f32", "f32", seed=6)
+    for b in range(4):  # force a rejection at position 0: disjoint supports
+        inp.target[b, 0, 350:] = -np.inf
+        inp.draft[b, 0, :350] = -np.inf
+        inp.tokens[b, 0] = 400
+    inp.tokens[0, 2] = 9999
+    inp.target[1, 3, 5] = np.nan
+    inp.draft[2, 1, :] = np.nan
+    inp.uniforms[3, 2] = 7.0
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    _check(inp, out, "unconsulted")
+    assert (out["n"] == 0).all()
+
+
+def test_strided_rows(gpu):
+    inp = synth.make_custom_sample(6, 3, 3000, "bf16", "f32", T=0.9, seed=8)
+    tens = H.sample_tensors(inp)
+    # embed in wider rows and a batch with gaps: row stride 3064, sequence stride 2 * 4 rows
+    t_big = torch.full((12, 4, 3064), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d_big = torch.full((12, 3, 3064), float("nan"), dtype=torch.float32, device="cuda")
+    t_big[::2, :, :3000] = tens["target"]
+    d_big[::2, :, :3000] = tens["draft"]
+    tens["target"] = t_big[::2, :, :3000]
+    tens["draft"] = d_big[::2, :, :3000]
+    assert tens["target"].stride() == (2 * 4 * 3064, 3064, 1)
+    _check(inp, H.run_sample(gpu, tens), "strided")
+
+
+def test_workspace_reuse_across_shapes_and_stages(gpu):
+    """A garbage-filled workspace reused across shapes gives the same results."""
+    ws = gpu.Workspace()
+    ws.buf = torch.randint(0, 255, (64 << 20,), dtype=torch.uint8, device="cuda")  # no initialisation needed
+    a = _custom(5, 3, 4000, "bf16", "bf16", seed=9)
+    b = _custom(17, 6, 1000, "f32", "bf16", seed=10)
+    ta, tb = H.sample_tensors(a), H.sample_tensors(b)
+    ra1 = H.run_sample(gpu, ta, workspace=ws)
+    rb = H.run_sample(gpu, tb, workspace=ws)
+    ra2 = H.run_sample(gpu, ta, workspace=ws)
+    _check(a, ra1, "ws a")
+    _check(b, rb, "ws b")
+    for k in ra1:
+        assert np.array_equal(ra1[k], ra2[k], equal_nan=True)
+    # staged entry point: stages 1, 2, 3, 4 equal the full call
+    n = torch.empty(5, dtype=torch.int32, device="cuda")
+    t = torch.empty((5, 4), dtype=torch.int32, device="cuda")
+    for stage in (1, 2, 3, 4):
+        gpu.spec_verify_sample_stage(stage, **ta, out_num_accepted=n, out_tokens=t, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(n.cpu().numpy(), ra1["n"]) and np.array_equal(t.cpu().numpy(), ra1["tokens"])
+    # no diagnostics requested
+    r = H.run_sample(gpu, ta, diag=False, workspace=ws)
+    assert np.array_equal(r["n"], ra1["n"])
+
+
+def test_bad_arguments_raise(gpu):
+    inp = _custom(2, 2, 64, "f32", "f32")
+    tens = H.sample_tensors(inp)
+    with pytest.raises(ValueError):
+        gpu.spec_verify_sample(tens["target"].to(torch.float16), tens["draft"], tens["draft_tokens"],
+                               tens["uniforms"], tens["temperature"])
+    bad = dict(tens)
+    bad["target"] = torch.zeros((2, 3, 70), dtype=torch.bfloat16, device="cuda")[:, :, 1:65]  # misaligned rows
+    with pytest.raises(ValueError):
+        gpu.spec_verify_sample(**bad)
+
+
+# ---------------------------------------------------------------------------
+# tree
+# ---------------------------------------------------------------------------
+def _tree_run_check(gpu, logits, parents, tokens, dt="f32"):
+    tens = dict(logits=H.dev_logits(logits, dt), parents=torch.from_numpy(parents).cuda(),
+                tokens=torch.from_numpy(tokens).cuda())
+    out = H.run_tree(gpu, tens)
+    fails = H.check_tree(logits, dt, parents, tokens, out)
+    assert not fails, fails[:3]
+    return out
+
+
+def test_tree_golden_cases(gpu):
+    from tests.golden_io import farray, load
+
+    for case in load("tree_cases.json"):
+        L = farray(case["logits"]).astype(np.float32)
+        V = L.shape[1]
+        Lp = np.zeros((L.shape[0], 4), np.float32)  # rows padded to 16 bytes
+        Lp[:, :V] = L
+        tens = dict(logits=H.dev_logits(Lp[None], "f32")[..., :V],
+                    parents=torch.tensor([case["parents"]], dtype=torch.int32, device="cuda"),
+                    tokens=torch.tensor([case["tokens"]], dtype=torch.int32, device="cuda"))
+        out = H.run_tree(gpu, tens)
+        if case["valid"]:
+            assert int(out["len"][0]) == case["accept_len"], case["name"]
+            assert list(out["path"][0][: len(case["path"])]) == case["path"], case["name"]
+            assert int(out["bonus"][0]) == case["bonus"], case["name"]
+            assert list(out["argmax"][0]) == case["argmax"], case["name"]
+        else:
+            assert int(out["len"][0]) == -1 and int(out["bonus"][0]) == -1, case["name"]
+
+
+def test_tree_ties_zero_masks(gpu):
+    g = np.random.default_rng(12)
+    B, N, V = 16, 40, 4099
+    parents = np.array([[-1] + [int(g.integers(0, j)) for j in range(1, N)] for _ in range(B)], np.int32)
+    L = g.integers(-3, 4, size=(B, N, V)).astype(np.float32)  # many exact ties
+    L[g.random(L.shape) < 0.1] = -0.0
+    L[g.random(L.shape) < 0.2] = -np.inf
+    L[3, 5, :] = -np.inf  # a row of -inf only
+    tokens = g.integers(0, 4, size=(B, N)).astype(np.int32)  # low tokens: many matches, duplicate siblings
+    for dt in ("f32", "bf16"):
+        Ld = L if dt == "f32" else synth.f32_to_bf16_bits(L)
+        Lp = np.full((B, N, 4104), np.nan, np.float32) if dt == "f32" else np.full((B, N, 4104), 0x7FC1, np.uint16)
+        Lp[..., :V] = Ld
+        tens = dict(logits=H.dev_logits(Lp, dt)[..., :V], parents=torch.from_numpy(parents).cuda(),
+                    tokens=torch.from_numpy(tokens).cuda())
+        out = H.run_tree(gpu, tens)
+        fails = H.check_tree(Ld, dt, parents, tokens, out)
+        assert not fails, fails[:3]
+
+
+def test_tree_invalid(gpu):
+    g = np.random.default_rng(13)
+    B, N, V = 6, 9, 256
+    L = g.normal(size=(B, N, V)).astype(np.float32)
+    parents = np.array([[-1] + list(range(N - 1))] * B, np.int32)
+    tokens = g.integers(0, V, size=(B, N)).astype(np.int32)
+    L[0, 3, 7] = np.nan
+    L[1, 8, 0] = np.inf
+    parents[2, 4] = 4
+    parents[3, 0] = 0
+    tokens[4, 2] = V
+    out = _tree_run_check(gpu, L, parents, tokens)
+    assert (out["len"][:5] == -1).all() and out["len"][5] >= 0
+    assert out["argmax"][0, 3] == -1 and out["argmax"][1, 8] == -1
+
+
+def test_tree_single_node_and_max_chain(gpu):
+    g = np.random.default_rng(14)
+    L = g.normal(size=(3, 1, 64)).astype(np.float32)
+    out = _tree_run_check(gpu, L, np.full((3, 1), -1, np.int32), np.zeros((3, 1), np.int32))
+    assert (out["len"] == 0).all()
+    N, V = 1024, 64
+    L = g.normal(size=(2, N, V)).astype(np.float32)
+    parents = np.array([[-1] + list(range(N - 1))] * 2, np.int32)
+    tokens = np.zeros((2, N), np.int32)
+    for j in range(1, N):
+        tokens[:, j] = np.argmax(L[:, j - 1], axis=1)  # every edge matches
+    tokens[1, 700] = (tokens[1, 700] + 1) % V  # second chain breaks at node 700
+    out = _tree_run_check(gpu, L, parents, tokens)
+    assert out["len"][0] == N - 1 and out["len"][1] == 699
+
+
+@pytest.mark.parametrize("V", [1, 7, 33])
+def test_tree_tiny_vocab(gpu, V):
+    ti = synth.make_tree_inputs(4, seed=V, B=5, N=30, V=max(V, 8), dtype="f32")
+    L = ti.logits[..., :V].copy()
+    Lp = np.full(ti.logits.shape[:2] + (8 * ((V + 7) // 8),), np.nan, np.float32)
+    Lp[..., :V] = L
+    tokens = np.minimum(ti.tokens, V - 1).astype(np.int32)
+    tens = dict(logits=H.dev_logits(Lp, "f32")[..., :V], parents=torch.from_numpy(ti.parents).cuda(),
+                tokens=torch.from_numpy(tokens).cuda())
+    out = H.run_tree(gpu, tens)
+    fails = H.check_tree(L, "f32", ti.parents, tokens, out)
+    assert not fails, fails[:3]
+
+
+def test_tree_stages_equal_full_call(gpu):
+    ti = synth.make_tree_inputs(4, seed=15, B=4, N=20, V=5000)
+    tens = H.tree_tensors(ti)
+    full = H.run_tree(gpu, tens)
+    ws = gpu.Workspace()
+    ws.buf = torch.randint(0, 255, (8 << 20,), dtype=torch.uint8, device="cuda")
+    outs = None
+    for stage in (1, 2):
+        outs = gpu.spec_verify_greedy_tree_stage(stage, **tens, workspace=ws) if outs is None else \
+            gpu.spec_verify_greedy_tree_stage(stage, **tens, out_accept_len=outs[0], out_path=outs[1],
+                                              out_bonus=outs[2], out_argmax=outs[3], workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0].cpu().numpy(), full["len"])
+    assert np.array_equal(outs[1].cpu().numpy(), full["path"])
+    assert np.array_equal(outs[2].cpu().numpy(), full["bonus"])
+    assert np.array_equal(outs[3].cpu().numpy(), full["argmax"])

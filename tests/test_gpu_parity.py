@@ -77,7 +77,7 @@ def test_tree_fp32_and_multichunk(gpu):
     H.log("tree fp32, V=300000 (several chunks per row), B=3 N=17")
     ti = synth.make_tree_inputs(4, seed=7, B=3, N=17, V=300000, dtype="f32")
     out = H.run_tree(gpu, H.tree_tensors(ti))
-    fails = H.check_tree(ti.logits, "f32", ti.parents, ti.tokens, out)
+    fails = H.check_tree(ti.logits, ti.dtype, ti.parents, ti.tokens, out)
     assert not fails, fails[:3]
 
 
