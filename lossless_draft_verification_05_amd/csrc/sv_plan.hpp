@@ -15,8 +15,8 @@ constexpr int kU2 = 4;                          // 8-token octets per lane per r
 constexpr int kStepOctets = kWave * kU2;        // 256 octets = 2048 tokens per residual step (one wave)
 constexpr int kStepTokens = kStepOctets * 8;
 constexpr int64_t kMinChunkBytes = 16 << 10;    // stats / argmax work unit bounds
-constexpr int64_t kMaxChunkBytes = 256 << 10;
-constexpr int64_t kTargetWGs = 4096;            // ~16 workgroups per CU on 256 CUs
+constexpr int64_t kMaxChunkBytes = 64 << 10;    // measured best for 4 KB-per-instruction streaming
+constexpr int64_t kTargetWGs = 8192;            // ~32 workgroups per CU on 256 CUs
 constexpr int kLog2MaxNodes = 10;               // 1024 tree nodes
 
 enum : int { kModeResidual = 0, kModeBonus = 1 };

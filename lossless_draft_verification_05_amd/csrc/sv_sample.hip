@@ -12,8 +12,8 @@
 // caller's stream (kernel boundaries are the only synchronisation: a
 // per-workgroup agent-scope release would write back the L2 of its XCD, which
 // serialises across the device and costs more than the streaming itself):
-//  stats  : one workgroup per (row, chunk) of every target and draft row. Each
-//           wave streams 16-byte units with coalesced loads and keeps a per-lane
+//  stats  : one workgroup per (row, chunk) of every target and draft row. It
+//           streams 16-byte units, 4 KB per load instruction, and keeps a per-lane
 //           tempered sum-exp against a lazily moved reference; one partial per
 //           workgroup goes to the workspace.
 //  accept : one workgroup per sequence merges its partials, gathers p(x), q(x),
@@ -67,21 +67,23 @@ __device__ __forceinline__ void sumexp_units(SumExp& st, const Unit<DT> (&un)[NU
   }
 }
 
-// One wave streams units [w_begin, w_end) of a row with V elements.
+// The workgroup streams units [c_begin, c_end) of a row with V elements; thread
+// t takes units c_begin + t + 256 k, so every load instruction of the
+// workgroup covers one contiguous 4 KB block.
 template <int DT>
-__device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int V, int64_t w_begin, int64_t w_end,
+__device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int V, int64_t c_begin, int64_t c_end,
                                               float kl, SumExp& st) {
   constexpr int E = Unit<DT>::kEpu;
-  const int lane = threadIdx.x & (kWave - 1);
+  const int tid = threadIdx.x;
   const int64_t nu_row = ((int64_t)V + E - 1) / E;
   const bool ragged = (V % E) != 0;
-  int64_t full_end = w_end;
+  int64_t full_end = c_end;
   if (ragged && full_end > nu_row - 1) full_end = nu_row - 1;
-  int64_t base = w_begin;
-  for (; base + (int64_t)kWave * kU1 <= full_end; base += (int64_t)kWave * kU1) {
+  int64_t base = c_begin;
+  for (; base + (int64_t)kThreads * kU1 <= full_end; base += (int64_t)kThreads * kU1) {
     uint4 w[kU1];
 #pragma unroll
-    for (int j = 0; j < kU1; ++j) w[j] = load16(row + (base + lane + kWave * j) * 16);
+    for (int j = 0; j < kU1; ++j) w[j] = load16(row + (base + tid + kThreads * j) * 16);
     Unit<DT> un[kU1];
 #pragma unroll
     for (int j = 0; j < kU1; ++j) un[j].unpack(w[j]);
@@ -89,8 +91,8 @@ __device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int 
   }
 #pragma unroll
   for (int j = 0; j < kU1; ++j) {
-    int64_t u = base + lane + kWave * j;
-    if (u < w_end) {
+    int64_t u = base + tid + kThreads * j;
+    if (u < c_end) {
       Unit<DT> un[1];
       un[0].unpack(load16(row + u * 16));
       if (ragged && u == nu_row - 1) mask_tail(un[0], u, V);
@@ -131,19 +133,17 @@ __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
     const int row = r / A.nct, c = r % A.nct;
     const char* p = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)row * A.t_row_b;
     const int64_t nu = ((int64_t)A.V * Unit<TD>::kEsz + 15) / 16;
-    const int64_t q = A.cut / kWaves;
-    int64_t u0 = (int64_t)c * A.cut + (int64_t)w * q, u1 = u0 + q;
-    if (u1 > nu) u1 = nu;
-    if (u0 < u1) stream_sumexp<TD>(p, A.V, u0, u1, kl, st);
+    const int64_t u0 = (int64_t)c * A.cut;
+    const int64_t u1 = u0 + A.cut < nu ? u0 + A.cut : nu;
+    stream_sumexp<TD>(p, A.V, u0, u1, kl, st);
   } else {
     const int rr = r - tchunks;
     const int row = rr / A.ncd, c = rr % A.ncd;
     const char* p = A.dft + (int64_t)b * A.d_seq_b + (int64_t)row * A.d_row_b;
     const int64_t nu = ((int64_t)A.V * Unit<DD>::kEsz + 15) / 16;
-    const int64_t q = A.cud / kWaves;
-    int64_t u0 = (int64_t)c * A.cud + (int64_t)w * q, u1 = u0 + q;
-    if (u1 > nu) u1 = nu;
-    if (u0 < u1) stream_sumexp<DD>(p, A.V, u0, u1, kl, st);
+    const int64_t u0 = (int64_t)c * A.cud;
+    const int64_t u1 = u0 + A.cud < nu ? u0 + A.cud : nu;
+    stream_sumexp<DD>(p, A.V, u0, u1, kl, st);
   }
 
   // wave -> workgroup merge of (reference, sum, max)

@@ -11,7 +11,8 @@
 // Two kernels on the caller's stream (the launch boundary is the only
 // synchronisation; see the sampling kernels for why no intra-kernel handoff):
 //  argmax : a workgroup per (sequence, node row, chunk) streams 16-byte units
-//           and keeps a per-lane (max, first index) pair; one partial each.
+//           (4 KB per load instruction) and keeps a per-lane (max, first
+//           index) pair; one partial each.
 //  tree   : a workgroup per tree merges the row partials and resolves the tree
 //           in LDS by pointer jumping over the parent array (log2 N rounds),
 //           which also leaves a binary-lifting table for writing the accepted
@@ -47,22 +48,26 @@ __device__ __forceinline__ void argmax_units(ArgState& st, const Unit<DT> (&un)[
   }
 }
 
+// The workgroup streams units [c_begin, c_end); thread t takes units
+// c_begin + t + 256 k (one contiguous 4 KB block per load instruction). Each
+// thread still sees its units in increasing order, so strict ">" keeps the
+// first index of a tie within a thread.
 template <int DT>
-__device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int V, int64_t w_begin, int64_t w_end,
+__device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int V, int64_t c_begin, int64_t c_end,
                                               ArgState& st) {
   constexpr int E = Unit<DT>::kEpu;
-  const int lane = threadIdx.x & (kWave - 1);
+  const int tid = threadIdx.x;
   const int64_t nu_row = ((int64_t)V + E - 1) / E;
   const bool ragged = (V % E) != 0;
-  int64_t full_end = w_end;
+  int64_t full_end = c_end;
   if (ragged && full_end > nu_row - 1) full_end = nu_row - 1;
-  int64_t base = w_begin;
-  for (; base + (int64_t)kWave * kU1 <= full_end; base += (int64_t)kWave * kU1) {
+  int64_t base = c_begin;
+  for (; base + (int64_t)kThreads * kU1 <= full_end; base += (int64_t)kThreads * kU1) {
     uint4 w[kU1];
     int64_t u[kU1];
 #pragma unroll
     for (int j = 0; j < kU1; ++j) {
-      u[j] = base + lane + kWave * j;
+      u[j] = base + tid + kThreads * j;
       w[j] = load16(row + u[j] * 16);
     }
     Unit<DT> un[kU1];
@@ -72,8 +77,8 @@ __device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int 
   }
 #pragma unroll
   for (int j = 0; j < kU1; ++j) {
-    int64_t uu[1] = {base + lane + kWave * j};
-    if (uu[0] < w_end) {
+    int64_t uu[1] = {base + tid + kThreads * j};
+    if (uu[0] < c_end) {
       Unit<DT> un[1];
       un[0].unpack(load16(row + uu[0] * 16));
       if (ragged && uu[0] == nu_row - 1) mask_tail(un[0], uu[0], V);
@@ -97,10 +102,9 @@ __global__ __launch_bounds__(kThreads) void sv_argmax_kernel(TreeLaunch A) {
   {
     const char* row = A.logits + (int64_t)b * A.seq_b + (int64_t)j * A.row_b;
     const int64_t nu = ((int64_t)A.V * Unit<DT>::kEsz + 15) / 16;
-    const int64_t q = A.cu / kWaves;
-    int64_t u0 = (int64_t)c * A.cu + (int64_t)w * q, u1 = u0 + q;
-    if (u1 > nu) u1 = nu;
-    if (u0 < u1) stream_argmax<DT>(row, A.V, u0, u1, st);
+    const int64_t u0 = (int64_t)c * A.cu;
+    const int64_t u1 = u0 + A.cu < nu ? u0 + A.cu : nu;
+    stream_argmax<DT>(row, A.V, u0, u1, st);
   }
   float bv = st.best;
   int bi = st.idx;
