@@ -112,12 +112,12 @@ def esz(dt):
 
 
 def sample_bytes(cfg, B, G, V, n_acc=None):
-    """(stats-kernel bytes, residual-kernel bytes) the method must move per call.
+    """(stats-kernel bytes, finish-kernel bytes) the method must move per call.
 
     The stats kernel reads every target and draft logit once (plus tokens,
-    uniforms and temperatures, counted with it). The residual kernel reads the
+    uniforms and temperatures, counted with it). The finish kernel reads the
     one row the draw needs again -- target and draft row n after a rejection,
-    target row gamma after full acceptance -- and the outputs are written."""
+    target row gamma after full acceptance -- and writes the outputs."""
     bt, bd = esz(cfg.target_dtype), esz(cfg.draft_dtype)
     s1 = B * ((G + 1) * V * bt + G * V * bd) + B * (G * 4 + (G + 1) * 4 + 4)
     if n_acc is None:
@@ -256,7 +256,7 @@ def main():
                                                             out_num_accepted=out_n, out_tokens=out_t, workspace=ws)
 
         def stages(c):
-            return [stage_call(k, c) for k in (1, 2, 3, 4)]
+            return [stage_call(k, c) for k in (1, 2)]
         units = B * G
         unit = "positions/s"
         s1_bytes, _ = sample_bytes(cfg, B, G, V)
@@ -264,7 +264,7 @@ def main():
         cfg_desc = {"workload": f"{args.workload}: {cfg.name}", "B": B, "gamma": G, "V": V,
                     "target_dtype": cfg.target_dtype, "draft_dtype": cfg.draft_dtype, "temperature": tdesc,
                     "seed": args.seed}
-        kernel_names = ["sv_stats_kernel", "sv_accept_kernel", "sv_resid_kernel", "sv_draw_kernel"]
+        kernel_names = ["sv_stats_kernel", "sv_finish_kernel"]
 
     torch.cuda.synchronize()
     for k in range(args.warmup):
@@ -305,8 +305,8 @@ def main():
         detail["mean_accepted"] = float(n_acc[valid].mean())
         detail["mean_tokens_per_verify"] = float(n_acc[valid].mean() + 1)
         detail["invalid"] = int((~valid).sum())
-        detail["kernels"]["sv_resid_kernel"]["alg_bytes"] = int(s2_bytes)
-        detail["kernels"]["sv_resid_kernel"]["gbps"] = round(s2_bytes / (stage_ms[2] * 1e-3) / 1e9, 1)
+        detail["kernels"]["sv_finish_kernel"]["alg_bytes"] = int(s2_bytes)
+        detail["kernels"]["sv_finish_kernel"]["gbps"] = round(s2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1)
     detail["kernels"][kernel_names[0]]["alg_bytes"] = int(s1_bytes)
     detail["kernels"][kernel_names[0]]["gbps"] = round(s1_bytes / (stage_ms[0] * 1e-3) / 1e9, 1)
     detail["step_alg_bytes"] = int(step_bytes)

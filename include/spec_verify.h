@@ -123,19 +123,17 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * spec_verify_sample_stage -- one of the four kernels of spec_verify_sample,
+ * spec_verify_sample_stage -- one of the two kernels of spec_verify_sample,
  * for callers that want to time or overlap them. Same arguments and meaning as
  * spec_verify_sample; `stage` selects:
- *   1: row statistics: streams every target and draft row once (max and
- *      tempered sum-exp per row chunk, into the workspace);
- *   2: accept tests: merges the statistics, computes p_i(x_i)/q_i(x_i), the
- *      accept decisions and the first rejection (plan in the workspace,
- *      diag->p_x / q_x written);
- *   3: residual / bonus masses: streams the one row (pair) each sequence draws
- *      from, writing per-step masses into the workspace;
- *   4: draw: inverse CDF at u[b][gamma] and every output.
- * Stages must run in order 1, 2, 3, 4 on one stream with the same arguments and
- * workspace. spec_verify_sample enqueues all four.
+ *   1: row statistics: streams every target and draft row once (maximum and
+ *      tempered sum-exp per wave and row chunk, into the workspace);
+ *   2: finish, one workgroup per sequence: merges the statistics, runs the
+ *      accept tests and the first-rejection scan, streams the one row (pair)
+ *      the draw needs, draws by inverse CDF at u[b][gamma] and writes every
+ *      output (and diag).
+ * Stage 2 must follow stage 1 on the same stream with the same arguments and
+ * workspace. spec_verify_sample enqueues both.
  */
 int spec_verify_sample_stage(int stage, const void* target_logits, int target_dtype,
                              int64_t target_seq_stride, int64_t target_row_stride, const void* draft_logits,

@@ -206,7 +206,7 @@ def spec_verify_sample(target, draft, draft_tokens, uniforms, temperature, *, ou
 
 def spec_verify_sample_stage(stage, target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
                              out_tokens=None, diag=False, workspace=None, stream=None):
-    """One stage of spec_verify_sample: 1 row statistics, 2 accept tests, 3 residual/bonus masses, 4 draw."""
+    """One stage of spec_verify_sample: 1 row statistics, 2 accept tests + residual/bonus draw + outputs."""
     return _sample_call(int(stage), target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
                         out_tokens, diag, workspace, stream)
 

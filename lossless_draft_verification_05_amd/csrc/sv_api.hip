@@ -112,29 +112,21 @@ static SampleLaunch plan_sample(const SampleArgs& a) {
   split_row(V, et, cb, &L.nct, &L.cut);
   split_row(V, ed, cb, &L.ncd, &L.cud);
   L.per_seq = (int)((G + 1) * L.nct + G * L.ncd);
-  // draw pass: chunks of whole 4-step groups, enough workgroups to cover the GPU
   L.ns2 = (int)draw_steps(V);
-  const int64_t max_chunks = max_draw_chunks(V);
-  int64_t nc2 = clamp64(ceil_div(2048, B), 1, max_chunks);
-  int64_t spc2 = round_up(ceil_div(L.ns2, nc2), kWaves);
-  L.spc2 = (int)spc2;
-  L.nc2 = (int)ceil_div(L.ns2, spc2);
   const SampleLayout lay = sample_layout(B, G, V);
   char* ws = (char*)a.ws;
   L.part = (RowPartial*)(ws + lay.off_part);
-  L.plan = (SeqPlan*)(ws + lay.off_plan);
   L.steptot = (double*)(ws + lay.off_step);
-  L.chunktot = (double*)(ws + lay.off_chunk);
   return L;
 }
 
-// stages 1..4 = stats, accept, resid, draw; first..last inclusive
+// stages 1..2 = stats, finish; first..last inclusive
 static int run_sample(int first, int last, const SampleArgs& a, hipStream_t stream) {
   int st = validate_sample(a);
   if (st) return st;
   const SampleLaunch L = plan_sample(a);
   // grid sizes fit a 32-bit dimension by construction of the limits; check anyway
-  if ((int64_t)L.B * L.per_seq > 0x7fffffffLL || (int64_t)L.B * L.nc2 > 0x7fffffffLL) return SV_ERR_SHAPE;
+  if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
   for (int s = first; s <= last; ++s) {
     st = hip_status(launch_sample_stage(L, a.tdt, a.ddt, s, stream));
     if (st) return st;
@@ -164,7 +156,7 @@ int spec_verify_sample_stage(int stage, const void* target_logits, int target_dt
                              const float* uniforms, const float* temperature, int B, int gamma, int V,
                              int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (stage < 1 || stage > 4) return SV_ERR_ARG;
+  if (stage < 1 || stage > 2) return SV_ERR_ARG;
   SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
@@ -180,7 +172,7 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
   SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
-  return run_sample(1, 4, a, (hipStream_t)stream);
+  return run_sample(1, 2, a, (hipStream_t)stream);
 }
 
 static int run_tree(int first, int last, const void* target_logits, int dtype, int64_t seq_stride,

@@ -79,24 +79,60 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
-// wave64 reductions (xor butterfly: fixed order, so results are deterministic)
+// wave64 reductions in registers (DPP). Within each 16-lane row a butterfly
+// over quad_perm / row_ror leaves the row's result in every lane; the four row
+// results are then read from lanes 0, 16, 32, 48 and combined in a fixed
+// order, so the result is the same in every lane and deterministic. All 64
+// lanes must be active.
 // ---------------------------------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = dpp_i32<CTRL>(__double2loint(v));
+  const int hi = dpp_i32<CTRL>(__double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+  return __hiloint2double(hi, lo);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ int wave_or(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppRowRor4>(v);
+  v += dpp_f64<kDppRowRor8>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 // (value desc, index asc) argmax; NaN values never enter (callers flag them).
@@ -107,22 +143,42 @@ __device__ __forceinline__ void arg_combine(float& v, int& i, float v2, int i2) 
   }
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float v2 = __shfl_xor(v, o, kWave);
-    int i2 = __shfl_xor(i, o, kWave);
-    arg_combine(v, i, v2, i2);
-  }
+template <int CTRL>
+__device__ __forceinline__ void arg_step(float& v, int& i) {
+  const float v2 = dpp_f32<CTRL>(v);
+  const int i2 = dpp_i32<CTRL>(i);
+  arg_combine(v, i, v2, i2);
 }
 
-// inclusive prefix sum over the wave, lane order
-__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  arg_step<kDppQuadXor1>(v, i);
+  arg_step<kDppQuadXor2>(v, i);
+  arg_step<kDppRowRor4>(v, i);
+  arg_step<kDppRowRor8>(v, i);
+  float rv = readlane_f32(v, 0);
+  int ri = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    double t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
+  for (int r = 16; r < 64; r += 16) arg_combine(rv, ri, readlane_f32(v, r), __builtin_amdgcn_readlane(i, r));
+  v = rv;
+  i = ri;
+}
+
+// inclusive prefix sum over the wave in lane order: Hillis-Steele within rows
+// (row_shr 1, 2, 4, 8 with zero fill), then row 15 / 31 broadcasts
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64_masked(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xf, true);
+  return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double wave_incl_scan(double v, int /*lane*/) {
+  v += dpp_f64_masked<kDppRowShr1, 0xf>(v);
+  v += dpp_f64_masked<kDppRowShr2, 0xf>(v);
+  v += dpp_f64_masked<kDppRowShr4, 0xf>(v);
+  v += dpp_f64_masked<kDppRowShr8, 0xf>(v);
+  v += dpp_f64_masked<kDppRowBcast15, 0xa>(v);
+  v += dpp_f64_masked<kDppRowBcast31, 0xc>(v);
   return v;
 }
 

@@ -7,29 +7,31 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;  // one workgroup = 4 wave64
+constexpr int kThreads = 256;  // streaming workgroups: 4 wave64
 constexpr int kWaves = 4;
+constexpr int kFinThreads = 512;  // per-sequence finish workgroup: 8 wave64
+constexpr int kFinWaves = 8;
 constexpr int kWave = 64;
 constexpr int kU1 = 4;                          // 16-byte units per lane per iteration (stats, argmax)
 constexpr int kU2 = 4;                          // 8-token octets per lane per residual step
 constexpr int kStepOctets = kWave * kU2;        // 256 octets = 2048 tokens per residual step (one wave)
 constexpr int kStepTokens = kStepOctets * 8;
 constexpr int64_t kMinChunkBytes = 16 << 10;    // stats / argmax work unit bounds
-constexpr int64_t kMaxChunkBytes = 64 << 10;    // measured best for 4 KB-per-instruction streaming
+constexpr int64_t kMaxChunkBytes = 128 << 10;   // measured best for the stats kernel on MI355X
 constexpr int64_t kTargetWGs = 8192;            // ~32 workgroups per CU on 256 CUs
 constexpr int kLog2MaxNodes = 10;               // 1024 tree nodes
 
 enum : int { kModeResidual = 0, kModeBonus = 1 };
 
-// Partial statistics of one chunk of one logits row (stats pass).
-// s = sum over the chunk of exp2((x - m_ref) * kl); m_true = max x.
+// Partial statistics of one wave's share of one chunk of one logits row
+// (stats pass): s = sum of exp2((x - m_ref) * kl); m_true = max x.
 struct RowPartial {
   float m_ref;
   float m_true;
   double s;
 };
 
-// What the accept kernel hands to the residual and draw kernels, per sequence.
+// The finish kernel's per-sequence plan for the draw (held in LDS).
 struct SeqPlan {
   int valid;   // 0: the sequence is invalid (all outputs -1)
   int n;       // accepted drafts
@@ -43,7 +45,7 @@ struct SeqPlan {
   double sq;   // same for draft row n
 };
 
-// Partial argmax of one chunk of one row (tree pass).
+// Partial argmax of one wave's share of one chunk of one row (tree pass).
 struct ArgPartial {
   float best;
   int idx;
@@ -69,15 +71,10 @@ struct SampleLaunch {
   int nct, ncd;  // chunks per target row / per draft row
   int cut, cud;  // 16-byte units per chunk (multiples of 256)
   int per_seq;   // (gamma + 1) * nct + gamma * ncd
-  // draw pass decomposition
-  int ns2;   // residual steps per row
-  int spc2;  // steps per draw-pass chunk
-  int nc2;   // draw-pass chunks per sequence
+  int ns2;  // 2048-token steps per row (draw)
   // workspace
-  RowPartial* part;  // [B][per_seq]
-  SeqPlan* plan;     // [B]
+  RowPartial* part;  // [B][per_seq][kWaves]
   double* steptot;   // [B][ns2]
-  double* chunktot;  // [B][nc2]
 };
 
 struct TreeLaunch {
@@ -92,7 +89,7 @@ struct TreeLaunch {
   int32_t* out_path;
   int32_t* out_bonus;
   int32_t* out_argmax;
-  ArgPartial* part;  // [B][N][nch]
+  ArgPartial* part;  // [B][N][nch][kWaves]
 };
 
 // ---------------------------------------------------------------------------
@@ -124,23 +121,18 @@ inline int64_t max_chunks_per_row(int64_t V) { return ceil_div(V * 4, kMinChunkB
 inline int64_t align256(int64_t x) { return round_up(x, 256); }
 
 struct SampleLayout {
-  int64_t off_part, off_plan, off_step, off_chunk, total;
+  int64_t off_part, off_step, total;
 };
 
 inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
-inline int64_t max_draw_chunks(int64_t V) { return ceil_div(draw_steps(V), kWaves); }
 
 inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
   SampleLayout L;
   int64_t o = 0;
   L.off_part = o;
-  o += align256(B * (2 * gamma + 1) * max_chunks_per_row(V) * (int64_t)sizeof(RowPartial));
-  L.off_plan = o;
-  o += align256(B * (int64_t)sizeof(SeqPlan));
+  o += align256(B * (2 * gamma + 1) * max_chunks_per_row(V) * kWaves * (int64_t)sizeof(RowPartial));
   L.off_step = o;
   o += align256(B * draw_steps(V) * 8);
-  L.off_chunk = o;
-  o += align256(B * max_draw_chunks(V) * 8);
   L.total = o;
   return L;
 }
@@ -153,7 +145,7 @@ inline TreeLayout tree_layout(int64_t B, int64_t N, int64_t V) {
   TreeLayout L;
   int64_t o = 0;
   L.off_part = o;
-  o += align256(B * N * max_chunks_per_row(V) * (int64_t)sizeof(ArgPartial));
+  o += align256(B * N * max_chunks_per_row(V) * kWaves * (int64_t)sizeof(ArgPartial));
   L.total = o;
   return L;
 }

@@ -8,23 +8,22 @@
 // max(0, p_n - q_n), or after full acceptance draw from p_gamma; the draw is an
 // inverse CDF in token order at u_gamma.
 //
-// Four kernels, each a flat grid of 256-thread workgroups, ordered on the
-// caller's stream (kernel boundaries are the only synchronisation: a
-// per-workgroup agent-scope release would write back the L2 of its XCD, which
-// serialises across the device and costs more than the streaming itself):
-//  stats  : one workgroup per (row, chunk) of every target and draft row. It
-//           streams 16-byte units, 4 KB per load instruction, and keeps a per-lane
-//           tempered sum-exp against a lazily moved reference; one partial per
-//           workgroup goes to the workspace.
-//  accept : one workgroup per sequence merges its partials, gathers p(x), q(x),
-//           runs the accept tests and the first-rejection scan (one ballot) and
-//           writes a plan for the draw.
-//  resid  : one workgroup per (sequence, chunk) of the one row pair the draw
-//           needs (residual) or the bonus row; each wave writes exact masses of
-//           2048-token steps and the workgroup a chunk total.
-//  draw   : one workgroup per sequence walks chunk totals -> step totals -> one
-//           rescanned step to the token whose running mass first exceeds
-//           u * total, and writes the outputs.
+// Two kernels on the caller's stream (the kernel boundary is the only
+// cross-workgroup synchronisation: a per-workgroup agent-scope release would
+// write back the L2 of its XCD, which serialises across the device and costs
+// more than the streaming itself):
+//  stats  : one 256-thread workgroup per (row, 128 KB chunk) of every target
+//           and draft row. It streams 16-byte units (4 KB per load
+//           instruction, non-temporal) and keeps a per-lane tempered sum-exp
+//           against a lazily moved reference; one partial per wave.
+//  finish : one 512-thread workgroup per sequence. It merges the partials of
+//           the sequence's rows (a wave per row), gathers p(x), q(x), runs the
+//           accept tests and the first-rejection ballot, streams the one row
+//           (pair) the draw needs -- max(0, p_n - q_n) after a rejection, p_gamma
+//           after full acceptance -- writing exact masses of 2048-token steps,
+//           then walks step masses -> one rescanned step -> one octet to the
+//           token whose running mass first exceeds u_gamma * total, and writes
+//           the outputs.
 #include "sv_device.hpp"
 
 namespace sv {
@@ -116,10 +115,7 @@ __device__ __forceinline__ float load_elem(const char* row, int v) {
 // ---------------------------------------------------------------------------
 template <int TD, int DD>
 __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
-  __shared__ float sh_m[kWaves], sh_mt[kWaves];
-  __shared__ double sh_s[kWaves];
-
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int64_t wg = blockIdx.x;
   const int b = (int)(wg / A.per_seq);
   const int r = (int)(wg % A.per_seq);
@@ -146,125 +142,17 @@ __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
     stream_sumexp<DD>(p, A.V, u0, u1, kl, st);
   }
 
-  // wave -> workgroup merge of (reference, sum, max)
+  // one partial per wave: (reference, sum relative to it, max)
   const float M = wave_max(st.m_ref);
   double s = st.s * (double)hw_exp2((st.m_ref - M) * kl);
   s = wave_sum(s);
   const float mt = wave_max(st.m_true);
   if (lane == 0) {
-    sh_m[w] = M;
-    sh_s[w] = s;
-    sh_mt[w] = mt;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float Mb = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
-    double sb = 0.0;
-    for (int k = 0; k < kWaves; ++k) sb += sh_s[k] * exp2(((double)sh_m[k] - (double)Mb) * (double)kl);
     RowPartial rp;
-    rp.m_ref = Mb;
-    rp.m_true = fmaxf(fmaxf(sh_mt[0], sh_mt[1]), fmaxf(sh_mt[2], sh_mt[3]));
-    rp.s = sb;
-    A.part[wg] = rp;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// accept kernel: one workgroup per sequence
-// ---------------------------------------------------------------------------
-template <int TD, int DD>
-__global__ __launch_bounds__(kThreads) void sv_accept_kernel(SampleLaunch A) {
-  __shared__ float rM[kMaxRows];
-  __shared__ double rS[kMaxRows];
-  __shared__ int rV[kMaxRows];
-
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
-  const int b = blockIdx.x;
-  const float T = A.temps[b];
-  const bool tv = temp_ok(T);
-  const float kl = tv ? log2e_over(T) : 1.0f;
-  const int G = A.gamma;
-  const int tchunks = (G + 1) * A.nct;
-
-  // merge the chunk partials of every row, in chunk order
-  const int nrows = 2 * G + 1;
-  for (int t = tid; t < nrows; t += kThreads) {
-    int nch, base;
-    if (t <= G) {
-      nch = A.nct;
-      base = t * A.nct;
-    } else {
-      nch = A.ncd;
-      base = tchunks + (t - G - 1) * A.ncd;
-    }
-    const RowPartial* P = A.part + (int64_t)b * A.per_seq + base;
-    float Mr = -FLT_MAX, mtr = -INFINITY;
-    for (int c = 0; c < nch; ++c) {
-      Mr = fmaxf(Mr, P[c].m_ref);
-      mtr = fmaxf(mtr, P[c].m_true);
-    }
-    double S = 0.0;
-    for (int c = 0; c < nch; ++c) S += P[c].s * exp2(((double)P[c].m_ref - (double)Mr) * (double)kl);
-    const double St = S * exp2(((double)Mr - (double)mtr) * (double)kl);
-    rM[t] = mtr;
-    rS[t] = St;
-    rV[t] = tv && __builtin_isfinite(St) && St > 0.0 && __builtin_isfinite(mtr);
-  }
-  __syncthreads();
-  if (w != 0) return;
-
-  int code = 1;  // 1 accepted, 0 rejected, 2 invalid
-  if (lane < G) {
-    const int i = lane;
-    const int xi = A.tokens[(int64_t)b * G + i];
-    const float ui = A.uniforms[(int64_t)b * (G + 1) + i];
-    bool ok = tv && rV[i] && rV[G + 1 + i] && xi >= 0 && xi < A.V && ui >= 0.0f && ui < 1.0f;
-    float pxo = __builtin_nanf(""), qxo = __builtin_nanf("");
-    if (ok) {
-      const float lt = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)i * A.t_row_b, xi);
-      const float ld = load_elem<DD>(A.dft + (int64_t)b * A.d_seq_b + (int64_t)i * A.d_row_b, xi);
-      if (ld == -INFINITY) ok = false;
-      if (ok) {
-        const double lp2 = ((double)lt - (double)rM[i]) * (double)kl;
-        const double lq2 = ((double)ld - (double)rM[G + 1 + i]) * (double)kl;
-        const double Sp = rS[i], Sq = rS[G + 1 + i];
-        const double rho = exp2(lp2 - lq2) * (Sq / Sp);
-        pxo = (float)(exp2(lp2) / Sp);
-        qxo = (float)(exp2(lq2) / Sq);
-        code = ((double)ui < rho) ? 1 : 0;
-      }
-    }
-    if (!ok) code = 2;
-    if (A.diag_px) A.diag_px[(int64_t)b * G + i] = pxo;
-    if (A.diag_qx) A.diag_qx[(int64_t)b * G + i] = qxo;
-  }
-  const unsigned long long stop = __ballot(code != 1);
-  const int n = stop ? (__ffsll((long long)stop) - 1) : G;
-  const int code_n = __shfl(code, n < G ? n : 0, kWave);
-  if (lane == 0) {
-    const float ug = A.uniforms[(int64_t)b * (G + 1) + G];
-    bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f;
-    if (n == G) valid = valid && rV[G];
-    SeqPlan P;
-    P.valid = valid;
-    P.n = n;
-    P.mode = (n == G) ? kModeBonus : kModeResidual;
-    P.kl = kl;
-    P.mp = rM[n];
-    P.sp = rS[n];
-    if (n < G) {
-      P.mq = rM[G + 1 + n];
-      P.sq = rS[G + 1 + n];
-      const double kap = P.sp / P.sq;
-      P.kap_hi = (float)kap;
-      P.kap_lo = (float)(kap - (double)P.kap_hi);
-    } else {
-      P.mq = 0.0f;
-      P.sq = 1.0;
-      P.kap_hi = 0.0f;
-      P.kap_lo = 0.0f;
-    }
-    A.plan[b] = P;
+    rp.m_ref = M;
+    rp.m_true = mt;
+    rp.s = s;
+    A.part[wg * kWaves + w] = rp;
   }
 }
 
@@ -329,36 +217,116 @@ __device__ __forceinline__ float sum8(const float (&r)[8]) {
   return ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
 }
 
-// Chunk c of the draw row(s) of sequence b: per-step masses and the chunk mass.
-// Called by a whole workgroup.
-template <int TD, int DD>
-__device__ void draw_chunk(const SampleLaunch& A, int b, const SeqPlan& P, int c, int mode, double* sh_w) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
-  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
-  const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
-  const int s0 = c * A.spc2;
-  const int s1 = min(s0 + A.spc2, A.ns2);
-  const int64_t noct = ((int64_t)A.V + 7) / 8;
-  double wacc = 0.0;
-  for (int s = s0 + w; s < s1; s += kWaves) {
-    double lacc = 0.0;
+// Raw 16-byte loads of one octet (8 tokens) of a row: bf16 needs one unit,
+// fp32 two. Only used where the whole octet lies inside the row.
+template <int DT>
+struct OctetRaw;
+template <>
+struct OctetRaw<1> {
+  uint4 w;
+  __device__ __forceinline__ void load(const char* row, int64_t oct) { w = load16(row + oct * 16); }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+    Unit<1> un;
+    un.unpack(w);
 #pragma unroll
-    for (int j = 0; j < kU2; ++j) {
-      const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
-      if (oct < noct) {
-        float rr[8];
-        octet_mass<TD, DD>(trow, drow, oct, A.V, mode, P, rr);
-        lacc += (double)sum8(rr);
+    for (int k = 0; k < 8; ++k) x[k] = un.x[k];
+  }
+};
+template <>
+struct OctetRaw<0> {
+  uint4 w0, w1;
+  __device__ __forceinline__ void load(const char* row, int64_t oct) {
+    w0 = load16(row + oct * 32);
+    w1 = load16(row + oct * 32 + 16);
+  }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+    x[0] = __uint_as_float(w0.x);
+    x[1] = __uint_as_float(w0.y);
+    x[2] = __uint_as_float(w0.z);
+    x[3] = __uint_as_float(w0.w);
+    x[4] = __uint_as_float(w1.x);
+    x[5] = __uint_as_float(w1.y);
+    x[6] = __uint_as_float(w1.z);
+    x[7] = __uint_as_float(w1.w);
+  }
+};
+
+template <int MODE>
+__device__ __forceinline__ void mass8(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P, float (&r)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float ep = hw_exp2((xt[k] - P.mp) * P.kl);
+    if constexpr (MODE == kModeResidual) {
+      const float eq = hw_exp2((xd[k] - P.mq) * P.kl);
+      float d = fmaf(-eq, P.kap_hi, ep);
+      d = fmaf(-eq, P.kap_lo, d);
+      r[k] = fmaxf(d, 0.0f);
+    } else {
+      r[k] = ep;
+    }
+  }
+}
+
+// Mass of one whole residual step (2048 tokens) of one wave: every load of the
+// step is issued before any arithmetic, so a wave keeps kU2 octets per row in
+// flight.
+template <int TD, int DD, int MODE>
+__device__ __forceinline__ double step_mass_full(const char* trow, const char* drow, int64_t s, const SeqPlan& P,
+                                                 int lane) {
+  OctetRaw<TD> t[kU2];
+  OctetRaw<DD> d[kU2];
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    t[j].load(trow, oct);
+    if constexpr (MODE == kModeResidual) d[j].load(drow, oct);
+  }
+  double lacc = 0.0;
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    float xt[8], xd[8], rr[8];
+    t[j].unpack(xt);
+    if constexpr (MODE == kModeResidual) d[j].unpack(xd);
+    mass8<MODE>(xt, xd, P, rr);
+    lacc += (double)sum8(rr);
+  }
+  return lacc;
+}
+
+// Masses of the draw row(s) of sequence b over all steps; wave w of nw takes
+// steps w, w + nw, ... and lane 0 writes each step's mass.
+template <int TD, int DD, int MODE>
+__device__ void step_masses(const SampleLaunch& A, int b, const SeqPlan& P, int w, int nw) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
+  const char* drow = (MODE == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
+  const int64_t noct = ((int64_t)A.V + 7) / 8;
+  const int full_steps = A.V / kStepTokens;  // steps that lie wholly inside the row
+  for (int s = w; s < A.ns2; s += nw) {
+    double lacc = 0.0;
+    if (s < full_steps) {
+      lacc = step_mass_full<TD, DD, MODE>(trow, drow, s, P, lane);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kU2; ++j) {
+        const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
+        if (oct < noct) {
+          float rr[8];
+          octet_mass<TD, DD>(trow, drow, oct, A.V, MODE, P, rr);
+          lacc += (double)sum8(rr);
+        }
       }
     }
     const double tot = wave_sum(lacc);
     if (lane == 0) A.steptot[(int64_t)b * A.ns2 + s] = tot;
-    wacc += tot;
   }
-  if (lane == 0) sh_w[w] = wacc;
-  __syncthreads();
-  if (tid == 0) A.chunktot[(int64_t)b * A.nc2 + c] = ((sh_w[0] + sh_w[1]) + sh_w[2]) + sh_w[3];
-  __syncthreads();
+}
+
+// Sum of arr[0..len) by one wave, in a fixed order.
+__device__ double wave_total(const double* arr, int len, int lane) {
+  double acc = 0.0;
+  for (int i = lane; i < len; i += kWave) acc += arr[i];
+  return wave_sum(acc);
 }
 
 // Wave-wide search over arr[0..len): the first i (in order) whose running mass
@@ -372,110 +340,211 @@ __device__ int wave_find(const double* arr, int len, double t, double& acc, int 
     const int i = base + lane;
     const double v = (i < len) ? arr[i] : 0.0;
     const double incl = wave_incl_scan(v, lane);
-    double excl = __shfl_up(incl, 1, kWave);
-    if (lane == 0) excl = 0.0;
+    const double excl = incl - v;  // only compared against t; exact enough for the search
     const unsigned long long hit = __ballot(v > 0.0 && run + incl > t);
     if (hit) {
       const int L = __ffsll((long long)hit) - 1;
-      acc = run + __shfl(excl, L, kWave);
+      acc = run + readlane_f64(excl, L);
       return base + L;
     }
     const unsigned long long pos = __ballot(v > 0.0);
     if (pos) {
       const int L = 63 - __clzll((long long)pos);
       last_i = base + L;
-      last_acc = run + __shfl(excl, L, kWave);
+      last_acc = run + readlane_f64(excl, L);
     }
-    run += __shfl(incl, kWave - 1, kWave);
+    run += readlane_f64(incl, kWave - 1);
   }
   acc = last_acc;
   return last_i;
 }
 
+// ---------------------------------------------------------------------------
+// finish kernel: one 512-thread workgroup per sequence
+// ---------------------------------------------------------------------------
 template <int TD, int DD>
-__global__ __launch_bounds__(kThreads) void sv_resid_kernel(SampleLaunch A) {
-  __shared__ double sh_w[kWaves];
-  const int b = blockIdx.x / A.nc2;
-  const int c = blockIdx.x % A.nc2;
-  const SeqPlan P = A.plan[b];
-  if (P.valid) draw_chunk<TD, DD>(A, b, P, c, P.mode, sh_w);
-}
-
-template <int TD, int DD>
-__global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
-  __shared__ double sh_w[kWaves];
+__global__ __launch_bounds__(kFinThreads) void sv_finish_kernel(SampleLaunch A) {
+  __shared__ float rM[kMaxRows];
+  __shared__ double rS[kMaxRows];
+  __shared__ int rV[kMaxRows];
+  __shared__ SeqPlan sP;
   __shared__ double sh_total;
   __shared__ int sh_y;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
   const int b = blockIdx.x;
-  const SeqPlan P = A.plan[b];
+  const float T = A.temps[b];
+  const bool tv = temp_ok(T);
+  const float kl = tv ? log2e_over(T) : 1.0f;
   const int G = A.gamma;
+  const int tchunks = (G + 1) * A.nct;
+
+  // (1) gathers of p(x), q(x) do not depend on the merge: issue them first
+  int xi = 0;
+  float ui = 0.0f, lt = 0.0f, ld = 0.0f;
+  bool tok_ok = false;
+  if (w == 0 && lane < G) {
+    xi = A.tokens[(int64_t)b * G + lane];
+    ui = A.uniforms[(int64_t)b * (G + 1) + lane];
+    tok_ok = xi >= 0 && xi < A.V;
+    if (tok_ok) {
+      lt = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)lane * A.t_row_b, xi);
+      ld = load_elem<DD>(A.dft + (int64_t)b * A.d_seq_b + (int64_t)lane * A.d_row_b, xi);
+    }
+  }
+
+  // (2) merge the partials of every row: one wave per row, lanes over partials
+  const int nrows = 2 * G + 1;
+  for (int t = w; t < nrows; t += kFinWaves) {
+    int nrec, base;
+    if (t <= G) {
+      nrec = A.nct * kWaves;
+      base = t * A.nct;
+    } else {
+      nrec = A.ncd * kWaves;
+      base = tchunks + (t - G - 1) * A.ncd;
+    }
+    const RowPartial* P = A.part + ((int64_t)b * A.per_seq + base) * kWaves;
+    float Mr = -FLT_MAX, mtr = -INFINITY;
+    for (int k = lane; k < nrec; k += kWave) {
+      Mr = fmaxf(Mr, P[k].m_ref);
+      mtr = fmaxf(mtr, P[k].m_true);
+    }
+    Mr = wave_max(Mr);
+    mtr = wave_max(mtr);
+    double S = 0.0;
+    for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(((double)P[k].m_ref - (double)Mr) * (double)kl);
+    S = wave_sum(S);
+    const double St = S * exp2(((double)Mr - (double)mtr) * (double)kl);
+    if (lane == 0) {
+      rM[t] = mtr;
+      rS[t] = St;
+      rV[t] = tv && __builtin_isfinite(St) && St > 0.0 && __builtin_isfinite(mtr);
+    }
+  }
+  __syncthreads();
+
+  // (3) accept tests and first rejection (wave 0)
+  if (w == 0) {
+    int code = 1;  // 1 accepted, 0 rejected, 2 invalid
+    if (lane < G) {
+      const int i = lane;
+      const bool ok = tv && rV[i] && rV[G + 1 + i] && tok_ok && ui >= 0.0f && ui < 1.0f && ld != -INFINITY;
+      float pxo = __builtin_nanf(""), qxo = __builtin_nanf("");
+      if (ok) {
+        const double lp2 = ((double)lt - (double)rM[i]) * (double)kl;
+        const double lq2 = ((double)ld - (double)rM[G + 1 + i]) * (double)kl;
+        const double Sp = rS[i], Sq = rS[G + 1 + i];
+        const double rho = exp2(lp2 - lq2) * (Sq / Sp);
+        pxo = (float)(exp2(lp2) / Sp);
+        qxo = (float)(exp2(lq2) / Sq);
+        code = ((double)ui < rho) ? 1 : 0;
+      } else {
+        code = 2;
+      }
+      if (A.diag_px) A.diag_px[(int64_t)b * G + i] = pxo;
+      if (A.diag_qx) A.diag_qx[(int64_t)b * G + i] = qxo;
+    }
+    const unsigned long long stop = __ballot(code != 1);
+    const int n = stop ? (__ffsll((long long)stop) - 1) : G;
+    const int code_n = __builtin_amdgcn_readlane(code, n < G ? n : 0);
+    if (lane == 0) {
+      const float ug = A.uniforms[(int64_t)b * (G + 1) + G];
+      bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f;
+      if (n == G) valid = valid && rV[G];
+      SeqPlan Q;
+      Q.valid = valid;
+      Q.n = n;
+      Q.mode = (n == G) ? kModeBonus : kModeResidual;
+      Q.kl = kl;
+      Q.mp = rM[n];
+      Q.sp = rS[n];
+      if (n < G) {
+        Q.mq = rM[G + 1 + n];
+        Q.sq = rS[G + 1 + n];
+        const double kap = Q.sp / Q.sq;
+        Q.kap_hi = (float)kap;
+        Q.kap_lo = (float)(kap - (double)Q.kap_hi);
+      } else {
+        Q.mq = 0.0f;
+        Q.sq = 1.0;
+        Q.kap_hi = 0.0f;
+        Q.kap_lo = 0.0f;
+      }
+      sP = Q;
+    }
+  }
+  __syncthreads();
+  const SeqPlan P = sP;
   int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
   if (!P.valid) {
-    for (int k = tid; k <= G; k += kThreads) otok[k] = -1;
+    for (int k = tid; k <= G; k += kFinThreads) otok[k] = -1;
     if (tid == 0) {
       A.out_n[b] = -1;
       if (A.diag_mass) A.diag_mass[b] = __builtin_nanf("");
     }
     return;
   }
-  const double* ctot = A.chunktot + (int64_t)b * A.nc2;
+
+  // (4) masses of the drawn distribution, every wave on its steps
+  int mode = P.mode;
+  if (mode == kModeResidual)
+    step_masses<TD, DD, kModeResidual>(A, b, P, w, kFinWaves);
+  else
+    step_masses<TD, DD, kModeBonus>(A, b, P, w, kFinWaves);
+  __syncthreads();  // every wave's step masses are visible to wave 0
   const double* stot = A.steptot + (int64_t)b * A.ns2;
-  if (tid == 0) {
-    double tot = 0.0;
-    for (int k = 0; k < A.nc2; ++k) tot += ctot[k];
-    sh_total = tot;
+  if (w == 0) {
+    const double tot = wave_total(stot, A.ns2, lane);
+    if (lane == 0) sh_total = tot;
   }
   __syncthreads();
-  int mode = P.mode;
   if (!(sh_total > 0.0) && mode == kModeResidual) {
     // Nothing left after the rejection (p_n == q_n up to rounding): draw from p_n.
-    // Rare slow path: this workgroup recomputes every chunk of target row n.
     mode = kModeBonus;
-    for (int k = 0; k < A.nc2; ++k) draw_chunk<TD, DD>(A, b, P, k, mode, sh_w);
-    // draw_chunk ends with a workgroup barrier: every step and chunk mass this
-    // workgroup wrote is visible to all of its waves
-    if (tid == 0) {
-      double tot = 0.0;
-      for (int k = 0; k < A.nc2; ++k) tot += ctot[k];
-      sh_total = tot;
+    step_masses<TD, DD, kModeBonus>(A, b, P, w, kFinWaves);
+    __syncthreads();
+    if (w == 0) {
+      const double tot = wave_total(stot, A.ns2, lane);
+      if (lane == 0) sh_total = tot;
     }
     __syncthreads();
   }
   const double total = sh_total;
+
+  // (5) inverse-CDF search (wave 0)
   if (w == 0) {
     const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
     double acc = 0.0;
-    // wave_find returns -1 only if every mass is zero, which valid rows rule out;
-    // clamp anyway so that no index can leave the arrays.
-    const int cc = max(wave_find(ctot, A.nc2, t, acc, lane), 0);
-    const int s0 = cc * A.spc2;
-    const int s1 = min(s0 + A.spc2, A.ns2);
-    const int ss = s0 + max(wave_find(stot + s0, s1 - s0, t, acc, lane), 0);
+    // wave_find returns -1 only if every mass is zero, which valid rows rule
+    // out; clamp anyway so that no index can leave the arrays.
+    const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
     // rescan the step in token order: octet j-major, then lane, then slot
     const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
     const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
     const int64_t noct = ((int64_t)A.V + 7) / 8;
+    float rr[kU2][8];
+#pragma unroll
+    for (int j = 0; j < kU2; ++j) {
+      const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
+      if (oct < noct) {
+        octet_mass<TD, DD>(trow, drow, oct, A.V, mode, P, rr[j]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
+      }
+    }
     int y = -1;
     int last_pos = -1;
     for (int j = 0; j < kU2 && y < 0; ++j) {
       const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
-      float rr[8];
-      if (oct < noct) {
-        octet_mass<TD, DD>(trow, drow, oct, A.V, mode, P, rr);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) rr[k] = 0.0f;
-      }
-      const double os = (double)sum8(rr);
+      const double os = (double)sum8(rr[j]);
       const double incl = wave_incl_scan(os, lane);
-      double excl = __shfl_up(incl, 1, kWave);
-      if (lane == 0) excl = 0.0;
+      const double excl = incl - os;
       int lk = -1;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (rr[k] > 0.0f) lk = k;
+        if (rr[j][k] > 0.0f) lk = k;
       if (lk >= 0) last_pos = (int)(oct * 8 + lk);  // later j / lanes have larger ids
       const unsigned long long hit = __ballot(os > 0.0 && acc + incl > t);
       if (hit) {
@@ -484,8 +553,8 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
         if (lane == L) {
           double run = acc + excl;
           for (int k = 0; k < 8; ++k) {
-            if (rr[k] > 0.0f) {
-              run += (double)rr[k];
+            if (rr[j][k] > 0.0f) {
+              run += (double)rr[j][k];
               if (run > t) {
                 yy = (int)(oct * 8 + k);
                 break;
@@ -494,9 +563,9 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
           }
           if (yy < 0) yy = (int)(oct * 8 + lk);
         }
-        y = __shfl(yy, L, kWave);
+        y = __builtin_amdgcn_readlane(yy, L);
       } else {
-        acc += __shfl(incl, kWave - 1, kWave);
+        acc += readlane_f64(incl, kWave - 1);
       }
     }
     if (y < 0) {
@@ -509,9 +578,11 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
     if (lane == 0) sh_y = y;
   }
   __syncthreads();
+
+  // (6) outputs
   const int y = sh_y;
   const int n = P.n;
-  for (int k = tid; k <= G; k += kThreads)
+  for (int k = tid; k <= G; k += kFinThreads)
     otok[k] = (k < n) ? A.tokens[(int64_t)b * G + k] : (k == n ? y : -1);
   if (tid == 0) {
     A.out_n[b] = n;
@@ -524,22 +595,11 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(SampleLaunch A) {
 // ---------------------------------------------------------------------------
 template <int TD, int DD>
 static hipError_t launch_pair(const SampleLaunch& A, int stage, hipStream_t stream) {
-  switch (stage) {
-    case 1:
-      hipLaunchKernelGGL((sv_stats_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.per_seq)), dim3(kThreads), 0,
-                         stream, A);
-      break;
-    case 2:
-      hipLaunchKernelGGL((sv_accept_kernel<TD, DD>), dim3((unsigned)A.B), dim3(kThreads), 0, stream, A);
-      break;
-    case 3:
-      hipLaunchKernelGGL((sv_resid_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.nc2)), dim3(kThreads), 0,
-                         stream, A);
-      break;
-    default:
-      hipLaunchKernelGGL((sv_draw_kernel<TD, DD>), dim3((unsigned)A.B), dim3(kThreads), 0, stream, A);
-      break;
-  }
+  if (stage == 1)
+    hipLaunchKernelGGL((sv_stats_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.per_seq)), dim3(kThreads), 0,
+                       stream, A);
+  else
+    hipLaunchKernelGGL((sv_finish_kernel<TD, DD>), dim3((unsigned)A.B), dim3(kFinThreads), 0, stream, A);
   return hipGetLastError();
 }
 

@@ -89,10 +89,7 @@ __device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int 
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void sv_argmax_kernel(TreeLaunch A) {
-  __shared__ float sh_v[kWaves];
-  __shared__ int sh_i[kWaves];
-  __shared__ int sh_n[kWaves];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int per_seq = A.N * A.nch;
   const int b = blockIdx.x / per_seq;
   const int r = blockIdx.x % per_seq;
@@ -109,23 +106,14 @@ __global__ __launch_bounds__(kThreads) void sv_argmax_kernel(TreeLaunch A) {
   float bv = st.best;
   int bi = st.idx;
   wave_argmax(bv, bi);
-  const int nn = wave_or((int)st.nan);
+  const bool nan = __ballot(st.nan) != 0ull;
   if (lane == 0) {
-    sh_v[w] = bv;
-    sh_i[w] = bi;
-    sh_n[w] = nn;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float v = sh_v[0];
-    int i = sh_i[0];
-    for (int k = 1; k < kWaves; ++k) arg_combine(v, i, sh_v[k], sh_i[k]);
     ArgPartial p;
-    p.best = v;
-    p.idx = i;
-    p.bad = sh_n[0] | sh_n[1] | sh_n[2] | sh_n[3];
+    p.best = bv;
+    p.idx = bi;
+    p.bad = nan ? 1 : 0;
     p.pad = 0;
-    A.part[blockIdx.x] = p;
+    A.part[(int64_t)blockIdx.x * kWaves + w] = p;
   }
 }
 
@@ -150,12 +138,12 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
   const int N = A.N;
   if (tid == 0) s_ok = 1;
   __syncthreads();
-  const ArgPartial* P = A.part + (int64_t)b * per_seq;
+  const ArgPartial* P = A.part + (int64_t)b * per_seq * kWaves;
   for (int jj = tid; jj < N; jj += kThreads) {
     float v = -INFINITY;
     int i = INT_MAX, bad = 0;
-    for (int cc = 0; cc < A.nch; ++cc) {
-      const ArgPartial* q = P + (int64_t)jj * A.nch + cc;
+    for (int cc = 0; cc < A.nch * kWaves; ++cc) {
+      const ArgPartial* q = P + (int64_t)jj * A.nch * kWaves + cc;
       arg_combine(v, i, q->best, q->idx);
       bad |= q->bad;
     }

@@ -88,12 +88,12 @@ def call_sample(lib, stage=None, **over):
 ])
 def test_sample_argument_errors(lib, over, want):
     assert call_sample(lib, **over) == want
-    for stage in (1, 2, 3, 4):
+    for stage in (1, 2):
         assert call_sample(lib, stage=stage, **over) == want
 
 
 def test_unknown_stage(lib):
-    assert call_sample(lib, stage=5) == -7
+    assert call_sample(lib, stage=3) == -7
     assert call_sample(lib, stage=0) == -7
     assert call_sample(lib, stage=-1) == -7
 

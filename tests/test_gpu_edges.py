@@ -146,10 +146,10 @@ def test_workspace_reuse_across_shapes_and_stages(gpu):
     _check(b, rb, "ws b")
     for k in ra1:
         assert np.array_equal(ra1[k], ra2[k], equal_nan=True)
-    # staged entry point: stages 1, 2, 3, 4 equal the full call
+    # staged entry point: stages 1, 2 equal the full call
     n = torch.empty(5, dtype=torch.int32, device="cuda")
     t = torch.empty((5, 4), dtype=torch.int32, device="cuda")
-    for stage in (1, 2, 3, 4):
+    for stage in (1, 2):
         gpu.spec_verify_sample_stage(stage, **ta, out_num_accepted=n, out_tokens=t, workspace=ws)
     torch.cuda.synchronize()
     assert np.array_equal(n.cpu().numpy(), ra1["n"]) and np.array_equal(t.cpu().numpy(), ra1["tokens"])
