@@ -13,7 +13,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspec_verify.so")
+# The in-tree build; SV_LIBRARY may name another build of the same library.
+LIB_PATH = os.environ.get("SV_LIBRARY") or os.path.join(HERE, "libspec_verify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_OK = 0

@@ -16,6 +16,7 @@ constexpr int kU1 = 4;                          // 16-byte units per lane per it
 constexpr int kU2 = 4;                          // 8-token octets per lane per residual step
 constexpr int kStepOctets = kWave * kU2;        // 256 octets = 2048 tokens per residual step (one wave)
 constexpr int kStepTokens = kStepOctets * 8;
+constexpr int kLdsSteps = 2048;                 // step masses kept in LDS up to this many steps (V <= 4.19M)
 constexpr int64_t kMinChunkBytes = 16 << 10;    // stats / argmax work unit bounds
 constexpr int64_t kMaxChunkBytes = 128 << 10;   // measured best for the stats kernel on MI355X
 constexpr int64_t kTargetWGs = 8192;            // ~32 workgroups per CU on 256 CUs
@@ -32,17 +33,33 @@ struct RowPartial {
 };
 
 // The finish kernel's per-sequence plan for the draw (held in LDS).
+//
+// Mass of token v of the drawn distribution, up to one positive factor per
+// sequence:
+//  form 1 (shifts folded into one FMA each):
+//    e_p = exp2(fma(x_t, kl, -cp)), e_q = exp2(fma(x_d, kl, -cq)),
+//    r = max(0, fma(e_q, corr, e_p - e_q)) after a rejection, r = e_p otherwise.
+//    cp = fp32(mp * kl); cq = fp32(mq * kl - log2(Sp / Sq) - (mp * kl - cp)),
+//    so e_q carries the ratio of the normalisers; corr = (exact cq - cq) * ln 2
+//    removes, to first order, the rounding of cq. r = F * Sp * max(0, p - q)
+//    with F = exp2(mp * kl - cp) (fscale).
+//  form 0 (used when a shift would leave the fp32 range):
+//    e_p = exp2((x_t - mp) * kl), e_q = exp2((x_d - mq) * kl),
+//    r = max(0, e_p - kappa e_q) with kappa = Sp / Sq as a float pair; F = 1.
 struct SeqPlan {
   int valid;   // 0: the sequence is invalid (all outputs -1)
   int n;       // accepted drafts
   int mode;    // kModeResidual (row n pair) or kModeBonus (target row n == gamma)
+  int form;    // 1: FMA shifts, 0: subtract-multiply
   float kl;    // log2(e) / T, fp32
-  float mp;    // reference (max) of target row n, logit units
-  float mq;    // reference (max) of draft row n
+  float mp;    // maximum of target row n, logit units
+  float mq;    // maximum of draft row n
   float kap_hi;  // kappa = Sp / Sq as a float pair (hi + lo)
   float kap_lo;
-  double sp;   // sum_v exp2((x_v - mp) * kl) over target row n
-  double sq;   // same for draft row n
+  float cp, cq, corr;
+  double sp;      // sum_v exp2((x_v - mp) * kl) over target row n
+  double sq;      // same for draft row n
+  double fscale;  // F
 };
 
 // Partial argmax of one wave's share of one chunk of one row (tree pass).

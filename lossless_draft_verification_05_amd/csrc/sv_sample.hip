@@ -191,28 +191,6 @@ __device__ __forceinline__ void load_octet(const char* row, int64_t oct, int V, 
   }
 }
 
-template <int TD, int DD>
-__device__ __forceinline__ void octet_mass(const char* trow, const char* drow, int64_t oct, int V, int mode,
-                                           const SeqPlan& P, float (&r)[8]) {
-  float xt[8];
-  load_octet<TD>(trow, oct, V, xt);
-  if (mode == kModeResidual) {
-    float xd[8];
-    load_octet<DD>(drow, oct, V, xd);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float ep = hw_exp2((xt[k] - P.mp) * P.kl);
-      const float eq = hw_exp2((xd[k] - P.mq) * P.kl);
-      float d = fmaf(-eq, P.kap_hi, ep);
-      d = fmaf(-eq, P.kap_lo, d);
-      r[k] = fmaxf(d, 0.0f);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = hw_exp2((xt[k] - P.mp) * P.kl);
-  }
-}
-
 __device__ __forceinline__ float sum8(const float (&r)[8]) {
   return ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
 }
@@ -251,74 +229,148 @@ struct OctetRaw<0> {
   }
 };
 
-template <int MODE>
+// Masses of 8 tokens (see SeqPlan for the two forms).
+template <int MODE, int FORM>
 __device__ __forceinline__ void mass8(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P, float (&r)[8]) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float ep = hw_exp2((xt[k] - P.mp) * P.kl);
-    if constexpr (MODE == kModeResidual) {
-      const float eq = hw_exp2((xd[k] - P.mq) * P.kl);
-      float d = fmaf(-eq, P.kap_hi, ep);
-      d = fmaf(-eq, P.kap_lo, d);
-      r[k] = fmaxf(d, 0.0f);
+    if constexpr (FORM == 1) {
+      const float ep = hw_exp2(fmaf(xt[k], P.kl, -P.cp));
+      if constexpr (MODE == kModeResidual) {
+        const float eq = hw_exp2(fmaf(xd[k], P.kl, -P.cq));
+        r[k] = fmaxf(fmaf(eq, P.corr, ep - eq), 0.0f);
+      } else {
+        r[k] = ep;
+      }
     } else {
-      r[k] = ep;
+      const float ep = hw_exp2((xt[k] - P.mp) * P.kl);
+      if constexpr (MODE == kModeResidual) {
+        const float eq = hw_exp2((xd[k] - P.mq) * P.kl);
+        float d = fmaf(-eq, P.kap_hi, ep);
+        d = fmaf(-eq, P.kap_lo, d);
+        r[k] = fmaxf(d, 0.0f);
+      } else {
+        r[k] = ep;
+      }
     }
   }
 }
 
-// Mass of one whole residual step (2048 tokens) of one wave: every load of the
-// step is issued before any arithmetic, so a wave keeps kU2 octets per row in
-// flight.
-template <int TD, int DD, int MODE>
-__device__ __forceinline__ double step_mass_full(const char* trow, const char* drow, int64_t s, const SeqPlan& P,
-                                                 int lane) {
-  OctetRaw<TD> t[kU2];
-  OctetRaw<DD> d[kU2];
-#pragma unroll
-  for (int j = 0; j < kU2; ++j) {
-    const int64_t oct = s * kStepOctets + kWave * j + lane;
-    t[j].load(trow, oct);
-    if constexpr (MODE == kModeResidual) d[j].load(drow, oct);
+template <int TD, int DD>
+__device__ __forceinline__ void octet_mass(const char* trow, const char* drow, int64_t oct, int V, int mode,
+                                           const SeqPlan& P, float (&r)[8]) {
+  float xt[8], xd[8];
+  load_octet<TD>(trow, oct, V, xt);
+  if (mode == kModeResidual) {
+    load_octet<DD>(drow, oct, V, xd);
+    if (P.form == 1)
+      mass8<kModeResidual, 1>(xt, xd, P, r);
+    else
+      mass8<kModeResidual, 0>(xt, xd, P, r);
+  } else {
+    if (P.form == 1)
+      mass8<kModeBonus, 1>(xt, xd, P, r);
+    else
+      mass8<kModeBonus, 0>(xt, xd, P, r);
   }
-  double lacc = 0.0;
-#pragma unroll
-  for (int j = 0; j < kU2; ++j) {
-    float xt[8], xd[8], rr[8];
-    t[j].unpack(xt);
-    if constexpr (MODE == kModeResidual) d[j].unpack(xd);
-    mass8<MODE>(xt, xd, P, rr);
-    lacc += (double)sum8(rr);
-  }
-  return lacc;
 }
 
-// Masses of the draw row(s) of sequence b over all steps; wave w of nw takes
-// steps w, w + nw, ... and lane 0 writes each step's mass.
+// Raw loads of half a step (1024 tokens) of the draw row(s) for one wave:
+// kU2 / 2 octets per lane per row. Only used where the step lies inside the row.
+constexpr int kHalfU = kU2 / 2;
 template <int TD, int DD, int MODE>
-__device__ void step_masses(const SampleLaunch& A, int b, const SeqPlan& P, int w, int nw) {
+struct HalfStep {
+  OctetRaw<TD> t[kHalfU];
+  OctetRaw<DD> d[kHalfU];
+  // half h (0 or 1) of step s: octets s * kStepOctets + kWave * (h * kHalfU + j) + lane
+  __device__ __forceinline__ void load(const char* trow, const char* drow, int64_t s, int h, int lane) {
+#pragma unroll
+    for (int j = 0; j < kHalfU; ++j) {
+      const int64_t oct = s * kStepOctets + kWave * (h * kHalfU + j) + lane;
+      t[j].load(trow, oct);
+      if constexpr (MODE == kModeResidual) d[j].load(drow, oct);
+    }
+  }
+  // This lane's share of the half step's mass, added to lacc in octet order.
+  template <int FORM>
+  __device__ __forceinline__ void mass(const SeqPlan& P, double& lacc) const {
+#pragma unroll
+    for (int j = 0; j < kHalfU; ++j) {
+      float xt[8], xd[8], rr[8];
+      t[j].unpack(xt);
+      if constexpr (MODE == kModeResidual) d[j].unpack(xd);
+      mass8<MODE, FORM>(xt, xd, P, rr);
+      lacc += (double)sum8(rr);
+    }
+  }
+};
+
+// Masses of the draw row(s) of sequence b over all steps; wave w of nw takes
+// steps w, w + nw, ... and lane 0 writes each step's mass to out[step].
+// Whole steps run as a two-buffer software pipeline over half steps: the loads
+// of the next half are in flight while the wave computes the current one, so
+// its memory and arithmetic overlap.
+template <int TD, int DD, int MODE, int FORM>
+__device__ __forceinline__ void step_masses(const SampleLaunch& A, int b, const SeqPlan& P, int w, int nw,
+                                            double* out) {
   const int lane = threadIdx.x & (kWave - 1);
   const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
   const char* drow = (MODE == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   const int full_steps = A.V / kStepTokens;  // steps that lie wholly inside the row
-  for (int s = w; s < A.ns2; s += nw) {
+  const int nmine = (full_steps > w) ? (full_steps - w + nw - 1) / nw : 0;  // this wave's whole steps
+  if (nmine > 0) {
+    // every load is unconditional inside its block, so no buffer is copied
+    // (a copy would wait for the loads in flight)
+    HalfStep<TD, DD, MODE> h0, h1;
+    h0.load(trow, drow, w, 0, lane);
+    int64_t st = w;
+    for (int i = 0; i + 1 < nmine; ++i, st += nw) {
+      double lacc = 0.0;
+      h1.load(trow, drow, st, 1, lane);
+      h0.template mass<FORM>(P, lacc);
+      h0.load(trow, drow, st + nw, 0, lane);
+      h1.template mass<FORM>(P, lacc);
+      const double tot = wave_sum(lacc);
+      if (lane == 0) out[st] = tot;
+    }
     double lacc = 0.0;
-    if (s < full_steps) {
-      lacc = step_mass_full<TD, DD, MODE>(trow, drow, s, P, lane);
-    } else {
+    h1.load(trow, drow, st, 1, lane);
+    h0.template mass<FORM>(P, lacc);
+    h1.template mass<FORM>(P, lacc);
+    const double tot = wave_sum(lacc);
+    if (lane == 0) out[st] = tot;
+  }
+  // the ragged last step (if any), octet by octet
+  for (int s = w + nmine * nw; s < A.ns2; s += nw) {
+    double lacc = 0.0;
 #pragma unroll
-      for (int j = 0; j < kU2; ++j) {
-        const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
-        if (oct < noct) {
-          float rr[8];
-          octet_mass<TD, DD>(trow, drow, oct, A.V, MODE, P, rr);
-          lacc += (double)sum8(rr);
-        }
+    for (int j = 0; j < kU2; ++j) {
+      const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
+      if (oct < noct) {
+        float rr[8];
+        octet_mass<TD, DD>(trow, drow, oct, A.V, MODE, P, rr);
+        lacc += (double)sum8(rr);
       }
     }
     const double tot = wave_sum(lacc);
-    if (lane == 0) A.steptot[(int64_t)b * A.ns2 + s] = tot;
+    if (lane == 0) out[s] = tot;
+  }
+}
+
+template <int TD, int DD>
+__device__ __forceinline__ void all_step_masses(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int w,
+                                                int nw, double* out) {
+  if (mode == kModeResidual) {
+    if (P.form == 1)
+      step_masses<TD, DD, kModeResidual, 1>(A, b, P, w, nw, out);
+    else
+      step_masses<TD, DD, kModeResidual, 0>(A, b, P, w, nw, out);
+  } else {
+    if (P.form == 1)
+      step_masses<TD, DD, kModeBonus, 1>(A, b, P, w, nw, out);
+    else
+      step_masses<TD, DD, kModeBonus, 0>(A, b, P, w, nw, out);
   }
 }
 
@@ -363,15 +415,19 @@ __device__ int wave_find(const double* arr, int len, double t, double& acc, int 
 // finish kernel: one 512-thread workgroup per sequence
 // ---------------------------------------------------------------------------
 template <int TD, int DD>
-__global__ __launch_bounds__(kFinThreads) void sv_finish_kernel(SampleLaunch A) {
+// At most 128 VGPRs, so that two 8-wave workgroups fit one CU.
+__global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))) void sv_finish_kernel(
+    SampleLaunch A) {
   __shared__ float rM[kMaxRows];
   __shared__ double rS[kMaxRows];
   __shared__ int rV[kMaxRows];
   __shared__ SeqPlan sP;
   __shared__ double sh_total;
   __shared__ int sh_y;
+  __shared__ double sh_steps[kLdsSteps];  // step masses when the row has at most kLdsSteps steps
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loops over steps stay scalar
   const int b = blockIdx.x;
   const float T = A.temps[b];
   const bool tv = temp_ok(T);
@@ -459,18 +515,32 @@ __global__ __launch_bounds__(kFinThreads) void sv_finish_kernel(SampleLaunch A) 
       Q.kl = kl;
       Q.mp = rM[n];
       Q.sp = rS[n];
+      const double kld = (double)kl;
+      const double cp = (double)Q.mp * kld;  // exact product of two floats
+      Q.cp = (float)cp;
+      const double dp = cp - (double)Q.cp;
+      Q.fscale = exp2(dp);
+      bool fma_ok = fabs(cp) < 0x1p100;
       if (n < G) {
         Q.mq = rM[G + 1 + n];
         Q.sq = rS[G + 1 + n];
         const double kap = Q.sp / Q.sq;
         Q.kap_hi = (float)kap;
         Q.kap_lo = (float)(kap - (double)Q.kap_hi);
+        const double cq = (double)Q.mq * kld - log2(kap) - dp;
+        Q.cq = (float)cq;
+        Q.corr = (float)((cq - (double)Q.cq) * 0.69314718055994530942);
+        fma_ok = fma_ok && fabs(cq) < 0x1p100;
       } else {
         Q.mq = 0.0f;
         Q.sq = 1.0;
         Q.kap_hi = 0.0f;
         Q.kap_lo = 0.0f;
+        Q.cq = 0.0f;
+        Q.corr = 0.0f;
       }
+      Q.form = fma_ok ? 1 : 0;
+      if (!fma_ok) Q.fscale = 1.0;
       sP = Q;
     }
   }
@@ -486,14 +556,19 @@ __global__ __launch_bounds__(kFinThreads) void sv_finish_kernel(SampleLaunch A) 
     return;
   }
 
-  // (4) masses of the drawn distribution, every wave on its steps
+  // (4) masses of the drawn distribution, every wave on its steps, into LDS
+  // when they fit, else the workspace. (The two calls differ only in the
+  // address space of the output, which keeps the stores of the streaming loop
+  // out of the generic path: after a generic store every wait for a load
+  // would drain all loads in flight.)
   int mode = P.mode;
-  if (mode == kModeResidual)
-    step_masses<TD, DD, kModeResidual>(A, b, P, w, kFinWaves);
+  const bool lds_steps = A.ns2 <= kLdsSteps;
+  double* stot = lds_steps ? sh_steps : A.steptot + (int64_t)b * A.ns2;
+  if (lds_steps)
+    all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, sh_steps);
   else
-    step_masses<TD, DD, kModeBonus>(A, b, P, w, kFinWaves);
+    all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, A.steptot + (int64_t)b * A.ns2);
   __syncthreads();  // every wave's step masses are visible to wave 0
-  const double* stot = A.steptot + (int64_t)b * A.ns2;
   if (w == 0) {
     const double tot = wave_total(stot, A.ns2, lane);
     if (lane == 0) sh_total = tot;
@@ -502,7 +577,10 @@ __global__ __launch_bounds__(kFinThreads) void sv_finish_kernel(SampleLaunch A) 
   if (!(sh_total > 0.0) && mode == kModeResidual) {
     // Nothing left after the rejection (p_n == q_n up to rounding): draw from p_n.
     mode = kModeBonus;
-    step_masses<TD, DD, kModeBonus>(A, b, P, w, kFinWaves);
+    if (lds_steps)
+      all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, sh_steps);
+    else
+      all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, A.steptot + (int64_t)b * A.ns2);
     __syncthreads();
     if (w == 0) {
       const double tot = wave_total(stot, A.ns2, lane);
@@ -586,7 +664,7 @@ __global__ __launch_bounds__(kFinThreads) void sv_finish_kernel(SampleLaunch A) 
     otok[k] = (k < n) ? A.tokens[(int64_t)b * G + k] : (k == n ? y : -1);
   if (tid == 0) {
     A.out_n[b] = n;
-    if (A.diag_mass) A.diag_mass[b] = (float)(total / P.sp);
+    if (A.diag_mass) A.diag_mass[b] = (float)(total / (P.sp * P.fscale));
   }
 }
 
