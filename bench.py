@@ -128,6 +128,17 @@ def sample_bytes(cfg, B, G, V, n_acc=None):
     return s1, s2
 
 
+def early_exit_bytes(cfg, B, G, V, n_acc):
+    """Bytes the early-exit path must move: target rows 0..n and draft rows
+    0..min(n, gamma-1) of every sequence (all rows for an invalid one), the
+    draw row(s) again, per-position inputs and outputs."""
+    bt, bd = esz(cfg.target_dtype), esz(cfg.draft_dtype)
+    n = np.where(n_acc < 0, G, n_acc).astype(np.int64)
+    stats = int(((n + 1) * V * bt + (np.minimum(n, G - 1) + 1) * V * bd).sum())
+    _, s2 = sample_bytes(cfg, B, G, V, n_acc)
+    return stats + s2 + B * (G * 4 + (G + 1) * 4 + 4)
+
+
 # ----------------------------------------------------------------------------
 def traffic_from_profiles(workload: str, sha: str):
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
@@ -163,6 +174,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--early-exit", action="store_true",
+                    help="time spec_verify_sample_early_exit (rows after a first rejection are not read)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -255,7 +268,14 @@ def main():
             return lambda: binding.spec_verify_sample_stage(stage, tcopies[c], dcopies[c], tokens, uni, temps,
                                                             out_num_accepted=out_n, out_tokens=out_t, workspace=ws)
 
+        def early_call(c):
+            return lambda: binding.spec_verify_sample_early_exit(tcopies[c], dcopies[c], tokens, uni, temps,
+                                                                 out_num_accepted=out_n, out_tokens=out_t,
+                                                                 workspace=ws)
+
         def stages(c):
+            if args.early_exit:
+                return [early_call(c)]
             return [stage_call(k, c) for k in (1, 2)]
         units = B * G
         unit = "positions/s"
@@ -265,6 +285,9 @@ def main():
                     "target_dtype": cfg.target_dtype, "draft_dtype": cfg.draft_dtype, "temperature": tdesc,
                     "seed": args.seed}
         kernel_names = ["sv_stats_kernel", "sv_finish_kernel"]
+        if args.early_exit:
+            kernel_names = ["spec_verify_sample_early_exit"]
+            cfg_desc["entry_point"] = "spec_verify_sample_early_exit"
 
     torch.cuda.synchronize()
     for k in range(args.warmup):
@@ -305,8 +328,12 @@ def main():
         detail["mean_accepted"] = float(n_acc[valid].mean())
         detail["mean_tokens_per_verify"] = float(n_acc[valid].mean() + 1)
         detail["invalid"] = int((~valid).sum())
-        detail["kernels"]["sv_finish_kernel"]["alg_bytes"] = int(s2_bytes)
-        detail["kernels"]["sv_finish_kernel"]["gbps"] = round(s2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1)
+        if args.early_exit:
+            s1_bytes = step_bytes = early_exit_bytes(inp.cfg, B, G, V, n_acc)
+            detail["one_pass_step_alg_bytes"] = int(s1_bytes + s2_bytes)
+        else:
+            detail["kernels"]["sv_finish_kernel"]["alg_bytes"] = int(s2_bytes)
+            detail["kernels"]["sv_finish_kernel"]["gbps"] = round(s2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1)
     detail["kernels"][kernel_names[0]]["alg_bytes"] = int(s1_bytes)
     detail["kernels"][kernel_names[0]]["gbps"] = round(s1_bytes / (stage_ms[0] * 1e-3) / 1e9, 1)
     detail["step_alg_bytes"] = int(step_bytes)

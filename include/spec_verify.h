@@ -123,6 +123,30 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spec_verify_sample_early_exit -- spec_verify_sample that reads no row after
+ * a sequence's first rejection.
+ *
+ * Defines: [SD] "The pith" (the longest accepted prefix is kept: nothing after
+ * the first rejection can change the output). Same arguments, outputs,
+ * validity rules and workspace as spec_verify_sample, and the same outputs for
+ * the same inputs: the accept decisions use the same statistics, merged in the
+ * same order. The work is ordered by position: one statistics launch per
+ * position 0..gamma, in which each workgroup first re-derives the accept
+ * decision of the position before it and streams its rows only if that
+ * position was accepted, then the finish kernel. Data moved: the rows of
+ * positions 0..n (plus the draw row(s)) instead of all 2*gamma+1 rows.
+ * Differences: diag p_x, q_x are NaN for positions after n (their rows are not
+ * read); gamma + 2 kernel launches instead of 2.
+ */
+int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, int64_t target_seq_stride,
+                                  int64_t target_row_stride, const void* draft_logits, int draft_dtype,
+                                  int64_t draft_seq_stride, int64_t draft_row_stride,
+                                  const int32_t* draft_tokens, const float* uniforms, const float* temperature,
+                                  int B, int gamma, int V, int32_t* out_num_accepted, int32_t* out_tokens,
+                                  const sv_sample_diag* diag, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * spec_verify_sample_stage -- one of the two kernels of spec_verify_sample,
  * for callers that want to time or overlap them. Same arguments and meaning as
  * spec_verify_sample; `stage` selects:

@@ -31,6 +31,8 @@ SIGNATURES = {
                                   _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sample_stage": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32,
                                         _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample_early_exit": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
+                                             _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy_tree": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                        _sz, _vp]),
     "spec_verify_greedy_tree_stage": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
@@ -185,6 +187,9 @@ def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_
     if stage is None:
         st = lib.spec_verify_sample(*args)
         _check(st, "spec_verify_sample")
+    elif stage == "early_exit":
+        st = lib.spec_verify_sample_early_exit(*args)
+        _check(st, "spec_verify_sample_early_exit")
     else:
         st = lib.spec_verify_sample_stage(stage, *args)
         _check(st, f"spec_verify_sample_stage({stage})")
@@ -203,6 +208,14 @@ def spec_verify_sample(target, draft, draft_tokens, uniforms, temperature, *, ou
     """
     return _sample_call(None, target, draft, draft_tokens, uniforms, temperature, out_num_accepted, out_tokens,
                         diag, workspace, stream)
+
+
+def spec_verify_sample_early_exit(target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
+                                  out_tokens=None, diag=False, workspace=None, stream=None):
+    """spec_verify_sample that reads no row after a sequence's first rejection: same arguments and
+    outputs (diag p_x, q_x are NaN after the first rejection)."""
+    return _sample_call("early_exit", target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
+                        out_tokens, diag, workspace, stream)
 
 
 def spec_verify_sample_stage(stage, target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,

@@ -11,6 +11,7 @@
 
 namespace sv {
 hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stage, hipStream_t stream);
+hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int pos, hipStream_t stream);
 hipError_t launch_tree(const TreeLaunch& A, int dt, int stage, hipStream_t stream);
 
 static thread_local int g_last_hip_error = 0;
@@ -134,6 +135,21 @@ static int run_sample(int first, int last, const SampleArgs& a, hipStream_t stre
   return SV_OK;
 }
 
+// Early exit: one statistics launch per position 0..gamma (each gated on the
+// accept decision of the position before it), then the finish kernel.
+static int run_sample_early(const SampleArgs& a, hipStream_t stream) {
+  int st = validate_sample(a);
+  if (st) return st;
+  SampleLaunch L = plan_sample(a);
+  if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
+  L.reach = (int32_t*)((char*)a.ws + sample_layout(a.B, a.gamma, a.V).off_reach);
+  for (int pos = 0; pos <= a.gamma; ++pos) {
+    st = hip_status(launch_sample_pos(L, a.tdt, a.ddt, pos, stream));
+    if (st) return st;
+  }
+  return hip_status(launch_sample_stage(L, a.tdt, a.ddt, 2, stream));
+}
+
 }  // namespace sv
 
 using namespace sv;
@@ -173,6 +189,18 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
   return run_sample(1, 2, a, (hipStream_t)stream);
+}
+
+int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, int64_t target_seq_stride,
+                                  int64_t target_row_stride, const void* draft_logits, int draft_dtype,
+                                  int64_t draft_seq_stride, int64_t draft_row_stride, const int32_t* draft_tokens,
+                                  const float* uniforms, const float* temperature, int B, int gamma, int V,
+                                  int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
+               draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
+               out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
+  return run_sample_early(a, (hipStream_t)stream);
 }
 
 static int run_tree(int first, int last, const void* target_logits, int dtype, int64_t seq_stride,

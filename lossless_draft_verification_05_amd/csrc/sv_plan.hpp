@@ -92,6 +92,7 @@ struct SampleLaunch {
   // workspace
   RowPartial* part;  // [B][per_seq][kWaves]
   double* steptot;   // [B][ns2]
+  int32_t* reach;    // [B] early exit only (else null): rows 0..reach-1 have statistics
 };
 
 struct TreeLaunch {
@@ -138,7 +139,7 @@ inline int64_t max_chunks_per_row(int64_t V) { return ceil_div(V * 4, kMinChunkB
 inline int64_t align256(int64_t x) { return round_up(x, 256); }
 
 struct SampleLayout {
-  int64_t off_part, off_step, total;
+  int64_t off_part, off_step, off_reach, total;
 };
 
 inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
@@ -150,6 +151,8 @@ inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
   o += align256(B * (2 * gamma + 1) * max_chunks_per_row(V) * kWaves * (int64_t)sizeof(RowPartial));
   L.off_step = o;
   o += align256(B * draw_steps(V) * 8);
+  L.off_reach = o;
+  o += align256(B * 4);
   L.total = o;
   return L;
 }

@@ -111,19 +111,15 @@ __device__ __forceinline__ float load_elem(const char* row, int v) {
 }
 
 // ---------------------------------------------------------------------------
-// stats kernel
+// stats kernels
 // ---------------------------------------------------------------------------
+// Partials of chunk slot r of sequence b: slots [0, (gamma+1) * nct) are the
+// target rows' chunks (row r / nct, chunk r % nct), the rest the draft rows'.
+// One partial per wave: (reference, sum relative to it, max).
 template <int TD, int DD>
-__global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
+__device__ __forceinline__ void stats_chunk(const SampleLaunch& A, int b, int r, float kl) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const int64_t wg = blockIdx.x;
-  const int b = (int)(wg / A.per_seq);
-  const int r = (int)(wg % A.per_seq);
-  const float T = A.temps[b];
-  const float kl = temp_ok(T) ? log2e_over(T) : 1.0f;
-  const int G = A.gamma;
-  const int tchunks = (G + 1) * A.nct;
-
+  const int tchunks = (A.gamma + 1) * A.nct;
   SumExp st{-FLT_MAX, -INFINITY, 0.0};
   if (r < tchunks) {
     const int row = r / A.nct, c = r % A.nct;
@@ -141,8 +137,6 @@ __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
     const int64_t u1 = u0 + A.cud < nu ? u0 + A.cud : nu;
     stream_sumexp<DD>(p, A.V, u0, u1, kl, st);
   }
-
-  // one partial per wave: (reference, sum relative to it, max)
   const float M = wave_max(st.m_ref);
   double s = st.s * (double)hw_exp2((st.m_ref - M) * kl);
   s = wave_sum(s);
@@ -152,8 +146,133 @@ __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
     rp.m_ref = M;
     rp.m_true = mt;
     rp.s = s;
-    A.part[wg * kWaves + w] = rp;
+    A.part[((int64_t)b * A.per_seq + r) * kWaves + w] = rp;
   }
+}
+
+// Statistics of a whole row from its nrec wave partials, computed by one wave
+// (every lane gets the result). Used by the finish kernel and by the gate of
+// the early-exit stats kernel, which must reach the same accept decisions bit
+// for bit; contraction is off so that inlining cannot change the rounding.
+struct RowStat {
+  float m;   // maximum
+  double s;  // sum_v exp2((x_v - m) * kl)
+  int valid;
+};
+__device__ __forceinline__ RowStat merge_row(const RowPartial* P, int nrec, float kl, bool tv, int lane) {
+#pragma clang fp contract(off)
+  float Mr = -FLT_MAX, mtr = -INFINITY;
+  for (int k = lane; k < nrec; k += kWave) {
+    Mr = fmaxf(Mr, P[k].m_ref);
+    mtr = fmaxf(mtr, P[k].m_true);
+  }
+  Mr = wave_max(Mr);
+  mtr = wave_max(mtr);
+  double S = 0.0;
+  for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(((double)P[k].m_ref - (double)Mr) * (double)kl);
+  S = wave_sum(S);
+  RowStat r;
+  r.m = mtr;
+  r.s = S * exp2(((double)Mr - (double)mtr) * (double)kl);
+  r.valid = tv && __builtin_isfinite(r.s) && r.s > 0.0 && __builtin_isfinite(mtr);
+  return r;
+}
+
+// Accept test of one position: rho = p(x) / q(x) in the log2 domain in fp64;
+// code 1 accepted, 0 rejected, 2 invalid; p(x), q(x) for the diagnostics (NaN
+// when invalid).
+struct AcceptOut {
+  int code;
+  float px, qx;
+};
+__device__ __forceinline__ AcceptOut accept_test(float lt, float ld, const RowStat& t, const RowStat& d, float kl,
+                                                 float u, bool tok_ok, bool tv) {
+#pragma clang fp contract(off)
+  AcceptOut o;
+  o.px = __builtin_nanf("");
+  o.qx = __builtin_nanf("");
+  const bool ok = tv && t.valid && d.valid && tok_ok && u >= 0.0f && u < 1.0f && ld != -INFINITY;
+  if (ok) {
+    const double lp2 = ((double)lt - (double)t.m) * (double)kl;
+    const double lq2 = ((double)ld - (double)d.m) * (double)kl;
+    const double rho = exp2(lp2 - lq2) * (d.s / t.s);
+    o.px = (float)(exp2(lp2) / t.s);
+    o.qx = (float)(exp2(lq2) / d.s);
+    o.code = ((double)u < rho) ? 1 : 0;
+  } else {
+    o.code = 2;
+  }
+  return o;
+}
+
+// One pass: one workgroup per (sequence, chunk slot) over every row.
+template <int TD, int DD>
+__global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
+  const int64_t wg = blockIdx.x;
+  const int b = (int)(wg / A.per_seq);
+  const int r = (int)(wg % A.per_seq);
+  const float T = A.temps[b];
+  const float kl = temp_ok(T) ? log2e_over(T) : 1.0f;
+  stats_chunk<TD, DD>(A, b, r, kl);
+}
+
+// Early exit: the statistics of position pos only (target row pos and, for
+// pos < gamma, draft row pos), one workgroup per (sequence, chunk of those
+// rows). reach[b] = k records that positions 0..k-2 were accepted, so rows
+// 0..k-1 have statistics. For pos > 0 a workgroup first re-derives the accept
+// decision of position pos - 1 from that position's partials (every workgroup
+// of the sequence derives the same one) and streams its chunk only after an
+// acceptance; after a rejection the sequence's later rows are never read.
+template <int TD, int DD>
+__global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, int pos) {
+  __shared__ RowStat sh_rs[2];
+  __shared__ float sh_g[2];
+  __shared__ int sh_go;
+  const int G = A.gamma;
+  const int cps = A.nct + (pos < G ? A.ncd : 0);
+  const int64_t wg = blockIdx.x;
+  const int b = (int)(wg / cps);
+  const int c = (int)(wg % cps);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float T = A.temps[b];
+  const bool tv = temp_ok(T);
+  const float kl = tv ? log2e_over(T) : 1.0f;
+  if (pos == 0) {
+    if (tid == 0) A.reach[b] = 1;  // every workgroup of the sequence writes the same value
+  } else {
+    if (A.reach[b] < pos) return;  // the sequence stopped at an earlier position
+    const int i = pos - 1;
+    if (w < 2) {
+      // wave 0 merges target row i, wave 1 draft row i
+      const int nrec = (w == 0 ? A.nct : A.ncd) * kWaves;
+      const int base = (w == 0) ? i * A.nct : (G + 1) * A.nct + i * A.ncd;
+      const RowStat rs = merge_row(A.part + ((int64_t)b * A.per_seq + base) * kWaves, nrec, kl, tv, lane);
+      if (lane == 0) sh_rs[w] = rs;
+    } else if (w == 2 && lane == 0) {
+      // the two logits of draft token x_i
+      const int xi = A.tokens[(int64_t)b * G + i];
+      float lt = 0.0f, ld = 0.0f;
+      if (xi >= 0 && xi < A.V) {
+        lt = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)i * A.t_row_b, xi);
+        ld = load_elem<DD>(A.dft + (int64_t)b * A.d_seq_b + (int64_t)i * A.d_row_b, xi);
+      }
+      sh_g[0] = lt;
+      sh_g[1] = ld;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const int xi = A.tokens[(int64_t)b * G + i];
+      const float ui = A.uniforms[(int64_t)b * (G + 1) + i];
+      const AcceptOut ao = accept_test(sh_g[0], sh_g[1], sh_rs[0], sh_rs[1], kl, ui, xi >= 0 && xi < A.V, tv);
+      sh_go = ao.code == 1;
+      if (ao.code == 1) A.reach[b] = pos + 1;
+    }
+    __syncthreads();
+    if (!sh_go) return;
+  }
+  const int r = (c < A.nct) ? pos * A.nct + c : (G + 1) * A.nct + pos * A.ncd + (c - A.nct);
+  stats_chunk<TD, DD>(A, b, r, kl);
 }
 
 // ---------------------------------------------------------------------------
@@ -434,12 +553,15 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   const float kl = tv ? log2e_over(T) : 1.0f;
   const int G = A.gamma;
   const int tchunks = (G + 1) * A.nct;
+  // rows 0..nst-1 (target and draft) have statistics: all of them after the
+  // one-pass stats kernel, those up to the first rejection after early exit
+  const int nst = A.reach ? min(max(A.reach[b], 0), G + 1) : G + 1;
 
   // (1) gathers of p(x), q(x) do not depend on the merge: issue them first
   int xi = 0;
   float ui = 0.0f, lt = 0.0f, ld = 0.0f;
   bool tok_ok = false;
-  if (w == 0 && lane < G) {
+  if (w == 0 && lane < G && lane < nst) {
     xi = A.tokens[(int64_t)b * G + lane];
     ui = A.uniforms[(int64_t)b * (G + 1) + lane];
     tok_ok = xi >= 0 && xi < A.V;
@@ -452,51 +574,48 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   // (2) merge the partials of every row: one wave per row, lanes over partials
   const int nrows = 2 * G + 1;
   for (int t = w; t < nrows; t += kFinWaves) {
-    int nrec, base;
+    int nrec, base, pos;
     if (t <= G) {
       nrec = A.nct * kWaves;
       base = t * A.nct;
+      pos = t;
     } else {
       nrec = A.ncd * kWaves;
       base = tchunks + (t - G - 1) * A.ncd;
+      pos = t - G - 1;
     }
-    const RowPartial* P = A.part + ((int64_t)b * A.per_seq + base) * kWaves;
-    float Mr = -FLT_MAX, mtr = -INFINITY;
-    for (int k = lane; k < nrec; k += kWave) {
-      Mr = fmaxf(Mr, P[k].m_ref);
-      mtr = fmaxf(mtr, P[k].m_true);
+    if (pos >= nst) {
+      if (lane == 0) {
+        rM[t] = 0.0f;
+        rS[t] = 0.0;
+        rV[t] = 0;
+      }
+      continue;
     }
-    Mr = wave_max(Mr);
-    mtr = wave_max(mtr);
-    double S = 0.0;
-    for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(((double)P[k].m_ref - (double)Mr) * (double)kl);
-    S = wave_sum(S);
-    const double St = S * exp2(((double)Mr - (double)mtr) * (double)kl);
+    const RowStat rs = merge_row(A.part + ((int64_t)b * A.per_seq + base) * kWaves, nrec, kl, tv, lane);
     if (lane == 0) {
-      rM[t] = mtr;
-      rS[t] = St;
-      rV[t] = tv && __builtin_isfinite(St) && St > 0.0 && __builtin_isfinite(mtr);
+      rM[t] = rs.m;
+      rS[t] = rs.s;
+      rV[t] = rs.valid;
     }
   }
   __syncthreads();
 
-  // (3) accept tests and first rejection (wave 0)
+  // (3) accept tests and first rejection (wave 0); code 3: position not reached
+  // (early exit stopped before it)
   if (w == 0) {
     int code = 1;  // 1 accepted, 0 rejected, 2 invalid
     if (lane < G) {
       const int i = lane;
-      const bool ok = tv && rV[i] && rV[G + 1 + i] && tok_ok && ui >= 0.0f && ui < 1.0f && ld != -INFINITY;
       float pxo = __builtin_nanf(""), qxo = __builtin_nanf("");
-      if (ok) {
-        const double lp2 = ((double)lt - (double)rM[i]) * (double)kl;
-        const double lq2 = ((double)ld - (double)rM[G + 1 + i]) * (double)kl;
-        const double Sp = rS[i], Sq = rS[G + 1 + i];
-        const double rho = exp2(lp2 - lq2) * (Sq / Sp);
-        pxo = (float)(exp2(lp2) / Sp);
-        qxo = (float)(exp2(lq2) / Sq);
-        code = ((double)ui < rho) ? 1 : 0;
+      if (i < nst) {
+        const RowStat ts{rM[i], rS[i], rV[i]}, ds{rM[G + 1 + i], rS[G + 1 + i], rV[G + 1 + i]};
+        const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv);
+        code = ao.code;
+        pxo = ao.px;
+        qxo = ao.qx;
       } else {
-        code = 2;
+        code = 3;
       }
       if (A.diag_px) A.diag_px[(int64_t)b * G + i] = pxo;
       if (A.diag_qx) A.diag_qx[(int64_t)b * G + i] = qxo;
@@ -506,7 +625,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     const int code_n = __builtin_amdgcn_readlane(code, n < G ? n : 0);
     if (lane == 0) {
       const float ug = A.uniforms[(int64_t)b * (G + 1) + G];
-      bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f;
+      bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f && n < nst;
       if (n == G) valid = valid && rV[G];
       SeqPlan Q;
       Q.valid = valid;
@@ -681,11 +800,26 @@ static hipError_t launch_pair(const SampleLaunch& A, int stage, hipStream_t stre
   return hipGetLastError();
 }
 
+template <int TD, int DD>
+static hipError_t launch_pos(const SampleLaunch& A, int pos, hipStream_t stream) {
+  const int64_t cps = A.nct + (pos < A.gamma ? A.ncd : 0);
+  hipLaunchKernelGGL((sv_stats_pos_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * cps)), dim3(kThreads), 0, stream,
+                     A, pos);
+  return hipGetLastError();
+}
+
 hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stage, hipStream_t stream) {
   if (tdt == 1 && ddt == 1) return launch_pair<1, 1>(A, stage, stream);
   if (tdt == 1 && ddt == 0) return launch_pair<1, 0>(A, stage, stream);
   if (tdt == 0 && ddt == 1) return launch_pair<0, 1>(A, stage, stream);
   return launch_pair<0, 0>(A, stage, stream);
+}
+
+hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int pos, hipStream_t stream) {
+  if (tdt == 1 && ddt == 1) return launch_pos<1, 1>(A, pos, stream);
+  if (tdt == 1 && ddt == 0) return launch_pos<1, 0>(A, pos, stream);
+  if (tdt == 0 && ddt == 1) return launch_pos<0, 1>(A, pos, stream);
+  return launch_pos<0, 0>(A, pos, stream);
 }
 
 }  // namespace sv

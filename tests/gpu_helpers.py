@@ -64,13 +64,42 @@ def sample_tensors(inp, device="cuda", pad_to=None):
                 temperature=torch.from_numpy(inp.temperature).to(device))
 
 
-def run_sample(binding, tens, diag=True, workspace=None):
-    n, tok, d = binding.spec_verify_sample(**tens, diag=diag, workspace=workspace)
+def run_sample(binding, tens, diag=True, workspace=None, early_exit=False):
+    fn = binding.spec_verify_sample_early_exit if early_exit else binding.spec_verify_sample
+    n, tok, d = fn(**tens, diag=diag, workspace=workspace)
     torch.cuda.synchronize()
     out = {"n": n.cpu().numpy(), "tokens": tok.cpu().numpy()}
     if d:
         out.update({k: v.cpu().numpy() for k, v in d.items()})
     return out
+
+
+def same_as_one_pass(one, ee):
+    """Early exit against the one-pass call on the same inputs: n and tokens
+    equal; for valid sequences p(x), q(x) of positions 0..n and the drawn
+    distribution's mass equal bit for bit (same statistics, same merge order)
+    and p(x), q(x) NaN after n. Returns a list of differences."""
+    bad = []
+    if not np.array_equal(one["n"], ee["n"]):
+        idx = np.flatnonzero(one["n"] != ee["n"])
+        bad.append(("n", idx[:5].tolist(), one["n"][idx[:5]].tolist(), ee["n"][idx[:5]].tolist()))
+    if not np.array_equal(one["tokens"], ee["tokens"]):
+        bad.append(("tokens", np.flatnonzero((one["tokens"] != ee["tokens"]).any(axis=1))[:5].tolist()))
+    if "p_x" in one and "p_x" in ee:
+        B, G = one["p_x"].shape
+        for b in range(B):
+            n = int(one["n"][b])
+            if n < 0 or n != int(ee["n"][b]):
+                continue
+            k = min(n + 1, G)
+            for key in ("p_x", "q_x"):
+                if not np.array_equal(one[key][b, :k].view(np.uint32), ee[key][b, :k].view(np.uint32)):
+                    bad.append((key, b))
+                if not np.isnan(ee[key][b, k:]).all():
+                    bad.append((key + " after n", b))
+            if one["resid_mass"][b].view(np.uint32) != ee["resid_mass"][b].view(np.uint32):
+                bad.append(("resid_mass", b))
+    return bad
 
 
 class Tally:

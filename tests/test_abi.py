@@ -72,6 +72,8 @@ def call_sample(lib, stage=None, **over):
             a["stream"]]
     if stage is None:
         return lib.spec_verify_sample(*args)
+    if stage == "early_exit":
+        return lib.spec_verify_sample_early_exit(*args)
     return lib.spec_verify_sample_stage(stage, *args)
 
 
@@ -88,7 +90,7 @@ def call_sample(lib, stage=None, **over):
 ])
 def test_sample_argument_errors(lib, over, want):
     assert call_sample(lib, **over) == want
-    for stage in (1, 2):
+    for stage in (1, 2, "early_exit"):
         assert call_sample(lib, stage=stage, **over) == want
 
 

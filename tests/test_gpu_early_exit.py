@@ -1,0 +1,109 @@
+"""GPU tests of the early-exit sampling verify (rows after a sequence's first
+rejection are never read): against the fp64 oracle with the parity contract,
+and against the one-pass entry point on the same inputs (same outputs bit for
+bit). Small multi-tile cases, the full-size workloads in the launch
+configuration the benchmark times, extreme gamma and the edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import gpu_helpers as H
+from tests import sample_cases as SC
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(gpu, inp, pad=None, seqs=None, name="", allow_flags=2, workspace=None):
+    tens = H.sample_tensors(inp, pad_to=pad)
+    one = H.run_sample(gpu, tens, workspace=workspace)
+    ee = H.run_sample(gpu, tens, workspace=workspace, early_exit=True)
+    bad = H.same_as_one_pass(one, ee)
+    assert not bad, (name, bad[:5])
+    t = H.check_sample(inp, ee, seqs)
+    H.log(f"[early exit {name}] {t.summary()}")
+    assert not t.fail, t.fail[:5]
+    assert t.flagged <= max(allow_flags, 0.01 * t.checked)
+    return ee
+
+
+@pytest.mark.parametrize("tdt,ddt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("V,pad", [(5000, None), (4099, 8)])
+def test_small_multitile(gpu, tdt, ddt, V, pad):
+    H.log(f"early exit small multitile tdt={tdt} ddt={ddt} V={V} pad={pad}")
+    inp = synth.make_custom_sample(6, 3, V, tdt, ddt, T=[0.5, 0.9, 1.0, 1.3, 2.0, 0.7], noise_sd=0.8, seed=V + 1)
+    _both(gpu, inp, pad=pad, name=f"{tdt}/{ddt} V={V}")
+
+
+def test_config1_tiny(gpu):
+    H.log("early exit config 1: 10^4 trials, gamma=4, V=32, shared logits")
+    _both(gpu, synth.make_sample_inputs(1, seed=0), name="config1")
+
+
+def test_config2(gpu):
+    H.log("early exit config 2: B=64 gamma=4 V=32000 bf16")
+    _both(gpu, synth.make_sample_inputs(2, seed=0), name="config2")
+
+
+def test_config3(gpu):
+    H.log("early exit config 3: B=256 gamma=8 V=128256 bf16 (all vs one pass, 32 vs oracle)")
+    inp = synth.make_sample_inputs(3, seed=0)
+    seqs = sorted(set(np.random.default_rng(33).choice(inp.B, 30, replace=False).tolist()) | {0, inp.B - 1})
+    ee = _both(gpu, inp, seqs=seqs, name="config3")
+    assert (ee["n"] >= 0).all()
+
+
+def test_config5(gpu):
+    H.log("early exit config 5: B=512 gamma=5 V=256000 bf16/fp32 (all vs one pass, 24 vs oracle)")
+    inp = synth.make_sample_inputs(5, seed=0)
+    rng = np.random.default_rng(55)
+    seqs = []
+    for cls in (0, 1, 2):
+        seqs += rng.choice(np.flatnonzero(inp.row_class == cls), 8, replace=False).tolist()
+    ee = _both(gpu, inp, seqs=sorted(seqs), name="config5")
+    assert (ee["n"][inp.row_class == 2] == inp.gamma).all()
+
+
+@pytest.mark.parametrize("G", [1, 16, 64])
+def test_gamma_extremes(gpu, G):
+    H.log(f"early exit gamma={G}")
+    inp = synth.make_custom_sample(5, G, 3000, "bf16", "f32", T=1.0, noise_sd=0.3, seed=G + 100)
+    _both(gpu, inp, name=f"gamma {G}")
+
+
+@pytest.mark.parametrize("case", ["masks_and_signed_zero", "identical_and_disjoint", "invalid_inputs",
+                                  "unconsulted_positions", "invalid_after_accepts"])
+def test_edge_cases(gpu, case):
+    H.log(f"early exit edge case {case}")
+    inp = getattr(SC, case)()
+    ee = _both(gpu, inp, name=case)
+    if case == "invalid_inputs":
+        assert (ee["n"] == -1).all()
+    if case == "invalid_after_accepts":
+        assert list(ee["n"]) == [-1, -1, -1, 1]
+
+
+def test_garbage_workspace_and_alternation(gpu):
+    """The workspace needs no initialisation, and the two entry points can
+    share one workspace in any order."""
+    H.log("early exit garbage workspace")
+    ws = gpu.Workspace()
+    ws.buf = torch.randint(0, 255, (64 << 20,), dtype=torch.uint8, device="cuda")
+    a = SC.custom(9, 6, 5000, "bf16", "bf16", seed=21)
+    b = SC.custom(3, 2, 800, "f32", "bf16", seed=22)
+    ta, tb = H.sample_tensors(a), H.sample_tensors(b)
+    ref_a = H.run_sample(gpu, ta, early_exit=True)
+    for early in (True, False, True):
+        H.run_sample(gpu, tb, workspace=ws, early_exit=not early)
+        r = H.run_sample(gpu, ta, workspace=ws, early_exit=early)
+        assert np.array_equal(r["n"], ref_a["n"]) and np.array_equal(r["tokens"], ref_a["tokens"])
+    assert not H.check_sample(a, ref_a).fail
+
+
+def test_repeat_calls_bit_identical(gpu):
+    inp = SC.custom(16, 5, 20000, "bf16", "f32", seed=23)
+    tens = H.sample_tensors(inp)
+    r1 = H.run_sample(gpu, tens, early_exit=True)
+    r2 = H.run_sample(gpu, tens, early_exit=True)
+    for k in r1:
+        assert np.array_equal(r1[k].view(np.uint8), r2[k].view(np.uint8)), k

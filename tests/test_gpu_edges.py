@@ -8,6 +8,7 @@ import torch
 import synth
 from oracle import spec_verify_oracle as O
 from tests import gpu_helpers as H
+from tests import sample_cases as SC
 
 pytestmark = pytest.mark.gpu
 
@@ -50,36 +51,16 @@ def test_batch_of_one(gpu):
     _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), "B=1")
 
 
-def _custom(B=6, G=4, V=1024, tdt="f32", ddt="f32", seed=0):
-    return synth.make_custom_sample(B, G, V, tdt, ddt, T=1.0, seed=seed)
+_custom = SC.custom
 
 
 def test_masks_and_signed_zero(gpu):
-    inp = _custom(8, 4, 1000, "bf16", "bf16", seed=2)
-    g = np.random.default_rng(2)
-    ninf = synth.f32_to_bf16_bits(np.array([-np.inf], np.float32))[0]
-    mz = synth.f32_to_bf16_bits(np.array([-0.0], np.float32))[0]
-    for arr in (inp.target, inp.draft):
-        m = g.random(arr.shape) < 0.3
-        arr[m] = ninf
-        arr[g.random(arr.shape) < 0.05] = mz
-        arr[g.random(arr.shape) < 0.05] = 0
-    # keep every draft token drawable
-    for b in range(inp.B):
-        for i in range(inp.gamma):
-            inp.draft[b, i, inp.tokens[b, i]] = 0
+    inp = SC.masks_and_signed_zero()
     _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), "masks")
 
 
 def test_identical_and_disjoint_rows(gpu):
-    inp = _custom(8, 5, 3000, "bf16", "bf16", seed=4)
-    inp.draft[:4] = inp.target[:4, :5]  # identical: rho == 1, accept all
-    ninf = synth.f32_to_bf16_bits(np.array([-np.inf], np.float32))[0]
-    for b in range(4, 8):  # disjoint supports at position 0
-        t = inp.target[b, 0].copy()
-        inp.target[b, 0, 1500:] = ninf
-        inp.draft[b, 0, :1500] = ninf
-        inp.tokens[b, 0] = 1500 + (b * 37) % 1500
+    inp = SC.identical_and_disjoint()
     out = H.run_sample(gpu, H.sample_tensors(inp))
     _check(inp, out, "identical/disjoint")
     assert (out["n"][:4] == 5).all() and (out["n"][4:] == 0).all()
@@ -87,16 +68,7 @@ def test_identical_and_disjoint_rows(gpu):
 
 
 def test_invalid_inputs(gpu):
-    inp = _custom(12, 4, 512, "f32", "f32", seed=5)
-    T = inp.temperature
-    T[0], T[1], T[2], T[3], T[4] = 0.0, -1.0, np.nan, np.inf, 1e-40
-    inp.tokens[5, 0] = 512  # out of range at a consumed position
-    inp.tokens[6, 0] = -1
-    inp.target[7, 0, 17] = np.nan
-    inp.draft[8, 0, 3] = np.inf
-    inp.target[9, 0, :] = -np.inf
-    inp.uniforms[10, 0] = 1.0
-    inp.uniforms[11, 4] = -0.5
+    inp = SC.invalid_inputs()
     out = H.run_sample(gpu, H.sample_tensors(inp))
     _check(inp, out, "invalid")
     assert (out["n"] == -1).all() and (out["tokens"] == -1).all()
@@ -104,18 +76,17 @@ def test_invalid_inputs(gpu):
 
 def test_unconsulted_positions_are_ignored(gpu):
     """Rows, tokens and uniforms after the first rejection do not matter."""
-    inp = _custom(4, 5, 700, "f32", "f32", seed=6)
-    for b in range(4):  # force a rejection at position 0: disjoint supports
-        inp.target[b, 0, 350:] = -np.inf
-        inp.draft[b, 0, :350] = -np.inf
-        inp.tokens[b, 0] = 400
-    inp.tokens[0, 2] = 9999
-    inp.target[1, 3, 5] = np.nan
-    inp.draft[2, 1, :] = np.nan
-    inp.uniforms[3, 2] = 7.0
+    inp = SC.unconsulted_positions()
     out = H.run_sample(gpu, H.sample_tensors(inp))
     _check(inp, out, "unconsulted")
     assert (out["n"] == 0).all()
+
+
+def test_invalid_after_accepts(gpu):
+    inp = SC.invalid_after_accepts()
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    _check(inp, out, "invalid after accepts")
+    assert list(out["n"]) == [-1, -1, -1, 1]
 
 
 def test_strided_rows(gpu):
