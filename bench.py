@@ -16,7 +16,11 @@ N=60, V=32000, bf16), c5 stress (B=512, gamma=5, V=256000, bf16 target, fp32
 draft, per-row T in [0.3, 1.5]). The default is c5, the largest single-GPU one.
 
 --calibrate-copy runs a plain 1 GiB device-to-device copy instead (used to
-scale the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 runs).
+scale the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 runs). For the
+sampling workloads the line's detail also times spec_verify_sample_early_exit
+on the same inputs (rows after a first rejection are not read; algorithmic
+bytes counted for the rows it must read); --early-exit makes that entry point
+the timed step.
 """
 from __future__ import annotations
 
@@ -309,6 +313,26 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # the early-exit entry point on the same inputs, timed the same way (reported in detail)
+    ee = None
+    if not tree and not args.early_exit:
+        ee_n = torch.empty_like(out_n)
+        ee_t = torch.empty_like(out_t)
+
+        def ee_call(c):
+            binding.spec_verify_sample_early_exit(tcopies[c], dcopies[c], tokens, uni, temps,
+                                                  out_num_accepted=ee_n, out_tokens=ee_t, workspace=ws)
+        for k in range(args.warmup):
+            ee_call(k % R)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for k in range(args.steps):
+            ee_call(k % R)
+        torch.cuda.synchronize()
+        ee_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+        ee = (ee_ms, ee_n.cpu().numpy(), ee_t.cpu().numpy())
+        log(f"[bench] early exit: {ee_ms:.4f} ms/step")
     stage_ms = [float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
                 for i in range(ns)]
     log(f"[bench] {ms_per_step:.4f} ms/step; kernel event means (ms): {stage_ms}")
@@ -329,13 +353,23 @@ def main():
         detail["mean_tokens_per_verify"] = float(n_acc[valid].mean() + 1)
         detail["invalid"] = int((~valid).sum())
         if args.early_exit:
-            s1_bytes = step_bytes = early_exit_bytes(inp.cfg, B, G, V, n_acc)
             detail["one_pass_step_alg_bytes"] = int(s1_bytes + s2_bytes)
+            s1_bytes = step_bytes = early_exit_bytes(inp.cfg, B, G, V, n_acc)
         else:
             detail["kernels"]["sv_finish_kernel"]["alg_bytes"] = int(s2_bytes)
             detail["kernels"]["sv_finish_kernel"]["gbps"] = round(s2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1)
     detail["kernels"][kernel_names[0]]["alg_bytes"] = int(s1_bytes)
     detail["kernels"][kernel_names[0]]["gbps"] = round(s1_bytes / (stage_ms[0] * 1e-3) / 1e9, 1)
+    if ee is not None:
+        ee_ms, ee_nacc, ee_tok = ee
+        ee_bytes = early_exit_bytes(inp.cfg, B, G, V, ee_nacc)
+        detail["early_exit"] = {
+            "entry_point": "spec_verify_sample_early_exit", "ms_per_step": round(ee_ms, 5),
+            "value": units / (ee_ms * 1e-3), "unit": unit, "alg_bytes": int(ee_bytes),
+            "gbps": round(ee_bytes / (ee_ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(ee_bytes / (ee_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "same_outputs_as_one_pass": bool(np.array_equal(ee_nacc, n_acc) and
+                                             np.array_equal(ee_tok, out_t.cpu().numpy()))}
     detail["step_alg_bytes"] = int(step_bytes)
     detail["step_gbps"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)
     detail["step_frac_of_peak"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)

@@ -128,15 +128,19 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
  *
  * Defines: [SD] "The pith" (the longest accepted prefix is kept: nothing after
  * the first rejection can change the output). Same arguments, outputs,
- * validity rules and workspace as spec_verify_sample, and the same outputs for
- * the same inputs: the accept decisions use the same statistics, merged in the
- * same order. The work is ordered by position: one statistics launch per
- * position 0..gamma, in which each workgroup first re-derives the accept
- * decision of the position before it and streams its rows only if that
- * position was accepted, then the finish kernel. Data moved: the rows of
- * positions 0..n (plus the draw row(s)) instead of all 2*gamma+1 rows.
- * Differences: diag p_x, q_x are NaN for positions after n (their rows are not
- * read); gamma + 2 kernel launches instead of 2.
+ * validity rules, workspace and parity with the definition as
+ * spec_verify_sample. The work is ordered by position: statistics launches
+ * over positions 0, 1, ..., k-1 one at a time and then k..gamma together (k
+ * from the sizes: a position gets its own launch while the bytes its gate is
+ * expected to save outweigh a launch), then the finish kernel. In every launch
+ * after the first, each workgroup re-derives the accept decision of the
+ * position before it and streams its rows only if that position was accepted.
+ * Data moved: the rows of positions 0..n (0..gamma for a sequence that reaches
+ * the tail group) plus the draw row(s), instead of all 2*gamma+1 rows.
+ * Differences from spec_verify_sample: the row statistics are taken in smaller
+ * chunks, so results can differ in rounding (an accept decision within ~1e-7
+ * of u, p_x and q_x in the last bits); diag p_x, q_x are NaN for positions
+ * whose rows were not read; more kernel launches (k + 2 instead of 2).
  */
 int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, int64_t target_seq_stride,
                                   int64_t target_row_stride, const void* draft_logits, int draft_dtype,

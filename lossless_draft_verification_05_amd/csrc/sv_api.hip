@@ -11,7 +11,7 @@
 
 namespace sv {
 hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stage, hipStream_t stream);
-hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int pos, hipStream_t stream);
+hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int p0, int p1, hipStream_t stream);
 hipError_t launch_tree(const TreeLaunch& A, int dt, int stage, hipStream_t stream);
 
 static thread_local int g_last_hip_error = 0;
@@ -84,7 +84,7 @@ static int validate_sample(const SampleArgs& a) {
   return SV_OK;
 }
 
-static SampleLaunch plan_sample(const SampleArgs& a) {
+static SampleLaunch plan_sample(const SampleArgs& a, bool early = false) {
   SampleLaunch L;
   memset(&L, 0, sizeof(L));
   const int et = esz_of(a.tdt), ed = esz_of(a.ddt);
@@ -109,7 +109,7 @@ static SampleLaunch plan_sample(const SampleArgs& a) {
   }
   const int64_t G = a.gamma, V = a.V, B = a.B;
   const int64_t total = B * ((G + 1) * V * et + G * V * ed);
-  const int64_t cb = chunk_bytes_for(total);
+  const int64_t cb = early ? early_chunk_bytes() : chunk_bytes_for(total);
   split_row(V, et, cb, &L.nct, &L.cut);
   split_row(V, ed, cb, &L.ncd, &L.cud);
   L.per_seq = (int)((G + 1) * L.nct + G * L.ncd);
@@ -135,17 +135,21 @@ static int run_sample(int first, int last, const SampleArgs& a, hipStream_t stre
   return SV_OK;
 }
 
-// Early exit: one statistics launch per position 0..gamma (each gated on the
-// accept decision of the position before it), then the finish kernel.
+// Early exit: statistics launches over positions 0, 1, ..., k-1 and then
+// k..gamma together (each gated on the accept decision of the position before
+// it), then the finish kernel.
 static int run_sample_early(const SampleArgs& a, hipStream_t stream) {
   int st = validate_sample(a);
   if (st) return st;
-  SampleLaunch L = plan_sample(a);
+  SampleLaunch L = plan_sample(a, true);
   if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
   L.reach = (int32_t*)((char*)a.ws + sample_layout(a.B, a.gamma, a.V).off_reach);
-  for (int pos = 0; pos <= a.gamma; ++pos) {
-    st = hip_status(launch_sample_pos(L, a.tdt, a.ddt, pos, stream));
+  const int k = early_tail_start(a.B, a.gamma, a.V, esz_of(a.tdt), esz_of(a.ddt));
+  for (int p0 = 0; p0 <= a.gamma;) {
+    const int p1 = (p0 < k) ? p0 : a.gamma;
+    st = hip_status(launch_sample_pos(L, a.tdt, a.ddt, p0, p1, stream));
     if (st) return st;
+    p0 = p1 + 1;
   }
   return hip_status(launch_sample_stage(L, a.tdt, a.ddt, 2, stream));
 }

@@ -21,6 +21,9 @@ constexpr int64_t kMinChunkBytes = 16 << 10;    // stats / argmax work unit boun
 constexpr int64_t kMaxChunkBytes = 128 << 10;   // measured best for the stats kernel on MI355X
 constexpr int64_t kTargetWGs = 8192;            // ~32 workgroups per CU on 256 CUs
 constexpr int kLog2MaxNodes = 10;               // 1024 tree nodes
+constexpr int64_t kEarlyChunkBytes = 64 << 10;  // early-exit statistics work unit
+constexpr double kEarlyAlpha = 0.7;             // acceptance rate assumed when grouping positions
+constexpr double kEarlyLaunchBytes = 64e6;      // bytes moved in about the time one extra launch costs
 
 enum : int { kModeResidual = 0, kModeBonus = 1 };
 
@@ -143,6 +146,43 @@ struct SampleLayout {
 };
 
 inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
+
+// ---------------------------------------------------------------------------
+// early exit
+// ---------------------------------------------------------------------------
+// Chunks per sequence of one launch over positions p0..p1 (target rows, and
+// draft rows of the positions below gamma).
+inline int64_t early_chunks(int64_t G, int64_t nct, int64_t ncd, int64_t p0, int64_t p1) {
+  const int64_t hi = p1 < G - 1 ? p1 : G - 1;
+  const int64_t npair = hi >= p0 ? hi - p0 + 1 : 0;
+  return npair * (nct + ncd) + (p1 == G ? nct : 0);
+}
+
+// Work unit of the early-exit statistics launches. Smaller than the one-pass
+// kernel's largest: a launch over the later positions holds few active
+// sequences, and its time is then one workgroup's chain of dependent loads.
+// Not much smaller: every workgroup of a gated launch first re-derives an
+// accept decision (a few dependent round trips), which a small unit does not
+// amortise (measured on MI355X: 64 KB beat 16 and 32 KB by 20-30% at
+// V = 128k, and matched them elsewhere).
+inline int64_t early_chunk_bytes() { return kEarlyChunkBytes; }
+
+// First position of the tail group: positions 0..k-1 get a launch each and
+// k..gamma share one. Position p gets its own launch while the bytes that its
+// gate is expected to save -- sequences still active at p (alpha^p) that
+// reject there (1 - alpha) skip the rows of p+1..gamma -- exceed what a launch
+// costs in time (kEarlyLaunchBytes at full bandwidth). alpha is an assumed
+// acceptance rate, not measured.
+inline int early_tail_start(int64_t B, int64_t G, int64_t V, int et, int ed) {
+  const double pair = (double)B * V * (et + ed), bonus = (double)B * V * et;
+  double active = 1.0;
+  for (int64_t p = 1; p <= G; ++p) {
+    active *= kEarlyAlpha;
+    const double later = (double)(G - p - 1 > 0 ? G - p - 1 : 0) * pair + (p < G ? bonus : 0.0);
+    if (active * (1.0 - kEarlyAlpha) * later < kEarlyLaunchBytes) return (int)p;
+  }
+  return (int)G;
+}
 
 inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
   SampleLayout L;

@@ -216,20 +216,22 @@ __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
   stats_chunk<TD, DD>(A, b, r, kl);
 }
 
-// Early exit: the statistics of position pos only (target row pos and, for
-// pos < gamma, draft row pos), one workgroup per (sequence, chunk of those
-// rows). reach[b] = k records that positions 0..k-2 were accepted, so rows
-// 0..k-1 have statistics. For pos > 0 a workgroup first re-derives the accept
-// decision of position pos - 1 from that position's partials (every workgroup
-// of the sequence derives the same one) and streams its chunk only after an
-// acceptance; after a rejection the sequence's later rows are never read.
+// Early exit: the statistics of positions p0..p1 (target rows, and draft rows
+// of positions below gamma), one workgroup per (sequence, chunk of those rows).
+// reach[b] = k records that positions 0..k-2 were accepted and rows 0..k-1
+// have statistics. For p0 > 0 a workgroup first re-derives the accept decision
+// of position p0 - 1 from that position's partials (every workgroup of the
+// sequence derives the same one) and streams its chunk only after an
+// acceptance, so after a rejection the sequence's later rows are never read.
 template <int TD, int DD>
-__global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, int pos) {
+__global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, int p0, int p1) {
   __shared__ RowStat sh_rs[2];
   __shared__ float sh_g[2];
   __shared__ int sh_go;
   const int G = A.gamma;
-  const int cps = A.nct + (pos < G ? A.ncd : 0);
+  const int pair = A.nct + A.ncd;
+  const int npair = max(0, min(p1, G - 1) - p0 + 1);  // positions below gamma in [p0, p1]
+  const int cps = npair * pair + (p1 == G ? A.nct : 0);
   const int64_t wg = blockIdx.x;
   const int b = (int)(wg / cps);
   const int c = (int)(wg % cps);
@@ -238,11 +240,11 @@ __global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, 
   const float T = A.temps[b];
   const bool tv = temp_ok(T);
   const float kl = tv ? log2e_over(T) : 1.0f;
-  if (pos == 0) {
-    if (tid == 0) A.reach[b] = 1;  // every workgroup of the sequence writes the same value
+  if (p0 == 0) {
+    if (tid == 0) A.reach[b] = p1 + 1;  // every workgroup of the sequence writes the same value
   } else {
-    if (A.reach[b] < pos) return;  // the sequence stopped at an earlier position
-    const int i = pos - 1;
+    if (A.reach[b] < p0) return;  // the sequence stopped at an earlier position
+    const int i = p0 - 1;
     if (w < 2) {
       // wave 0 merges target row i, wave 1 draft row i
       const int nrec = (w == 0 ? A.nct : A.ncd) * kWaves;
@@ -266,12 +268,18 @@ __global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, 
       const float ui = A.uniforms[(int64_t)b * (G + 1) + i];
       const AcceptOut ao = accept_test(sh_g[0], sh_g[1], sh_rs[0], sh_rs[1], kl, ui, xi >= 0 && xi < A.V, tv);
       sh_go = ao.code == 1;
-      if (ao.code == 1) A.reach[b] = pos + 1;
+      if (ao.code == 1) A.reach[b] = p1 + 1;
     }
     __syncthreads();
     if (!sh_go) return;
   }
-  const int r = (c < A.nct) ? pos * A.nct + c : (G + 1) * A.nct + pos * A.ncd + (c - A.nct);
+  int r;
+  if (c < npair * pair) {
+    const int pos = p0 + c / pair, cc = c % pair;
+    r = (cc < A.nct) ? pos * A.nct + cc : (G + 1) * A.nct + pos * A.ncd + (cc - A.nct);
+  } else {
+    r = G * A.nct + (c - npair * pair);  // the bonus row
+  }
   stats_chunk<TD, DD>(A, b, r, kl);
 }
 
@@ -801,10 +809,10 @@ static hipError_t launch_pair(const SampleLaunch& A, int stage, hipStream_t stre
 }
 
 template <int TD, int DD>
-static hipError_t launch_pos(const SampleLaunch& A, int pos, hipStream_t stream) {
-  const int64_t cps = A.nct + (pos < A.gamma ? A.ncd : 0);
+static hipError_t launch_pos(const SampleLaunch& A, int p0, int p1, hipStream_t stream) {
+  const int64_t cps = early_chunks(A.gamma, A.nct, A.ncd, p0, p1);
   hipLaunchKernelGGL((sv_stats_pos_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * cps)), dim3(kThreads), 0, stream,
-                     A, pos);
+                     A, p0, p1);
   return hipGetLastError();
 }
 
@@ -815,11 +823,11 @@ hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stag
   return launch_pair<0, 0>(A, stage, stream);
 }
 
-hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int pos, hipStream_t stream) {
-  if (tdt == 1 && ddt == 1) return launch_pos<1, 1>(A, pos, stream);
-  if (tdt == 1 && ddt == 0) return launch_pos<1, 0>(A, pos, stream);
-  if (tdt == 0 && ddt == 1) return launch_pos<0, 1>(A, pos, stream);
-  return launch_pos<0, 0>(A, pos, stream);
+hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int p0, int p1, hipStream_t stream) {
+  if (tdt == 1 && ddt == 1) return launch_pos<1, 1>(A, p0, p1, stream);
+  if (tdt == 1 && ddt == 0) return launch_pos<1, 0>(A, p0, p1, stream);
+  if (tdt == 0 && ddt == 1) return launch_pos<0, 1>(A, p0, p1, stream);
+  return launch_pos<0, 0>(A, p0, p1, stream);
 }
 
 }  // namespace sv

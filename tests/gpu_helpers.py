@@ -74,32 +74,32 @@ def run_sample(binding, tens, diag=True, workspace=None, early_exit=False):
     return out
 
 
-def same_as_one_pass(one, ee):
-    """Early exit against the one-pass call on the same inputs: n and tokens
-    equal; for valid sequences p(x), q(x) of positions 0..n and the drawn
-    distribution's mass equal bit for bit (same statistics, same merge order)
-    and p(x), q(x) NaN after n. Returns a list of differences."""
+def compare_one_pass(one, ee):
+    """Early exit against the one-pass call on the same inputs. Returns
+    (differing, bad): the sequences whose n or tokens differ (both results are
+    judged against the oracle by the caller), and a list of other problems:
+    for sequences that agree and are valid, p(x), q(x) of positions 0..n and
+    the drawn distribution's mass must agree within PROB_RTOL, and p(x), q(x)
+    of every position the early-exit call reports after n must be NaN or equal
+    to the one-pass value within PROB_RTOL (tail-group rows are read)."""
+    differ = np.flatnonzero((one["n"] != ee["n"]) | (one["tokens"] != ee["tokens"]).any(axis=1))
     bad = []
-    if not np.array_equal(one["n"], ee["n"]):
-        idx = np.flatnonzero(one["n"] != ee["n"])
-        bad.append(("n", idx[:5].tolist(), one["n"][idx[:5]].tolist(), ee["n"][idx[:5]].tolist()))
-    if not np.array_equal(one["tokens"], ee["tokens"]):
-        bad.append(("tokens", np.flatnonzero((one["tokens"] != ee["tokens"]).any(axis=1))[:5].tolist()))
     if "p_x" in one and "p_x" in ee:
         B, G = one["p_x"].shape
         for b in range(B):
             n = int(one["n"][b])
-            if n < 0 or n != int(ee["n"][b]):
+            if n < 0 or b in differ:
                 continue
-            k = min(n + 1, G)
             for key in ("p_x", "q_x"):
-                if not np.array_equal(one[key][b, :k].view(np.uint32), ee[key][b, :k].view(np.uint32)):
-                    bad.append((key, b))
-                if not np.isnan(ee[key][b, k:]).all():
-                    bad.append((key + " after n", b))
-            if one["resid_mass"][b].view(np.uint32) != ee["resid_mass"][b].view(np.uint32):
+                for i in range(G):
+                    o, e = float(one[key][b, i]), float(ee[key][b, i])
+                    if i > n and np.isnan(e):
+                        continue
+                    if not (np.isfinite(o) and np.isfinite(e) and _rel(e, o) <= PROB_RTOL):
+                        bad.append((key, b, i, o, e))
+            if _rel(ee["resid_mass"][b], one["resid_mass"][b]) > PROB_RTOL:
                 bad.append(("resid_mass", b))
-    return bad
+    return differ, bad
 
 
 class Tally:
