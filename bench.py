@@ -9,6 +9,10 @@ for the sampling workloads, spec_verify_greedy_tree for the tree workload.
 Inputs are seeded synthetic logits already resident in HBM. Prints ONE JSON
 line on stdout; progress goes to stderr.
 
+Workloads d3, d5 time the draft-side sampler (spec_draft_sample) on the draft
+rows of configurations 3 and 5 (256 x 128256 bf16 at T 0.7; 512 x 256000
+fp32 at per-row T); they print the same kind of line with their own metric.
+
 Workloads (the five input configurations): c1 tiny sampling (B=10^4 trials,
 gamma=4, V=32, fp32), c2 7B-class vocab (B=64, gamma=4, V=32000, bf16), c3
 large vocab (B=256, gamma=8, V=128256, bf16, T=0.7), c4 greedy tree (B=32,
@@ -39,7 +43,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 PEAK_HBM_GBPS = float(os.environ.get("SV_PEAK_HBM_GBPS", "8000"))
-WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "d3": 3, "d5": 5}
 CSRC = os.path.join(ROOT, "lossless_draft_verification_05_amd", "csrc")
 
 
@@ -77,6 +81,108 @@ def _oracle_tree(b):
 
     ti = _CPU_DATA
     return O.verify_tree_sequence(O.widen(ti.logits[b], ti.dtype), ti.parents[b], ti.tokens[b]).accept_len
+
+
+def _oracle_draft(b):
+    from oracle import spec_verify_oracle as O
+
+    d = _CPU_DATA
+    return O.draft_sample_row(O.widen(d.logits[b], d.dtype), float(d.temperature[b]), float(d.uniforms[b])).y
+
+
+def cpu_baseline_draft(d, budget_s: float = 15.0):
+    """The oracle's draft sampler over a bounded sample of rows (cycled), in a
+    pool of worker processes forked before the GPU is touched."""
+    import multiprocessing as mp
+
+    global _CPU_DATA
+    _CPU_DATA = d
+    _oracle_draft(0)
+    t0 = time.perf_counter()
+    _oracle_draft(0)
+    t_one = max(time.perf_counter() - t0, 1e-5)
+    workers = max(1, min(16, os.cpu_count() or 1))
+    S = int(min(50 * d.B, max(workers, budget_s * workers / t_one)))
+    with mp.get_context("fork").Pool(workers) as pool:
+        t0 = time.perf_counter()
+        pool.map(_oracle_draft, [i % d.B for i in range(S)], chunksize=max(1, S // (4 * workers)))
+        dt = time.perf_counter() - t0
+    _CPU_DATA = None
+    return {"value": S / dt, "unit": "draft tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{S} rows (index mod {d.B}) of the same inputs, numpy fp64, {workers} worker processes, "
+                      f"{dt:.1f} s"}
+
+
+def bench_draft(args, cid):
+    """Time spec_draft_sample (stats kernel + draw kernel, HIP events on the
+    stream they run on) on the draft rows of configuration cid."""
+    log(f"[bench] building draft rows of config {cid} (seed {args.seed})")
+    d = synth.make_draft_workload(cid, seed=args.seed)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_draft(d)
+    if cpu:
+        log(f"[bench] cpu baseline: {cpu}")
+    import torch
+
+    from lossless_draft_verification_05_amd import binding
+
+    binding.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    a = np.ascontiguousarray(d.logits)
+    L0 = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev) if d.dtype == "bf16" else \
+        torch.from_numpy(a).to(dev)
+    per_copy = L0.numel() * L0.element_size()
+    R = int(min(64, max(1, -(-(512 << 20) // per_copy)))) if per_copy < (512 << 20) else 1
+    copies = [L0] + [L0.clone() for _ in range(R - 1)]
+    u = torch.from_numpy(d.uniforms).to(dev)
+    T = torch.from_numpy(d.temperature).to(dev)
+    y = torch.empty(d.B, dtype=torch.int32, device=dev)
+    ws = binding.Workspace()
+
+    def stages(c):
+        return [lambda s=s: binding.spec_draft_sample(copies[c], u, T, out_tokens=y, workspace=ws, stage=s)
+                for s in (1, 2)]
+    for k in range(args.warmup):
+        for f in stages(k % R):
+            f()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        e = evs[k]
+        e[0].record()
+        for i, f in enumerate(stages(k % R)):
+            f()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    st = [float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)])) for i in range(2)]
+    log(f"[bench] {ms:.4f} ms/step; kernel event means (ms): {st}")
+    row_bytes = d.V * (2 if d.dtype == "bf16" else 4)
+    s1 = d.B * row_bytes + d.B * 8          # every logit once + temperatures, uniforms
+    s2 = d.B * row_bytes + d.B * 4          # the row again for the draw + the tokens
+    sha = kernel_source_sha()
+    achieved = s1 / (st[0] * 1e-3) / 1e9
+    yy = y.cpu().numpy()
+    line = {
+        "metric": "sampled draft tokens/sec + achieved HBM GB/s (% peak), spec_draft_sample at 1 GPU",
+        "value": d.B / (ms * 1e-3), "unit": "draft tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic: seeded logits standing in for draft model outputs",
+        "config": {"workload": f"{args.workload}: draft rows of configuration {cid}", "B": d.B, "V": d.V,
+                   "dtype": d.dtype, "seed": args.seed},
+        "roofline": {"bound": "hbm", "kernel": "sv_stats_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_from_profiles(args.workload, sha)},
+        "cpu_baseline": cpu,
+        "detail": {"kernels": {"sv_stats_kernel": {"mean_us": round(st[0] * 1e3, 3), "alg_bytes": s1,
+                                                   "gbps": round(achieved, 1)},
+                               "sv_finish_kernel": {"mean_us": round(st[1] * 1e3, 3), "alg_bytes": s2,
+                                                    "gbps": round(s2 / (st[1] * 1e-3) / 1e9, 1)}},
+                   "input_copies": R, "kernel_source_sha": sha, "invalid": int((yy < 0).sum()),
+                   "step_alg_bytes": s1 + s2, "step_gbps": round((s1 + s2) / (ms * 1e-3) / 1e9, 1)},
+    }
+    print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(inp, tree: bool, budget_s: float = 15.0):
@@ -192,6 +298,9 @@ def main():
         return
 
     cid = WORKLOADS[args.workload]
+    if args.workload.startswith("d"):
+        bench_draft(args, cid)
+        return
     tree = cid == 4
     log(f"[bench] building inputs for {args.workload} (seed {args.seed})")
     t0 = time.perf_counter()

@@ -172,6 +172,40 @@ int spec_verify_sample_stage(int stage, const void* target_logits, int target_dt
                              void* stream);
 
 /*
+ * spec_draft_sample -- draft-side sampler: one token per row from the
+ * tempered softmax of the row, by inverse CDF.
+ *
+ * Defines: [SD] "The pith" and the abstract (the fast approximation model
+ * proposes the speculative tokens by sampling from its own distribution q;
+ * spec_verify_sample then needs x_i ~ q_i). For row b with temperature T:
+ *   q = softmax(logits[b] / T); out_tokens[b] = the smallest v whose running
+ *   mass in token-id order exceeds uniforms[b] * (total mass).
+ * The same row statistics and draw as spec_verify_sample's bonus-row draw.
+ *
+ * logits      : [B][V], dtype, rows row_stride elements apart (>= V, 16-byte
+ *               aligned rows).
+ * uniforms    : [B] float in [0, 1).
+ * temperature : [B] float, finite, positive and normal.
+ * out_tokens  : [B] int32: the drawn token, or -1 for an invalid row (bad
+ *               temperature or uniform, NaN or +inf in the row, no finite value).
+ * out_prob    : [B] float or NULL: q(out_token) (fp32 rounding of an fp64
+ *               value; NaN for an invalid row).
+ * workspace   : at least sv_draft_workspace_bytes(B, V), 256-byte aligned, no
+ *               initialisation needed. Errors as for spec_verify_sample.
+ */
+size_t sv_draft_workspace_bytes(int B, int V);
+int spec_draft_sample(const void* logits, int dtype, int64_t row_stride, const float* uniforms,
+                      const float* temperature, int B, int V, int32_t* out_tokens, float* out_prob, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* One of the two kernels of spec_draft_sample (same arguments): stage 1 row
+ * statistics, stage 2 the draw and the outputs; stage 2 must follow stage 1 on
+ * the same stream with the same arguments and workspace. */
+int spec_draft_sample_stage(int stage, const void* logits, int dtype, int64_t row_stride, const float* uniforms,
+                            const float* temperature, int B, int V, int32_t* out_tokens, float* out_prob,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * spec_verify_greedy_tree -- greedy verification of B draft trees.
  *
  * Defines: [Falcon] "What carries the argument" (the drafter proposes a tree of

@@ -9,7 +9,7 @@ call does, and fails loudly if the library is missing.
 
 
 def __getattr__(name):
-    if name in ("spec_verify_sample", "spec_verify_sample_stage", "spec_verify_sample_early_exit",
+    if name in ("spec_verify_sample", "spec_verify_sample_stage", "spec_verify_sample_early_exit", "spec_draft_sample",
                 "spec_verify_greedy_tree",
                 "spec_verify_greedy_tree_stage",
                 "sv_sample_workspace_bytes", "sv_tree_workspace_bytes", "Workspace"):

@@ -37,6 +37,9 @@ SIGNATURES = {
                                        _sz, _vp]),
     "spec_verify_greedy_tree_stage": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
                                              _vp, _vp, _sz, _vp]),
+    "sv_draft_workspace_bytes": (_sz, [_i32, _i32]),
+    "spec_draft_sample": (_i32, [_vp, _i32, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "spec_draft_sample_stage": (_i32, [_i32, _vp, _i32, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "sv_status_string": (ctypes.c_char_p, [_i32]),
     "sv_last_hip_error": (_i32, []),
     "sv_version": (ctypes.c_char_p, []),
@@ -223,6 +226,37 @@ def spec_verify_sample_stage(stage, target, draft, draft_tokens, uniforms, tempe
     """One stage of spec_verify_sample: 1 row statistics, 2 accept tests + residual/bonus draw + outputs."""
     return _sample_call(int(stage), target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
                         out_tokens, diag, workspace, stream)
+
+
+def spec_draft_sample(logits, uniforms, temperature, *, out_tokens=None, want_prob=False, workspace=None,
+                      stream=None, stage=None):
+    """Draft-side sampler (see include/spec_verify.h): one token per row of logits [B][V] (bf16 or fp32,
+    contiguous 16-byte aligned rows) from softmax(row / T) at the row's uniform. Returns (tokens [B] int32,
+    q(token) [B] float32 or None). ``stage`` 1 or 2 runs one of its two kernels."""
+    lib = load()
+    if not isinstance(logits, torch.Tensor) or not logits.is_cuda or logits.dim() != 2:
+        raise ValueError("logits must be a 2-d CUDA tensor [B][V]")
+    B, V = logits.shape
+    if logits.stride(1) != 1 and V > 1:
+        raise ValueError("logits rows must be contiguous (last stride 1)")
+    dev = logits.device
+    _need(uniforms, "uniforms", torch.float32, (B,))
+    _need(temperature, "temperature", torch.float32, (B,))
+    if out_tokens is None:
+        out_tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(out_tokens, "out_tokens", torch.int32, (B,))
+    prob = torch.empty(B, dtype=torch.float32, device=dev) if want_prob else None
+    nbytes = int(lib.sv_draft_workspace_bytes(B, V))
+    if nbytes == 0:
+        raise ValueError(f"shape B={B} V={V} out of range")
+    ws = _workspace(workspace, nbytes, dev)
+    args = (_ptr(logits), _dtype_code(logits), logits.stride(0), _ptr(uniforms), _ptr(temperature), B, V,
+            _ptr(out_tokens), _ptr(prob) if prob is not None else None, _ptr(ws), ws.numel(), _stream(stream))
+    if stage is None:
+        _check(lib.spec_draft_sample(*args), "spec_draft_sample")
+    else:
+        _check(lib.spec_draft_sample_stage(int(stage), *args), f"spec_draft_sample_stage({stage})")
+    return out_tokens, prob
 
 
 def _tree_call(stage, logits, parents, tokens, out_accept_len, out_path, out_bonus, out_argmax, want_argmax,

@@ -135,6 +135,33 @@ static int run_sample(int first, int last, const SampleArgs& a, hipStream_t stre
   return SV_OK;
 }
 
+// Draft-side sampler: the path with gamma = 0 (statistics of one row per
+// sequence, then the bonus-mode draw from it).
+static int run_draft(int first, int last, const void* logits, int dtype, int64_t row_stride, const float* uniforms,
+                     const float* temperature, int B, int V, int32_t* out_tokens, float* out_prob, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !uniforms || !temperature || !out_tokens) return SV_ERR_NULL;
+  if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+  if (B < 1 || B > SV_MAX_BATCH || V < 1 || V > SV_MAX_VOCAB) return SV_ERR_SHAPE;
+  int st = check_rows(logits, dtype, row_stride, row_stride, B, 1, V);
+  if (st) return st;
+  if (!aligned(uniforms, 4) || !aligned(temperature, 4) || !aligned(out_tokens, 4) || !aligned(out_prob, 4))
+    return SV_ERR_ALIGN;
+  if (!ws) return SV_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SV_ERR_ALIGN;
+  if (ws_bytes < (size_t)sample_layout(B, 0, V).total) return SV_ERR_WORKSPACE;
+  SampleArgs a{logits, dtype, row_stride, row_stride, nullptr, dtype, 0, 0, nullptr, uniforms, temperature, B, 0, V,
+               nullptr, out_tokens, nullptr, ws, ws_bytes};
+  SampleLaunch L = plan_sample(a);
+  L.out_py = out_prob;
+  if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
+  for (int s = first; s <= last; ++s) {
+    st = hip_status(launch_sample_stage(L, dtype, dtype, s, stream));
+    if (st) return st;
+  }
+  return SV_OK;
+}
+
 // Early exit: statistics launches over positions 0, 1, ..., k-1 and then
 // k..gamma together (each gated on the accept decision of the position before
 // it), then the finish kernel.
@@ -205,6 +232,26 @@ int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, i
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
   return run_sample_early(a, (hipStream_t)stream);
+}
+
+size_t sv_draft_workspace_bytes(int B, int V) {
+  if (B < 1 || B > SV_MAX_BATCH || V < 1 || V > SV_MAX_VOCAB) return 0;
+  return (size_t)sample_layout(B, 0, V).total;
+}
+
+int spec_draft_sample(const void* logits, int dtype, int64_t row_stride, const float* uniforms,
+                      const float* temperature, int B, int V, int32_t* out_tokens, float* out_prob, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return run_draft(1, 2, logits, dtype, row_stride, uniforms, temperature, B, V, out_tokens, out_prob, workspace,
+                   workspace_bytes, (hipStream_t)stream);
+}
+
+int spec_draft_sample_stage(int stage, const void* logits, int dtype, int64_t row_stride, const float* uniforms,
+                            const float* temperature, int B, int V, int32_t* out_tokens, float* out_prob,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < 1 || stage > 2) return SV_ERR_ARG;
+  return run_draft(stage, stage, logits, dtype, row_stride, uniforms, temperature, B, V, out_tokens, out_prob,
+                   workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 static int run_tree(int first, int last, const void* target_logits, int dtype, int64_t seq_stride,

@@ -82,8 +82,9 @@ struct SampleLaunch {
   const float* uniforms;
   const float* temps;
   int B, gamma, V;
-  int32_t* out_n;
+  int32_t* out_n;    // may be null (draft sampler)
   int32_t* out_tok;
+  float* out_py;     // may be null: probability of the drawn token (bonus-mode draws; draft sampler)
   float* diag_px;
   float* diag_qx;
   float* diag_mass;

@@ -677,7 +677,8 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   if (!P.valid) {
     for (int k = tid; k <= G; k += kFinThreads) otok[k] = -1;
     if (tid == 0) {
-      A.out_n[b] = -1;
+      if (A.out_n) A.out_n[b] = -1;
+      if (A.out_py) A.out_py[b] = __builtin_nanf("");
       if (A.diag_mass) A.diag_mass[b] = __builtin_nanf("");
     }
     return;
@@ -790,8 +791,17 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   for (int k = tid; k <= G; k += kFinThreads)
     otok[k] = (k < n) ? A.tokens[(int64_t)b * G + k] : (k == n ? y : -1);
   if (tid == 0) {
-    A.out_n[b] = n;
+    if (A.out_n) A.out_n[b] = n;
     if (A.diag_mass) A.diag_mass[b] = (float)(total / (P.sp * P.fscale));
+    if (A.out_py) {
+      // p(y) of a bonus-mode draw, from the row's statistics in fp64
+      float py = __builtin_nanf("");
+      if (mode == kModeBonus) {
+        const float x = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)n * A.t_row_b, y);
+        py = (float)(exp2(((double)x - (double)P.mp) * (double)P.kl) / P.sp);
+      }
+      A.out_py[b] = py;
+    }
   }
 }
 

@@ -258,6 +258,29 @@ def verify_sample_batch(Lt_all, Ld_all, tokens, uniforms, temps, t_dtype="f32", 
 # greedy tree verify
 # ----------------------------------------------------------------------------
 @dataclass
+class DraftResult:
+    valid: bool
+    y: int = -1
+    q_y: float = float("nan")
+    cdf: np.ndarray | None = None
+
+
+def draft_sample_row(L: np.ndarray, T: float, u: float, keep_cdf: bool = False) -> DraftResult:
+    """The draft-side step that produces the inputs of the verify: x ~ q with
+    q = softmax(L / T) ([SD] "The pith" and the abstract: the fast
+    approximation model proposes the speculative tokens by sampling from its
+    own distribution). Drawn by inverse CDF in token-id order at u, the same
+    rule as the verify's final draw. Invalid (y = -1) for an unusable
+    temperature, a uniform outside [0, 1) or a row with NaN, +inf or no finite
+    value."""
+    if not temperature_is_valid(T) or not (0.0 <= u < 1.0) or not row_is_valid(L):
+        return DraftResult(False)
+    q, _, _ = tempered_softmax(L, T)
+    y, C, S = inverse_cdf(q, u)
+    return DraftResult(True, y, float(q[y]), C / S if keep_cdf else None)
+
+
+@dataclass
 class TreeResult:
     valid: bool
     accept_len: int = -1

@@ -462,3 +462,48 @@ def make_custom_sample(B: int, gamma: int, V: int, target_dtype: str = "bf16", d
     _pmap(one, range(B))
     u = uniforms_u24(gen(seed, cid, S_UNIFORM), (B, gamma + 1))
     return SampleInputs(cfg, seed, tgt, dft, tokens, u, temps, np.zeros(B, np.int8), {"shared_logits": False})
+
+
+# --------------------------------------------------------------------------
+# draft-side sampler inputs
+# --------------------------------------------------------------------------
+@dataclass
+class DraftRows:
+    name: str
+    seed: int
+    dtype: str
+    logits: np.ndarray       # [B][V]: bf16 bits (uint16) or float32
+    uniforms: np.ndarray     # [B] float32, exact k * 2^-24
+    temperature: np.ndarray  # [B] float32
+
+    @property
+    def B(self):
+        return self.logits.shape[0]
+
+    @property
+    def V(self):
+        return self.logits.shape[1]
+
+
+def make_draft_rows(B: int, V: int, dtype: str = "f32", T=1.0, seed: int = 0, sd: float = 2.0,
+                    cid: int = 200, name: str = "custom draft rows") -> DraftRows:
+    """One draft logit row per sequence, N(0, sd), rounded to dtype; one exact
+    u24 uniform per row; T a float or B temperatures."""
+    temps = np.broadcast_to(np.asarray(T, dtype=np.float32), (B,)).copy()
+    out = np.empty((B, V), dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def one(b):
+        z = gen(seed, cid, S_TARGET, b).standard_normal(V, dtype=np.float32) * np.float32(sd)
+        out[b] = _to_dtype(z, dtype)
+
+    _pmap(one, range(B))
+    u = uniforms_u24(gen(seed, cid, S_UNIFORM), (B,))
+    return DraftRows(name, seed, dtype, out, u, temps)
+
+
+def make_draft_workload(cid: int, seed: int = 0) -> DraftRows:
+    """The draft sampler's share of sampling configuration cid: B rows of V
+    draft logits in the configuration's draft dtype and temperatures."""
+    cfg = CONFIGS[cid]
+    return make_draft_rows(cfg.B, cfg.V, cfg.draft_dtype, temperatures(cfg, seed, cfg.B), seed, cfg.target_sd,
+                           cid=200 + cid, name=f"draft rows of config {cid}")

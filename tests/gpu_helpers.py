@@ -237,3 +237,59 @@ def check_tree(logits_np, dt, parents, tokens, gpu, seqs=None):
             fails.append((b, "tree", int(gpu["len"][b]), o.accept_len, int(gpu["bonus"][b]), o.bonus, path[:8],
                           want_path[:8]))
     return fails
+
+
+# ---------------------------------------------------------------------------
+# draft-side sampler
+# ---------------------------------------------------------------------------
+def draft_tensors(d, device="cuda", pad_to=None):
+    t = padded_logits(d.logits, d.dtype, pad_to, device) if pad_to else dev_logits(d.logits, d.dtype, device)
+    return dict(logits=t, uniforms=torch.from_numpy(d.uniforms).to(device),
+                temperature=torch.from_numpy(d.temperature).to(device))
+
+
+def run_draft(binding, tens, workspace=None, stage=None):
+    if stage is None:
+        y, p = binding.spec_draft_sample(**tens, want_prob=True, workspace=workspace)
+    else:
+        y = p = None
+        for s in (1, 2):
+            y, p = binding.spec_draft_sample(**tens, want_prob=True, workspace=workspace, stage=s,
+                                             out_tokens=y)
+    torch.cuda.synchronize()
+    return {"y": y.cpu().numpy(), "p": p.cpu().numpy()}
+
+
+def check_draft(d, gpu, rows=None, tally=None):
+    """Judge draft-sampler outputs against the oracle: the token equal, or u
+    within FLAG_WINDOW of the oracle's CDF interval of the GPU's token
+    (flagged); q(token) within PROB_RTOL; invalid rows -1 exactly."""
+    tally = tally or Tally()
+    rows = range(d.B) if rows is None else rows
+    for b in rows:
+        L = O.widen(d.logits[b], d.dtype)
+        u = float(d.uniforms[b])
+        o = O.draft_sample_row(L, float(d.temperature[b]), u, keep_cdf=True)
+        tally.checked += 1
+        gy, gp = int(gpu["y"][b]), float(gpu["p"][b])
+        if not o.valid:
+            if gy != -1 or not np.isnan(gp):
+                tally.fail.append((b, "oracle invalid, gpu valid", gy))
+            continue
+        if gy != o.y:
+            if not (0 <= gy < len(o.cdf)):
+                tally.fail.append((b, "token out of range", gy))
+                continue
+            lo = o.cdf[gy - 1] if gy > 0 else 0.0
+            hi = o.cdf[gy]
+            dist = 0.0 if lo <= u < hi else min(abs(u - lo), abs(u - hi))
+            if dist < FLAG_WINDOW:
+                tally.flag_draw += 1
+            else:
+                tally.fail.append((b, "draw", gy, o.y, u, lo, hi))
+            continue
+        r = _rel(gp, o.q_y)
+        tally.max_prob_rel = max(tally.max_prob_rel, r)
+        if r > PROB_RTOL:
+            tally.fail.append((b, "q_y", gp, o.q_y))
+    return tally

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sv_\w+|spec_verify_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:sv|spec)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -139,3 +139,33 @@ def test_tree_unknown_stage(lib):
     bad = list(args)
     bad[0] = None
     assert lib.spec_verify_greedy_tree_stage(1, *bad) == -1
+
+
+def call_draft(lib, stage=None, **over):
+    A = 0x10000000
+    a = dict(logits=A, dt=0, rs=1024, uniforms=A + 0x800000, temps=A + 0x900000, B=4, V=1000,
+             out=A + 0xA00000, prob=A + 0xB00000, ws=A + 0xC00000, wsb=1 << 24, stream=None)
+    a.update(over)
+    args = [a["logits"], a["dt"], a["rs"], a["uniforms"], a["temps"], a["B"], a["V"], a["out"], a["prob"], a["ws"],
+            a["wsb"], a["stream"]]
+    if stage is None:
+        return lib.spec_draft_sample(*args)
+    return lib.spec_draft_sample_stage(stage, *args)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(logits=None), -1), (dict(uniforms=None), -1), (dict(temps=None), -1), (dict(out=None), -1),
+    (dict(dt=2), -3), (dict(B=0), -2), (dict(V=0), -2), (dict(rs=999), -2), (dict(V=(1 << 30) + 1), -2),
+    (dict(logits=0x10000002), -4), (dict(rs=1026), -4), (dict(out=0x10A00002), -4), (dict(prob=0x10B00001), -4),
+    (dict(ws=None), -5), (dict(wsb=100), -5), (dict(ws=0x10C00010), -4),
+])
+def test_draft_argument_errors(lib, over, want):
+    assert call_draft(lib, **over) == want
+    for stage in (1, 2):
+        assert call_draft(lib, stage=stage, **over) == want
+
+
+def test_draft_unknown_stage_and_workspace_query(lib):
+    assert call_draft(lib, stage=3) == -7 and call_draft(lib, stage=0) == -7
+    assert lib.sv_draft_workspace_bytes(0, 10) == 0 and lib.sv_draft_workspace_bytes(4, 0) == 0
+    assert lib.sv_draft_workspace_bytes(4, 1000) > 0
