@@ -13,6 +13,11 @@ Workloads d3, d5 time the draft-side sampler (spec_draft_sample) on the draft
 rows of configurations 3 and 5 (256 x 128256 bf16 at T 0.7; 512 x 256000
 fp32 at per-row T); they print the same kind of line with their own metric.
 
+Workload m runs the end-to-end loop on a synthetic Markov-chain model pair
+(512 chains, V = 16384 bf16 transition-logit tables, gamma = 5, T = 1): per
+iteration gamma draft-sampler calls, the target-row gathers and one verify;
+value = emitted tokens per second.
+
 Workloads (the five input configurations): c1 tiny sampling (B=10^4 trials,
 gamma=4, V=32, fp32), c2 7B-class vocab (B=64, gamma=4, V=32000, bf16), c3
 large vocab (B=256, gamma=8, V=128256, bf16, T=0.7), c4 greedy tree (B=32,
@@ -43,7 +48,8 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 PEAK_HBM_GBPS = float(os.environ.get("SV_PEAK_HBM_GBPS", "8000"))
-WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "d3": 3, "d5": 5}
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "d3": 3, "d5": 5, "m": 0}
+MARKOV = dict(B=512, V=16384, gamma=5, T=1.0, dtype="bf16", noise_sd=0.8)
 CSRC = os.path.join(ROOT, "lossless_draft_verification_05_amd", "csrc")
 
 
@@ -185,6 +191,107 @@ def bench_draft(args, cid):
     print(json.dumps(line), flush=True)
 
 
+def _oracle_markov(job):
+    from oracle import spec_verify_oracle as O
+
+    tabs, T, K, G = _CPU_DATA
+    b = job
+    g = np.random.default_rng(1000 + b)
+    res = O.markov_loop(tabs[0], tabs[1], T, b % tabs[0].shape[0], g.random((K, G)), g.random((K, G + 1)))
+    return sum(n + 1 for n, _ in res)
+
+
+def bench_markov(args):
+    """End-to-end loop on a Markov-chain model pair: emitted tokens per second
+    (HIP events around the timed iterations on the current stream)."""
+    from oracle import spec_verify_oracle as O  # noqa: F401  (CPU baseline only)
+
+    c = MARKOV
+    B, V, G, T = c["B"], c["V"], c["gamma"], c["T"]
+    log(f"[bench] building Markov tables V={V} ({c['dtype']}, seed {args.seed})")
+    tabs = synth.make_markov_tables(V, c["dtype"], seed=args.seed, noise_sd=c["noise_sd"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        import multiprocessing as mp
+
+        global _CPU_DATA
+        Lt = synth.decode(tabs.target, c["dtype"]).astype(np.float64)
+        Ld = synth.decode(tabs.draft, c["dtype"]).astype(np.float64)
+        K = 4
+        _CPU_DATA = ((Lt, Ld), T, K, G)
+        t0 = time.perf_counter()
+        _oracle_markov(0)
+        t_one = max(time.perf_counter() - t0, 1e-4)
+        workers = max(1, min(16, os.cpu_count() or 1))
+        S = int(max(workers, min(4 * B, 15.0 * workers / t_one)))
+        with mp.get_context("fork").Pool(workers) as pool:
+            t0 = time.perf_counter()
+            toks = sum(pool.map(_oracle_markov, range(S), chunksize=max(1, S // (4 * workers))))
+            dt = time.perf_counter() - t0
+        _CPU_DATA = None
+        cpu = {"value": toks / dt, "unit": "emitted tokens/s", "cores": workers, "kind": "oracle",
+               "sample": f"{S} chains x {K} iterations of the oracle loop (draft_sample_row + "
+                         f"verify_sample_sequence, numpy fp64), {workers} worker processes, {dt:.1f} s"}
+        log(f"[bench] cpu baseline: {cpu}")
+    import torch
+
+    from lossless_draft_verification_05_amd import binding
+    from lossless_draft_verification_05_amd.markov import MarkovLoop
+
+    binding.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if c["dtype"] == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+    loop = MarkovLoop(up(tabs.target), up(tabs.draft), G, torch.full((B,), T, dtype=torch.float32, device=dev))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    n_it = args.warmup + args.steps
+    ud = torch.rand((n_it, B, G), generator=gen, device=dev)
+    uv = torch.rand((n_it, B, G + 1), generator=gen, device=dev)
+    state = torch.arange(B, device=dev, dtype=torch.int64) % V
+    emitted = torch.zeros((), dtype=torch.int64, device=dev)
+    for k in range(args.warmup):
+        _, _, state = loop.step(state, ud[k], uv[k])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for k in range(args.warmup, n_it):
+        n, _, state = loop.step(state, ud[k], uv[k])
+        emitted += (n.long() + 1).sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    tok = int(emitted.item())
+    esz_ = 2 if c["dtype"] == "bf16" else 4
+    # hot-path bytes per iteration: gamma draft-sampler calls (row read twice) + the verify's one pass over
+    # 2 gamma + 1 rows + its draw row(s) (counted as a row pair)
+    it_bytes = B * V * esz_ * (2 * G + (2 * G + 1) + 2)
+    achieved = it_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "emitted tokens/sec, end-to-end speculative decoding on a Markov-chain model pair "
+                  "(spec_draft_sample + spec_verify_sample) at 1 GPU",
+        "value": tok / (args.steps * ms * 1e-3), "unit": "emitted tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic: seeded Markov transition-logit tables",
+        "config": {"workload": "m: Markov-chain loop", "B": B, "V": V, "gamma": G, "temperature": T,
+                   "table_dtype": c["dtype"], "seed": args.seed},
+        "roofline": {"bound": "hbm", "kernel": "whole iteration (gamma draft-sampler calls, row gathers, verify)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "detail": {"tokens_per_call": tok / (args.steps * B), "ms_per_step_wall": ms_wall,
+                   "hot_path_bytes_per_iteration": it_bytes, "kernel_source_sha": kernel_source_sha()},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(inp, tree: bool, budget_s: float = 15.0):
     """Time the oracle over the first S sequences in a pool of worker processes
     (fork, before the GPU is touched). S is sized from a one-sequence probe so
@@ -298,6 +405,9 @@ def main():
         return
 
     cid = WORKLOADS[args.workload]
+    if args.workload == "m":
+        bench_markov(args)
+        return
     if args.workload.startswith("d"):
         bench_draft(args, cid)
         return

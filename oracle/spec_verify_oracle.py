@@ -395,3 +395,67 @@ def verify_tree_batch(logits, parents, tokens, dtype="bf16", seqs=None):
     B = parents.shape[0]
     seqs = range(B) if seqs is None else seqs
     return [verify_tree_sequence(widen(logits[b], dtype), parents[b], tokens[b]) for b in seqs]
+
+
+# ----------------------------------------------------------------------------
+# end-to-end loop on a Markov-chain model pair
+# ----------------------------------------------------------------------------
+def markov_transitions(table: np.ndarray, T: float) -> np.ndarray:
+    """P[s] = softmax(table[s] / T): the tempered next-token law after token s
+    of a first-order Markov 'model' whose logits after s are table[s]."""
+    return np.stack([tempered_softmax(table[s], T)[0] for s in range(table.shape[0])])
+
+
+def expected_tokens_per_call(P: np.ndarray, Q: np.ndarray, gamma: int) -> np.ndarray:
+    """E[n + 1 | s0] for every start token s0: tokens emitted by one verify call
+    (accepted drafts plus the corrected or bonus token) when the draft chain
+    has law Q and the target chain law P.
+
+    A draft x ~ q is accepted with probability min(1, p(x)/q(x)), so a position
+    after token s emits an accepted token v with probability min(P[s, v],
+    Q[s, v]) ([SD] "Referee Report", second minor comment: the accepted count
+    rests on this overlap). With M = min(P, Q) element-wise, the probability
+    that the first k drafts are all accepted, from s0, is (M^k 1)[s0]; the call
+    emits n + 1 tokens and E[n + 1] = sum_{k=0..gamma} (M^k 1)[s0]. For i.i.d.
+    positions this is the closed form (1 - alpha^(gamma+1)) / (1 - alpha)."""
+    M = np.minimum(P, Q)
+    v = np.ones(P.shape[0])
+    total = v.copy()
+    for _ in range(gamma):
+        v = M @ v
+        total += v
+    return total
+
+
+def markov_loop(Lt_table: np.ndarray, Ld_table: np.ndarray, T: float, state0: int, u_draft: np.ndarray,
+                u_verify: np.ndarray):
+    """Speculative decoding of one chain for len(u_draft) iterations ([SD]
+    "The pith": the draft proposes gamma tokens from its own law, the target
+    scores them in one pass, the longest accepted prefix and one corrected or
+    bonus token are kept). Iteration k draws x_i ~ q(. | previous token) with
+    draft_sample_row at u_draft[k][i], then verifies with verify_sample_sequence
+    on target rows Lt_table[s], Lt_table[x_0], ..., Lt_table[x_{gamma-1}] and
+    draft rows Ld_table[s], Ld_table[x_0], ..., Ld_table[x_{gamma-2}] at
+    u_verify[k]. Returns a list of (n, emitted tokens) per iteration; stops at
+    an invalid step."""
+    out = []
+    s = int(state0)
+    K, gamma = u_draft.shape
+    for k in range(K):
+        prev = s
+        x = []
+        for i in range(gamma):
+            r = draft_sample_row(Ld_table[prev], T, float(u_draft[k, i]))
+            if not r.valid:
+                return out
+            x.append(r.y)
+            prev = r.y
+        rows_t = Lt_table[[s] + x]
+        rows_d = Ld_table[[s] + x[:-1]]
+        res = verify_sample_sequence(rows_t, rows_d, x, u_verify[k].astype(np.float64), T)
+        if not res.valid:
+            return out
+        emitted = list(x[: res.n]) + [res.y]
+        out.append((res.n, emitted))
+        s = emitted[-1]
+    return out

@@ -507,3 +507,34 @@ def make_draft_workload(cid: int, seed: int = 0) -> DraftRows:
     cfg = CONFIGS[cid]
     return make_draft_rows(cfg.B, cfg.V, cfg.draft_dtype, temperatures(cfg, seed, cfg.B), seed, cfg.target_sd,
                            cid=200 + cid, name=f"draft rows of config {cid}")
+
+
+# --------------------------------------------------------------------------
+# synthetic Markov-chain models (end-to-end loop)
+# --------------------------------------------------------------------------
+@dataclass
+class MarkovTables:
+    """Next-token logits of a first-order Markov 'target model' and a perturbed
+    'draft model': row s holds the logits after token s. Stored in dtype."""
+    V: int
+    dtype: str
+    target: np.ndarray  # [V][V]
+    draft: np.ndarray   # [V][V]
+    seed: int
+
+
+def make_markov_tables(V: int, dtype: str = "f32", seed: int = 0, target_sd: float = 2.0,
+                       noise_sd: float = 0.8, cid: int = 300) -> MarkovTables:
+    st = np.uint16 if dtype == "bf16" else np.float32
+    tq = np.empty((V, V), dtype=st)
+    dq = np.empty((V, V), dtype=st)
+
+    def rows(r0):  # one generator per block of 64 rows, so blocks run in parallel
+        r1 = min(V, r0 + 64)
+        t32 = gen(seed, cid, S_TARGET, r0).standard_normal((r1 - r0, V), dtype=np.float32) * np.float32(target_sd)
+        tq[r0:r1] = _to_dtype(t32, dtype)
+        z = gen(seed, cid, S_DRAFT, r0).standard_normal((r1 - r0, V), dtype=np.float32) * np.float32(noise_sd)
+        dq[r0:r1] = _to_dtype(decode(tq[r0:r1], dtype) + z, dtype)
+
+    _pmap(rows, range(0, V, 64))
+    return MarkovTables(V, dtype, tq, dq, seed)
