@@ -122,3 +122,33 @@ def test_stream_law_and_tokens_per_call(gpu):
         mean = c[s, 0] / m[s]
         sd = np.sqrt(max(c[s, 1] / m[s] - mean ** 2, 1e-12))
         assert abs(mean - E[s]) < 5 * sd / np.sqrt(m[s]), (s, mean, E[s])
+
+
+def test_graph_replay_matches_eager(gpu):
+    """The captured iteration, replayed with eager work and synchronisations
+    between replays, gives the eager loop's outputs at every iteration."""
+    from lossless_draft_verification_05_amd.markov import MarkovLoop
+
+    V, G, B, K, T = 203, 4, 12, 8, 0.9
+    H.log(f"markov graph replay vs eager: V={V} gamma={G} chains={B} iterations={K}")
+    tabs = synth.make_markov_tables(V, "f32", seed=9)
+    temps = torch.full((B,), T, dtype=torch.float32, device="cuda")
+    g = np.random.default_rng(10)
+    ud = torch.from_numpy(synth.uniforms_u24(g, (K, B, G))).cuda()
+    uv = torch.from_numpy(synth.uniforms_u24(g, (K, B, G + 1))).cuda()
+    s0 = torch.from_numpy(np.arange(B) * 5 % V).long().cuda()
+    eager = MarkovLoop(_dev(tabs.target, "f32"), _dev(tabs.draft, "f32"), G, temps)
+    state = s0.clone()
+    ref = []
+    for k in range(K):
+        n, tok, state = eager.step(state, ud[k], uv[k])
+        ref.append((n.cpu().numpy().copy(), tok.cpu().numpy().copy()))
+    graphed = MarkovLoop(_dev(tabs.target, "f32"), _dev(tabs.draft, "f32"), G, temps)
+    graphed.capture(s0, ud[0], uv[0])
+    graphed.g_state.copy_(s0)
+    for k in range(K):
+        n, tok = graphed.replay(ud[k], uv[k])
+        got = (n.cpu().numpy().copy(), tok.cpu().numpy().copy())
+        torch.randn(1000, device="cuda").sum().item()  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(got[0], ref[k][0]) and np.array_equal(got[1], ref[k][1]), k
