@@ -18,6 +18,10 @@ Workload m runs the end-to-end loop on a synthetic Markov-chain model pair
 iteration gamma draft-sampler calls, the target-row gathers and one verify;
 value = emitted tokens per second.
 
+Workloads t4 and t1024 time the draft-tree mask builder (spec_tree_mask: tree
+mask, relaxed block mask and depths): the configuration-4 trees (32 x 60
+nodes, 2-token blocks) and 32 random trees of 1024 nodes.
+
 Workloads (the five input configurations): c1 tiny sampling (B=10^4 trials,
 gamma=4, V=32, fp32), c2 7B-class vocab (B=64, gamma=4, V=32000, bf16), c3
 large vocab (B=256, gamma=8, V=128256, bf16, T=0.7), c4 greedy tree (B=32,
@@ -48,7 +52,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 PEAK_HBM_GBPS = float(os.environ.get("SV_PEAK_HBM_GBPS", "8000"))
-WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "d3": 3, "d5": 5, "m": 0}
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "d3": 3, "d5": 5, "m": 0, "t4": 4, "t1024": 4}
 MARKOV = dict(B=512, V=16384, gamma=5, T=1.0, dtype="bf16", noise_sd=0.8)
 CSRC = os.path.join(ROOT, "lossless_draft_verification_05_amd", "csrc")
 
@@ -295,6 +299,92 @@ def bench_markov(args):
     print(json.dumps(line), flush=True)
 
 
+def _oracle_masks(b):
+    from oracle import spec_verify_oracle as O
+
+    P, Bl = _CPU_DATA
+    O.tree_masks(P[b], Bl[b])
+    return 1
+
+
+def bench_masks(args):
+    """spec_tree_mask on the configuration-4 trees (t4) or 32 random
+    1024-node trees (t1024); HIP events around each call."""
+    if args.workload == "t4":
+        ti = synth.make_tree_inputs(4, seed=args.seed)
+        P = ti.parents
+        desc = "t4: masks of the configuration-4 draft trees"
+    else:
+        g = synth.gen(args.seed, 4, 2, 1024)
+        P = np.stack([[-1] + [int(g.integers(max(0, j - 16), j)) for j in range(1, 1024)] for _ in range(32)])
+        P = P.astype(np.int32)
+        desc = "t1024: masks of 32 random 1024-node trees"
+    Bl = np.stack([synth.tree_blocks(p) for p in P]).astype(np.int32)
+    B, N = P.shape
+    cpu = None
+    if not args.no_cpu_baseline:
+        import multiprocessing as mp
+
+        global _CPU_DATA
+        _CPU_DATA = (P, Bl)
+        t0 = time.perf_counter()
+        _oracle_masks(0)
+        t_one = max(time.perf_counter() - t0, 1e-5)
+        workers = max(1, min(16, os.cpu_count() or 1))
+        S = int(min(50 * B, max(workers, 10.0 * workers / t_one)))
+        with mp.get_context("fork").Pool(workers) as pool:
+            t0 = time.perf_counter()
+            pool.map(_oracle_masks, [i % B for i in range(S)], chunksize=max(1, S // (4 * workers)))
+            dt = time.perf_counter() - t0
+        _CPU_DATA = None
+        cpu = {"value": S / dt, "unit": "trees/s", "cores": workers, "kind": "oracle",
+               "sample": f"{S} trees (index mod {B}), python loops, {workers} worker processes, {dt:.1f} s"}
+        log(f"[bench] cpu baseline: {cpu}")
+    import torch
+
+    from lossless_draft_verification_05_amd import binding
+
+    binding.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    Pt, Blt = torch.from_numpy(P).to(dev), torch.from_numpy(Bl).to(dev)
+    R = int(min(64, max(1, -(-(512 << 20) // (2 * B * N * N)))))
+    outs = [(torch.empty((B, N, N), dtype=torch.uint8, device=dev), torch.empty((B, N, N), dtype=torch.uint8,
+             device=dev), torch.empty((B, N), dtype=torch.int32, device=dev)) for _ in range(R)]
+
+    def call(k):
+        m, r, d = outs[k % R]
+        binding.spec_tree_mask(Pt, Blt, want_relaxed=True, out_mask=m, out_relaxed=r, out_depth=d)
+    for k in range(args.warmup):
+        call(k)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k][0].record()
+        call(k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = 2 * B * N * N + B * N * 4 * 3  # both masks written, parents and blocks read, depths written
+    achieved = nbytes / (kern * 1e-3) / 1e9
+    line = {
+        "metric": "draft-tree masks/sec + achieved HBM GB/s (% peak), spec_tree_mask at 1 GPU",
+        "value": B / (ms * 1e-3), "unit": "trees/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic: seeded draft-tree parent arrays",
+        "config": {"workload": desc, "B": B, "N": N, "block": 2, "seed": args.seed},
+        "roofline": {"bound": "hbm", "kernel": "sv_mask_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_from_profiles(args.workload, kernel_source_sha())},
+        "cpu_baseline": cpu,
+        "detail": {"kernels": {"sv_mask_kernel": {"mean_us": round(kern * 1e3, 3), "alg_bytes": nbytes}},
+                   "output_copies": R, "kernel_source_sha": kernel_source_sha()},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(inp, tree: bool, budget_s: float = 15.0):
     """Time the oracle over the first S sequences in a pool of worker processes
     (fork, before the GPU is touched). S is sized from a one-sequence probe so
@@ -410,6 +500,9 @@ def main():
     cid = WORKLOADS[args.workload]
     if args.workload == "m":
         bench_markov(args)
+        return
+    if args.workload.startswith("t"):
+        bench_masks(args)
         return
     if args.workload.startswith("d"):
         bench_draft(args, cid)

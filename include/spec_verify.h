@@ -253,6 +253,30 @@ int spec_verify_greedy_tree_stage(int stage, const void* target_logits, int dtyp
                                   int32_t* out_argmax, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Text of a status code (static storage). */
+/*
+ * spec_tree_mask -- attention masks and positions of B draft trees.
+ *
+ * Defines: [Falcon] "What carries the argument" (the target verifies the
+ * tree's candidate branches in one parallel pass; the drafter uses a relaxed
+ * causal mask under which the tokens of one k-token block attend to each
+ * other) and "Assumptions & free parameters" (the relaxed mask must keep the
+ * causality verification needs). For tree b with parent array parents[b]
+ * (parents[b][0] = -1, 0 <= parents[b][j] < j):
+ *   out_mask[b][i][j]    = 1 iff node j is node i or one of its ancestors
+ *                          (the target's tree-attention mask), else 0;
+ *   out_relaxed[b][i][j] = out_mask[b][i][j] or (blocks[b][i] >= 0 and
+ *                          blocks[b][i] == blocks[b][j]) (the drafter's mask);
+ *   out_depth[b][i]      = depth of node i (root 0): its position offset.
+ * blocks [B][N] int32 (nodes proposed together share an id, -1 = none) is
+ * needed only for out_relaxed. Masks are uint8 [B][N][N], row-major, any
+ * alignment; int32 arrays 4-byte aligned. Any output may be NULL. A tree with
+ * an invalid parent array gets all-zero masks and depth -1. No workspace.
+ * Errors: SV_ERR_NULL (parents NULL, or out_relaxed without blocks),
+ * SV_ERR_SHAPE (B or N out of range), SV_ERR_ALIGN, SV_ERR_HIP.
+ */
+int spec_tree_mask(const int32_t* parents, const int32_t* blocks, int B, int N, uint8_t* out_mask,
+                   uint8_t* out_relaxed, int32_t* out_depth, void* stream);
+
 const char* sv_status_string(int status);
 
 /* hipError_t of the last failed HIP call made by this thread inside the library (0 = none). */

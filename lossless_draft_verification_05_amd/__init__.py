@@ -11,7 +11,7 @@ call does, and fails loudly if the library is missing.
 def __getattr__(name):
     if name in ("spec_verify_sample", "spec_verify_sample_stage", "spec_verify_sample_early_exit", "spec_draft_sample",
                 "spec_verify_greedy_tree",
-                "spec_verify_greedy_tree_stage",
+                "spec_verify_greedy_tree_stage", "spec_tree_mask",
                 "sv_sample_workspace_bytes", "sv_tree_workspace_bytes", "Workspace"):
         from . import binding
 

@@ -40,6 +40,7 @@ SIGNATURES = {
     "sv_draft_workspace_bytes": (_sz, [_i32, _i32]),
     "spec_draft_sample": (_i32, [_vp, _i32, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "spec_draft_sample_stage": (_i32, [_i32, _vp, _i32, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "spec_tree_mask": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "sv_status_string": (ctypes.c_char_p, [_i32]),
     "sv_last_hip_error": (_i32, []),
     "sv_version": (ctypes.c_char_p, []),
@@ -309,3 +310,32 @@ def spec_verify_greedy_tree_stage(stage, logits, parents, tokens, *, out_accept_
 
 def version() -> str:
     return load().sv_version().decode()
+
+
+def spec_tree_mask(parents, blocks=None, *, want_mask=True, want_relaxed=False, want_depth=True, out_mask=None,
+                   out_relaxed=None, out_depth=None, stream=None):
+    """Tree-attention masks of B draft trees (see include/spec_verify.h). parents [B][N] int32 (and blocks
+    [B][N] int32 for the relaxed mask). Returns (mask uint8 [B][N][N] or None, relaxed or None, depth int32
+    [B][N] or None)."""
+    lib = load()
+    if not isinstance(parents, torch.Tensor) or parents.dim() != 2:
+        raise ValueError("parents must be a 2-d tensor [B][N]")
+    B, N = parents.shape
+    dev = parents.device
+    _need(parents, "parents", torch.int32, (B, N))
+    if blocks is not None:
+        _need(blocks, "blocks", torch.int32, (B, N))
+    if want_mask and out_mask is None:
+        out_mask = torch.empty((B, N, N), dtype=torch.uint8, device=dev)
+    if want_relaxed and out_relaxed is None:
+        out_relaxed = torch.empty((B, N, N), dtype=torch.uint8, device=dev)
+    if want_depth and out_depth is None:
+        out_depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    for t, name in ((out_mask, "out_mask"), (out_relaxed, "out_relaxed")):
+        if t is not None:
+            _need(t, name, torch.uint8, (B, N, N))
+    if out_depth is not None:
+        _need(out_depth, "out_depth", torch.int32, (B, N))
+    _check(lib.spec_tree_mask(_ptr(parents), _ptr(blocks), B, N, _ptr(out_mask), _ptr(out_relaxed),
+                              _ptr(out_depth), _stream(stream)), "spec_tree_mask")
+    return out_mask, out_relaxed, out_depth

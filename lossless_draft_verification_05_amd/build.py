@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspec_verify.so")
-SOURCES = ["sv_api.hip", "sv_sample.hip", "sv_tree.hip"]
+SOURCES = ["sv_api.hip", "sv_sample.hip", "sv_tree.hip", "sv_mask.hip"]
 ARCH = os.environ.get("SV_OFFLOAD_ARCH", "gfx950")
 
 

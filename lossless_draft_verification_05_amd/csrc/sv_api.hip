@@ -5,6 +5,7 @@
 
 #include <stdint.h>
 #include <string.h>
+#include <algorithm>
 
 #include "../../include/spec_verify.h"
 #include "sv_plan.hpp"
@@ -13,6 +14,7 @@ namespace sv {
 hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stage, hipStream_t stream);
 hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int p0, int p1, hipStream_t stream);
 hipError_t launch_tree(const TreeLaunch& A, int dt, int stage, hipStream_t stream);
+hipError_t launch_mask(const MaskLaunch& A, hipStream_t stream);
 
 static thread_local int g_last_hip_error = 0;
 
@@ -232,6 +234,30 @@ int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, i
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
   return run_sample_early(a, (hipStream_t)stream);
+}
+
+int spec_tree_mask(const int32_t* parents, const int32_t* blocks, int B, int N, uint8_t* out_mask,
+                   uint8_t* out_relaxed, int32_t* out_depth, void* stream) {
+  if (!parents || (out_relaxed && !blocks)) return SV_ERR_NULL;
+  if (B < 1 || B > SV_MAX_BATCH || N < 1 || N > SV_MAX_TREE_NODES) return SV_ERR_SHAPE;
+  if (!aligned(parents, 4) || !aligned(blocks, 4) || !aligned(out_depth, 4)) return SV_ERR_ALIGN;
+  if (!out_mask && !out_relaxed && !out_depth) return SV_OK;
+  MaskLaunch L;
+  L.parents = parents;
+  L.blocks = blocks;
+  L.B = B;
+  L.N = N;
+  // rows per workgroup: about kMaskSlabBytes of mask, and their ancestor
+  // bitsets (ceil(N / 32) words per row) within the kernel's LDS array
+  const int64_t nslab0 = ceil_div((int64_t)N * N, kMaskSlabBytes);
+  const int64_t words = ceil_div(N, 32);
+  L.rows_per_slab = (int)std::min<int64_t>(ceil_div(N, nslab0), kMaskSlabBytes / 32 / words);
+  L.nslab = (int)ceil_div(N, L.rows_per_slab);
+  if ((int64_t)B * L.nslab > 0x7fffffffLL) return SV_ERR_SHAPE;
+  L.out_mask = out_mask;
+  L.out_relaxed = out_relaxed;
+  L.out_depth = out_depth;
+  return hip_status(launch_mask(L, (hipStream_t)stream));
 }
 
 size_t sv_draft_workspace_bytes(int B, int V) {

@@ -114,6 +114,19 @@ struct TreeLaunch {
   ArgPartial* part;  // [B][N][nch][kWaves]
 };
 
+constexpr int kMaxMaskNodes = 1024;  // tree masks: nodes per tree
+constexpr int64_t kMaskSlabBytes = 64 << 10;  // tree masks: mask bytes per workgroup
+
+struct MaskLaunch {
+  const int32_t* parents;  // [B][N]
+  const int32_t* blocks;   // [B][N] or null
+  int B, N;
+  int nslab, rows_per_slab;
+  uint8_t* out_mask;     // [B][N][N] or null
+  uint8_t* out_relaxed;  // [B][N][N] or null
+  int32_t* out_depth;    // [B][N] or null
+};
+
 // ---------------------------------------------------------------------------
 // host-side decomposition helpers (pure integer arithmetic)
 // ---------------------------------------------------------------------------

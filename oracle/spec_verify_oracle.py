@@ -459,3 +459,44 @@ def markov_loop(Lt_table: np.ndarray, Ld_table: np.ndarray, T: float, state0: in
         out.append((res.n, emitted))
         s = emitted[-1]
     return out
+
+
+# ----------------------------------------------------------------------------
+# draft-tree attention masks
+# ----------------------------------------------------------------------------
+def parents_valid(parents) -> bool:
+    """parents[0] = -1 and 0 <= parents[j] < j for j >= 1."""
+    N = len(parents)
+    if N == 0 or int(parents[0]) != -1:
+        return False
+    return all(0 <= int(parents[j]) < j for j in range(1, N))
+
+
+def tree_masks(parents, blocks=None):
+    """Attention masks of one draft tree ([Falcon] "What carries the
+    argument": the target checks every branch of the tree in one pass, so a
+    node sees exactly its own path to the root; the drafter's relaxed causal
+    mask also lets the tokens of one block see each other).
+
+    Returns (mask, relaxed, depth): mask[i][j] = 1 iff j == i or j is an
+    ancestor of i; relaxed = mask or (blocks[i] >= 0 and blocks[i] ==
+    blocks[j]) (None without blocks); depth[i] = number of parent steps to the
+    root. An invalid parent array gives all-zero masks and depth -1."""
+    N = len(parents)
+    mask = np.zeros((N, N), dtype=np.uint8)
+    depth = np.full(N, -1, dtype=np.int32)
+    relaxed = None if blocks is None else np.zeros((N, N), dtype=np.uint8)
+    if not parents_valid(parents):
+        return mask, relaxed, depth
+    for i in range(N):
+        a, d = i, 0
+        while a >= 0:
+            mask[i, a] = 1
+            a = int(parents[a])
+            d += 1
+        depth[i] = d - 1
+    if blocks is not None:
+        for i in range(N):
+            for j in range(N):
+                relaxed[i, j] = 1 if mask[i, j] or (blocks[i] >= 0 and blocks[i] == blocks[j]) else 0
+    return mask, relaxed, depth

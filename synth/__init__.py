@@ -538,3 +538,19 @@ def make_markov_tables(V: int, dtype: str = "f32", seed: int = 0, target_sd: flo
 
     _pmap(rows, range(0, V, 64))
     return MarkovTables(V, dtype, tq, dq, seed)
+
+
+def tree_blocks(parents: np.ndarray, block: int = 2) -> np.ndarray:
+    """Block ids of a draft tree built by tree_shape: the nodes a drafter
+    proposes together in one block of ``block`` tokens share an id (the index
+    of the block's first node); a node at depth d >= 1 starts a block when
+    (d - 1) is a multiple of ``block``, else it continues its parent's. The
+    root (the already accepted token) has id -1."""
+    N = len(parents)
+    depth = np.zeros(N, dtype=np.int64)
+    blk = np.full(N, -1, dtype=np.int32)
+    for j in range(1, N):
+        p = int(parents[j])
+        depth[j] = depth[p] + 1
+        blk[j] = j if (depth[j] - 1) % block == 0 else blk[p]
+    return blk

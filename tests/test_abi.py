@@ -169,3 +169,17 @@ def test_draft_unknown_stage_and_workspace_query(lib):
     assert call_draft(lib, stage=3) == -7 and call_draft(lib, stage=0) == -7
     assert lib.sv_draft_workspace_bytes(0, 10) == 0 and lib.sv_draft_workspace_bytes(4, 0) == 0
     assert lib.sv_draft_workspace_bytes(4, 1000) > 0
+
+
+def test_tree_mask_argument_errors(lib):
+    A = 0x10000000
+    f = lib.spec_tree_mask
+    assert f(None, None, 2, 5, A, None, None, None) == -1             # parents NULL
+    assert f(A, None, 2, 5, A, A + 0x1000, None, None) == -1          # relaxed without blocks
+    assert f(A, None, 0, 5, A, None, None, None) == -2                # B = 0
+    assert f(A, None, 2, 0, A, None, None, None) == -2                # N = 0
+    assert f(A, None, 2, 1025, A, None, None, None) == -2             # N too large
+    assert f(A + 2, None, 2, 5, A, None, None, None) == -4            # parents misaligned
+    assert f(A, A + 1, 2, 5, A, A + 0x1000, None, None) == -4         # blocks misaligned
+    assert f(A, None, 2, 5, None, None, A + 0x2002, None) == -4       # depth misaligned
+    assert f(A, None, 2, 5, None, None, None, None) == 0              # nothing requested: no launch
