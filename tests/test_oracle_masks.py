@@ -69,3 +69,19 @@ def test_closed_forms():
 def test_invalid(parents):
     m, r, d = O.tree_masks(np.array(parents, np.int32), np.zeros(len(parents), np.int32))
     assert not m.any() and not r.any() and (d == -1).all()
+
+
+def test_nodes_without_a_block_see_only_their_path():
+    """Block id -1 means 'no block': with no blocks at all the relaxed mask is
+    the tree mask, and two unblocked nodes never see each other through it."""
+    g = np.random.default_rng(9)
+    N = 25
+    parents = np.array([-1] + [int(g.integers(0, j)) for j in range(1, N)], dtype=np.int32)
+    mask, relaxed, _ = O.tree_masks(parents, np.full(N, -1, np.int32))
+    assert np.array_equal(relaxed, mask)
+    blocks = np.where(np.arange(N) % 3 == 0, -1, np.arange(N) // 6).astype(np.int32)
+    mask, relaxed, _ = O.tree_masks(parents, blocks)
+    for i in range(N):
+        for j in range(N):
+            if blocks[i] == -1 or blocks[j] == -1:
+                assert relaxed[i, j] == mask[i, j]
