@@ -112,7 +112,7 @@ def cpu_baseline_draft(d, budget_s: float = 15.0):
     _oracle_draft(0)
     t_one = max(time.perf_counter() - t0, 1e-5)
     workers = max(1, min(16, os.cpu_count() or 1))
-    S = int(min(50 * d.B, max(workers, budget_s * workers / t_one)))
+    S = int(min(2_000_000, max(workers, budget_s * workers / t_one)))
     with mp.get_context("fork").Pool(workers) as pool:
         t0 = time.perf_counter()
         pool.map(_oracle_draft, [i % d.B for i in range(S)], chunksize=max(1, S // (4 * workers)))
@@ -331,7 +331,7 @@ def bench_masks(args):
         _oracle_masks(0)
         t_one = max(time.perf_counter() - t0, 1e-5)
         workers = max(1, min(16, os.cpu_count() or 1))
-        S = int(min(50 * B, max(workers, 10.0 * workers / t_one)))
+        S = int(min(200_000, max(workers, 10.0 * workers / t_one)))
         with mp.get_context("fork").Pool(workers) as pool:
             t0 = time.perf_counter()
             pool.map(_oracle_masks, [i % B for i in range(S)], chunksize=max(1, S // (4 * workers)))
@@ -401,7 +401,7 @@ def cpu_baseline(inp, tree: bool, budget_s: float = 15.0):
     t_one = max(time.perf_counter() - t0, 1e-5)
     workers = max(1, min(16, os.cpu_count() or 1))
     # cycle over the batch (b mod B) when the whole batch takes less than the budget
-    S = int(min(50 * B, max(workers, budget_s * workers / t_one)))
+    S = int(min(2_000_000, max(workers, budget_s * workers / t_one)))
     ctx = mp.get_context("fork")
     with ctx.Pool(workers) as pool:
         t0 = time.perf_counter()

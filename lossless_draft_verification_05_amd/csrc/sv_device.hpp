@@ -127,6 +127,14 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dpp_f64<kDppQuadXor1>(v));
+  v = fmax(v, dpp_f64<kDppQuadXor2>(v));
+  v = fmax(v, dpp_f64<kDppRowRor4>(v));
+  v = fmax(v, dpp_f64<kDppRowRor8>(v));
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
   v += dpp_f64<kDppQuadXor1>(v);
   v += dpp_f64<kDppQuadXor2>(v);

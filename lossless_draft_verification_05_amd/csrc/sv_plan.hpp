@@ -28,10 +28,13 @@ constexpr double kEarlyLaunchBytes = 64e6;      // bytes moved in about the time
 enum : int { kModeResidual = 0, kModeBonus = 1 };
 
 // Partial statistics of one wave's share of one chunk of one logits row
-// (stats pass): s = sum of exp2((x - m_ref) * kl); m_true = max x.
+// (stats pass), against a reference logit m (a value of the share, or -inf if
+// every value was -inf):
+//   form 1: s = sum of exp2(x * kl - c), c = fp32(m * kl) rounded once;
+//   form 0: s = sum of exp2((x - m) * kl)  (reference m * kl, exact in fp64).
 struct RowPartial {
-  float m_ref;
-  float m_true;
+  float m;
+  int form;
   double s;
 };
 
@@ -46,7 +49,8 @@ struct RowPartial {
 //    so e_q carries the ratio of the normalisers; corr = (exact cq - cq) * ln 2
 //    removes, to first order, the rounding of cq. r = F * Sp * max(0, p - q)
 //    with F = exp2(mp * kl - cp) (fscale).
-//  form 0 (used when a shift would leave the fp32 range):
+//  form 0 (used when a shift is 2^24 or more in magnitude, where its fp32
+//  rounding would be half a log2 unit or more):
 //    e_p = exp2((x_t - mp) * kl), e_q = exp2((x_d - mq) * kl),
 //    r = max(0, e_p - kappa e_q) with kappa = Sp / Sq as a float pair; F = 1.
 struct SeqPlan {

@@ -33,21 +33,87 @@ constexpr int kMaxRows = 2 * 64 + 1;
 // ---------------------------------------------------------------------------
 // streaming tempered sum-exp
 // ---------------------------------------------------------------------------
+// Per-lane state of the statistics pass. Terms are taken against a reference
+// logit m that moves up only when a new value would make a term exceed 2^64
+// (about once per lane and row), so the common case computes no maximum:
+//  FMA form: term = exp2(fma(x, kl, -c)) with c = fp32(m * kl) rounded once,
+//   so s sums 2^(x * kl - c) exactly up to the rounding of each term;
+//  subtract form, used when |m * kl| >= 2^24 (c would then round by half a
+//   log2 unit or more): term = exp2((x - m) * kl).
+// m = c = -inf while every value seen was -inf.
 struct SumExp {
-  float m_ref;   // terms are exp2((x - m_ref) * kl)
-  float m_true;  // running maximum
+  float m;
+  float c;
+  double s;
+  int ovf;  // |m * kl| >= 2^24: the chunk is redone in the subtract form
+};
+
+template <int DT, int NU>
+__device__ __forceinline__ float terms_fma(const Unit<DT> (&un)[NU], float kl, float c) {
+  constexpr int E = Unit<DT>::kEpu;
+  float u[NU];
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
+    float e[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) e[k] = hw_exp2(fmaf(un[j].x[k], kl, -c));
+    if constexpr (E == 8)
+      u[j] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    else
+      u[j] = (e[0] + e[1]) + (e[2] + e[3]);
+  }
+  if constexpr (NU == 8)
+    return ((u[0] + u[1]) + (u[2] + u[3])) + ((u[4] + u[5]) + (u[6] + u[7]));
+  else if constexpr (NU == 4)
+    return (u[0] + u[1]) + (u[2] + u[3]);
+  else if constexpr (NU == 2)
+    return u[0] + u[1];
+  else
+    return u[0];
+}
+
+template <int DT, int NU>
+__device__ __forceinline__ void sumexp_fma(SumExp& st, const Unit<DT> (&un)[NU], float kl) {
+  float a = terms_fma<DT, NU>(un, kl, st.c);
+  if (!(a <= 0x1p64f)) {
+    // a value above the reference by more than 64 / kl, the first finite
+    // value, +inf or NaN: move the reference to the batch maximum and redo
+    float gm = unit_max(un[0]);
+    bool nan = false;
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+      gm = fmaxf(gm, unit_max(un[j]));
+#pragma unroll
+      for (int k = 0; k < Unit<DT>::kEpu; ++k) nan |= un[j].x[k] != un[j].x[k];
+    }
+    if (gm > st.m) {
+      const float cn = __fmul_rn(gm, kl);
+      // c must round by less than half a log2 unit, or the terms near the
+      // maximum leave the fp32 range: |c| < 2^24, else the subtract form
+      if (!(fabsf(cn) < 0x1p24f) && __builtin_isfinite(gm)) st.ovf = 1;
+      st.s *= exp2((double)st.c - (double)cn);
+      st.m = gm;
+      st.c = cn;
+    }
+    a = (st.c == -INFINITY) ? 0.0f : terms_fma<DT, NU>(un, kl, st.c);
+    if (nan) a = __builtin_nanf("");
+  }
+  st.s += (double)a;
+}
+
+// Subtract form: reference m_ref starts at -FLT_MAX and moves to the batch
+// maximum when that exceeds it by more than 64 / kl.
+struct SumExpSub {
+  float m_ref;
   double s;
 };
 
 template <int DT, int NU>
-__device__ __forceinline__ void sumexp_units(SumExp& st, const Unit<DT> (&un)[NU], float kl) {
+__device__ __forceinline__ void sumexp_sub(SumExpSub& st, const Unit<DT> (&un)[NU], float kl) {
   constexpr int E = Unit<DT>::kEpu;
   float gm = unit_max(un[0]);
 #pragma unroll
   for (int j = 1; j < NU; ++j) gm = fmaxf(gm, unit_max(un[j]));
-  st.m_true = fmaxf(st.m_true, gm);
-  // The reference only moves when new values would push a term past 2^64, so
-  // the rescale below is taken about once per lane and per row.
   if ((gm - st.m_ref) * kl > 64.0f) {
     st.s *= (double)hw_exp2((st.m_ref - gm) * kl);
     st.m_ref = gm;
@@ -66,12 +132,20 @@ __device__ __forceinline__ void sumexp_units(SumExp& st, const Unit<DT> (&un)[NU
   }
 }
 
+template <int DT, int NU, class St>
+__device__ __forceinline__ void sumexp(St& st, const Unit<DT> (&un)[NU], float kl) {
+  if constexpr (sizeof(St) == sizeof(SumExp))
+    sumexp_fma<DT, NU>(st, un, kl);
+  else
+    sumexp_sub<DT, NU>(st, un, kl);
+}
+
 // The workgroup streams units [c_begin, c_end) of a row with V elements; thread
 // t takes units c_begin + t + 256 k, so every load instruction of the
 // workgroup covers one contiguous 4 KB block.
-template <int DT>
+template <int DT, class St>
 __device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int V, int64_t c_begin, int64_t c_end,
-                                              float kl, SumExp& st) {
+                                              float kl, St& st) {
   constexpr int E = Unit<DT>::kEpu;
   const int tid = threadIdx.x;
   const int64_t nu_row = ((int64_t)V + E - 1) / E;
@@ -86,7 +160,7 @@ __device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int 
     Unit<DT> un[kU1];
 #pragma unroll
     for (int j = 0; j < kU1; ++j) un[j].unpack(w[j]);
-    sumexp_units<DT, kU1>(st, un, kl);
+    sumexp<DT, kU1>(st, un, kl);
   }
 #pragma unroll
   for (int j = 0; j < kU1; ++j) {
@@ -95,7 +169,7 @@ __device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int 
       Unit<DT> un[1];
       un[0].unpack(load16(row + u * 16));
       if (ragged && u == nu_row - 1) mask_tail(un[0], u, V);
-      sumexp_units<DT, 1>(st, un, kl);
+      sumexp<DT, 1>(st, un, kl);
     }
   }
 }
@@ -116,38 +190,64 @@ __device__ __forceinline__ float load_elem(const char* row, int v) {
 // Partials of chunk slot r of sequence b: slots [0, (gamma+1) * nct) are the
 // target rows' chunks (row r / nct, chunk r % nct), the rest the draft rows'.
 // One partial per wave: (reference, sum relative to it, max).
-template <int TD, int DD>
-__device__ __forceinline__ void stats_chunk(const SampleLaunch& A, int b, int r, float kl) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+template <int DT, class St>
+__device__ __forceinline__ void stream_slot(const SampleLaunch& A, int b, int r, float kl, St& st) {
   const int tchunks = (A.gamma + 1) * A.nct;
-  SumExp st{-FLT_MAX, -INFINITY, 0.0};
   if (r < tchunks) {
     const int row = r / A.nct, c = r % A.nct;
     const char* p = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)row * A.t_row_b;
-    const int64_t nu = ((int64_t)A.V * Unit<TD>::kEsz + 15) / 16;
+    const int64_t nu = ((int64_t)A.V * Unit<DT>::kEsz + 15) / 16;
     const int64_t u0 = (int64_t)c * A.cut;
     const int64_t u1 = u0 + A.cut < nu ? u0 + A.cut : nu;
-    stream_sumexp<TD>(p, A.V, u0, u1, kl, st);
+    stream_sumexp<DT>(p, A.V, u0, u1, kl, st);
   } else {
     const int rr = r - tchunks;
     const int row = rr / A.ncd, c = rr % A.ncd;
     const char* p = A.dft + (int64_t)b * A.d_seq_b + (int64_t)row * A.d_row_b;
-    const int64_t nu = ((int64_t)A.V * Unit<DD>::kEsz + 15) / 16;
+    const int64_t nu = ((int64_t)A.V * Unit<DT>::kEsz + 15) / 16;
     const int64_t u0 = (int64_t)c * A.cud;
     const int64_t u1 = u0 + A.cud < nu ? u0 + A.cud : nu;
-    stream_sumexp<DD>(p, A.V, u0, u1, kl, st);
+    stream_sumexp<DT>(p, A.V, u0, u1, kl, st);
   }
-  const float M = wave_max(st.m_ref);
-  double s = st.s * (double)hw_exp2((st.m_ref - M) * kl);
-  s = wave_sum(s);
-  const float mt = wave_max(st.m_true);
-  if (lane == 0) {
-    RowPartial rp;
-    rp.m_ref = M;
-    rp.m_true = mt;
-    rp.s = s;
-    A.part[((int64_t)b * A.per_seq + r) * kWaves + w] = rp;
+}
+
+// Partials of chunk slot r of sequence b: slots [0, (gamma+1) * nct) are the
+// target rows' chunks (row r / nct, chunk r % nct), the rest the draft rows'.
+// One partial per wave. The chunk is streamed in the FMA form; if any lane's
+// reference needs the subtract form (|m * kl| >= 2^24: tiny temperatures or
+// huge logits), the workgroup streams the chunk again in that form.
+template <int TD, int DD>
+__device__ __forceinline__ void stats_chunk(const SampleLaunch& A, int b, int r, float kl) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const bool tgt = r < (A.gamma + 1) * A.nct;
+  RowPartial rp;
+  SumExp st{-INFINITY, -INFINITY, 0.0, 0};
+  if (tgt)
+    stream_slot<TD>(A, b, r, kl, st);
+  else
+    stream_slot<DD>(A, b, r, kl, st);
+  if (!__syncthreads_or(st.ovf)) {
+    const float Mc = wave_max(st.c);
+    if (Mc == -INFINITY) {
+      rp.s = wave_sum(st.s);  // every value -inf (s = 0) or NaN seen
+      rp.m = -INFINITY;
+    } else {
+      rp.s = wave_sum(st.s * (double)hw_exp2(st.c - Mc));
+      rp.m = wave_max(st.c == Mc ? st.m : -INFINITY);  // a lane whose reference is Mc
+    }
+    rp.form = 1;
+  } else {
+    SumExpSub ss{-FLT_MAX, 0.0};
+    if (tgt)
+      stream_slot<TD>(A, b, r, kl, ss);
+    else
+      stream_slot<DD>(A, b, r, kl, ss);
+    const float M = wave_max(ss.m_ref);
+    rp.s = wave_sum(ss.s * (double)hw_exp2((ss.m_ref - M) * kl));
+    rp.m = M;
+    rp.form = 0;
   }
+  if (lane == 0) A.part[((int64_t)b * A.per_seq + r) * kWaves + w] = rp;
 }
 
 // Statistics of a whole row from its nrec wave partials, computed by one wave
@@ -155,26 +255,31 @@ __device__ __forceinline__ void stats_chunk(const SampleLaunch& A, int b, int r,
 // the early-exit stats kernel, which must reach the same accept decisions bit
 // for bit; contraction is off so that inlining cannot change the rounding.
 struct RowStat {
-  float m;   // maximum
+  float m;   // reference logit: a value of the row, within 64 / kl of its maximum
   double s;  // sum_v exp2((x_v - m) * kl)
   int valid;
 };
+// Reference of a partial in log2 units, exactly as its terms were taken.
+__device__ __forceinline__ double partial_shift(const RowPartial& p, float kl) {
+  return p.form ? (double)__fmul_rn(p.m, kl) : (double)p.m * (double)kl;
+}
+
 __device__ __forceinline__ RowStat merge_row(const RowPartial* P, int nrec, float kl, bool tv, int lane) {
 #pragma clang fp contract(off)
-  float Mr = -FLT_MAX, mtr = -INFINITY;
-  for (int k = lane; k < nrec; k += kWave) {
-    Mr = fmaxf(Mr, P[k].m_ref);
-    mtr = fmaxf(mtr, P[k].m_true);
-  }
-  Mr = wave_max(Mr);
-  mtr = wave_max(mtr);
+  double Ms = -INFINITY;
+  for (int k = lane; k < nrec; k += kWave) Ms = fmax(Ms, partial_shift(P[k], kl));
+  Ms = wave_max_f64(Ms);
+  float Mm = -INFINITY;  // the reference logit of a partial at Ms (the largest such)
+  for (int k = lane; k < nrec; k += kWave)
+    if (partial_shift(P[k], kl) == Ms) Mm = fmaxf(Mm, P[k].m);
+  Mm = wave_max(Mm);
   double S = 0.0;
-  for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(((double)P[k].m_ref - (double)Mr) * (double)kl);
+  for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(partial_shift(P[k], kl) - Ms);
   S = wave_sum(S);
   RowStat r;
-  r.m = mtr;
-  r.s = S * exp2(((double)Mr - (double)mtr) * (double)kl);
-  r.valid = tv && __builtin_isfinite(r.s) && r.s > 0.0 && __builtin_isfinite(mtr);
+  r.m = Mm;
+  r.s = S * exp2(Ms - (double)Mm * (double)kl);
+  r.valid = tv && __builtin_isfinite(r.s) && r.s > 0.0 && __builtin_isfinite(Mm);
   return r;
 }
 
@@ -647,7 +752,8 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       Q.cp = (float)cp;
       const double dp = cp - (double)Q.cp;
       Q.fscale = exp2(dp);
-      bool fma_ok = fabs(cp) < 0x1p100;
+      // the shifts must round by less than half a log2 unit: |c| < 2^24
+      bool fma_ok = fabs(cp) < 0x1p24;
       if (n < G) {
         Q.mq = rM[G + 1 + n];
         Q.sq = rS[G + 1 + n];
@@ -657,7 +763,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
         const double cq = (double)Q.mq * kld - log2(kap) - dp;
         Q.cq = (float)cq;
         Q.corr = (float)((cq - (double)Q.cq) * 0.69314718055994530942);
-        fma_ok = fma_ok && fabs(cq) < 0x1p100;
+        fma_ok = fma_ok && fabs(cq) < 0x1p24;
       } else {
         Q.mq = 0.0f;
         Q.sq = 1.0;

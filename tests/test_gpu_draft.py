@@ -108,3 +108,15 @@ def test_bad_arguments_raise(gpu):
         gpu.spec_draft_sample(tens["logits"][:, :50].contiguous(), tens["uniforms"][:1], tens["temperature"])
     with pytest.raises(ValueError):
         gpu.spec_draft_sample(tens["logits"].double(), tens["uniforms"], tens["temperature"])
+
+
+@pytest.mark.parametrize("T", [1e-6, 1e-12, 1e-30])
+def test_temperature_extremes(gpu, T):
+    d = synth.make_draft_rows(6, 3000, "bf16", T=T, seed=31)
+    _assert(H.check_draft(d, H.run_draft(gpu, H.draft_tensors(d))), f"T={T}")
+
+
+def test_huge_logits(gpu):
+    """Logits around 10^8: the statistics pass takes its subtract form."""
+    d = synth.make_draft_rows(6, 4000, "f32", T=[0.5, 1.0, 1.0, 2.0, 1.0, 0.7], seed=32, sd=2e7)
+    _assert(H.check_draft(d, H.run_draft(gpu, H.draft_tensors(d))), "huge logits")

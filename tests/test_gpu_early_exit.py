@@ -115,3 +115,16 @@ def test_repeat_calls_bit_identical(gpu):
     r2 = H.run_sample(gpu, tens, early_exit=True)
     for k in r1:
         assert np.array_equal(r1[k].view(np.uint8), r2[k].view(np.uint8)), k
+
+
+@pytest.mark.parametrize("T", [1e-6, 1e-12, 1e-30])
+def test_temperature_extremes(gpu, T):
+    H.log(f"early exit T={T}")
+    inp = synth.make_custom_sample(6, 4, 2048, "bf16", "f32", T=T, noise_sd=0.5, seed=12)
+    _both(gpu, inp, name=f"T={T}")
+
+
+def test_huge_logits(gpu):
+    """Logits around 10^8 (N(0, 2e7)): the statistics pass takes its subtract form."""
+    inp = synth.make_custom_sample(6, 3, 3000, "f32", "f32", T=1.0, noise_sd=1e6, target_sd=2e7, seed=13)
+    _both(gpu, inp, name="huge logits")

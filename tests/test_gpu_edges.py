@@ -39,7 +39,7 @@ def test_gamma_extremes(gpu, G):
     _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), f"gamma={G}")
 
 
-@pytest.mark.parametrize("T", [0.05, 10.0, 1e-30])
+@pytest.mark.parametrize("T", [0.05, 10.0, 1e-6, 1e-12, 1e-30])
 def test_temperature_extremes(gpu, T):
     H.log(f"T={T}")
     inp = synth.make_custom_sample(6, 4, 2048, "bf16", "f32", T=T, noise_sd=0.5, seed=11)
