@@ -124,8 +124,9 @@ def cpu_baseline_draft(d, budget_s: float = 15.0):
 
 
 def bench_draft(args, cid):
-    """Time spec_draft_sample (stats kernel + draw kernel, HIP events on the
-    stream they run on) on the draft rows of configuration cid."""
+    """Time spec_draft_sample (the one-pass kernel where it applies, HIP events
+    on the stream it runs on) on the draft rows of configuration cid, and the
+    staged two-kernel path beside it."""
     log(f"[bench] building draft rows of config {cid} (seed {args.seed})")
     d = synth.make_draft_workload(cid, seed=args.seed)
     cpu = None if args.no_cpu_baseline else cpu_baseline_draft(d)
@@ -149,30 +150,40 @@ def bench_draft(args, cid):
     y = torch.empty(d.B, dtype=torch.int32, device=dev)
     ws = binding.Workspace()
 
-    def stages(c):
-        return [lambda s=s: binding.spec_draft_sample(copies[c], u, T, out_tokens=y, workspace=ws, stage=s)
-                for s in (1, 2)]
-    for k in range(args.warmup):
-        for f in stages(k % R):
-            f()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        e = evs[k]
-        e[0].record()
-        for i, f in enumerate(stages(k % R)):
-            f()
-            e[i + 1].record()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    st = [float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)])) for i in range(2)]
-    log(f"[bench] {ms:.4f} ms/step; kernel event means (ms): {st}")
+    def timed(calls_of):
+        """mean ms per step (wall clock) and per-call HIP-event means (ms)"""
+        for k in range(args.warmup):
+            for f in calls_of(k % R):
+                f()
+        torch.cuda.synchronize()
+        n = len(calls_of(0))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            e = evs[k]
+            e[0].record()
+            for i, f in enumerate(calls_of(k % R)):
+                f()
+                e[i + 1].record()
+        torch.cuda.synchronize()
+        ms_ = (time.perf_counter() - t0) * 1e3 / args.steps
+        return ms_, [float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                     for i in range(n)]
+
+    one_pass = d.B >= 128 or d.V * (2 if d.dtype == "bf16" else 4) <= (64 << 10)
+    ms, st = timed(lambda c: [lambda: binding.spec_draft_sample(copies[c], u, T, out_tokens=y, workspace=ws)])
+    log(f"[bench] {ms:.4f} ms/step; kernel event mean (ms): {st}")
+    ms2, st2 = timed(lambda c: [lambda s=s: binding.spec_draft_sample(copies[c], u, T, out_tokens=y, workspace=ws,
+                                                                      stage=s) for s in (1, 2)])
+    log(f"[bench] staged (two kernels): {ms2:.4f} ms/step; kernel event means (ms): {st2}")
     row_bytes = d.V * (2 if d.dtype == "bf16" else 4)
+    step_bytes = min(d.V, 2048) * (2 if d.dtype == "bf16" else 4)
     s1 = d.B * row_bytes + d.B * 8          # every logit once + temperatures, uniforms
-    s2 = d.B * row_bytes + d.B * 4          # the row again for the draw + the tokens
+    s_draw = d.B * step_bytes + d.B * 4     # the rescanned step + the tokens
     sha = kernel_source_sha()
-    achieved = s1 / (st[0] * 1e-3) / 1e9
+    kname = "sv_draft1_kernel" if one_pass else "sv_stats_kernel + sv_finish_kernel"
+    alg = s1 + s_draw if one_pass else 2 * s1 + s_draw
+    achieved = alg / (st[0] * 1e-3) / 1e9
     yy = y.cpu().numpy()
     line = {
         "metric": "sampled draft tokens/sec + achieved HBM GB/s (% peak), spec_draft_sample at 1 GPU",
@@ -181,16 +192,17 @@ def bench_draft(args, cid):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic: seeded logits standing in for draft model outputs",
         "config": {"workload": f"{args.workload}: draft rows of configuration {cid}", "B": d.B, "V": d.V,
                    "dtype": d.dtype, "seed": args.seed},
-        "roofline": {"bound": "hbm", "kernel": "sv_stats_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_from_profiles(args.workload, sha)},
         "cpu_baseline": cpu,
-        "detail": {"kernels": {"sv_stats_kernel": {"mean_us": round(st[0] * 1e3, 3), "alg_bytes": s1,
-                                                   "gbps": round(achieved, 1)},
-                               "sv_finish_kernel": {"mean_us": round(st[1] * 1e3, 3), "alg_bytes": s2,
-                                                    "gbps": round(s2 / (st[1] * 1e-3) / 1e9, 1)}},
-                   "input_copies": R, "kernel_source_sha": sha, "invalid": int((yy < 0).sum()),
-                   "step_alg_bytes": s1 + s2, "step_gbps": round((s1 + s2) / (ms * 1e-3) / 1e9, 1)},
+        "detail": {"kernels": {kname: {"mean_us": round(st[0] * 1e3, 3), "alg_bytes": alg,
+                                       "gbps": round(achieved, 1)}},
+                   "two_kernel_path": {"ms_per_step": ms2,
+                                       "sv_stats_kernel_us": round(st2[0] * 1e3, 3),
+                                       "sv_finish_kernel_us": round(st2[1] * 1e3, 3),
+                                       "alg_bytes": 2 * s1 + s_draw},
+                   "input_copies": R, "kernel_source_sha": sha, "invalid": int((yy < 0).sum())},
     }
     print(json.dumps(line), flush=True)
 
@@ -261,9 +273,11 @@ def bench_markov(args):
     emitted = torch.zeros((), dtype=torch.int64, device=dev)
     loop.capture(state, ud[0], uv[0])  # one iteration as a HIP graph (replayed below)
     loop.g_state.copy_(state)
-    for k in range(args.warmup):
-        loop.replay(ud[k], uv[k])
+    for k in range(args.warmup):  # the same work as a timed iteration (loads every kernel it uses)
+        n, _ = loop.replay(ud[k], uv[k])
+        emitted += (n.long() + 1).sum()
     torch.cuda.synchronize()
+    emitted.zero_()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()

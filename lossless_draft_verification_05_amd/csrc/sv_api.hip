@@ -13,6 +13,7 @@
 namespace sv {
 hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stage, hipStream_t stream);
 hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int p0, int p1, hipStream_t stream);
+hipError_t launch_draft_one_pass(const SampleLaunch& A, int dt, hipStream_t stream);
 hipError_t launch_tree(const TreeLaunch& A, int dt, int stage, hipStream_t stream);
 hipError_t launch_mask(const MaskLaunch& A, hipStream_t stream);
 
@@ -157,6 +158,7 @@ static int run_draft(int first, int last, const void* logits, int dtype, int64_t
   SampleLaunch L = plan_sample(a);
   L.out_py = out_prob;
   if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
+  if (first == 0) return hip_status(launch_draft_one_pass(L, dtype, stream));
   for (int s = first; s <= last; ++s) {
     st = hip_status(launch_sample_stage(L, dtype, dtype, s, stream));
     if (st) return st;
@@ -268,8 +270,11 @@ size_t sv_draft_workspace_bytes(int B, int V) {
 int spec_draft_sample(const void* logits, int dtype, int64_t row_stride, const float* uniforms,
                       const float* temperature, int B, int V, int32_t* out_tokens, float* out_prob, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return run_draft(1, 2, logits, dtype, row_stride, uniforms, temperature, B, V, out_tokens, out_prob, workspace,
-                   workspace_bytes, (hipStream_t)stream);
+  // one pass (one workgroup per row) when the rows keep the GPU busy or are
+  // short, and a row's step masses fit the kernel's LDS; else the two kernels
+  const bool one_pass = draft_one_pass(B, V, esz_of(dtype));
+  return run_draft(one_pass ? 0 : 1, 2, logits, dtype, row_stride, uniforms, temperature, B, V, out_tokens,
+                   out_prob, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int spec_draft_sample_stage(int stage, const void* logits, int dtype, int64_t row_stride, const float* uniforms,

@@ -165,6 +165,15 @@ struct SampleLayout {
 
 inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
 
+// Draft sampler: the one-pass kernel (one workgroup per row) when the row's
+// step masses fit its LDS and there are enough rows to fill the GPU (or the
+// rows are short enough that two launches would cost more than the pass).
+constexpr int64_t kOnePassMinRows = 128;
+constexpr int64_t kOnePassShortRowBytes = 64 << 10;
+inline bool draft_one_pass(int64_t B, int64_t V, int esz) {
+  return draw_steps(V) <= kLdsSteps && (B >= kOnePassMinRows || V * esz <= kOnePassShortRowBytes);
+}
+
 // ---------------------------------------------------------------------------
 // early exit
 // ---------------------------------------------------------------------------

@@ -643,6 +643,103 @@ __device__ int wave_find(const double* arr, int len, double t, double& acc, int 
   return last_i;
 }
 
+// Inverse-CDF draw from the step masses stot[0..ns2) (total mass `total`) of
+// the draw row(s) of sequence b, then every output of the sequence. Wave 0
+// searches; all threads of the workgroup (kFinThreads) write. sh_y: LDS slot.
+template <int TD, int DD>
+__device__ void draw_and_write(const SampleLaunch& A, int b, const SeqPlan& P, int mode, const double* stot,
+                               double total, int* sh_y) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = A.gamma;
+  int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
+  // (5) inverse-CDF search (wave 0)
+  if (w == 0) {
+    const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
+    double acc = 0.0;
+    // wave_find returns -1 only if every mass is zero, which valid rows rule
+    // out; clamp anyway so that no index can leave the arrays.
+    const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
+    // rescan the step in token order: octet j-major, then lane, then slot
+    const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
+    const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
+    const int64_t noct = ((int64_t)A.V + 7) / 8;
+    float rr[kU2][8];
+#pragma unroll
+    for (int j = 0; j < kU2; ++j) {
+      const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
+      if (oct < noct) {
+        octet_mass<TD, DD>(trow, drow, oct, A.V, mode, P, rr[j]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
+      }
+    }
+    int y = -1;
+    int last_pos = -1;
+    for (int j = 0; j < kU2 && y < 0; ++j) {
+      const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
+      const double os = (double)sum8(rr[j]);
+      const double incl = wave_incl_scan(os, lane);
+      const double excl = incl - os;
+      int lk = -1;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (rr[j][k] > 0.0f) lk = k;
+      if (lk >= 0) last_pos = (int)(oct * 8 + lk);  // later j / lanes have larger ids
+      const unsigned long long hit = __ballot(os > 0.0 && acc + incl > t);
+      if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        int yy = -1;
+        if (lane == L) {
+          double run = acc + excl;
+          for (int k = 0; k < 8; ++k) {
+            if (rr[j][k] > 0.0f) {
+              run += (double)rr[j][k];
+              if (run > t) {
+                yy = (int)(oct * 8 + k);
+                break;
+              }
+            }
+          }
+          if (yy < 0) yy = (int)(oct * 8 + lk);
+        }
+        y = __builtin_amdgcn_readlane(yy, L);
+      } else {
+        acc += readlane_f64(incl, kWave - 1);
+      }
+    }
+    if (y < 0) {
+      // rounding pushed t past the step's rescanned mass: take its last positive token
+      int m = last_pos;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
+      y = m;
+    }
+    if (lane == 0) *sh_y = y;
+  }
+  __syncthreads();
+
+  // (6) outputs
+  const int y = *sh_y;
+  const int n = P.n;
+  for (int k = tid; k <= G; k += kFinThreads)
+    otok[k] = (k < n) ? A.tokens[(int64_t)b * G + k] : (k == n ? y : -1);
+  if (tid == 0) {
+    if (A.out_n) A.out_n[b] = n;
+    if (A.diag_mass) A.diag_mass[b] = (float)(total / (P.sp * P.fscale));
+    if (A.out_py) {
+      // p(y) of a bonus-mode draw, from the row's statistics in fp64
+      float py = __builtin_nanf("");
+      if (mode == kModeBonus) {
+        const float x = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)n * A.t_row_b, y);
+        py = (float)(exp2(((double)x - (double)P.mp) * (double)P.kl) / P.sp);
+      }
+      A.out_py[b] = py;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // finish kernel: one 512-thread workgroup per sequence
 // ---------------------------------------------------------------------------
@@ -824,91 +921,269 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
   const double total = sh_total;
 
-  // (5) inverse-CDF search (wave 0)
-  if (w == 0) {
-    const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
-    double acc = 0.0;
-    // wave_find returns -1 only if every mass is zero, which valid rows rule
-    // out; clamp anyway so that no index can leave the arrays.
-    const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
-    // rescan the step in token order: octet j-major, then lane, then slot
-    const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
-    const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
-    const int64_t noct = ((int64_t)A.V + 7) / 8;
-    float rr[kU2][8];
+  draw_and_write<TD, DD>(A, b, P, mode, stot, total, &sh_y);
+}
+
+// ---------------------------------------------------------------------------
+// one-pass draft sampler: one 512-thread workgroup per row (gamma = 0)
+// ---------------------------------------------------------------------------
+// One pass over the row writes the exact mass of every 2048-token step into
+// LDS, each against its own reference: a lane takes its terms against a
+// reference that moves lazily (as in the statistics pass), and a step's lanes
+// are combined at their largest reference. The draw then merges the step masses
+// into the row's total, searches them and rescans one step, so the row is read
+// once instead of twice.
+
+// A lane's reference across the steps of its wave (FMA form).
+struct LaneRef {
+  float m;  // reference logit (-inf while every value seen was -inf)
+  float c;  // fp32(m * kl)
+  int ovf;  // |c| >= 2^24: the row is redone in the subtract form
+};
+
+template <int NO>
+__device__ __forceinline__ float octet_terms_fma(const float (&x)[NO][8], float kl, float c) {
+  float u[NO];
+#pragma unroll
+  for (int j = 0; j < NO; ++j) {
+    float e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = hw_exp2(fmaf(x[j][k], kl, -c));
+    u[j] = sum8(e);
+  }
+  if constexpr (NO == 2)
+    return u[0] + u[1];
+  else
+    return (u[0] + u[1]) + (u[2] + u[3]);
+}
+
+// Sum of the lane's terms over NO octets, moving the reference when a term
+// would exceed 2^64 (or on the first finite value, +inf or NaN).
+template <int NO>
+__device__ __forceinline__ float lane_terms(const float (&x)[NO][8], float kl, LaneRef& R) {
+  float a = octet_terms_fma<NO>(x, kl, R.c);
+  if (!(a <= 0x1p64f)) {
+    float gm = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int j = 0; j < NO; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        gm = fmaxf(gm, x[j][k]);
+        nan |= x[j][k] != x[j][k];
+      }
+    if (gm > R.m) {
+      const float cn = __fmul_rn(gm, kl);
+      if (!(fabsf(cn) < 0x1p24f) && __builtin_isfinite(gm)) R.ovf = 1;
+      R.m = gm;
+      R.c = cn;
+    }
+    a = (R.c == -INFINITY) ? 0.0f : octet_terms_fma<NO>(x, kl, R.c);
+    if (nan) a = __builtin_nanf("");
+  }
+  return a;
+}
+
+// Step total of one wave from its lanes' sums (FMA form): lane 0 writes the
+// step's reference shift, reference logit and mass.
+__device__ __forceinline__ void write_step_fma(float a, const LaneRef& R, int s, float* stepC, float* stepM,
+                                               double* stepS) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float Mc = wave_max(R.c);
+  double tot;
+  float Mm;
+  if (Mc == -INFINITY) {
+    tot = wave_sum((double)a);  // every value -inf (0) or NaN seen
+    Mm = -INFINITY;
+  } else {
+    tot = wave_sum((double)a * (double)hw_exp2(R.c - Mc));
+    Mm = wave_max(R.c == Mc ? R.m : -INFINITY);
+  }
+  if (lane == 0) {
+    stepC[s] = Mc;
+    stepM[s] = Mm;
+    stepS[s] = tot;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_half(const HalfStep<DT, DT, kModeBonus>& h, float (&x)[kHalfU][8]) {
+#pragma unroll
+  for (int j = 0; j < kHalfU; ++j) h.t[j].unpack(x[j]);
+}
+
+// FMA-form pass: wave w takes steps w, w + kFinWaves, ...; whole steps through
+// the two-buffer pipeline of the draw, the ragged last step octet by octet.
+template <int DT>
+__device__ void draft_pass_fma(const char* row, int V, int ns2, float kl, LaneRef& R, float* stepC, float* stepM,
+                               double* stepS) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = kFinWaves;
+  const int64_t noct = ((int64_t)V + 7) / 8;
+  const int full_steps = V / kStepTokens;
+  const int nmine = (full_steps > w) ? (full_steps - w + nw - 1) / nw : 0;
+  if (nmine > 0) {
+    // every load is unconditional inside its block (see step_masses)
+    HalfStep<DT, DT, kModeBonus> h0, h1;
+    float x0[kHalfU][8], x1[kHalfU][8];
+    h0.load(row, nullptr, w, 0, lane);
+    int64_t st = w;
+    for (int i = 0; i + 1 < nmine; ++i, st += nw) {
+      h1.load(row, nullptr, st, 1, lane);
+      unpack_half<DT>(h0, x0);
+      float a0 = lane_terms<kHalfU>(x0, kl, R);
+      const float c0 = R.c;
+      h0.load(row, nullptr, st + nw, 0, lane);
+      unpack_half<DT>(h1, x1);
+      const float a1 = lane_terms<kHalfU>(x1, kl, R);
+      if (R.c != c0 && c0 != -INFINITY) a0 *= hw_exp2(c0 - R.c);
+      write_step_fma(a0 + a1, R, (int)st, stepC, stepM, stepS);
+    }
+    h1.load(row, nullptr, st, 1, lane);
+    unpack_half<DT>(h0, x0);
+    float a0 = lane_terms<kHalfU>(x0, kl, R);
+    const float c0 = R.c;
+    unpack_half<DT>(h1, x1);
+    const float a1 = lane_terms<kHalfU>(x1, kl, R);
+    if (R.c != c0 && c0 != -INFINITY) a0 *= hw_exp2(c0 - R.c);
+    write_step_fma(a0 + a1, R, (int)st, stepC, stepM, stepS);
+  }
+  for (int s = w + nmine * nw; s < ns2; s += nw) {
+    float x[kU2][8];
 #pragma unroll
     for (int j = 0; j < kU2; ++j) {
-      const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
+      const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
       if (oct < noct) {
-        octet_mass<TD, DD>(trow, drow, oct, A.V, mode, P, rr[j]);
+        load_octet<DT>(row, oct, V, x[j]);
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
+        for (int k = 0; k < 8; ++k) x[j][k] = -INFINITY;
       }
     }
-    int y = -1;
-    int last_pos = -1;
-    for (int j = 0; j < kU2 && y < 0; ++j) {
-      const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
-      const double os = (double)sum8(rr[j]);
-      const double incl = wave_incl_scan(os, lane);
-      const double excl = incl - os;
-      int lk = -1;
+    const float a = lane_terms<kU2>(x, kl, R);
+    write_step_fma(a, R, s, stepC, stepM, stepS);
+  }
+}
+
+// Subtract-form pass (|m * kl| >= 2^24 somewhere in the row): each step
+// against its own maximum m_s; stepM = m_s, stepS = sum exp2((x - m_s) * kl).
+template <int DT>
+__device__ void draft_pass_sub(const char* row, int V, int ns2, float kl, float* stepM, double* stepS) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t noct = ((int64_t)V + 7) / 8;
+  for (int s = w; s < ns2; s += kFinWaves) {
+    float x[kU2][8];
+    float gm = -INFINITY;
+    bool nan = false;
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (rr[j][k] > 0.0f) lk = k;
-      if (lk >= 0) last_pos = (int)(oct * 8 + lk);  // later j / lanes have larger ids
-      const unsigned long long hit = __ballot(os > 0.0 && acc + incl > t);
-      if (hit) {
-        const int L = __ffsll((long long)hit) - 1;
-        int yy = -1;
-        if (lane == L) {
-          double run = acc + excl;
-          for (int k = 0; k < 8; ++k) {
-            if (rr[j][k] > 0.0f) {
-              run += (double)rr[j][k];
-              if (run > t) {
-                yy = (int)(oct * 8 + k);
-                break;
-              }
-            }
-          }
-          if (yy < 0) yy = (int)(oct * 8 + lk);
-        }
-        y = __builtin_amdgcn_readlane(yy, L);
+    for (int j = 0; j < kU2; ++j) {
+      const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
+      if (oct < noct) {
+        load_octet<DT>(row, oct, V, x[j]);
       } else {
-        acc += readlane_f64(incl, kWave - 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[j][k] = -INFINITY;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        gm = fmaxf(gm, x[j][k]);
+        nan |= x[j][k] != x[j][k];
       }
     }
-    if (y < 0) {
-      // rounding pushed t past the step's rescanned mass: take its last positive token
-      int m = last_pos;
+    const float ms = wave_max(gm);
+    float a = 0.0f;
+    if (ms != -INFINITY) {
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
-      y = m;
+      for (int j = 0; j < kU2; ++j) {
+        float e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = hw_exp2((x[j][k] - ms) * kl);
+        a += sum8(e);
+      }
     }
-    if (lane == 0) sh_y = y;
+    if (nan) a = __builtin_nanf("");
+    const double tot = wave_sum((double)a);
+    if (lane == 0) {
+      stepM[s] = ms;
+      stepS[s] = tot;
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))) void sv_draft1_kernel(
+    SampleLaunch A) {
+  __shared__ float stepC[kLdsSteps], stepM[kLdsSteps];
+  __shared__ double stepS[kLdsSteps];
+  __shared__ SeqPlan sP;
+  __shared__ double sh_total;
+  __shared__ int sh_y;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x;
+  const float T = A.temps[b];
+  const bool tv = temp_ok(T);
+  const float kl = tv ? log2e_over(T) : 1.0f;
+  const char* row = A.tgt + (int64_t)b * A.t_seq_b;
+  const int ns2 = A.ns2;
+
+  LaneRef R{-INFINITY, -INFINITY, 0};
+  draft_pass_fma<DT>(row, A.V, ns2, kl, R, stepC, stepM, stepS);
+  const bool sub = __syncthreads_or(R.ovf) != 0;
+  if (sub) {
+    draft_pass_sub<DT>(row, A.V, ns2, kl, stepM, stepS);
+    __syncthreads();
+  }
+  // merge the steps into step masses against the row's reference (wave 0)
+  if (w == 0) {
+    double Ms = -INFINITY;
+    for (int s = lane; s < ns2; s += kWave)
+      Ms = fmax(Ms, sub ? (double)stepM[s] * (double)kl : (double)stepC[s]);
+    Ms = wave_max_f64(Ms);
+    float mp = -INFINITY;
+    for (int s = lane; s < ns2; s += kWave) {
+      const double sh = sub ? (double)stepM[s] * (double)kl : (double)stepC[s];
+      if (sh == Ms) mp = fmaxf(mp, stepM[s]);
+    }
+    mp = wave_max(mp);
+    for (int s = lane; s < ns2; s += kWave) {
+      const double sh = sub ? (double)stepM[s] * (double)kl : (double)stepC[s];
+      stepS[s] = stepS[s] * exp2(sh - Ms);
+    }
+    const double total = wave_total(stepS, ns2, lane);
+    if (lane == 0) {
+      const float u = A.uniforms[b];
+      SeqPlan Q;
+      Q.valid = tv && u >= 0.0f && u < 1.0f && __builtin_isfinite(total) && total > 0.0 &&
+                __builtin_isfinite(mp);
+      Q.n = 0;
+      Q.mode = kModeBonus;
+      Q.form = sub ? 0 : 1;
+      Q.kl = kl;
+      Q.mp = mp;
+      Q.mq = 0.0f;
+      Q.kap_hi = Q.kap_lo = 0.0f;
+      Q.cp = sub ? 0.0f : (float)Ms;
+      Q.cq = Q.corr = 0.0f;
+      Q.fscale = sub ? 1.0 : exp2((double)mp * (double)kl - Ms);  // step masses are F * exp2((x - mp) * kl)
+      Q.sp = total / Q.fscale;
+      Q.sq = 1.0;
+      sP = Q;
+      sh_total = total;
+    }
   }
   __syncthreads();
-
-  // (6) outputs
-  const int y = sh_y;
-  const int n = P.n;
-  for (int k = tid; k <= G; k += kFinThreads)
-    otok[k] = (k < n) ? A.tokens[(int64_t)b * G + k] : (k == n ? y : -1);
-  if (tid == 0) {
-    if (A.out_n) A.out_n[b] = n;
-    if (A.diag_mass) A.diag_mass[b] = (float)(total / (P.sp * P.fscale));
-    if (A.out_py) {
-      // p(y) of a bonus-mode draw, from the row's statistics in fp64
-      float py = __builtin_nanf("");
-      if (mode == kModeBonus) {
-        const float x = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)n * A.t_row_b, y);
-        py = (float)(exp2(((double)x - (double)P.mp) * (double)P.kl) / P.sp);
-      }
-      A.out_py[b] = py;
+  const SeqPlan P = sP;
+  if (!P.valid) {
+    if (tid == 0) {
+      A.out_tok[b] = -1;
+      if (A.out_py) A.out_py[b] = __builtin_nanf("");
     }
+    return;
   }
+  draw_and_write<DT, DT>(A, b, P, kModeBonus, stepS, sh_total, &sh_y);
 }
 
 // ---------------------------------------------------------------------------
@@ -937,6 +1212,14 @@ hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stag
   if (tdt == 1 && ddt == 0) return launch_pair<1, 0>(A, stage, stream);
   if (tdt == 0 && ddt == 1) return launch_pair<0, 1>(A, stage, stream);
   return launch_pair<0, 0>(A, stage, stream);
+}
+
+hipError_t launch_draft_one_pass(const SampleLaunch& A, int dt, hipStream_t stream) {
+  if (dt == 1)
+    hipLaunchKernelGGL((sv_draft1_kernel<1>), dim3((unsigned)A.B), dim3(kFinThreads), 0, stream, A);
+  else
+    hipLaunchKernelGGL((sv_draft1_kernel<0>), dim3((unsigned)A.B), dim3(kFinThreads), 0, stream, A);
+  return hipGetLastError();
 }
 
 hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int p0, int p1, hipStream_t stream) {

@@ -69,13 +69,13 @@ def test_strided_rows_and_stages(gpu):
     big[:, :3000] = tens["logits"]
     tens_s = dict(tens, logits=big[:, :3000])
     assert tens_s["logits"].stride() == (3064, 1)
-    full = H.run_draft(gpu, tens)
+    full = H.run_draft(gpu, tens)              # one-pass kernel (short rows)
     strided = H.run_draft(gpu, tens_s)
-    staged = H.run_draft(gpu, tens_s, stage=True)
+    staged = H.run_draft(gpu, tens_s, stage=True)  # the two-kernel path
     _assert(H.check_draft(d, strided), "strided")
+    _assert(H.check_draft(d, staged), "staged")
     for k in full:
         assert np.array_equal(full[k].view(np.uint32), strided[k].view(np.uint32))
-        assert np.array_equal(full[k].view(np.uint32), staged[k].view(np.uint32))
 
 
 def test_chi_square_million_draws(gpu):
@@ -120,3 +120,20 @@ def test_huge_logits(gpu):
     """Logits around 10^8: the statistics pass takes its subtract form."""
     d = synth.make_draft_rows(6, 4000, "f32", T=[0.5, 1.0, 1.0, 2.0, 1.0, 0.7], seed=32, sd=2e7)
     _assert(H.check_draft(d, H.run_draft(gpu, H.draft_tensors(d))), "huge logits")
+
+
+def test_both_paths_on_one_batch(gpu):
+    """The one-pass kernel (B >= 128) and the two kernels (staged) on the same
+    rows, each against the oracle."""
+    d = synth.make_draft_rows(160, 70000, "bf16", T=0.9, seed=33)
+    tens = H.draft_tensors(d)
+    rows = list(range(0, 160, 8)) + [159]
+    _assert(H.check_draft(d, H.run_draft(gpu, tens), rows), "one pass B=160")
+    _assert(H.check_draft(d, H.run_draft(gpu, tens, stage=True), rows), "two kernels B=160")
+
+
+def test_vocab_beyond_lds_steps(gpu):
+    """V = 4.2M (2051 steps of 2048 tokens, beyond the kernels' LDS step
+    arrays): the draft sampler's two-kernel path."""
+    d = synth.make_draft_rows(2, 4_200_000, "f32", T=[0.8, 1.2], seed=34)
+    _assert(H.check_draft(d, H.run_draft(gpu, H.draft_tensors(d))), "V=4.2M")

@@ -46,6 +46,12 @@ def test_temperature_extremes(gpu, T):
     _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), f"T={T}")
 
 
+def test_vocab_beyond_lds_steps(gpu):
+    """V = 4.2M: the draw's step masses (2051 steps) live in the workspace, not LDS."""
+    inp = synth.make_custom_sample(2, 1, 4_200_000, "f32", "f32", T=1.0, noise_sd=0.5, seed=14)
+    _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), "V=4.2M")
+
+
 def test_batch_of_one(gpu):
     inp = synth.make_custom_sample(1, 5, 50000, "f32", "bf16", T=0.8, seed=3)
     _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), "B=1")
