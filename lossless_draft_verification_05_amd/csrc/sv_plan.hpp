@@ -18,7 +18,7 @@ constexpr int kStepOctets = kWave * kU2;        // 256 octets = 2048 tokens per 
 constexpr int kStepTokens = kStepOctets * 8;
 constexpr int kLdsSteps = 2048;                 // step masses kept in LDS up to this many steps (V <= 4.19M)
 constexpr int64_t kMinChunkBytes = 16 << 10;    // stats / argmax work unit bounds
-constexpr int64_t kMaxChunkBytes = 128 << 10;   // measured best for the stats kernel on MI355X
+constexpr int64_t kMaxChunkBytes = 256 << 10;   // measured best for the stats kernel on MI355X (128/256/512 KB)
 constexpr int64_t kTargetWGs = 8192;            // ~32 workgroups per CU on 256 CUs
 constexpr int kLog2MaxNodes = 10;               // 1024 tree nodes
 constexpr int64_t kEarlyChunkBytes = 64 << 10;  // early-exit statistics work unit
