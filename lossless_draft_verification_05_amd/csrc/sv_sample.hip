@@ -24,6 +24,8 @@
 //           then walks step masses -> one rescanned step -> one octet to the
 //           token whose running mass first exceeds u_gamma * total, and writes
 //           the outputs.
+#include <type_traits>
+
 #include "sv_device.hpp"
 
 namespace sv {
@@ -134,7 +136,7 @@ __device__ __forceinline__ void sumexp_sub(SumExpSub& st, const Unit<DT> (&un)[N
 
 template <int DT, int NU, class St>
 __device__ __forceinline__ void sumexp(St& st, const Unit<DT> (&un)[NU], float kl) {
-  if constexpr (sizeof(St) == sizeof(SumExp))
+  if constexpr (std::is_same<St, SumExp>::value)
     sumexp_fma<DT, NU>(st, un, kl);
   else
     sumexp_sub<DT, NU>(st, un, kl);
