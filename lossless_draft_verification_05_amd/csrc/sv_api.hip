@@ -314,7 +314,7 @@ static int run_tree(int first, int last, const void* target_logits, int dtype, i
   L.N = N;
   L.V = V;
   const int64_t total = (int64_t)B * N * V * esz;
-  split_row(V, esz, chunk_bytes_for(total), &L.nch, &L.cu);
+  split_row(V, esz, tree_chunk_bytes_for(total), &L.nch, &L.cu);
   L.out_len = out_accept_len;
   L.out_path = out_path;
   L.out_bonus = out_bonus;

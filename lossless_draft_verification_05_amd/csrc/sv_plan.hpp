@@ -115,7 +115,7 @@ struct TreeLaunch {
   int32_t* out_path;
   int32_t* out_bonus;
   int32_t* out_argmax;
-  ArgPartial* part;  // [B][N][nch][kWaves]
+  ArgPartial* part;  // [B][N][nch]
 };
 
 constexpr int kMaxMaskNodes = 1024;  // tree masks: nodes per tree
@@ -141,6 +141,13 @@ inline int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo :
 // Bytes of work per stats/argmax workgroup for a call that streams total_bytes.
 inline int64_t chunk_bytes_for(int64_t total_bytes) {
   int64_t c = clamp64(total_bytes / kTargetWGs, kMinChunkBytes, kMaxChunkBytes);
+  return round_up(c, (int64_t)kThreads * 16);
+}
+
+// Work unit of the tree's argmax kernel: the same rule with its own lower bound.
+constexpr int64_t kTreeMinChunkBytes = 16 << 10;
+inline int64_t tree_chunk_bytes_for(int64_t total_bytes) {
+  int64_t c = clamp64(total_bytes / kTargetWGs, kTreeMinChunkBytes, kMaxChunkBytes);
   return round_up(c, (int64_t)kThreads * 16);
 }
 
@@ -232,7 +239,7 @@ inline TreeLayout tree_layout(int64_t B, int64_t N, int64_t V) {
   TreeLayout L;
   int64_t o = 0;
   L.off_part = o;
-  o += align256(B * N * max_chunks_per_row(V) * kWaves * (int64_t)sizeof(ArgPartial));
+  o += align256(B * N * max_chunks_per_row(V) * (int64_t)sizeof(ArgPartial));
   L.total = o;
   return L;
 }

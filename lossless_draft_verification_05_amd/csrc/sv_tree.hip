@@ -12,7 +12,7 @@
 // synchronisation; see the sampling kernels for why no intra-kernel handoff):
 //  argmax : a workgroup per (sequence, node row, chunk) streams 16-byte units
 //           (4 KB per load instruction) and keeps a per-lane (max, first
-//           index) pair; one partial each.
+//           index) pair; one partial per workgroup.
 //  tree   : a workgroup per tree merges the row partials and resolves the tree
 //           in LDS by pointer jumping over the parent array (log2 N rounds),
 //           which also leaves a binary-lifting table for writing the accepted
@@ -107,13 +107,29 @@ __global__ __launch_bounds__(kThreads) void sv_argmax_kernel(TreeLaunch A) {
   int bi = st.idx;
   wave_argmax(bv, bi);
   const bool nan = __ballot(st.nan) != 0ull;
+  // one partial per workgroup: the waves' results combined in LDS
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves], s_n[kWaves];
   if (lane == 0) {
+    s_v[w] = bv;
+    s_i[w] = bi;
+    s_n[w] = nan ? 1 : 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = s_v[0];
+    int i = s_i[0], bad = s_n[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+      arg_combine(v, i, s_v[k], s_i[k]);
+      bad |= s_n[k];
+    }
     ArgPartial p;
-    p.best = bv;
-    p.idx = bi;
-    p.bad = nan ? 1 : 0;
+    p.best = v;
+    p.idx = i;
+    p.bad = bad;
     p.pad = 0;
-    A.part[(int64_t)blockIdx.x * kWaves + w] = p;
+    A.part[blockIdx.x] = p;
   }
 }
 
@@ -138,14 +154,23 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
   const int N = A.N;
   if (tid == 0) s_ok = 1;
   __syncthreads();
-  const ArgPartial* P = A.part + (int64_t)b * per_seq * kWaves;
+  const ArgPartial* P = A.part + (int64_t)b * per_seq;
   for (int jj = tid; jj < N; jj += kThreads) {
     float v = -INFINITY;
     int i = INT_MAX, bad = 0;
-    for (int cc = 0; cc < A.nch * kWaves; ++cc) {
-      const ArgPartial* q = P + (int64_t)jj * A.nch * kWaves + cc;
-      arg_combine(v, i, q->best, q->idx);
-      bad |= q->bad;
+    const ArgPartial* q = P + (int64_t)jj * A.nch;
+    // the row's chunk partials, four loads in flight at a time, combined in chunk order
+    for (int c0 = 0; c0 < A.nch; c0 += 4) {
+      ArgPartial r[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c0 + k < A.nch) r[k] = q[c0 + k];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c0 + k < A.nch) {
+          arg_combine(v, i, r[k].best, r[k].idx);
+          bad |= r[k].bad;
+        }
     }
     if (v == INFINITY) bad = 1;  // +inf makes the row unusable
     if (v == -INFINITY) i = 0;   // a row of -inf only: first index
