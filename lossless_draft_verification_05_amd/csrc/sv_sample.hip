@@ -269,14 +269,30 @@ __device__ __forceinline__ double partial_shift(const RowPartial& p, float kl) {
 __device__ __forceinline__ RowStat merge_row(const RowPartial* P, int nrec, float kl, bool tv, int lane) {
 #pragma clang fp contract(off)
   double Ms = -INFINITY;
-  for (int k = lane; k < nrec; k += kWave) Ms = fmax(Ms, partial_shift(P[k], kl));
-  Ms = wave_max_f64(Ms);
   float Mm = -INFINITY;  // the reference logit of a partial at Ms (the largest such)
-  for (int k = lane; k < nrec; k += kWave)
-    if (partial_shift(P[k], kl) == Ms) Mm = fmaxf(Mm, P[k].m);
-  Mm = wave_max(Mm);
   double S = 0.0;
-  for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(partial_shift(P[k], kl) - Ms);
+  if (nrec <= kWave) {
+    // at most one partial per lane, loaded once: the same operations as below
+    const bool have = lane < nrec;
+    RowPartial q{};
+    double sh = -INFINITY;
+    if (have) {
+      q = P[lane];
+      sh = partial_shift(q, kl);
+      Ms = fmax(Ms, sh);
+    }
+    Ms = wave_max_f64(Ms);
+    if (have && sh == Ms) Mm = fmaxf(Mm, q.m);
+    Mm = wave_max(Mm);
+    if (have) S += q.s * exp2(sh - Ms);
+  } else {
+    for (int k = lane; k < nrec; k += kWave) Ms = fmax(Ms, partial_shift(P[k], kl));
+    Ms = wave_max_f64(Ms);
+    for (int k = lane; k < nrec; k += kWave)
+      if (partial_shift(P[k], kl) == Ms) Mm = fmaxf(Mm, P[k].m);
+    Mm = wave_max(Mm);
+    for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(partial_shift(P[k], kl) - Ms);
+  }
   S = wave_sum(S);
   RowStat r;
   r.m = Mm;
