@@ -147,6 +147,27 @@ def _workspace(ws, nbytes, device):
     return buf
 
 
+class Prepared:
+    """A call whose arguments were checked and marshalled once. Calling it
+    enqueues the same kernels again, on the same tensors and stream (a serving
+    loop's fixed buffers), with no per-call Python checks; it returns the same
+    outputs as the call it was prepared from. It keeps its tensors alive."""
+
+    __slots__ = ("_cfn", "_args", "_name", "outputs", "_keep")
+
+    def __init__(self, cfn, args, name, outputs, keep):
+        self._cfn, self._args, self._name, self.outputs, self._keep = cfn, args, name, outputs, keep
+
+    def __call__(self):
+        _check(self._cfn(*self._args), self._name)
+        return self.outputs
+
+
+def _launch(cfn, args, name, outputs, keep, prepare):
+    call = Prepared(cfn, args, name, outputs, keep)
+    return call if prepare else call()
+
+
 def sv_sample_workspace_bytes(B: int, gamma: int, V: int) -> int:
     return int(load().sv_sample_workspace_bytes(B, gamma, V))
 
@@ -156,7 +177,7 @@ def sv_tree_workspace_bytes(B: int, N: int, V: int) -> int:
 
 
 def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_num_accepted, out_tokens, diag,
-                 workspace, stream):
+                 workspace, stream, prepare=False):
     lib = load()
     B, G1, V = target.shape
     G = G1 - 1
@@ -188,20 +209,19 @@ def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_
     args = (_ptr(target), _dtype_code(target), ts, tr, _ptr(draft), _dtype_code(draft), ds, dr, _ptr(draft_tokens),
             _ptr(uniforms), _ptr(temperature), B, G, V, _ptr(out_num_accepted), _ptr(out_tokens),
             ctypes.byref(dptr) if dptr is not None else None, _ptr(ws), ws.numel(), _stream(stream))
+    keep = (target, draft, draft_tokens, uniforms, temperature, ws, d, dptr)
+    outputs = (out_num_accepted, out_tokens, d)
     if stage is None:
-        st = lib.spec_verify_sample(*args)
-        _check(st, "spec_verify_sample")
-    elif stage == "early_exit":
-        st = lib.spec_verify_sample_early_exit(*args)
-        _check(st, "spec_verify_sample_early_exit")
-    else:
-        st = lib.spec_verify_sample_stage(stage, *args)
-        _check(st, f"spec_verify_sample_stage({stage})")
-    return out_num_accepted, out_tokens, d
+        return _launch(lib.spec_verify_sample, args, "spec_verify_sample", outputs, keep, prepare)
+    if stage == "early_exit":
+        return _launch(lib.spec_verify_sample_early_exit, args, "spec_verify_sample_early_exit", outputs, keep,
+                       prepare)
+    return _launch(lib.spec_verify_sample_stage, (stage,) + args, f"spec_verify_sample_stage({stage})", outputs,
+                   keep, prepare)
 
 
 def spec_verify_sample(target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
-                       out_tokens=None, diag=False, workspace=None, stream=None):
+                       out_tokens=None, diag=False, workspace=None, stream=None, prepare=False):
     """Speculative-sampling verify of B sequences on the GPU (see include/spec_verify.h).
 
     target [B][gamma+1][V] and draft [B][gamma][V] are bf16 or fp32 CUDA tensors
@@ -209,28 +229,31 @@ def spec_verify_sample(target, draft, draft_tokens, uniforms, temperature, *, ou
     is allowed); draft_tokens int32 [B][gamma]; uniforms fp32 [B][gamma+1];
     temperature fp32 [B]. Returns (num_accepted [B], tokens [B][gamma+1], diag
     dict or None). Work is enqueued on ``stream`` (default: current stream).
+    With ``prepare=True`` nothing is enqueued: the result is a Prepared call
+    that enqueues the work each time it is called. (The same holds for every
+    entry point below.)
     """
     return _sample_call(None, target, draft, draft_tokens, uniforms, temperature, out_num_accepted, out_tokens,
-                        diag, workspace, stream)
+                        diag, workspace, stream, prepare)
 
 
 def spec_verify_sample_early_exit(target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
-                                  out_tokens=None, diag=False, workspace=None, stream=None):
+                                  out_tokens=None, diag=False, workspace=None, stream=None, prepare=False):
     """spec_verify_sample that reads no row after a sequence's first rejection: same arguments and
     outputs (diag p_x, q_x are NaN after the first rejection)."""
     return _sample_call("early_exit", target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
-                        out_tokens, diag, workspace, stream)
+                        out_tokens, diag, workspace, stream, prepare)
 
 
 def spec_verify_sample_stage(stage, target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
-                             out_tokens=None, diag=False, workspace=None, stream=None):
+                             out_tokens=None, diag=False, workspace=None, stream=None, prepare=False):
     """One stage of spec_verify_sample: 1 row statistics, 2 accept tests + residual/bonus draw + outputs."""
     return _sample_call(int(stage), target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
-                        out_tokens, diag, workspace, stream)
+                        out_tokens, diag, workspace, stream, prepare)
 
 
 def spec_draft_sample(logits, uniforms, temperature, *, out_tokens=None, want_prob=False, workspace=None,
-                      stream=None, stage=None):
+                      stream=None, stage=None, prepare=False):
     """Draft-side sampler (see include/spec_verify.h): one token per row of logits [B][V] (bf16 or fp32,
     contiguous 16-byte aligned rows) from softmax(row / T) at the row's uniform. Returns (tokens [B] int32,
     q(token) [B] float32 or None). ``stage`` 1 or 2 runs one of its two kernels."""
@@ -253,15 +276,15 @@ def spec_draft_sample(logits, uniforms, temperature, *, out_tokens=None, want_pr
     ws = _workspace(workspace, nbytes, dev)
     args = (_ptr(logits), _dtype_code(logits), logits.stride(0), _ptr(uniforms), _ptr(temperature), B, V,
             _ptr(out_tokens), _ptr(prob) if prob is not None else None, _ptr(ws), ws.numel(), _stream(stream))
+    keep = (logits, uniforms, temperature, ws)
     if stage is None:
-        _check(lib.spec_draft_sample(*args), "spec_draft_sample")
-    else:
-        _check(lib.spec_draft_sample_stage(int(stage), *args), f"spec_draft_sample_stage({stage})")
-    return out_tokens, prob
+        return _launch(lib.spec_draft_sample, args, "spec_draft_sample", (out_tokens, prob), keep, prepare)
+    return _launch(lib.spec_draft_sample_stage, (int(stage),) + args, f"spec_draft_sample_stage({stage})",
+                   (out_tokens, prob), keep, prepare)
 
 
 def _tree_call(stage, logits, parents, tokens, out_accept_len, out_path, out_bonus, out_argmax, want_argmax,
-               workspace, stream):
+               workspace, stream, prepare=False):
     lib = load()
     B, N, V = logits.shape
     s0, s1 = _logits3(logits, "logits", N)
@@ -282,15 +305,16 @@ def _tree_call(stage, logits, parents, tokens, out_accept_len, out_path, out_bon
     ws = _workspace(workspace, nbytes, dev)
     args = (_ptr(logits), _dtype_code(logits), s0, s1, _ptr(parents), _ptr(tokens), B, N, V, _ptr(out_accept_len),
             _ptr(out_path), _ptr(out_bonus), _ptr(out_argmax), _ptr(ws), ws.numel(), _stream(stream))
+    keep = (logits, parents, tokens, ws)
+    outputs = (out_accept_len, out_path, out_bonus, out_argmax)
     if stage is None:
-        _check(lib.spec_verify_greedy_tree(*args), "spec_verify_greedy_tree")
-    else:
-        _check(lib.spec_verify_greedy_tree_stage(stage, *args), f"spec_verify_greedy_tree_stage({stage})")
-    return out_accept_len, out_path, out_bonus, out_argmax
+        return _launch(lib.spec_verify_greedy_tree, args, "spec_verify_greedy_tree", outputs, keep, prepare)
+    return _launch(lib.spec_verify_greedy_tree_stage, (stage,) + args, f"spec_verify_greedy_tree_stage({stage})",
+                   outputs, keep, prepare)
 
 
 def spec_verify_greedy_tree(logits, parents, tokens, *, out_accept_len=None, out_path=None, out_bonus=None,
-                            out_argmax=None, want_argmax=True, workspace=None, stream=None):
+                            out_argmax=None, want_argmax=True, workspace=None, stream=None, prepare=False):
     """Greedy decoding-tree verify of B trees (see include/spec_verify.h).
 
     logits [B][N][V] bf16/fp32 (rows contiguous, 16-byte aligned); parents and
@@ -298,14 +322,15 @@ def spec_verify_greedy_tree(logits, parents, tokens, *, out_accept_len=None, out
     argmax [B][N] or None).
     """
     return _tree_call(None, logits, parents, tokens, out_accept_len, out_path, out_bonus, out_argmax, want_argmax,
-                      workspace, stream)
+                      workspace, stream, prepare)
 
 
 def spec_verify_greedy_tree_stage(stage, logits, parents, tokens, *, out_accept_len=None, out_path=None,
-                                  out_bonus=None, out_argmax=None, want_argmax=True, workspace=None, stream=None):
+                                  out_bonus=None, out_argmax=None, want_argmax=True, workspace=None, stream=None,
+                                  prepare=False):
     """One stage of spec_verify_greedy_tree: 1 per-row argmax, 2 tree resolve and outputs."""
     return _tree_call(int(stage), logits, parents, tokens, out_accept_len, out_path, out_bonus, out_argmax,
-                      want_argmax, workspace, stream)
+                      want_argmax, workspace, stream, prepare)
 
 
 def version() -> str:
@@ -313,7 +338,7 @@ def version() -> str:
 
 
 def spec_tree_mask(parents, blocks=None, *, want_mask=True, want_relaxed=False, want_depth=True, out_mask=None,
-                   out_relaxed=None, out_depth=None, stream=None):
+                   out_relaxed=None, out_depth=None, stream=None, prepare=False):
     """Tree-attention masks of B draft trees (see include/spec_verify.h). parents [B][N] int32 (and blocks
     [B][N] int32 for the relaxed mask). Returns (mask uint8 [B][N][N] or None, relaxed or None, depth int32
     [B][N] or None)."""
@@ -336,6 +361,6 @@ def spec_tree_mask(parents, blocks=None, *, want_mask=True, want_relaxed=False, 
             _need(t, name, torch.uint8, (B, N, N))
     if out_depth is not None:
         _need(out_depth, "out_depth", torch.int32, (B, N))
-    _check(lib.spec_tree_mask(_ptr(parents), _ptr(blocks), B, N, _ptr(out_mask), _ptr(out_relaxed),
-                              _ptr(out_depth), _stream(stream)), "spec_tree_mask")
-    return out_mask, out_relaxed, out_depth
+    args = (_ptr(parents), _ptr(blocks), B, N, _ptr(out_mask), _ptr(out_relaxed), _ptr(out_depth), _stream(stream))
+    return _launch(lib.spec_tree_mask, args, "spec_tree_mask", (out_mask, out_relaxed, out_depth), (parents, blocks),
+                   prepare)

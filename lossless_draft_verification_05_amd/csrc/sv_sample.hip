@@ -76,7 +76,9 @@ __device__ __forceinline__ float terms_fma(const Unit<DT> (&un)[NU], float kl, f
 
 template <int DT, int NU>
 __device__ __forceinline__ void sumexp_fma(SumExp& st, const Unit<DT> (&un)[NU], float kl) {
-  float a = terms_fma<DT, NU>(un, kl, st.c);
+  // no reference yet (the first batch of every chunk): straight to the batch maximum
+  float a = __builtin_inff();
+  if (st.c != -INFINITY) a = terms_fma<DT, NU>(un, kl, st.c);
   if (!(a <= 0x1p64f)) {
     // a value above the reference by more than 64 / kl, the first finite
     // value, +inf or NaN: move the reference to the batch maximum and redo
@@ -93,7 +95,7 @@ __device__ __forceinline__ void sumexp_fma(SumExp& st, const Unit<DT> (&un)[NU],
       // c must round by less than half a log2 unit, or the terms near the
       // maximum leave the fp32 range: |c| < 2^24, else the subtract form
       if (!(fabsf(cn) < 0x1p24f) && __builtin_isfinite(gm)) st.ovf = 1;
-      st.s *= exp2((double)st.c - (double)cn);
+      if (st.c != -INFINITY) st.s *= exp2((double)st.c - (double)cn);  // else s is 0
       st.m = gm;
       st.c = cn;
     }

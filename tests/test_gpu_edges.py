@@ -262,3 +262,50 @@ def test_tree_stages_equal_full_call(gpu):
     assert np.array_equal(outs[1].cpu().numpy(), full["path"])
     assert np.array_equal(outs[2].cpu().numpy(), full["bonus"])
     assert np.array_equal(outs[3].cpu().numpy(), full["argmax"])
+
+
+def test_prepared_calls_repeat_the_direct_calls(gpu):
+    """Calls prepared once (prepare=True) enqueue the same work each time they
+    are called: their outputs equal the direct calls' on every repetition."""
+    inp = _custom(9, 4, 20000, "bf16", "f32", seed=21)
+    tens = H.sample_tensors(inp)
+    ws = gpu.Workspace()
+    direct = H.run_sample(gpu, tens, diag=False, workspace=ws)
+    call = gpu.spec_verify_sample(**tens, workspace=ws, prepare=True)
+    ee = gpu.spec_verify_sample_early_exit(**tens, workspace=ws, prepare=True)
+    for rep in range(3):
+        for c in (call, ee):
+            c.outputs[0].fill_(-7)
+            n, t, _ = c()
+            torch.cuda.synchronize()
+            assert np.array_equal(n.cpu().numpy(), direct["n"]), rep
+            assert np.array_equal(t.cpu().numpy(), direct["tokens"]), rep
+
+    ti = synth.make_tree_inputs(4, seed=16, B=3, N=25, V=3000)
+    tt = H.tree_tensors(ti)
+    full = H.run_tree(gpu, tt)
+    tcall = gpu.spec_verify_greedy_tree(**tt, prepare=True)
+    for rep in range(2):
+        tcall.outputs[0].fill_(-7)
+        out = tcall()
+        torch.cuda.synchronize()
+        assert np.array_equal(out[0].cpu().numpy(), full["len"]) and np.array_equal(out[2].cpu().numpy(),
+                                                                                      full["bonus"]), rep
+
+    d = synth.make_draft_rows(6, 5000, "bf16", T=0.9, seed=22)
+    dt = H.draft_tensors(d)
+    y0, p0 = gpu.spec_draft_sample(**dt, want_prob=True)
+    dcall = gpu.spec_draft_sample(**dt, want_prob=True, prepare=True)
+    for rep in range(2):
+        dcall.outputs[0].fill_(-7)
+        y, p = dcall()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0) and torch.equal(p, p0), rep
+
+    par = torch.from_numpy(ti.parents).cuda()
+    m0, _, d0 = gpu.spec_tree_mask(par)
+    mcall = gpu.spec_tree_mask(par, prepare=True)
+    mcall.outputs[0].fill_(7)
+    m, _, dd = mcall()
+    torch.cuda.synchronize()
+    assert torch.equal(m, m0) and torch.equal(dd, d0)
