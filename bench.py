@@ -52,7 +52,8 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 PEAK_HBM_GBPS = float(os.environ.get("SV_PEAK_HBM_GBPS", "8000"))
-WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "d3": 3, "d5": 5, "m": 0, "t4": 4, "t1024": 4}
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "d3": 3, "d5": 5, "m": 0, "t4": 4, "t1024": 4,
+             "b3": 3, "b5": 5}  # b3, b5: configurations 3 and 5 at a batch of one sequence (latency)
 MARKOV = dict(B=512, V=16384, gamma=5, T=1.0, dtype="bf16", noise_sd=0.8)
 CSRC = os.path.join(ROOT, "lossless_draft_verification_05_amd", "csrc")
 
@@ -539,7 +540,9 @@ def main():
     tree = cid == 4
     log(f"[bench] building inputs for {args.workload} (seed {args.seed})")
     t0 = time.perf_counter()
-    inp = synth.make_tree_inputs(4, seed=args.seed) if tree else synth.make_sample_inputs(cid, seed=args.seed)
+    batch1 = args.workload.startswith("b")
+    inp = synth.make_tree_inputs(4, seed=args.seed) if tree else \
+        synth.make_sample_inputs(cid, seed=args.seed, B=1 if batch1 else None)
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
 
     cpu = None
@@ -638,7 +641,8 @@ def main():
         unit = "positions/s"
         s1_bytes, _ = sample_bytes(cfg, B, G, V)
         tdesc = cfg.temperature if not isinstance(cfg.temperature, tuple) else f"U[{cfg.temperature[1]}, {cfg.temperature[2]}] per row"
-        cfg_desc = {"workload": f"{args.workload}: {cfg.name}", "B": B, "gamma": G, "V": V,
+        cfg_desc = {"workload": f"{args.workload}: {cfg.name}" + (" at a batch of one" if batch1 else ""),
+                    "B": B, "gamma": G, "V": V,
                     "target_dtype": cfg.target_dtype, "draft_dtype": cfg.draft_dtype, "temperature": tdesc,
                     "seed": args.seed}
         kernel_names = ["sv_stats_kernel", "sv_finish_kernel"]

@@ -117,10 +117,12 @@ static SampleLaunch plan_sample(const SampleArgs& a, bool early = false) {
   split_row(V, ed, cb, &L.ncd, &L.cud);
   L.per_seq = (int)((G + 1) * L.nct + G * L.ncd);
   L.ns2 = (int)draw_steps(V);
+  L.parts = finish_parts(B, L.ns2);
   const SampleLayout lay = sample_layout(B, G, V);
   char* ws = (char*)a.ws;
   L.part = (RowPartial*)(ws + lay.off_part);
   L.steptot = (double*)(ws + lay.off_step);
+  L.done = (int32_t*)(ws + lay.off_done);
   return L;
 }
 

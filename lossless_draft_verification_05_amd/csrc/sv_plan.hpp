@@ -24,6 +24,7 @@ constexpr int kLog2MaxNodes = 10;               // 1024 tree nodes
 constexpr int64_t kEarlyChunkBytes = 64 << 10;  // early-exit statistics work unit
 constexpr double kEarlyAlpha = 0.7;             // acceptance rate assumed when grouping positions
 constexpr double kEarlyLaunchBytes = 64e6;      // bytes moved in about the time one extra launch costs
+constexpr int64_t kFinTargetWGs = 256;          // finish: split sequences over parts up to one workgroup per CU
 
 enum : int { kModeResidual = 0, kModeBonus = 1 };
 
@@ -97,10 +98,12 @@ struct SampleLaunch {
   int cut, cud;  // 16-byte units per chunk (multiples of 256)
   int per_seq;   // (gamma + 1) * nct + gamma * ncd
   int ns2;  // 2048-token steps per row (draw)
+  int parts;  // finish workgroups per sequence, each streaming a share of the draw's steps
   // workspace
   RowPartial* part;  // [B][per_seq][kWaves]
-  double* steptot;   // [B][ns2]
+  double* steptot;   // [B][ns2]; with parts > 1 it holds -1 (no mass yet) before each finish launch
   int32_t* reach;    // [B] early exit only (else null): rows 0..reach-1 have statistics
+  int32_t* done;     // [B] finish parts done; zeroed by the statistics pass and by the drawing part
 };
 
 struct TreeLaunch {
@@ -167,10 +170,27 @@ inline int64_t max_chunks_per_row(int64_t V) { return ceil_div(V * 4, kMinChunkB
 inline int64_t align256(int64_t x) { return round_up(x, 256); }
 
 struct SampleLayout {
-  int64_t off_part, off_step, off_reach, total;
+  int64_t off_part, off_step, off_reach, off_done, total;
 };
 
 inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
+
+// Finish workgroups per sequence. With fewer sequences than CUs, one
+// workgroup per sequence leaves most of the GPU idle while each streams its
+// draw row(s) alone (a 256k-token residual pair is 1.5 MB), so each sequence's
+// steps are split over up to kFinTargetWGs / B parts, at least one step per
+// wave each. Every part repeats the (small) merge and accept tests; the part
+// that finishes last gathers the step masses into its LDS and draws, so only
+// rows whose steps fit in LDS are split. With B at or above the CU count one
+// part per sequence is faster (measured: the repeated merges cost more than
+// the balance gains).
+inline int finish_parts(int64_t B, int64_t ns2) {
+  if (ns2 > kLdsSteps) return 1;
+  int64_t k = ceil_div(kFinTargetWGs, B);
+  const int64_t cap = ns2 / kFinWaves;
+  if (k > cap) k = cap;
+  return (int)(k < 1 ? 1 : k);
+}
 
 // Draft sampler: the one-pass kernel (one workgroup per row) when the row's
 // step masses fit its LDS and there are enough rows to fill the GPU (or the
@@ -226,6 +246,8 @@ inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
   L.off_step = o;
   o += align256(B * draw_steps(V) * 8);
   L.off_reach = o;
+  o += align256(B * 4);
+  L.off_done = o;
   o += align256(B * 4);
   L.total = o;
   return L;

@@ -330,6 +330,14 @@ __device__ __forceinline__ AcceptOut accept_test(float lt, float ld, const RowSt
   return o;
 }
 
+// The finish parts' hand-off state of sequence b before a finish launch: no
+// part done, no step mass yet (one workgroup of the sequence calls this).
+__device__ __forceinline__ void reset_handoff(const SampleLaunch& A, int b) {
+  if (threadIdx.x == 0) A.done[b] = 0;
+  if (A.parts > 1)
+    for (int s = threadIdx.x; s < A.ns2; s += blockDim.x) A.steptot[(int64_t)b * A.ns2 + s] = -1.0;
+}
+
 // One pass: one workgroup per (sequence, chunk slot) over every row.
 template <int TD, int DD>
 __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
@@ -338,6 +346,7 @@ __global__ __launch_bounds__(kThreads) void sv_stats_kernel(SampleLaunch A) {
   const int r = (int)(wg % A.per_seq);
   const float T = A.temps[b];
   const float kl = temp_ok(T) ? log2e_over(T) : 1.0f;
+  if (r == 0) reset_handoff(A, b);
   stats_chunk<TD, DD>(A, b, r, kl);
 }
 
@@ -367,6 +376,7 @@ __global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, 
   const float kl = tv ? log2e_over(T) : 1.0f;
   if (p0 == 0) {
     if (tid == 0) A.reach[b] = p1 + 1;  // every workgroup of the sequence writes the same value
+    if (c == 0) reset_handoff(A, b);
   } else {
     if (A.reach[b] < p0) return;  // the sequence stopped at an earlier position
     const int i = p0 - 1;
@@ -557,6 +567,25 @@ struct HalfStep {
   }
 };
 
+// Mass of step s of the draw row(s), octet by octet with bounds checks (every
+// lane gets it). Inside the row these are the same operations in the same
+// order as the pipelined loop below, so both give the same bits for a step.
+template <int TD, int DD, int MODE>
+__device__ __forceinline__ double direct_step_mass(const char* trow, const char* drow, int64_t s, int64_t noct, int V,
+                                                   const SeqPlan& P, int lane) {
+  double lacc = 0.0;
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float rr[8];
+      octet_mass<TD, DD>(trow, drow, oct, V, MODE, P, rr);
+      lacc += (double)sum8(rr);
+    }
+  }
+  return wave_sum(lacc);
+}
+
 // Masses of the draw row(s) of sequence b over all steps; wave w of nw takes
 // steps w, w + nw, ... and lane 0 writes each step's mass to out[step].
 // Whole steps run as a two-buffer software pipeline over half steps: the loads
@@ -595,17 +624,7 @@ __device__ __forceinline__ void step_masses(const SampleLaunch& A, int b, const 
   }
   // the ragged last step (if any), octet by octet
   for (int s = w + nmine * nw; s < A.ns2; s += nw) {
-    double lacc = 0.0;
-#pragma unroll
-    for (int j = 0; j < kU2; ++j) {
-      const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
-      if (oct < noct) {
-        float rr[8];
-        octet_mass<TD, DD>(trow, drow, oct, A.V, MODE, P, rr);
-        lacc += (double)sum8(rr);
-      }
-    }
-    const double tot = wave_sum(lacc);
+    const double tot = direct_step_mass<TD, DD, MODE>(trow, drow, s, noct, A.V, P, lane);
     if (lane == 0) out[s] = tot;
   }
 }
@@ -623,6 +642,44 @@ __device__ __forceinline__ void all_step_masses(const SampleLaunch& A, int b, co
       step_masses<TD, DD, kModeBonus, 1>(A, b, P, w, nw, out);
     else
       step_masses<TD, DD, kModeBonus, 0>(A, b, P, w, nw, out);
+  }
+}
+
+// The drawing part's copy of every step mass of sequence b into LDS (wave w
+// of kFinWaves takes 64-step blocks w, w + kFinWaves, ...). Steps of other
+// parts come from the workspace; one whose mass is not visible yet still holds
+// the sentinel (negative: masses are >= 0) and is recomputed here with the
+// same bits, so no result depends on which stores have landed and no part
+// ever waits for another. The slots are then reset to the sentinel.
+template <int TD, int DD>
+__device__ __forceinline__ void gather_steps(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int part,
+                                             double* sh_steps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gnw = A.parts * kFinWaves;
+  double* g = A.steptot + (int64_t)b * A.ns2;
+  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
+  const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
+  const int64_t noct = ((int64_t)A.V + 7) / 8;
+  for (int base = w * kWave; base < A.ns2; base += kFinWaves * kWave) {
+    const int s = base + lane;
+    const bool in = s < A.ns2;
+    const bool mine = (s % gnw) / kFinWaves == part;  // computed by this workgroup: already in LDS
+    double v = 0.0;
+    if (in) v = mine ? sh_steps[s] : __hip_atomic_load(g + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long miss = __ballot(in && !(v >= 0.0));
+    while (miss) {
+      const int L = __ffsll((long long)miss) - 1;
+      miss &= miss - 1;
+      const double m = (mode == kModeResidual)
+                           ? direct_step_mass<TD, DD, kModeResidual>(trow, drow, base + L, noct, A.V, P, lane)
+                           : direct_step_mass<TD, DD, kModeBonus>(trow, drow, base + L, noct, A.V, P, lane);
+      if (lane == L) v = m;
+    }
+    if (in) {
+      sh_steps[s] = v;
+      __hip_atomic_store(g + s, -1.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -773,11 +830,14 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   __shared__ SeqPlan sP;
   __shared__ double sh_total;
   __shared__ int sh_y;
+  __shared__ int sh_last;
   __shared__ double sh_steps[kLdsSteps];  // step masses when the row has at most kLdsSteps steps
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loops over steps stay scalar
-  const int b = blockIdx.x;
+  const int K = A.parts;  // workgroups per sequence
+  const int b = (int)(blockIdx.x / (unsigned)K);
+  const int part = (int)blockIdx.x - b * K;
   const float T = A.temps[b];
   const bool tv = temp_ok(T);
   const float kl = tv ? log2e_over(T) : 1.0f;
@@ -898,11 +958,14 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   const SeqPlan P = sP;
   int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
   if (!P.valid) {
-    for (int k = tid; k <= G; k += kFinThreads) otok[k] = -1;
-    if (tid == 0) {
-      if (A.out_n) A.out_n[b] = -1;
-      if (A.out_py) A.out_py[b] = __builtin_nanf("");
-      if (A.diag_mass) A.diag_mass[b] = __builtin_nanf("");
+    // every part reaches the same plan; part 0 writes the outputs
+    if (part == 0) {
+      for (int k = tid; k <= G; k += kFinThreads) otok[k] = -1;
+      if (tid == 0) {
+        if (A.out_n) A.out_n[b] = -1;
+        if (A.out_py) A.out_py[b] = __builtin_nanf("");
+        if (A.diag_mass) A.diag_mass[b] = __builtin_nanf("");
+      }
     }
     return;
   }
@@ -912,14 +975,33 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   // address space of the output, which keeps the stores of the streaming loop
   // out of the generic path: after a generic store every wait for a load
   // would drain all loads in flight.)
+  // With K parts the waves of all parts share the steps round-robin: wave w of
+  // part p is wave p * kFinWaves + w of K * kFinWaves (K > 1 only when the
+  // steps fit in LDS).
   int mode = P.mode;
   const bool lds_steps = A.ns2 <= kLdsSteps;
   double* stot = lds_steps ? sh_steps : A.steptot + (int64_t)b * A.ns2;
   if (lds_steps)
-    all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, sh_steps);
+    all_step_masses<TD, DD>(A, b, P, mode, part * kFinWaves + w, K * kFinWaves, sh_steps);
   else
     all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, A.steptot + (int64_t)b * A.ns2);
-  __syncthreads();  // every wave's step masses are visible to wave 0
+  __syncthreads();  // every wave's step masses are visible to the workgroup
+  if (K > 1) {
+    // Hand-off: each part publishes its step masses (relaxed device-scope
+    // atomic stores, which no cache of this XCD holds back) and counts itself
+    // done; the part that counts last gathers every mass and draws.
+    double* g = A.steptot + (int64_t)b * A.ns2;
+    for (int s = tid; s < A.ns2; s += kFinThreads)
+      if ((s % (K * kFinWaves)) / kFinWaves == part)
+        __hip_atomic_store(g + s, sh_steps[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid == 0) sh_last = __hip_atomic_fetch_add(A.done + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == K - 1;
+    __syncthreads();
+    if (!sh_last) return;
+    if (tid == 0) A.done[b] = 0;  // ready for the next finish launch on this workspace
+    gather_steps<TD, DD>(A, b, P, mode, part, sh_steps);
+    __syncthreads();
+  }
   if (w == 0) {
     const double tot = wave_total(stot, A.ns2, lane);
     if (lane == 0) sh_total = tot;
@@ -1215,7 +1297,8 @@ static hipError_t launch_pair(const SampleLaunch& A, int stage, hipStream_t stre
     hipLaunchKernelGGL((sv_stats_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.per_seq)), dim3(kThreads), 0,
                        stream, A);
   else
-    hipLaunchKernelGGL((sv_finish_kernel<TD, DD>), dim3((unsigned)A.B), dim3(kFinThreads), 0, stream, A);
+    hipLaunchKernelGGL((sv_finish_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.parts)), dim3(kFinThreads), 0,
+                       stream, A);
   return hipGetLastError();
 }
 

@@ -135,6 +135,40 @@ def test_workspace_reuse_across_shapes_and_stages(gpu):
     assert np.array_equal(r["n"], ra1["n"])
 
 
+@pytest.mark.parametrize("B,G,V,tdt,ddt", [(24, 3, 70000, "bf16", "f32"), (3, 2, 300000, "f32", "bf16"),
+                                         (40, 2, 128256, "bf16", "bf16"), (1, 4, 256000, "bf16", "f32")])
+def test_finish_split_over_parts(gpu, B, G, V, tdt, ddt):
+    """Few sequences with long rows: each sequence's draw is split over several
+    finish workgroups (the last to finish gathers the step masses and draws).
+    Results against the oracle; then the finish stage alone, run three times
+    after one statistics stage on a garbage-filled workspace, gives the full
+    call's outputs every time (the hand-off state is reset by the statistics
+    pass and again by the drawing part)."""
+    H.log(f"finish parts B={B} G={G} V={V} {tdt}/{ddt}")
+    inp = synth.make_custom_sample(B, G, V, tdt, ddt, T=0.8, noise_sd=0.6, seed=B + V)
+    tens = H.sample_tensors(inp)
+    ws = gpu.Workspace()
+    ws.buf = torch.randint(0, 255, (gpu.sv_sample_workspace_bytes(B, G, V) + 4096,), dtype=torch.uint8,
+                           device="cuda")
+    full = H.run_sample(gpu, tens, workspace=ws)
+    _check(inp, full, f"parts B={B} V={V}")
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    t = torch.empty((B, G + 1), dtype=torch.int32, device="cuda")
+    ws.buf.random_(0, 255)
+    gpu.spec_verify_sample_stage(1, **tens, out_num_accepted=n, out_tokens=t, workspace=ws)
+    for rep in range(3):
+        n.fill_(-7)
+        t.fill_(-7)
+        gpu.spec_verify_sample_stage(2, **tens, out_num_accepted=n, out_tokens=t, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(n.cpu().numpy(), full["n"]), rep
+        assert np.array_equal(t.cpu().numpy(), full["tokens"]), rep
+    ee = H.run_sample(gpu, tens, workspace=ws, early_exit=True)
+    differ, bad = H.compare_one_pass(full, ee)
+    assert not bad, bad[:5]
+    _check(inp, ee, f"parts early exit B={B} V={V}")
+
+
 def test_bad_arguments_raise(gpu):
     inp = _custom(2, 2, 64, "f32", "f32")
     tens = H.sample_tensors(inp)
