@@ -132,7 +132,9 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
  * spec_verify_sample. The work is ordered by position: statistics launches
  * over positions 0, 1, ..., k-1 one at a time and then k..gamma together (k
  * from the sizes: a position gets its own launch while the bytes its gate is
- * expected to save outweigh a launch), then the finish kernel. In every launch
+ * expected to save, at an assumed acceptance rate of 0.7, outweigh a launch;
+ * small batches get k = 0, one launch with no gate), then the finish kernel.
+ * spec_verify_sample_early_exit_grouped takes k from the caller. In every launch
  * after the first, each workgroup re-derives the accept decision of the
  * position before it and streams its rows only if that position was accepted.
  * Data moved: the rows of positions 0..n (0..gamma for a sequence that reaches
@@ -149,6 +151,25 @@ int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, i
                                   int B, int gamma, int V, int32_t* out_num_accepted, int32_t* out_tokens,
                                   const sv_sample_diag* diag, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * spec_verify_sample_early_exit_grouped -- spec_verify_sample_early_exit with
+ * the grouping of positions chosen by the caller (who may know the
+ * acceptance rate): tail_start = k in 0..gamma gives positions 0..k-1 a
+ * statistics launch each and k..gamma one together (k = 0: one launch, no
+ * gate; k = gamma: every position gated); tail_start < 0 chooses k from the
+ * sizes exactly as spec_verify_sample_early_exit. Same definition ([SD] "The
+ * pith"), arguments, outputs and parity. Errors: tail_start > gamma ->
+ * SV_ERR_ARG, otherwise as spec_verify_sample.
+ */
+int spec_verify_sample_early_exit_grouped(int tail_start, const void* target_logits, int target_dtype,
+                                          int64_t target_seq_stride, int64_t target_row_stride,
+                                          const void* draft_logits, int draft_dtype, int64_t draft_seq_stride,
+                                          int64_t draft_row_stride, const int32_t* draft_tokens,
+                                          const float* uniforms, const float* temperature, int B, int gamma,
+                                          int V, int32_t* out_num_accepted, int32_t* out_tokens,
+                                          const sv_sample_diag* diag, void* workspace, size_t workspace_bytes,
+                                          void* stream);
 
 /*
  * spec_verify_sample_stage -- one of the two kernels of spec_verify_sample,

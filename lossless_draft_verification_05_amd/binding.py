@@ -33,6 +33,8 @@ SIGNATURES = {
                                         _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sample_early_exit": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
                                              _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample_early_exit_grouped": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp,
+                                                     _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy_tree": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                        _sz, _vp]),
     "spec_verify_greedy_tree_stage": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
@@ -216,6 +218,9 @@ def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_
     if stage == "early_exit":
         return _launch(lib.spec_verify_sample_early_exit, args, "spec_verify_sample_early_exit", outputs, keep,
                        prepare)
+    if isinstance(stage, tuple):  # ("early_exit", tail_start)
+        return _launch(lib.spec_verify_sample_early_exit_grouped, (int(stage[1]),) + args,
+                       f"spec_verify_sample_early_exit_grouped({stage[1]})", outputs, keep, prepare)
     return _launch(lib.spec_verify_sample_stage, (stage,) + args, f"spec_verify_sample_stage({stage})", outputs,
                    keep, prepare)
 
@@ -243,6 +248,16 @@ def spec_verify_sample_early_exit(target, draft, draft_tokens, uniforms, tempera
     outputs (diag p_x, q_x are NaN after the first rejection)."""
     return _sample_call("early_exit", target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
                         out_tokens, diag, workspace, stream, prepare)
+
+
+def spec_verify_sample_early_exit_grouped(tail_start, target, draft, draft_tokens, uniforms, temperature, *,
+                                          out_num_accepted=None, out_tokens=None, diag=False, workspace=None,
+                                          stream=None, prepare=False):
+    """spec_verify_sample_early_exit with the grouping chosen by the caller: positions
+    0..tail_start-1 get a statistics launch each, tail_start..gamma share one (tail_start < 0:
+    chosen from the sizes)."""
+    return _sample_call(("early_exit", int(tail_start)), target, draft, draft_tokens, uniforms, temperature,
+                        out_num_accepted, out_tokens, diag, workspace, stream, prepare)
 
 
 def spec_verify_sample_stage(stage, target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,

@@ -171,13 +171,14 @@ static int run_draft(int first, int last, const void* logits, int dtype, int64_t
 // Early exit: statistics launches over positions 0, 1, ..., k-1 and then
 // k..gamma together (each gated on the accept decision of the position before
 // it), then the finish kernel.
-static int run_sample_early(const SampleArgs& a, hipStream_t stream) {
+static int run_sample_early(const SampleArgs& a, int tail_start, hipStream_t stream) {
   int st = validate_sample(a);
   if (st) return st;
+  if (tail_start > a.gamma) return SV_ERR_ARG;
   SampleLaunch L = plan_sample(a, true);
   if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
   L.reach = (int32_t*)((char*)a.ws + sample_layout(a.B, a.gamma, a.V).off_reach);
-  const int k = early_tail_start(a.B, a.gamma, a.V, esz_of(a.tdt), esz_of(a.ddt));
+  const int k = tail_start >= 0 ? tail_start : early_tail_start(a.B, a.gamma, a.V, esz_of(a.tdt), esz_of(a.ddt));
   for (int p0 = 0; p0 <= a.gamma;) {
     const int p1 = (p0 < k) ? p0 : a.gamma;
     st = hip_status(launch_sample_pos(L, a.tdt, a.ddt, p0, p1, stream));
@@ -237,7 +238,21 @@ int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, i
   SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
-  return run_sample_early(a, (hipStream_t)stream);
+  return run_sample_early(a, -1, (hipStream_t)stream);
+}
+
+int spec_verify_sample_early_exit_grouped(int tail_start, const void* target_logits, int target_dtype,
+                                          int64_t target_seq_stride, int64_t target_row_stride,
+                                          const void* draft_logits, int draft_dtype, int64_t draft_seq_stride,
+                                          int64_t draft_row_stride, const int32_t* draft_tokens,
+                                          const float* uniforms, const float* temperature, int B, int gamma,
+                                          int V, int32_t* out_num_accepted, int32_t* out_tokens,
+                                          const sv_sample_diag* diag, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
+               draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
+               out_num_accepted, out_tokens, diag, workspace, workspace_bytes};
+  return run_sample_early(a, tail_start < 0 ? -1 : tail_start, (hipStream_t)stream);
 }
 
 int spec_tree_mask(const int32_t* parents, const int32_t* blocks, int B, int N, uint8_t* out_mask,

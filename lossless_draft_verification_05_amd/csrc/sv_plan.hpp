@@ -226,14 +226,15 @@ inline int64_t early_chunk_bytes() { return kEarlyChunkBytes; }
 // gate is expected to save -- sequences still active at p (alpha^p) that
 // reject there (1 - alpha) skip the rows of p+1..gamma -- exceed what a launch
 // costs in time (kEarlyLaunchBytes at full bandwidth). alpha is an assumed
-// acceptance rate, not measured.
+// acceptance rate, not measured. k = 0 (small batches) is one launch over
+// every row, with no gate.
 inline int early_tail_start(int64_t B, int64_t G, int64_t V, int et, int ed) {
   const double pair = (double)B * V * (et + ed), bonus = (double)B * V * et;
   double active = 1.0;
-  for (int64_t p = 1; p <= G; ++p) {
-    active *= kEarlyAlpha;
-    const double later = (double)(G - p - 1 > 0 ? G - p - 1 : 0) * pair + (p < G ? bonus : 0.0);
+  for (int64_t p = 0; p < G; ++p) {
+    const double later = (double)(G - p - 1) * pair + bonus;
     if (active * (1.0 - kEarlyAlpha) * later < kEarlyLaunchBytes) return (int)p;
+    active *= kEarlyAlpha;
   }
   return (int)G;
 }

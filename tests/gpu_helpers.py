@@ -64,9 +64,14 @@ def sample_tensors(inp, device="cuda", pad_to=None):
                 temperature=torch.from_numpy(inp.temperature).to(device))
 
 
-def run_sample(binding, tens, diag=True, workspace=None, early_exit=False):
-    fn = binding.spec_verify_sample_early_exit if early_exit else binding.spec_verify_sample
-    n, tok, d = fn(**tens, diag=diag, workspace=workspace)
+def run_sample(binding, tens, diag=True, workspace=None, early_exit=False, tail_start=None):
+    """early_exit: the early-exit entry point; tail_start (with early_exit) the
+    grouped one with that grouping of positions."""
+    if early_exit and tail_start is not None:
+        n, tok, d = binding.spec_verify_sample_early_exit_grouped(tail_start, **tens, diag=diag, workspace=workspace)
+    else:
+        fn = binding.spec_verify_sample_early_exit if early_exit else binding.spec_verify_sample
+        n, tok, d = fn(**tens, diag=diag, workspace=workspace)
     torch.cuda.synchronize()
     out = {"n": n.cpu().numpy(), "tokens": tok.cpu().numpy()}
     if d:

@@ -74,6 +74,8 @@ def call_sample(lib, stage=None, **over):
         return lib.spec_verify_sample(*args)
     if stage == "early_exit":
         return lib.spec_verify_sample_early_exit(*args)
+    if stage == "grouped":
+        return lib.spec_verify_sample_early_exit_grouped(1, *args)
     return lib.spec_verify_sample_stage(stage, *args)
 
 
@@ -90,8 +92,19 @@ def call_sample(lib, stage=None, **over):
 ])
 def test_sample_argument_errors(lib, over, want):
     assert call_sample(lib, **over) == want
-    for stage in (1, 2, "early_exit"):
+    for stage in (1, 2, "early_exit", "grouped"):
         assert call_sample(lib, stage=stage, **over) == want
+
+
+def test_grouping_beyond_gamma(lib):
+    a = sample_args()
+    args = [a["target"], a["tdt"], a["tss"], a["trs"], a["draft"], a["ddt"], a["dss"], a["drs"], a["tokens"],
+            a["uniforms"], a["temps"], a["B"], a["G"], a["V"], a["out_n"], a["out_tok"], a["diag"], a["ws"], a["wsb"],
+            a["stream"]]
+    assert lib.spec_verify_sample_early_exit_grouped(a["G"] + 1, *args) == -7
+    bad = list(args)
+    bad[0] = None
+    assert lib.spec_verify_sample_early_exit_grouped(a["G"] + 1, *bad) == -1  # argument errors first
 
 
 def test_unknown_stage(lib):

@@ -14,13 +14,23 @@ from tests import sample_cases as SC
 pytestmark = pytest.mark.gpu
 
 
-def _both(gpu, inp, pad=None, seqs=None, name="", allow_flags=2, workspace=None):
+# Groupings of positions: chosen from the sizes (small cases get one launch
+# with no gate), position 0 alone and then the rest, every position gated.
+GROUPINGS = ["auto", "first", "all"]
+
+
+def _tail_start(grouping, inp):
+    return {"auto": None, "first": 1, "all": int(inp.tokens.shape[1])}[grouping]
+
+
+def _both(gpu, inp, pad=None, seqs=None, name="", allow_flags=2, workspace=None, grouping="auto"):
     """Early exit against the oracle (on `seqs`, default all) and against the
     one-pass call; a sequence where the two calls differ must be within the
     parity contract (a flagged case) for both of them."""
     tens = H.sample_tensors(inp, pad_to=pad)
     one = H.run_sample(gpu, tens, workspace=workspace)
-    ee = H.run_sample(gpu, tens, workspace=workspace, early_exit=True)
+    ee = H.run_sample(gpu, tens, workspace=workspace, early_exit=True, tail_start=_tail_start(grouping, inp))
+    name = f"{name} ({grouping})"
     differ, bad = H.compare_one_pass(one, ee)
     assert not bad, (name, bad[:5])
     B = inp.tokens.shape[0]
@@ -35,12 +45,13 @@ def _both(gpu, inp, pad=None, seqs=None, name="", allow_flags=2, workspace=None)
     return ee
 
 
+@pytest.mark.parametrize("grouping", GROUPINGS)
 @pytest.mark.parametrize("tdt,ddt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f32")])
 @pytest.mark.parametrize("V,pad", [(5000, None), (4099, 8)])
-def test_small_multitile(gpu, tdt, ddt, V, pad):
+def test_small_multitile(gpu, tdt, ddt, V, pad, grouping):
     H.log(f"early exit small multitile tdt={tdt} ddt={ddt} V={V} pad={pad}")
     inp = synth.make_custom_sample(6, 3, V, tdt, ddt, T=[0.5, 0.9, 1.0, 1.3, 2.0, 0.7], noise_sd=0.8, seed=V + 1)
-    _both(gpu, inp, pad=pad, name=f"{tdt}/{ddt} V={V}")
+    _both(gpu, inp, pad=pad, name=f"{tdt}/{ddt} V={V}", grouping=grouping)
 
 
 def test_config1_tiny(gpu):
@@ -72,19 +83,21 @@ def test_config5(gpu):
     assert (ee["n"][inp.row_class == 2] == inp.gamma).all()
 
 
+@pytest.mark.parametrize("grouping", GROUPINGS)
 @pytest.mark.parametrize("G", [1, 16, 64])
-def test_gamma_extremes(gpu, G):
+def test_gamma_extremes(gpu, G, grouping):
     H.log(f"early exit gamma={G}")
     inp = synth.make_custom_sample(5, G, 3000, "bf16", "f32", T=1.0, noise_sd=0.3, seed=G + 100)
-    _both(gpu, inp, name=f"gamma {G}")
+    _both(gpu, inp, name=f"gamma {G}", grouping=grouping)
 
 
+@pytest.mark.parametrize("grouping", GROUPINGS)
 @pytest.mark.parametrize("case", ["masks_and_signed_zero", "identical_and_disjoint", "invalid_inputs",
                                   "unconsulted_positions", "invalid_after_accepts"])
-def test_edge_cases(gpu, case):
-    H.log(f"early exit edge case {case}")
+def test_edge_cases(gpu, case, grouping):
+    H.log(f"early exit edge case {case} ({grouping})")
     inp = getattr(SC, case)()
-    ee = _both(gpu, inp, name=case)
+    ee = _both(gpu, inp, name=case, grouping=grouping)
     if case == "invalid_inputs":
         assert (ee["n"] == -1).all()
     if case == "invalid_after_accepts":
@@ -117,14 +130,16 @@ def test_repeat_calls_bit_identical(gpu):
         assert np.array_equal(r1[k].view(np.uint8), r2[k].view(np.uint8)), k
 
 
+@pytest.mark.parametrize("grouping", GROUPINGS)
 @pytest.mark.parametrize("T", [1e-6, 1e-12, 1e-30])
-def test_temperature_extremes(gpu, T):
+def test_temperature_extremes(gpu, T, grouping):
     H.log(f"early exit T={T}")
     inp = synth.make_custom_sample(6, 4, 2048, "bf16", "f32", T=T, noise_sd=0.5, seed=12)
-    _both(gpu, inp, name=f"T={T}")
+    _both(gpu, inp, name=f"T={T}", grouping=grouping)
 
 
-def test_huge_logits(gpu):
+@pytest.mark.parametrize("grouping", GROUPINGS)
+def test_huge_logits(gpu, grouping):
     """Logits around 10^8 (N(0, 2e7)): the statistics pass takes its subtract form."""
     inp = synth.make_custom_sample(6, 3, 3000, "f32", "f32", T=1.0, noise_sd=1e6, target_sd=2e7, seed=13)
-    _both(gpu, inp, name="huge logits")
+    _both(gpu, inp, name="huge logits", grouping=grouping)
