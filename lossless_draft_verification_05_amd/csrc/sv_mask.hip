@@ -13,7 +13,8 @@
 // node to the root (parents[j] < j bounds the walk by j steps), setting the
 // bits of the row's ancestors in an LDS bitset and counting the depth. The
 // slab (at most 64 KB of mask bytes, so at most 8 KB of bits) is then written
-// as a flat byte range with 16-byte stores.
+// as a flat byte range with 16-byte stores, each built from at most two
+// bitset words.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,42 +30,84 @@ __device__ __forceinline__ uint8_t mask_byte(int i, int j, int r0, int W, const 
   return anc || (blk[i] >= 0 && blk[i] == blk[j]);
 }
 
-// Writes bytes [e0, e1) of a tree's [N][N] mask (flat index e = i * N + j);
-// zero: write zeros (invalid tree).
-__device__ void write_mask_range(uint8_t* out, int64_t e0, int64_t e1, int N, int r0, int W, const uint32_t* bits,
+// Four mask bits (x in 0..15) as four 0/1 bytes, bit k in byte k: the shifted
+// copies of x (by 0, 7, 14, 21) occupy disjoint bit ranges, so the product
+// has no carries.
+__device__ __forceinline__ uint32_t bits_to_bytes(uint32_t x) { return (x * 0x204081u) & 0x01010101u; }
+
+// Bits j..j+15 of a bitset row of W words (j + 16 <= the row's bit count).
+__device__ __forceinline__ uint32_t row_bits16(const uint32_t* row, int j, int W) {
+  const int wi = j >> 5;
+  const uint64_t two = (uint64_t)row[wi] | ((uint64_t)(wi + 1 < W ? row[wi + 1] : 0u) << 32);
+  return (uint32_t)(two >> (j & 31)) & 0xffffu;
+}
+
+// Writes bytes [e0, e1) of a tree's [N][N] mask (flat index e = i * N + j < 2^20);
+// zero: write zeros (invalid tree). Each thread writes 16-byte vectors; a
+// vector inside one row takes its 16 ancestor bits from at most two bitset
+// words and, for the relaxed mask, compares its 16 block ids with the row's
+// (read 4 at a time when aligned: the lanes' 64-byte strides make single-id
+// reads collide in the LDS banks); one that crosses a row end is built byte by
+// byte.
+__device__ void write_mask_range(uint8_t* out, int e0, int e1, int N, int r0, int W, const uint32_t* bits,
                                  const int* blk, bool relaxed, bool zero) {
   const int tid = threadIdx.x;
   // head: bytes up to the first 16-byte boundary
-  int64_t a = (int64_t)(((uintptr_t)(out + e0) + 15) & ~(uintptr_t)15) - (int64_t)(uintptr_t)out;
+  int a = (int)((((uintptr_t)(out + e0) + 15) & ~(uintptr_t)15) - (uintptr_t)out);
   if (a > e1) a = e1;
-  for (int64_t e = e0 + tid; e < a; e += blockDim.x)
-    out[e] = zero ? 0 : mask_byte((int)(e / N), (int)(e % N), r0, W, bits, blk, relaxed);
+  for (int e = e0 + tid; e < a; e += blockDim.x)
+    out[e] = zero ? 0 : mask_byte(e / N, e % N, r0, W, bits, blk, relaxed);
   // body: 16 bytes per thread per iteration
-  const int64_t nvec = (e1 - a) / 16;
-  for (int64_t v = tid; v < nvec; v += blockDim.x) {
-    const int64_t e = a + v * 16;
+  const int nvec = (e1 - a) / 16;
+  for (int v = tid; v < nvec; v += blockDim.x) {
+    const int e = a + v * 16;
     uint32_t w[4] = {0, 0, 0, 0};
     if (!zero) {
-      int i = (int)(e / N), j = (int)(e % N);
+      const int i = e / N, j = e % N;
+      if (j + 16 <= N) {
+        uint32_t m = row_bits16(bits + (i - r0) * W, j, W);
+        if (relaxed) {
+          const int bi = blk[i];
+          if (bi >= 0) {
+            if ((j & 3) == 0) {
+              const int4* q4 = reinterpret_cast<const int4*>(blk + j);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        w[k >> 2] |= (uint32_t)mask_byte(i, j, r0, W, bits, blk, relaxed) << (8 * (k & 3));
-        if (++j == N) {
-          j = 0;
-          ++i;
+              for (int q = 0; q < 4; ++q) {
+                const int4 v = q4[q];
+                m |= ((uint32_t)(v.x == bi) | (uint32_t)(v.y == bi) << 1 | (uint32_t)(v.z == bi) << 2 |
+                      (uint32_t)(v.w == bi) << 3) << (4 * q);
+              }
+            } else {
+#pragma unroll
+              for (int k = 0; k < 16; ++k) m |= (uint32_t)(blk[j + k] == bi) << k;
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = bits_to_bytes((m >> (4 * q)) & 0xfu);
+      } else {
+        int ii = i, jj = j;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          w[k >> 2] |= (uint32_t)mask_byte(ii, jj, r0, W, bits, blk, relaxed) << (8 * (k & 3));
+          if (++jj == N) {
+            jj = 0;
+            ++ii;
+          }
         }
       }
     }
     *reinterpret_cast<uint4*>(out + e) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   // tail
-  for (int64_t e = a + nvec * 16 + tid; e < e1; e += blockDim.x)
-    out[e] = zero ? 0 : mask_byte((int)(e / N), (int)(e % N), r0, W, bits, blk, relaxed);
+  for (int e = a + nvec * 16 + tid; e < e1; e += blockDim.x)
+    out[e] = zero ? 0 : mask_byte(e / N, e % N, r0, W, bits, blk, relaxed);
 }
 
 __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
-  __shared__ int par[kMaxMaskNodes], blk[kMaxMaskNodes];
-  __shared__ uint32_t bits[kMaskSlabBytes / 32];  // slab rows x W words
+  __shared__ int par[kMaxMaskNodes];
+  __shared__ __align__(16) int blk[kMaxMaskNodes];
+  __shared__ uint32_t bits[kMaskSlabBytes / 32];  // slab rows x W words: ancestors (and the node itself)
   __shared__ int sh_bad;
   const int N = A.N, tid = threadIdx.x;
   const int b = blockIdx.x / A.nslab, slab = blockIdx.x % A.nslab;
@@ -82,16 +125,25 @@ __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
   }
   __syncthreads();
   const bool bad = sh_bad != 0;
-  const int64_t e0 = (int64_t)r0 * N, e1 = (int64_t)r1 * N;
+  const int e0 = r0 * N, e1 = r1 * N;  // N <= 1024: a tree's mask has at most 2^20 bytes
   if (!bad) {
-    // one thread per row: the path to the root
+    // one thread per row: the path to the root. Ancestors strictly decrease,
+    // so each bitset word is visited in one run: it is built in a register and
+    // stored once when the walk leaves it (the bitset was cleared above).
     for (int i = r0 + tid; i < r1; i += kThreads) {
       uint32_t* row = bits + (i - r0) * W;
-      int d = 0;
+      int d = 0, cw = i >> 5;
+      uint32_t cur = 0;
       for (int a = i; a >= 0; a = par[a]) {
-        row[a >> 5] |= 1u << (a & 31);
+        if ((a >> 5) != cw) {
+          row[cw] = cur;
+          cw = a >> 5;
+          cur = 0;
+        }
+        cur |= 1u << (a & 31);
         ++d;
       }
+      row[cw] = cur;
       if (A.out_depth) A.out_depth[(int64_t)b * N + i] = d - 1;
     }
   } else if (A.out_depth) {
