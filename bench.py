@@ -646,6 +646,10 @@ def main():
                     "target_dtype": cfg.target_dtype, "draft_dtype": cfg.draft_dtype, "temperature": tdesc,
                     "seed": args.seed}
         kernel_names = ["sv_stats_kernel", "sv_finish_kernel"]
+        small = V <= 2048 and not args.early_exit  # the full call is one kernel, a wave per sequence
+        if small:
+            kernel_names = ["sv_small_kernel"]
+            prep = {c: [whole[c]] for c in range(R)}
         if args.early_exit:
             kernel_names = ["spec_verify_sample_early_exit"]
             cfg_desc["entry_point"] = "spec_verify_sample_early_exit"
@@ -723,6 +727,8 @@ def main():
         if args.early_exit:
             detail["one_pass_step_alg_bytes"] = int(s1_bytes + s2_bytes)
             s1_bytes = step_bytes = early_exit_bytes(inp.cfg, B, G, V, n_acc)
+        elif small:
+            s1_bytes = step_bytes  # one kernel reads the rows once and the draw row(s) again
         else:
             detail["kernels"]["sv_finish_kernel"]["alg_bytes"] = int(s2_bytes)
             detail["kernels"]["sv_finish_kernel"]["gbps"] = round(s2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1)

@@ -14,6 +14,7 @@ namespace sv {
 hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stage, hipStream_t stream);
 hipError_t launch_sample_pos(const SampleLaunch& A, int tdt, int ddt, int p0, int p1, hipStream_t stream);
 hipError_t launch_draft_one_pass(const SampleLaunch& A, int dt, hipStream_t stream);
+hipError_t launch_sample_small(const SampleLaunch& A, int tdt, int ddt, hipStream_t stream);
 hipError_t launch_tree(const TreeLaunch& A, int dt, int stage, hipStream_t stream);
 hipError_t launch_mask(const MaskLaunch& A, hipStream_t stream);
 
@@ -133,6 +134,8 @@ static int run_sample(int first, int last, const SampleArgs& a, hipStream_t stre
   const SampleLaunch L = plan_sample(a);
   // grid sizes fit a 32-bit dimension by construction of the limits; check anyway
   if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
+  // the whole call on rows of one draw step: one kernel, a wave per sequence
+  if (first == 1 && last == 2 && a.V <= kStepTokens) return hip_status(launch_sample_small(L, a.tdt, a.ddt, stream));
   for (int s = first; s <= last; ++s) {
     st = hip_status(launch_sample_stage(L, a.tdt, a.ddt, s, stream));
     if (st) return st;

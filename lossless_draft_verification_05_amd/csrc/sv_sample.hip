@@ -684,7 +684,7 @@ __device__ __forceinline__ void gather_steps(const SampleLaunch& A, int b, const
 }
 
 // Sum of arr[0..len) by one wave, in a fixed order.
-__device__ double wave_total(const double* arr, int len, int lane) {
+__device__ __forceinline__ double wave_total(const double* arr, int len, int lane) {
   double acc = 0.0;
   for (int i = lane; i < len; i += kWave) acc += arr[i];
   return wave_sum(acc);
@@ -693,7 +693,7 @@ __device__ double wave_total(const double* arr, int len, int lane) {
 // Wave-wide search over arr[0..len): the first i (in order) whose running mass
 // acc + arr[0] + ... + arr[i] exceeds t, with arr[i] > 0. If rounding leaves no
 // such i, the last i with arr[i] > 0. On return acc holds the mass before i.
-__device__ int wave_find(const double* arr, int len, double t, double& acc, int lane) {
+__device__ __forceinline__ int wave_find(const double* arr, int len, double t, double& acc, int lane) {
   double run = acc;
   int last_i = -1;
   double last_acc = acc;
@@ -720,89 +720,80 @@ __device__ int wave_find(const double* arr, int len, double t, double& acc, int 
   return last_i;
 }
 
-// Inverse-CDF draw from the step masses stot[0..ns2) (total mass `total`) of
-// the draw row(s) of sequence b, then every output of the sequence. Wave 0
-// searches; all threads of the workgroup (kFinThreads) write. sh_y: LDS slot.
+// Rescan of step ss of the draw row(s) of sequence b by one wave, in token
+// order (octet j-major, then lane, then slot): the first token whose running
+// mass acc + ... exceeds t (acc: the mass of the steps before ss). If rounding
+// leaves none, the step's last token with positive mass. Every lane returns y.
 template <int TD, int DD>
-__device__ void draw_and_write(const SampleLaunch& A, int b, const SeqPlan& P, int mode, const double* stot,
-                               double total, int* sh_y) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = A.gamma;
-  int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
-  // (5) inverse-CDF search (wave 0)
-  if (w == 0) {
-    const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
-    double acc = 0.0;
-    // wave_find returns -1 only if every mass is zero, which valid rows rule
-    // out; clamp anyway so that no index can leave the arrays.
-    const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
-    // rescan the step in token order: octet j-major, then lane, then slot
-    const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
-    const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
-    const int64_t noct = ((int64_t)A.V + 7) / 8;
-    float rr[kU2][8];
+__device__ __forceinline__ int rescan_step(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int ss, double t,
+                                           double acc, int lane) {
+  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
+  const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
+  const int64_t noct = ((int64_t)A.V + 7) / 8;
+  float rr[kU2][8];
 #pragma unroll
-    for (int j = 0; j < kU2; ++j) {
-      const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
-      if (oct < noct) {
-        octet_mass<TD, DD>(trow, drow, oct, A.V, mode, P, rr[j]);
-      } else {
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      octet_mass<TD, DD>(trow, drow, oct, A.V, mode, P, rr[j]);
+    } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
-      }
+      for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
     }
-    int y = -1;
-    int last_pos = -1;
-    for (int j = 0; j < kU2 && y < 0; ++j) {
-      const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
-      const double os = (double)sum8(rr[j]);
-      const double incl = wave_incl_scan(os, lane);
-      const double excl = incl - os;
-      int lk = -1;
+  }
+  int y = -1;
+  int last_pos = -1;
+  for (int j = 0; j < kU2 && y < 0; ++j) {
+    const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
+    const double os = (double)sum8(rr[j]);
+    const double incl = wave_incl_scan(os, lane);
+    const double excl = incl - os;
+    int lk = -1;
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (rr[j][k] > 0.0f) lk = k;
-      if (lk >= 0) last_pos = (int)(oct * 8 + lk);  // later j / lanes have larger ids
-      const unsigned long long hit = __ballot(os > 0.0 && acc + incl > t);
-      if (hit) {
-        const int L = __ffsll((long long)hit) - 1;
-        int yy = -1;
-        if (lane == L) {
-          double run = acc + excl;
-          for (int k = 0; k < 8; ++k) {
-            if (rr[j][k] > 0.0f) {
-              run += (double)rr[j][k];
-              if (run > t) {
-                yy = (int)(oct * 8 + k);
-                break;
-              }
+    for (int k = 0; k < 8; ++k)
+      if (rr[j][k] > 0.0f) lk = k;
+    if (lk >= 0) last_pos = (int)(oct * 8 + lk);  // later j / lanes have larger ids
+    const unsigned long long hit = __ballot(os > 0.0 && acc + incl > t);
+    if (hit) {
+      const int L = __ffsll((long long)hit) - 1;
+      int yy = -1;
+      if (lane == L) {
+        double run = acc + excl;
+        for (int k = 0; k < 8; ++k) {
+          if (rr[j][k] > 0.0f) {
+            run += (double)rr[j][k];
+            if (run > t) {
+              yy = (int)(oct * 8 + k);
+              break;
             }
           }
-          if (yy < 0) yy = (int)(oct * 8 + lk);
         }
-        y = __builtin_amdgcn_readlane(yy, L);
-      } else {
-        acc += readlane_f64(incl, kWave - 1);
+        if (yy < 0) yy = (int)(oct * 8 + lk);
       }
+      y = __builtin_amdgcn_readlane(yy, L);
+    } else {
+      acc += readlane_f64(incl, kWave - 1);
     }
-    if (y < 0) {
-      // rounding pushed t past the step's rescanned mass: take its last positive token
-      int m = last_pos;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
-      y = m;
-    }
-    if (lane == 0) *sh_y = y;
   }
-  __syncthreads();
+  if (y < 0) {
+    // rounding pushed t past the step's rescanned mass: take its last positive token
+    int m = last_pos;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
+    y = m;
+  }
+  return y;
+}
 
-  // (6) outputs
-  const int y = *sh_y;
-  const int n = P.n;
-  for (int k = tid; k <= G; k += kFinThreads)
-    otok[k] = (k < n) ? A.tokens[(int64_t)b * G + k] : (k == n ? y : -1);
-  if (tid == 0) {
+// Every output of a valid sequence b once y is drawn: threads t0, t0 + nt, ...
+// write the tokens; thread t0 the scalars.
+template <int TD>
+__device__ __forceinline__ void write_outputs(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int y,
+                                              double total, int t, int t0, int nt) {
+  const int G = A.gamma, n = P.n;
+  int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
+  for (int k = t - t0; k <= G; k += nt) otok[k] = (k < n) ? A.tokens[(int64_t)b * G + k] : (k == n ? y : -1);
+  if (t == t0) {
     if (A.out_n) A.out_n[b] = n;
     if (A.diag_mass) A.diag_mass[b] = (float)(total / (P.sp * P.fscale));
     if (A.out_py) {
@@ -815,6 +806,86 @@ __device__ void draw_and_write(const SampleLaunch& A, int b, const SeqPlan& P, i
       A.out_py[b] = py;
     }
   }
+}
+
+// The outputs of an invalid sequence (every token -1).
+__device__ __forceinline__ void write_invalid(const SampleLaunch& A, int b, int t, int t0, int nt) {
+  const int G = A.gamma;
+  int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
+  for (int k = t - t0; k <= G; k += nt) otok[k] = -1;
+  if (t == t0) {
+    if (A.out_n) A.out_n[b] = -1;
+    if (A.out_py) A.out_py[b] = __builtin_nanf("");
+    if (A.diag_mass) A.diag_mass[b] = __builtin_nanf("");
+  }
+}
+
+// Inverse-CDF draw from the step masses stot[0..ns2) (total mass `total`) of
+// the draw row(s) of sequence b, then every output of the sequence. Wave 0
+// searches; all threads of the workgroup (kFinThreads) write. sh_y: LDS slot.
+template <int TD, int DD>
+__device__ __forceinline__ void draw_and_write(const SampleLaunch& A, int b, const SeqPlan& P, int mode, const double* stot,
+                               double total, int* sh_y) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = A.gamma;
+  // (5) inverse-CDF search (wave 0)
+  if (w == 0) {
+    const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
+    double acc = 0.0;
+    // wave_find returns -1 only if every mass is zero, which valid rows rule
+    // out; clamp anyway so that no index can leave the arrays.
+    const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
+    const int y = rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane);
+    if (lane == 0) *sh_y = y;
+  }
+  __syncthreads();
+  // (6) outputs
+  write_outputs<TD>(A, b, P, mode, *sh_y, total, tid, 0, kFinThreads);
+}
+
+// The plan of the draw of a sequence whose first stop is n (gamma: every
+// draft accepted) with accept code code_n there; tn, dn: the statistics of
+// target row n and (n < gamma) draft row n. nst: rows with statistics.
+__device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, bool tv, float kl, float ug,
+                                             const RowStat& tn, const RowStat& dn) {
+  bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f && n < nst;
+  if (n == G) valid = valid && tn.valid;
+  SeqPlan Q;
+  Q.valid = valid;
+  Q.n = n;
+  Q.mode = (n == G) ? kModeBonus : kModeResidual;
+  Q.kl = kl;
+  Q.mp = tn.m;
+  Q.sp = tn.s;
+  const double kld = (double)kl;
+  const double cp = (double)Q.mp * kld;  // exact product of two floats
+  Q.cp = (float)cp;
+  const double dp = cp - (double)Q.cp;
+  Q.fscale = exp2(dp);
+  // the shifts must round by less than half a log2 unit: |c| < 2^24
+  bool fma_ok = fabs(cp) < 0x1p24;
+  if (n < G) {
+    Q.mq = dn.m;
+    Q.sq = dn.s;
+    const double kap = Q.sp / Q.sq;
+    Q.kap_hi = (float)kap;
+    Q.kap_lo = (float)(kap - (double)Q.kap_hi);
+    const double cq = (double)Q.mq * kld - log2(kap) - dp;
+    Q.cq = (float)cq;
+    Q.corr = (float)((cq - (double)Q.cq) * 0.69314718055994530942);
+    fma_ok = fma_ok && fabs(cq) < 0x1p24;
+  } else {
+    Q.mq = 0.0f;
+    Q.sq = 1.0;
+    Q.kap_hi = 0.0f;
+    Q.kap_lo = 0.0f;
+    Q.cq = 0.0f;
+    Q.corr = 0.0f;
+  }
+  Q.form = fma_ok ? 1 : 0;
+  if (!fma_ok) Q.fscale = 1.0;
+  return Q;
 }
 
 // ---------------------------------------------------------------------------
@@ -914,59 +985,16 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     const int n = stop ? (__ffsll((long long)stop) - 1) : G;
     const int code_n = __builtin_amdgcn_readlane(code, n < G ? n : 0);
     if (lane == 0) {
-      const float ug = A.uniforms[(int64_t)b * (G + 1) + G];
-      bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f && n < nst;
-      if (n == G) valid = valid && rV[G];
-      SeqPlan Q;
-      Q.valid = valid;
-      Q.n = n;
-      Q.mode = (n == G) ? kModeBonus : kModeResidual;
-      Q.kl = kl;
-      Q.mp = rM[n];
-      Q.sp = rS[n];
-      const double kld = (double)kl;
-      const double cp = (double)Q.mp * kld;  // exact product of two floats
-      Q.cp = (float)cp;
-      const double dp = cp - (double)Q.cp;
-      Q.fscale = exp2(dp);
-      // the shifts must round by less than half a log2 unit: |c| < 2^24
-      bool fma_ok = fabs(cp) < 0x1p24;
-      if (n < G) {
-        Q.mq = rM[G + 1 + n];
-        Q.sq = rS[G + 1 + n];
-        const double kap = Q.sp / Q.sq;
-        Q.kap_hi = (float)kap;
-        Q.kap_lo = (float)(kap - (double)Q.kap_hi);
-        const double cq = (double)Q.mq * kld - log2(kap) - dp;
-        Q.cq = (float)cq;
-        Q.corr = (float)((cq - (double)Q.cq) * 0.69314718055994530942);
-        fma_ok = fma_ok && fabs(cq) < 0x1p24;
-      } else {
-        Q.mq = 0.0f;
-        Q.sq = 1.0;
-        Q.kap_hi = 0.0f;
-        Q.kap_lo = 0.0f;
-        Q.cq = 0.0f;
-        Q.corr = 0.0f;
-      }
-      Q.form = fma_ok ? 1 : 0;
-      if (!fma_ok) Q.fscale = 1.0;
-      sP = Q;
+      const RowStat tn{rM[n], rS[n], rV[n]};
+      const RowStat dn = (n < G) ? RowStat{rM[G + 1 + n], rS[G + 1 + n], rV[G + 1 + n]} : RowStat{0.0f, 1.0, 0};
+      sP = make_plan(n, code_n, G, nst, tv, kl, A.uniforms[(int64_t)b * (G + 1) + G], tn, dn);
     }
   }
   __syncthreads();
   const SeqPlan P = sP;
-  int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
   if (!P.valid) {
     // every part reaches the same plan; part 0 writes the outputs
-    if (part == 0) {
-      for (int k = tid; k <= G; k += kFinThreads) otok[k] = -1;
-      if (tid == 0) {
-        if (A.out_n) A.out_n[b] = -1;
-        if (A.out_py) A.out_py[b] = __builtin_nanf("");
-        if (A.diag_mass) A.diag_mass[b] = __builtin_nanf("");
-      }
-    }
+    if (part == 0) write_invalid(A, b, tid, 0, kFinThreads);
     return;
   }
 
@@ -1289,6 +1317,151 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
 }
 
 // ---------------------------------------------------------------------------
+// small vocabularies (V <= kStepTokens): one wave per sequence, every step
+// ---------------------------------------------------------------------------
+// Statistics of one row from this lane's PL values x (value v = lane + 64 k;
+// -inf past V) by one wave: the reference is the row's maximum, s = sum_v
+// exp2((x_v - m) * kl) with fp32 terms summed in fp64 (each lane's values in
+// order, then the wave sum). NaN or +inf values make the row invalid, as in the
+// statistics pass.
+template <int PL>
+__device__ __forceinline__ RowStat small_row_stat(const float (&x)[PL], float kl, bool tv) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < PL; ++k) m = fmaxf(m, x[k]);
+  m = wave_max(m);
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < PL; ++k) {
+    const bool nan = x[k] != x[k];
+    if (nan || x[k] != -INFINITY) s += nan ? (double)x[k] : (double)hw_exp2((x[k] - m) * kl);
+  }
+  s = wave_sum(s);
+  RowStat r;
+  r.m = m;
+  r.s = s;
+  r.valid = tv && __builtin_isfinite(s) && s > 0.0 && __builtin_isfinite(m);
+  return r;
+}
+
+// The whole verify of sequences with V <= kStepTokens: wave w of workgroup g
+// takes sequence 4 g + w. Row statistics straight from the rows (no
+// partials), the accept tests, the plan, the one step's mass, the rescan and
+// the outputs, with the same functions as the two-kernel path from the plan
+// on. Needs no workspace.
+// PL: values of a row per lane (V <= 64 PL); rows are loaded RB at a time, so
+// that their loads overlap.
+template <int TD, int DD, int PL>
+__global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
+  constexpr int RB = PL == 1 ? 16 : (PL <= 4 ? 4 : 1);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.x * kWaves + w;
+  if (b >= A.B) return;  // the whole wave; this kernel has no workgroup barrier
+  const float T = A.temps[b];
+  const bool tv = temp_ok(T);
+  const float kl = tv ? log2e_over(T) : 1.0f;
+  const int G = A.gamma;
+
+  // the draft tokens, their uniforms and logits (position = lane)
+  int xi = 0;
+  float ui = 0.0f, lt = 0.0f, ld = 0.0f;
+  bool tok_ok = false;
+  if (lane < G) {
+    xi = A.tokens[(int64_t)b * G + lane];
+    ui = A.uniforms[(int64_t)b * (G + 1) + lane];
+    tok_ok = xi >= 0 && xi < A.V;
+    if (tok_ok) {
+      lt = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)lane * A.t_row_b, xi);
+      ld = load_elem<DD>(A.dft + (int64_t)b * A.d_seq_b + (int64_t)lane * A.d_row_b, xi);
+    }
+  }
+  // statistics of target rows 0..G (slots 0..G) and draft rows 0..G-1 (slots
+  // G+1..2G); slot t is kept by lane t % 64 in register set t / 64
+  float m0 = 0.0f, m1 = 0.0f;
+  double s0 = 0.0, s1 = 0.0;
+  int v0 = 0, v1 = 0;
+  for (int t0 = 0; t0 <= 2 * G; t0 += RB) {
+    float x[RB][PL];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int t = t0 + r;
+      const char* row = (t <= G) ? A.tgt + (int64_t)b * A.t_seq_b + (int64_t)t * A.t_row_b
+                                 : A.dft + (int64_t)b * A.d_seq_b + (int64_t)(t - G - 1) * A.d_row_b;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const int v = lane + kWave * k;
+        x[r][k] = -INFINITY;
+        if (t <= 2 * G && v < A.V) x[r][k] = (t <= G) ? load_elem<TD>(row, v) : load_elem<DD>(row, v);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int t = t0 + r;
+      if (t > 2 * G) break;
+      const RowStat st = small_row_stat<PL>(x[r], kl, tv);
+      if (lane == (t & (kWave - 1))) {
+        if (t < kWave) {
+          m0 = st.m;
+          s0 = st.s;
+          v0 = st.valid;
+        } else {
+          m1 = st.m;
+          s1 = st.s;
+          v1 = st.valid;
+        }
+      }
+    }
+  }
+  // slot t's statistics: in every lane for a uniform t, from lane j % 64 for a per-lane j
+  auto slot_uniform = [&](int t) {
+    return (t < kWave) ? RowStat{readlane_f32(m0, t), readlane_f64(s0, t), __builtin_amdgcn_readlane(v0, t)}
+                       : RowStat{readlane_f32(m1, t - kWave), readlane_f64(s1, t - kWave),
+                                 __builtin_amdgcn_readlane(v1, t - kWave)};
+  };
+  // accept tests (lane i: position i; target slot i is its own) and the first stop
+  const int j = G + 1 + lane;  // this lane's draft slot
+  const int jl = j & (kWave - 1);
+  const float dm0 = __shfl(m0, jl, kWave), dm1 = __shfl(m1, jl, kWave);
+  const double ds0 = __shfl(s0, jl, kWave), ds1 = __shfl(s1, jl, kWave);
+  const int dv0 = __shfl(v0, jl, kWave), dv1 = __shfl(v1, jl, kWave);
+  int code = 1;
+  if (lane < G) {
+    const RowStat ts{m0, s0, v0};
+    const RowStat ds = (j < kWave) ? RowStat{dm0, ds0, dv0} : RowStat{dm1, ds1, dv1};
+    const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv);
+    code = ao.code;
+    if (A.diag_px) A.diag_px[(int64_t)b * G + lane] = ao.px;
+    if (A.diag_qx) A.diag_qx[(int64_t)b * G + lane] = ao.qx;
+  }
+  const unsigned long long stop = __ballot(code != 1);
+  const int n = stop ? (__ffsll((long long)stop) - 1) : G;
+  const int code_n = __builtin_amdgcn_readlane(code, n < G ? n : 0);
+  const RowStat tn = slot_uniform(n);
+  const RowStat dn = (n < G) ? slot_uniform(G + 1 + n) : RowStat{0.0f, 1.0, 0};
+  const SeqPlan P = make_plan(n, code_n, G, G + 1, tv, kl, A.uniforms[(int64_t)b * (G + 1) + G], tn, dn);
+  if (!P.valid) {
+    write_invalid(A, b, lane, 0, kWave);
+    return;
+  }
+  // the drawn distribution's one step, then the draw
+  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)n * A.t_row_b;
+  const char* drow = (n < G) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)n * A.d_row_b : nullptr;
+  const int64_t noct = ((int64_t)A.V + 7) / 8;
+  int mode = P.mode;
+  double total = (mode == kModeResidual) ? direct_step_mass<TD, DD, kModeResidual>(trow, drow, 0, noct, A.V, P, lane)
+                                         : direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
+  if (!(total > 0.0) && mode == kModeResidual) {
+    // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
+    mode = kModeBonus;
+    total = direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
+  }
+  const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
+  const int y = rescan_step<TD, DD>(A, b, P, mode, 0, t, 0.0, lane);
+  write_outputs<TD>(A, b, P, mode, y, total, lane, 0, kWave);
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 template <int TD, int DD>
@@ -1315,6 +1488,25 @@ hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stag
   if (tdt == 1 && ddt == 0) return launch_pair<1, 0>(A, stage, stream);
   if (tdt == 0 && ddt == 1) return launch_pair<0, 1>(A, stage, stream);
   return launch_pair<0, 0>(A, stage, stream);
+}
+
+template <int TD, int DD>
+static hipError_t launch_small_t(const SampleLaunch& A, hipStream_t stream) {
+  const dim3 grid((unsigned)(((int64_t)A.B + kWaves - 1) / kWaves));
+  if (A.V <= kWave)
+    hipLaunchKernelGGL((sv_small_kernel<TD, DD, 1>), grid, dim3(kThreads), 0, stream, A);
+  else if (A.V <= 4 * kWave)
+    hipLaunchKernelGGL((sv_small_kernel<TD, DD, 4>), grid, dim3(kThreads), 0, stream, A);
+  else
+    hipLaunchKernelGGL((sv_small_kernel<TD, DD, kStepTokens / kWave>), grid, dim3(kThreads), 0, stream, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_small(const SampleLaunch& A, int tdt, int ddt, hipStream_t stream) {
+  if (tdt == 1 && ddt == 1) return launch_small_t<1, 1>(A, stream);
+  if (tdt == 1 && ddt == 0) return launch_small_t<1, 0>(A, stream);
+  if (tdt == 0 && ddt == 1) return launch_small_t<0, 1>(A, stream);
+  return launch_small_t<0, 0>(A, stream);
 }
 
 hipError_t launch_draft_one_pass(const SampleLaunch& A, int dt, hipStream_t stream) {

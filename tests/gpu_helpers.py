@@ -79,6 +79,19 @@ def run_sample(binding, tens, diag=True, workspace=None, early_exit=False, tail_
     return out
 
 
+def run_sample_staged(binding, tens, workspace=None):
+    """The two kernels of spec_verify_sample called one stage at a time (the
+    statistics pass, then the finish), whatever the vocabulary size."""
+    ws = workspace if workspace is not None else binding.Workspace()
+    n, tok, _ = binding.spec_verify_sample_stage(1, **tens, workspace=ws)
+    n, tok, d = binding.spec_verify_sample_stage(2, **tens, out_num_accepted=n, out_tokens=tok, diag=True,
+                                                 workspace=ws)
+    torch.cuda.synchronize()
+    out = {"n": n.cpu().numpy(), "tokens": tok.cpu().numpy()}
+    out.update({k: v.cpu().numpy() for k, v in d.items()})
+    return out
+
+
 def compare_one_pass(one, ee):
     """Early exit against the one-pass call on the same inputs. Returns
     (differing, bad): the sequences whose n or tokens differ (both results are

@@ -21,29 +21,34 @@ def _check(inp, out, name, allow_flags=2):
     return t
 
 
-@pytest.mark.parametrize("V", [1, 7, 8, 9, 31, 33, 4097, 128257])
+@pytest.mark.parametrize("V", [1, 7, 8, 9, 31, 33, 2047, 2048, 2049, 4097, 128257])
 @pytest.mark.parametrize("tdt,ddt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
 def test_vocab_sizes(gpu, V, tdt, ddt):
+    """Up to 2048 tokens the full call runs the one-wave-per-sequence kernel;
+    the staged (two-kernel) path is checked at every size too."""
     H.log(f"vocab V={V} {tdt}/{ddt}")
     inp = synth.make_custom_sample(5, 3, V, tdt, ddt, T=[0.6, 1.0, 1.0, 1.5, 0.9], seed=V + 1)
-    out = H.run_sample(gpu, H.sample_tensors(inp, pad_to=8))
+    tens = H.sample_tensors(inp, pad_to=8)
+    out = H.run_sample(gpu, tens)
     _check(inp, out, f"V={V}")
     if V == 1:
         assert (out["n"] == 3).all() and (out["tokens"] == 0).all()
+    _check(inp, H.run_sample_staged(gpu, tens), f"V={V} staged")
 
 
+@pytest.mark.parametrize("V", [3000, 696])
 @pytest.mark.parametrize("G", [1, 16, 64])
-def test_gamma_extremes(gpu, G):
-    H.log(f"gamma={G}")
-    inp = synth.make_custom_sample(4, G, 3000, "bf16", "bf16", T=1.0, noise_sd=0.3, seed=G)
-    _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), f"gamma={G}")
+def test_gamma_extremes(gpu, G, V):
+    H.log(f"gamma={G} V={V}")
+    inp = synth.make_custom_sample(4, G, V, "bf16", "bf16", T=1.0, noise_sd=0.3, seed=G)
+    _full_and_staged(gpu, inp, f"gamma={G} V={V}")
 
 
 @pytest.mark.parametrize("T", [0.05, 10.0, 1e-6, 1e-12, 1e-30])
 def test_temperature_extremes(gpu, T):
     H.log(f"T={T}")
     inp = synth.make_custom_sample(6, 4, 2048, "bf16", "f32", T=T, noise_sd=0.5, seed=11)
-    _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), f"T={T}")
+    _full_and_staged(gpu, inp, f"T={T}")
 
 
 def test_vocab_beyond_lds_steps(gpu):
@@ -60,39 +65,42 @@ def test_batch_of_one(gpu):
 _custom = SC.custom
 
 
+def _full_and_staged(gpu, inp, name):
+    """The full call and the two kernels one stage at a time, both against the
+    oracle (at up to 2048 tokens the full call is the one-wave kernel); returns
+    both results."""
+    tens = H.sample_tensors(inp)
+    out = H.run_sample(gpu, tens)
+    _check(inp, out, name)
+    staged = H.run_sample_staged(gpu, tens)
+    _check(inp, staged, name + " staged")
+    return out, staged
+
+
 def test_masks_and_signed_zero(gpu):
-    inp = SC.masks_and_signed_zero()
-    _check(inp, H.run_sample(gpu, H.sample_tensors(inp)), "masks")
+    _full_and_staged(gpu, SC.masks_and_signed_zero(), "masks")
 
 
 def test_identical_and_disjoint_rows(gpu):
-    inp = SC.identical_and_disjoint()
-    out = H.run_sample(gpu, H.sample_tensors(inp))
-    _check(inp, out, "identical/disjoint")
-    assert (out["n"][:4] == 5).all() and (out["n"][4:] == 0).all()
-    assert (out["tokens"][4:, 0] < 1500).all()
+    for out in _full_and_staged(gpu, SC.identical_and_disjoint(), "identical/disjoint"):
+        assert (out["n"][:4] == 5).all() and (out["n"][4:] == 0).all()
+        assert (out["tokens"][4:, 0] < 1500).all()
 
 
 def test_invalid_inputs(gpu):
-    inp = SC.invalid_inputs()
-    out = H.run_sample(gpu, H.sample_tensors(inp))
-    _check(inp, out, "invalid")
-    assert (out["n"] == -1).all() and (out["tokens"] == -1).all()
+    for out in _full_and_staged(gpu, SC.invalid_inputs(), "invalid"):
+        assert (out["n"] == -1).all() and (out["tokens"] == -1).all()
 
 
 def test_unconsulted_positions_are_ignored(gpu):
     """Rows, tokens and uniforms after the first rejection do not matter."""
-    inp = SC.unconsulted_positions()
-    out = H.run_sample(gpu, H.sample_tensors(inp))
-    _check(inp, out, "unconsulted")
-    assert (out["n"] == 0).all()
+    for out in _full_and_staged(gpu, SC.unconsulted_positions(), "unconsulted"):
+        assert (out["n"] == 0).all()
 
 
 def test_invalid_after_accepts(gpu):
-    inp = SC.invalid_after_accepts()
-    out = H.run_sample(gpu, H.sample_tensors(inp))
-    _check(inp, out, "invalid after accepts")
-    assert list(out["n"]) == [-1, -1, -1, 1]
+    for out in _full_and_staged(gpu, SC.invalid_after_accepts(), "invalid after accepts"):
+        assert list(out["n"]) == [-1, -1, -1, 1]
 
 
 def test_strided_rows(gpu):
