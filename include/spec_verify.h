@@ -114,6 +114,10 @@ typedef struct {
  * token outside [0, V), a draft token whose draft logit is -inf, a uniform
  * outside [0, 1), or a target/draft row with NaN, +inf or no finite value.
  * Rows after the first rejection are not consulted.
+ *
+ * Work on `stream`: the statistics kernel then the finish kernel (see
+ * spec_verify_sample_stage); with V <= 2048 a single kernel, one wave per
+ * sequence. The paths round differently and agree within the parity contract.
  */
 int spec_verify_sample(const void* target_logits, int target_dtype, int64_t target_seq_stride,
                        int64_t target_row_stride, const void* draft_logits, int draft_dtype,

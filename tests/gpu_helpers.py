@@ -1,5 +1,5 @@
 """Shared code of the GPU tests: upload inputs, call the C ABI through the
-binding, and judge results against the fp64 oracle with the parity contract.
+binding, and check results against the fp64 oracle with the parity contract.
 
 Parity contract (sampling):
   * accept decisions equal at every position both sides reached; a differing
@@ -95,7 +95,7 @@ def run_sample_staged(binding, tens, workspace=None):
 def compare_one_pass(one, ee):
     """Early exit against the one-pass call on the same inputs. Returns
     (differing, bad): the sequences whose n or tokens differ (both results are
-    judged against the oracle by the caller), and a list of other problems:
+    checked against the oracle by the caller), and a list of other problems:
     for sequences that agree and are valid, p(x), q(x) of positions 0..n and
     the drawn distribution's mass must agree within PROB_RTOL, and p(x), q(x)
     of every position the early-exit call reports after n must be NaN or equal
@@ -145,7 +145,7 @@ def _rel(a, b):
 
 
 def check_sample_seq(tally: Tally, b: int, Lt, Ld, x, u, T, gpu, lb=None):
-    """Judge sequence b of a GPU result against the oracle (Lt, Ld already float64)."""
+    """Check sequence b of a GPU result against the oracle (Lt, Ld already float64)."""
     o = O.verify_sample_sequence(Lt, Ld, x, u, T, keep_cdf=True)
     tally.checked += 1
     gn = int(gpu["n"][b])
@@ -279,7 +279,7 @@ def run_draft(binding, tens, workspace=None, stage=None):
 
 
 def check_draft(d, gpu, rows=None, tally=None):
-    """Judge draft-sampler outputs against the oracle: the token equal, or u
+    """Check draft-sampler outputs against the oracle: the token equal, or u
     within FLAG_WINDOW of the oracle's CDF interval of the GPU's token
     (flagged); q(token) within PROB_RTOL; invalid rows -1 exactly."""
     tally = tally or Tally()
