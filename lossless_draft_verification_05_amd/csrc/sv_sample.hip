@@ -8,22 +8,27 @@
 // max(0, p_n - q_n), or after full acceptance draw from p_gamma; the draw is an
 // inverse CDF in token order at u_gamma.
 //
-// Two kernels on the caller's stream (the kernel boundary is the only
-// cross-workgroup synchronisation: a per-workgroup agent-scope release would
-// write back the L2 of its XCD, which serialises across the device and costs
-// more than the streaming itself):
-//  stats  : one 256-thread workgroup per (row, 128 KB chunk) of every target
-//           and draft row. It streams 16-byte units (4 KB per load
+// Two kernels on the caller's stream (no fence-based hand-off between
+// workgroups: a per-workgroup agent-scope release would write back the L2 of
+// its XCD, which serialises across the device and costs more than the
+// streaming itself):
+//  stats  : one 256-thread workgroup per (row, chunk of 16-256 KB) of every
+//           target and draft row. It streams 16-byte units (4 KB per load
 //           instruction, non-temporal) and keeps a per-lane tempered sum-exp
 //           against a lazily moved reference; one partial per wave.
-//  finish : one 512-thread workgroup per sequence. It merges the partials of
-//           the sequence's rows (a wave per row), gathers p(x), q(x), runs the
-//           accept tests and the first-rejection ballot, streams the one row
-//           (pair) the draw needs -- max(0, p_n - q_n) after a rejection, p_gamma
-//           after full acceptance -- writing exact masses of 2048-token steps,
-//           then walks step masses -> one rescanned step -> one octet to the
-//           token whose running mass first exceeds u_gamma * total, and writes
-//           the outputs.
+//  finish : one 512-thread workgroup per sequence (with fewer sequences than
+//           CUs, several per sequence that hand their step masses to the last
+//           one through relaxed device-scope atomics, no fence and no wait).
+//           It merges the partials of the sequence's rows (a wave per row),
+//           gathers p(x), q(x), runs the accept tests and the first-rejection
+//           ballot, streams the one row (pair) the draw needs -- max(0, p_n -
+//           q_n) after a rejection, p_gamma after full acceptance -- writing
+//           exact masses of 2048-token steps, then walks step masses -> one
+//           rescanned step -> one octet to the token whose running mass first
+//           exceeds u_gamma * total, and writes the outputs.
+// With V <= 2048 the whole call is one kernel instead (small: one wave per
+// sequence). Also here: the early-exit statistics kernel (stats_pos) and the
+// one-pass draft sampler (draft1).
 #include <type_traits>
 
 #include "sv_device.hpp"
