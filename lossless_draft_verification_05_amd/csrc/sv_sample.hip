@@ -1382,10 +1382,10 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
     }
   }
   // statistics of target rows 0..G (slots 0..G) and draft rows 0..G-1 (slots
-  // G+1..2G); slot t is kept by lane t % 64 in register set t / 64
-  float m0 = 0.0f, m1 = 0.0f;
-  double s0 = 0.0, s1 = 0.0;
-  int v0 = 0, v1 = 0;
+  // G+1..2G <= 128); slot t is kept by lane t % 64 in register set t / 64
+  float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+  int v0 = 0, v1 = 0, v2 = 0;
   for (int t0 = 0; t0 <= 2 * G; t0 += RB) {
     float x[RB][PL];
 #pragma unroll
@@ -1410,30 +1410,36 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
           m0 = st.m;
           s0 = st.s;
           v0 = st.valid;
-        } else {
+        } else if (t < 2 * kWave) {
           m1 = st.m;
           s1 = st.s;
           v1 = st.valid;
+        } else {
+          m2 = st.m;
+          s2 = st.s;
+          v2 = st.valid;
         }
       }
     }
   }
   // slot t's statistics: in every lane for a uniform t, from lane j % 64 for a per-lane j
   auto slot_uniform = [&](int t) {
-    return (t < kWave) ? RowStat{readlane_f32(m0, t), readlane_f64(s0, t), __builtin_amdgcn_readlane(v0, t)}
-                       : RowStat{readlane_f32(m1, t - kWave), readlane_f64(s1, t - kWave),
-                                 __builtin_amdgcn_readlane(v1, t - kWave)};
+    const int l = t & (kWave - 1);
+    if (t < kWave) return RowStat{readlane_f32(m0, l), readlane_f64(s0, l), __builtin_amdgcn_readlane(v0, l)};
+    if (t < 2 * kWave) return RowStat{readlane_f32(m1, l), readlane_f64(s1, l), __builtin_amdgcn_readlane(v1, l)};
+    return RowStat{readlane_f32(m2, l), readlane_f64(s2, l), __builtin_amdgcn_readlane(v2, l)};
   };
   // accept tests (lane i: position i; target slot i is its own) and the first stop
   const int j = G + 1 + lane;  // this lane's draft slot
   const int jl = j & (kWave - 1);
-  const float dm0 = __shfl(m0, jl, kWave), dm1 = __shfl(m1, jl, kWave);
-  const double ds0 = __shfl(s0, jl, kWave), ds1 = __shfl(s1, jl, kWave);
-  const int dv0 = __shfl(v0, jl, kWave), dv1 = __shfl(v1, jl, kWave);
+  const float dm0 = __shfl(m0, jl, kWave), dm1 = __shfl(m1, jl, kWave), dm2 = __shfl(m2, jl, kWave);
+  const double ds0 = __shfl(s0, jl, kWave), ds1 = __shfl(s1, jl, kWave), ds2 = __shfl(s2, jl, kWave);
+  const int dv0 = __shfl(v0, jl, kWave), dv1 = __shfl(v1, jl, kWave), dv2 = __shfl(v2, jl, kWave);
   int code = 1;
   if (lane < G) {
     const RowStat ts{m0, s0, v0};
-    const RowStat ds = (j < kWave) ? RowStat{dm0, ds0, dv0} : RowStat{dm1, ds1, dv1};
+    const RowStat ds = (j < kWave) ? RowStat{dm0, ds0, dv0}
+                                   : (j < 2 * kWave ? RowStat{dm1, ds1, dv1} : RowStat{dm2, ds2, dv2});
     const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv);
     code = ao.code;
     if (A.diag_px) A.diag_px[(int64_t)b * G + lane] = ao.px;

@@ -365,3 +365,13 @@ def test_split_finish_repeats_bit_identical(gpu):
         again = H.run_sample(gpu, tens)
         for k in first:
             assert np.array_equal(first[k].view(np.uint8), again[k].view(np.uint8)), (rep, k)
+
+
+@pytest.mark.parametrize("G", [31, 32, 63, 64])
+def test_full_acceptance_at_large_gamma(gpu, G):
+    """Draft rows equal to the target rows: every draft is accepted and the
+    token comes from the bonus row gamma, whose statistics are the last of the
+    2 gamma + 1 rows (more rows than lanes in the one-wave kernel)."""
+    inp = synth.make_custom_sample(4, G, 696, "bf16", "bf16", T=0.9, noise_sd=0.0, seed=40 + G)
+    for out in _full_and_staged(gpu, inp, f"full acceptance gamma={G}"):
+        assert (out["n"] == G).all()
