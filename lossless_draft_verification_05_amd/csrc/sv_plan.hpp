@@ -21,7 +21,7 @@ constexpr int64_t kMinChunkBytes = 16 << 10;    // stats / argmax work unit boun
 constexpr int64_t kMaxChunkBytes = 256 << 10;   // measured best for the stats kernel on MI355X (128/256/512 KB)
 constexpr int64_t kTargetWGs = 8192;            // ~32 workgroups per CU on 256 CUs
 constexpr int kLog2MaxNodes = 10;               // 1024 tree nodes
-constexpr int64_t kEarlyChunkBytes = 64 << 10;  // early-exit statistics work unit
+constexpr int64_t kEarlyChunkBytes = 128 << 10;  // early-exit statistics work unit
 constexpr double kEarlyAlpha = 0.7;             // acceptance rate assumed when grouping positions
 constexpr double kEarlyLaunchBytes = 64e6;      // bytes moved in about the time one extra launch costs
 constexpr int64_t kFinTargetWGs = 256;          // finish: split sequences over parts up to one workgroup per CU
@@ -217,8 +217,9 @@ inline int64_t early_chunks(int64_t G, int64_t nct, int64_t ncd, int64_t p0, int
 // sequences, and its time is then one workgroup's chain of dependent loads.
 // Not much smaller: every workgroup of a gated launch first re-derives an
 // accept decision (a few dependent round trips), which a small unit does not
-// amortise (measured on MI355X: 64 KB beat 16 and 32 KB by 20-30% at
-// V = 128k, and matched them elsewhere).
+// amortise (measured on MI355X at V = 128k: 64 KB beat 16 and 32 KB by
+// 20-30%, 128 KB beat 64 KB by 4% and 256 KB by 20%; at V = 256k 64 and
+// 128 KB matched).
 inline int64_t early_chunk_bytes() { return kEarlyChunkBytes; }
 
 // First position of the tail group: positions 0..k-1 get a launch each and
