@@ -101,7 +101,7 @@ def _oracle_draft(b):
     return O.draft_sample_row(O.widen(d.logits[b], d.dtype), float(d.temperature[b]), float(d.uniforms[b])).y
 
 
-def cpu_baseline_draft(d, budget_s: float = 15.0):
+def cpu_baseline_draft(d, budget_s: float = 10.0):
     """The oracle's draft sampler over a bounded sample of rows (cycled), in a
     pool of worker processes forked before the GPU is touched."""
     import multiprocessing as mp
@@ -249,7 +249,7 @@ def bench_markov(args):
         _oracle_markov(0)
         t_one = max(time.perf_counter() - t0, 1e-4)
         workers = max(1, min(16, os.cpu_count() or 1))
-        S = int(max(workers, min(4 * B, 15.0 * workers / t_one)))
+        S = int(max(workers, min(4 * B, 10.0 * workers / t_one)))
         with mp.get_context("fork").Pool(workers) as pool:
             t0 = time.perf_counter()
             toks = sum(pool.map(_oracle_markov, range(S), chunksize=max(1, S // (4 * workers))))
@@ -415,7 +415,7 @@ def bench_masks(args):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(inp, tree: bool, budget_s: float = 15.0):
+def cpu_baseline(inp, tree: bool, budget_s: float = 10.0):
     """Time the oracle over the first S sequences in a pool of worker processes
     (fork, before the GPU is touched). S is sized from a one-sequence probe so
     the timed part takes about ``budget_s`` seconds."""
