@@ -171,14 +171,26 @@ __device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int 
     for (int j = 0; j < kU1; ++j) un[j].unpack(w[j]);
     sumexp<DT, kU1>(st, un, kl);
   }
+  // The tail (fewer than kU1 units per thread left): every load is issued
+  // before the first term is taken, so the chunk ends one memory round trip
+  // later instead of one per unit. A lane past c_end loads the chunk's last
+  // unit (in bounds) and skips it.
+  if (base < c_end) {
+    uint4 w[kU1];
 #pragma unroll
-  for (int j = 0; j < kU1; ++j) {
-    int64_t u = base + tid + kThreads * j;
-    if (u < c_end) {
-      Unit<DT> un[1];
-      un[0].unpack(load16(row + u * 16));
-      if (ragged && u == nu_row - 1) mask_tail(un[0], u, V);
-      sumexp<DT, 1>(st, un, kl);
+    for (int j = 0; j < kU1; ++j) {
+      const int64_t u = base + tid + kThreads * j;
+      w[j] = load16(row + (u < c_end ? u : c_end - 1) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kU1; ++j) {
+      const int64_t u = base + tid + kThreads * j;
+      if (u < c_end) {
+        Unit<DT> un[1];
+        un[0].unpack(w[j]);
+        if (ragged && u == nu_row - 1) mask_tail(un[0], u, V);
+        sumexp<DT, 1>(st, un, kl);
+      }
     }
   }
 }
@@ -273,25 +285,46 @@ __device__ __forceinline__ double partial_shift(const RowPartial& p, float kl) {
   return p.form ? (double)__fmul_rn(p.m, kl) : (double)p.m * (double)kl;
 }
 
+__device__ __forceinline__ RowStat row_stat(float Mm, double Ms, double S, float kl, bool tv) {
+#pragma clang fp contract(off)
+  RowStat r;
+  r.m = Mm;
+  r.s = S * exp2(Ms - (double)Mm * (double)kl);
+  r.valid = tv && __builtin_isfinite(r.s) && r.s > 0.0 && __builtin_isfinite(Mm);
+  return r;
+}
+
+// The merge of a row with at most one partial per lane (have: this lane holds
+// partial q), taken with the same operations as the general merge below.
+__device__ __forceinline__ RowStat merge_row_one(const RowPartial& q, bool have, float kl, bool tv) {
+#pragma clang fp contract(off)
+  double Ms = -INFINITY;
+  float Mm = -INFINITY;  // the reference logit of a partial at Ms (the largest such)
+  double S = 0.0;
+  double sh = -INFINITY;
+  if (have) {
+    sh = partial_shift(q, kl);
+    Ms = fmax(Ms, sh);
+  }
+  Ms = wave_max_f64(Ms);
+  if (have && sh == Ms) Mm = fmaxf(Mm, q.m);
+  Mm = wave_max(Mm);
+  if (have) S += q.s * exp2(sh - Ms);
+  S = wave_sum(S);
+  return row_stat(Mm, Ms, S, kl, tv);
+}
+
 __device__ __forceinline__ RowStat merge_row(const RowPartial* P, int nrec, float kl, bool tv, int lane) {
 #pragma clang fp contract(off)
   double Ms = -INFINITY;
   float Mm = -INFINITY;  // the reference logit of a partial at Ms (the largest such)
   double S = 0.0;
   if (nrec <= kWave) {
-    // at most one partial per lane, loaded once: the same operations as below
+    // at most one partial per lane, loaded once
     const bool have = lane < nrec;
     RowPartial q{};
-    double sh = -INFINITY;
-    if (have) {
-      q = P[lane];
-      sh = partial_shift(q, kl);
-      Ms = fmax(Ms, sh);
-    }
-    Ms = wave_max_f64(Ms);
-    if (have && sh == Ms) Mm = fmaxf(Mm, q.m);
-    Mm = wave_max(Mm);
-    if (have) S += q.s * exp2(sh - Ms);
+    if (have) q = P[lane];
+    return merge_row_one(q, have, kl, tv);
   } else {
     for (int k = lane; k < nrec; k += kWave) Ms = fmax(Ms, partial_shift(P[k], kl));
     Ms = wave_max_f64(Ms);
@@ -301,11 +334,7 @@ __device__ __forceinline__ RowStat merge_row(const RowPartial* P, int nrec, floa
     for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(partial_shift(P[k], kl) - Ms);
   }
   S = wave_sum(S);
-  RowStat r;
-  r.m = Mm;
-  r.s = S * exp2(Ms - (double)Mm * (double)kl);
-  r.valid = tv && __builtin_isfinite(r.s) && r.s > 0.0 && __builtin_isfinite(Mm);
-  return r;
+  return row_stat(Mm, Ms, S, kl, tv);
 }
 
 // Accept test of one position: rho = p(x) / q(x) in the log2 domain in fp64;
@@ -429,34 +458,58 @@ __global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, 
 // Unnormalised mass of the 8 tokens of octet `oct` (token ids 8*oct .. 8*oct+7):
 // residual mode r_v = max(0, e^p_v - kappa e^q_v) = Sp * max(0, p_v - q_v);
 // bonus mode r_v = e^p_v = Sp * p_v. Tokens at or beyond V get 0.
+//
+// Raw words of one octet of a row, loaded with no branch so that the loads of
+// several octets are all in flight before the first is used: an octet at or
+// past the row's end (oct >= noct) loads the row's last octet instead, and an
+// fp32 octet whose second half lies at or past V loads its first half twice.
+// to_float() gives the octet's 8 values, -inf at and past V; the values of an
+// octet past the end are never used.
 template <int DT>
-__device__ __forceinline__ void load_octet(const char* row, int64_t oct, int V, float (&x)[8]) {
-  if constexpr (DT == 1) {
+struct OctetIn;
+template <>
+struct OctetIn<1> {
+  uint4 w;
+  __device__ __forceinline__ void load(const char* row, int64_t oct, int64_t noct, int V) {
+    w = load16(row + (oct < noct ? oct : noct - 1) * 16);
+  }
+  __device__ __forceinline__ void to_float(int64_t oct, int V, float (&x)[8]) const {
     Unit<1> un;
-    un.unpack(load16(row + oct * 16));
+    un.unpack(w);
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] = un.x[k];
-  } else {
-    Unit<0> a, c;
-    a.unpack(load16(row + oct * 32));
-    if (oct * 8 + 4 < V) {
-      c.unpack(load16(row + oct * 32 + 16));
-    } else {
+    if (oct * 8 + 8 > V) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) c.x[k] = -INFINITY;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[k] = a.x[k];
-      x[4 + k] = c.x[k];
+      for (int k = 0; k < 8; ++k)
+        if (oct * 8 + k >= V) x[k] = -INFINITY;
     }
   }
-  if (oct * 8 + 8 > V) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (oct * 8 + k >= V) x[k] = -INFINITY;
+};
+template <>
+struct OctetIn<0> {
+  uint4 w0, w1;
+  __device__ __forceinline__ void load(const char* row, int64_t oct, int64_t noct, int V) {
+    const int64_t o = oct < noct ? oct : noct - 1;
+    w0 = load16(row + o * 32);
+    w1 = load16(row + o * 32 + (o * 8 + 4 < V ? 16 : 0));
   }
-}
+  __device__ __forceinline__ void to_float(int64_t oct, int V, float (&x)[8]) const {
+    x[0] = __uint_as_float(w0.x);
+    x[1] = __uint_as_float(w0.y);
+    x[2] = __uint_as_float(w0.z);
+    x[3] = __uint_as_float(w0.w);
+    const bool hi = oct * 8 + 4 < V;
+    x[4] = hi ? __uint_as_float(w1.x) : -INFINITY;
+    x[5] = hi ? __uint_as_float(w1.y) : -INFINITY;
+    x[6] = hi ? __uint_as_float(w1.z) : -INFINITY;
+    x[7] = hi ? __uint_as_float(w1.w) : -INFINITY;
+    if (oct * 8 + 8 > V) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (oct * 8 + k >= V) x[k] = -INFINITY;
+    }
+  }
+};
 
 __device__ __forceinline__ float sum8(const float (&r)[8]) {
   return ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
@@ -523,13 +576,41 @@ __device__ __forceinline__ void mass8(const float (&xt)[8], const float (&xd)[8]
   }
 }
 
-template <int TD, int DD>
-__device__ __forceinline__ void octet_mass(const char* trow, const char* drow, int64_t oct, int V, int mode,
-                                           const SeqPlan& P, float (&r)[8]) {
-  float xt[8], xd[8];
-  load_octet<TD>(trow, oct, V, xt);
+// The 8 values of octet oct < noct of a row, -inf at and past V, with each
+// load made only where the row has the bytes (the same values as OctetIn).
+template <int DT>
+__device__ __forceinline__ void load_octet(const char* row, int64_t oct, int V, float (&x)[8]) {
+  if constexpr (DT == 1) {
+    Unit<1> un;
+    un.unpack(load16(row + oct * 16));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = un.x[k];
+  } else {
+    Unit<0> a, c;
+    a.unpack(load16(row + oct * 32));
+    if (oct * 8 + 4 < V) {
+      c.unpack(load16(row + oct * 32 + 16));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c.x[k] = -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[k] = a.x[k];
+      x[4 + k] = c.x[k];
+    }
+  }
+  if (oct * 8 + 8 > V) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (oct * 8 + k >= V) x[k] = -INFINITY;
+  }
+}
+
+// Masses of 8 tokens in the draw's mode and the plan's form.
+__device__ __forceinline__ void mass8_of(const float (&xt)[8], const float (&xd)[8], int mode, const SeqPlan& P,
+                                         float (&r)[8]) {
   if (mode == kModeResidual) {
-    load_octet<DD>(drow, oct, V, xd);
     if (P.form == 1)
       mass8<kModeResidual, 1>(xt, xd, P, r);
     else
@@ -539,6 +620,59 @@ __device__ __forceinline__ void octet_mass(const char* trow, const char* drow, i
       mass8<kModeBonus, 1>(xt, xd, P, r);
     else
       mass8<kModeBonus, 0>(xt, xd, P, r);
+  }
+}
+
+// Token masses of step s of the draw row(s) for one wave: rr[j] is octet
+// s * kStepOctets + kWave * j + lane, all zero past the row's end. kBatch:
+// every load of the step is issued before the first mass is taken (one memory
+// round trip per step, not one per octet). Otherwise each octet is loaded
+// only where it exists, which needs fewer registers and, for rows of at most
+// kWave octets (only j = 0 exists), the same single round trip.
+template <int TD, int DD, bool kBatch = true>
+__device__ __forceinline__ void step_octet_masses(const char* trow, const char* drow, int64_t s, int64_t noct, int V,
+                                                  int mode, const SeqPlan& P, int lane, float (&rr)[kU2][8]) {
+  if constexpr (!kBatch) {
+#pragma unroll
+    for (int j = 0; j < kU2; ++j) {
+      const int64_t oct = s * kStepOctets + kWave * j + lane;
+      if (oct < noct) {
+        float xt[8], xd[8];
+        load_octet<TD>(trow, oct, V, xt);
+        if (mode == kModeResidual) load_octet<DD>(drow, oct, V, xd);
+        mass8_of(xt, xd, mode, P, rr[j]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
+      }
+    }
+    return;
+  }
+  OctetIn<TD> t[kU2];
+  OctetIn<DD> d[kU2];
+  if (mode == kModeResidual) {
+#pragma unroll
+    for (int j = 0; j < kU2; ++j) {
+      const int64_t oct = s * kStepOctets + kWave * j + lane;
+      t[j].load(trow, oct, noct, V);
+      d[j].load(drow, oct, noct, V);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kU2; ++j) t[j].load(trow, s * kStepOctets + kWave * j + lane, noct, V);
+  }
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float xt[8], xd[8];
+      t[j].to_float(oct, V, xt);
+      if (mode == kModeResidual) d[j].to_float(oct, V, xd);
+      mass8_of(xt, xd, mode, P, rr[j]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
+    }
   }
 }
 
@@ -575,17 +709,27 @@ struct HalfStep {
 // Mass of step s of the draw row(s), octet by octet with bounds checks (every
 // lane gets it). Inside the row these are the same operations in the same
 // order as the pipelined loop below, so both give the same bits for a step.
-template <int TD, int DD, int MODE>
+template <int TD, int DD, int MODE, bool kBatch = true>
 __device__ __forceinline__ double direct_step_mass(const char* trow, const char* drow, int64_t s, int64_t noct, int V,
                                                    const SeqPlan& P, int lane) {
   double lacc = 0.0;
+  if constexpr (kBatch) {
+    float rr[kU2][8];
+    step_octet_masses<TD, DD>(trow, drow, s, noct, V, MODE, P, lane, rr);
 #pragma unroll
-  for (int j = 0; j < kU2; ++j) {
-    const int64_t oct = s * kStepOctets + kWave * j + lane;
-    if (oct < noct) {
-      float rr[8];
-      octet_mass<TD, DD>(trow, drow, oct, V, MODE, P, rr);
-      lacc += (double)sum8(rr);
+    for (int j = 0; j < kU2; ++j)
+      if (s * kStepOctets + kWave * j + lane < noct) lacc += (double)sum8(rr[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kU2; ++j) {
+      const int64_t oct = s * kStepOctets + kWave * j + lane;
+      if (oct < noct) {
+        float xt[8], xd[8], rr[8];
+        load_octet<TD>(trow, oct, V, xt);
+        if (MODE == kModeResidual) load_octet<DD>(drow, oct, V, xd);
+        mass8_of(xt, xd, MODE, P, rr);
+        lacc += (double)sum8(rr);
+      }
     }
   }
   return wave_sum(lacc);
@@ -729,23 +873,14 @@ __device__ __forceinline__ int wave_find(const double* arr, int len, double t, d
 // order (octet j-major, then lane, then slot): the first token whose running
 // mass acc + ... exceeds t (acc: the mass of the steps before ss). If rounding
 // leaves none, the step's last token with positive mass. Every lane returns y.
-template <int TD, int DD>
+template <int TD, int DD, bool kBatch = true>
 __device__ __forceinline__ int rescan_step(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int ss, double t,
                                            double acc, int lane) {
   const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
   const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   float rr[kU2][8];
-#pragma unroll
-  for (int j = 0; j < kU2; ++j) {
-    const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
-    if (oct < noct) {
-      octet_mass<TD, DD>(trow, drow, oct, A.V, mode, P, rr[j]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
-    }
-  }
+  step_octet_masses<TD, DD, kBatch>(trow, drow, ss, noct, A.V, mode, P, lane, rr);
   int y = -1;
   int last_pos = -1;
   for (int j = 0; j < kU2 && y < 0; ++j) {
@@ -896,6 +1031,7 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
 // ---------------------------------------------------------------------------
 // finish kernel: one 512-thread workgroup per sequence
 // ---------------------------------------------------------------------------
+constexpr int kMergeRows = 3;  // rows per wave merged from one batch of loads: 2 * gamma + 1 <= 24
 template <int TD, int DD>
 // At most 128 VGPRs, so that two 8-wave workgroups fit one CU.
 __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))) void sv_finish_kernel(
@@ -937,32 +1073,63 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     }
   }
 
-  // (2) merge the partials of every row: one wave per row, lanes over partials
+  // (2) merge the partials of every row: one wave per row, lanes over partials.
+  // When every row has at most one partial per lane and each wave has at most
+  // kMergeRows rows, a wave loads the partials of all its rows before merging
+  // any (one memory round trip instead of one per row).
   const int nrows = 2 * G + 1;
-  for (int t = w; t < nrows; t += kFinWaves) {
-    int nrec, base, pos;
-    if (t <= G) {
-      nrec = A.nct * kWaves;
-      base = t * A.nct;
-      pos = t;
-    } else {
-      nrec = A.ncd * kWaves;
-      base = tchunks + (t - G - 1) * A.ncd;
-      pos = t - G - 1;
+  if (A.nct * kWaves <= kWave && A.ncd * kWaves <= kWave && nrows <= kMergeRows * kFinWaves) {
+    RowPartial q[kMergeRows];
+    bool have[kMergeRows];
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      const int t = w + k * kFinWaves;
+      const int pos = t <= G ? t : t - G - 1;
+      const int nrec = (t <= G ? A.nct : A.ncd) * kWaves;
+      const int base = t <= G ? t * A.nct : tchunks + pos * A.ncd;
+      have[k] = t < nrows && pos < nst && lane < nrec;
+      q[k] = RowPartial{};
+      if (have[k]) q[k] = A.part[((int64_t)b * A.per_seq + base) * kWaves + lane];
     }
-    if (pos >= nst) {
+#pragma unroll
+    for (int k = 0; k < kMergeRows; ++k) {
+      const int t = w + k * kFinWaves;
+      if (t >= nrows) break;
+      const int pos = t <= G ? t : t - G - 1;
+      RowStat rs{0.0f, 0.0, 0};
+      if (pos < nst) rs = merge_row_one(q[k], have[k], kl, tv);
       if (lane == 0) {
-        rM[t] = 0.0f;
-        rS[t] = 0.0;
-        rV[t] = 0;
+        rM[t] = rs.m;
+        rS[t] = rs.s;
+        rV[t] = rs.valid;
       }
-      continue;
     }
-    const RowStat rs = merge_row(A.part + ((int64_t)b * A.per_seq + base) * kWaves, nrec, kl, tv, lane);
-    if (lane == 0) {
-      rM[t] = rs.m;
-      rS[t] = rs.s;
-      rV[t] = rs.valid;
+  } else {
+    for (int t = w; t < nrows; t += kFinWaves) {
+      int nrec, base, pos;
+      if (t <= G) {
+        nrec = A.nct * kWaves;
+        base = t * A.nct;
+        pos = t;
+      } else {
+        nrec = A.ncd * kWaves;
+        base = tchunks + (t - G - 1) * A.ncd;
+        pos = t - G - 1;
+      }
+      if (pos >= nst) {
+        if (lane == 0) {
+          rM[t] = 0.0f;
+          rS[t] = 0.0;
+          rV[t] = 0;
+        }
+        continue;
+      }
+      const RowStat rs = merge_row(A.part + ((int64_t)b * A.per_seq + base) * kWaves, nrec, kl, tv, lane);
+      if (lane == 0) {
+        rM[t] = rs.m;
+        rS[t] = rs.s;
+        rV[t] = rs.valid;
+      }
     }
   }
   __syncthreads();
@@ -1147,6 +1314,27 @@ __device__ __forceinline__ void unpack_half(const HalfStep<DT, DT, kModeBonus>& 
   for (int j = 0; j < kHalfU; ++j) h.t[j].unpack(x[j]);
 }
 
+// The values of step s of a row for one wave: x[j] is octet
+// s * kStepOctets + kWave * j + lane, -inf at and past V. Every load is issued
+// before the first value is used.
+template <int DT>
+__device__ __forceinline__ void load_step(const char* row, int64_t s, int64_t noct, int V, int lane,
+                                          float (&x)[kU2][8]) {
+  OctetIn<DT> o[kU2];
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) o[j].load(row, s * kStepOctets + kWave * j + lane, noct, V);
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      o[j].to_float(oct, V, x[j]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[j][k] = -INFINITY;
+    }
+  }
+}
+
 // FMA-form pass: wave w takes steps w, w + kFinWaves, ...; whole steps through
 // the two-buffer pipeline of the draw, the ragged last step octet by octet.
 template <int DT>
@@ -1186,16 +1374,7 @@ __device__ void draft_pass_fma(const char* row, int V, int ns2, float kl, LaneRe
   }
   for (int s = w + nmine * nw; s < ns2; s += nw) {
     float x[kU2][8];
-#pragma unroll
-    for (int j = 0; j < kU2; ++j) {
-      const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
-      if (oct < noct) {
-        load_octet<DT>(row, oct, V, x[j]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[j][k] = -INFINITY;
-      }
-    }
+    load_step<DT>(row, s, noct, V, lane, x);
     const float a = lane_terms<kU2>(x, kl, R);
     write_step_fma(a, R, s, stepC, stepM, stepS);
   }
@@ -1212,15 +1391,9 @@ __device__ void draft_pass_sub(const char* row, int V, int ns2, float kl, float*
     float x[kU2][8];
     float gm = -INFINITY;
     bool nan = false;
+    load_step<DT>(row, s, noct, V, lane, x);
 #pragma unroll
     for (int j = 0; j < kU2; ++j) {
-      const int64_t oct = (int64_t)s * kStepOctets + kWave * j + lane;
-      if (oct < noct) {
-        load_octet<DT>(row, oct, V, x[j]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[j][k] = -INFINITY;
-      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         gm = fmaxf(gm, x[j][k]);
@@ -1460,15 +1633,16 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
   const char* drow = (n < G) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   int mode = P.mode;
-  double total = (mode == kModeResidual) ? direct_step_mass<TD, DD, kModeResidual>(trow, drow, 0, noct, A.V, P, lane)
-                                         : direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
+  constexpr bool kB = PL > 4;  // rows of more than kWave octets: batch the step's loads
+  double total = (mode == kModeResidual) ? direct_step_mass<TD, DD, kModeResidual, kB>(trow, drow, 0, noct, A.V, P, lane)
+                                         : direct_step_mass<TD, DD, kModeBonus, kB>(trow, drow, 0, noct, A.V, P, lane);
   if (!(total > 0.0) && mode == kModeResidual) {
     // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
     mode = kModeBonus;
-    total = direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
+    total = direct_step_mass<TD, DD, kModeBonus, kB>(trow, drow, 0, noct, A.V, P, lane);
   }
   const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
-  const int y = rescan_step<TD, DD>(A, b, P, mode, 0, t, 0.0, lane);
+  const int y = rescan_step<TD, DD, kB>(A, b, P, mode, 0, t, 0.0, lane);
   write_outputs<TD>(A, b, P, mode, y, total, lane, 0, kWave);
 }
 

@@ -75,14 +75,25 @@ __device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int 
     for (int j = 0; j < kU1; ++j) un[j].unpack(w[j]);
     argmax_units<DT, kU1>(st, un, u);
   }
+  // The tail: every load first, then the units in order (one memory round
+  // trip, not one per unit); a lane past c_end loads the chunk's last unit and
+  // skips it.
+  if (base < c_end) {
+    uint4 w[kU1];
 #pragma unroll
-  for (int j = 0; j < kU1; ++j) {
-    int64_t uu[1] = {base + tid + kThreads * j};
-    if (uu[0] < c_end) {
-      Unit<DT> un[1];
-      un[0].unpack(load16(row + uu[0] * 16));
-      if (ragged && uu[0] == nu_row - 1) mask_tail(un[0], uu[0], V);
-      argmax_units<DT, 1>(st, un, uu);
+    for (int j = 0; j < kU1; ++j) {
+      const int64_t u = base + tid + kThreads * j;
+      w[j] = load16(row + (u < c_end ? u : c_end - 1) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kU1; ++j) {
+      int64_t uu[1] = {base + tid + kThreads * j};
+      if (uu[0] < c_end) {
+        Unit<DT> un[1];
+        un[0].unpack(w[j]);
+        if (ragged && uu[0] == nu_row - 1) mask_tail(un[0], uu[0], V);
+        argmax_units<DT, 1>(st, un, uu);
+      }
     }
   }
 }
