@@ -12,9 +12,10 @@
 // the parent array into LDS; one thread per row of the slab walks from its
 // node to the root (parents[j] < j bounds the walk by j steps), setting the
 // bits of the row's ancestors in an LDS bitset and counting the depth. The
-// slab (at most 64 KB of mask bytes, so at most 8 KB of bits) is then written
-// as a flat byte range with 16-byte stores, each built from at most two
-// bitset words.
+// slab (at most 16 KB of mask bytes, so at most 2 KB of bits) is then written
+// with 16-byte stores, each built from at most two bitset words. When N is a
+// multiple of 16 and the outputs are 16-byte aligned, both masks come from one
+// pass over the slab's vectors, each inside one row and one bitset word.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -104,6 +105,54 @@ __device__ void write_mask_range(uint8_t* out, int e0, int e1, int N, int r0, in
     out[e] = zero ? 0 : mask_byte(e / N, e % N, r0, W, bits, blk, relaxed);
 }
 
+// Both masks of the slab's rows [r0, r1) when N is a multiple of 16 and both
+// outputs are 16-byte aligned: every 16-byte vector lies inside one row, its
+// 16 ancestor bits inside one bitset word, and its 16 block ids in four
+// aligned int4 reads. Thread t takes vectors t, t + 256, ... of the slab; its
+// (row, column) advances by a constant step, so no vector needs a division,
+// and each vector's ancestor bits serve both masks. out_t / out_r may be NULL
+// (not written); zero: write zeros (invalid tree).
+__device__ void write_masks_aligned(uint8_t* out_t, uint8_t* out_r, int N, int r0, int r1, int W,
+                                    const uint32_t* bits, const int* blk, bool zero) {
+  const int vpr = N >> 4;  // vectors per row, at most 64
+  const int nv = (r1 - r0) * vpr;
+  const int di = kThreads / vpr, dc = kThreads % vpr;
+  int i = r0 + (int)threadIdx.x / vpr, c = (int)threadIdx.x % vpr;
+  for (int v = threadIdx.x; v < nv; v += kThreads) {
+    const int j = c << 4;
+    uint32_t wt[4] = {0, 0, 0, 0}, wr[4] = {0, 0, 0, 0};
+    if (!zero) {
+      const uint32_t anc = (bits[(i - r0) * W + (j >> 5)] >> (j & 16)) & 0xffffu;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wt[q] = bits_to_bytes((anc >> (4 * q)) & 0xfu);
+      if (out_r) {
+        uint32_t m = anc;
+        const int bi = blk[i];
+        if (bi >= 0) {
+          const int4* q4 = reinterpret_cast<const int4*>(blk + j);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int4 b4 = q4[q];
+            m |= ((uint32_t)(b4.x == bi) | (uint32_t)(b4.y == bi) << 1 | (uint32_t)(b4.z == bi) << 2 |
+                  (uint32_t)(b4.w == bi) << 3) << (4 * q);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wr[q] = bits_to_bytes((m >> (4 * q)) & 0xfu);
+      }
+    }
+    const int e = i * N + j;  // < 2^20
+    if (out_t) *reinterpret_cast<uint4*>(out_t + e) = make_uint4(wt[0], wt[1], wt[2], wt[3]);
+    if (out_r) *reinterpret_cast<uint4*>(out_r + e) = make_uint4(wr[0], wr[1], wr[2], wr[3]);
+    c += dc;
+    i += di;
+    if (c >= vpr) {
+      c -= vpr;
+      ++i;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
   __shared__ int par[kMaxMaskNodes];
   __shared__ __align__(16) int blk[kMaxMaskNodes];
@@ -117,11 +166,29 @@ __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
   if (tid == 0) sh_bad = 0;
   for (int k = tid; k < (r1 - r0) * W; k += kThreads) bits[k] = 0;
   __syncthreads();
-  for (int j = tid; j < N; j += kThreads) {
-    const int p = P[j];
-    par[j] = p;
-    blk[j] = A.blocks ? A.blocks[(int64_t)b * N + j] : -1;
-    if (j == 0 ? p != -1 : (p < 0 || p >= j)) sh_bad = 1;  // same value from every writer
+  // every thread's loads of the parent and block arrays first, then the LDS
+  // stores (one memory round trip, not one per element)
+  constexpr int kPer = kMaxMaskNodes / kThreads;
+  int pv[kPer], bv[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int j = tid + k * kThreads;
+    pv[k] = 0;
+    bv[k] = -1;
+    if (j < N) {
+      pv[k] = P[j];
+      if (A.blocks) bv[k] = A.blocks[(int64_t)b * N + j];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int j = tid + k * kThreads;
+    if (j < N) {
+      const int p = pv[k];
+      par[j] = p;
+      blk[j] = bv[k];
+      if (j == 0 ? p != -1 : (p < 0 || p >= j)) sh_bad = 1;  // same value from every writer
+    }
   }
   __syncthreads();
   const bool bad = sh_bad != 0;
@@ -150,10 +217,14 @@ __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
     for (int i = r0 + tid; i < r1; i += kThreads) A.out_depth[(int64_t)b * N + i] = -1;
   }
   __syncthreads();
-  if (A.out_mask)
-    write_mask_range(A.out_mask + (int64_t)b * N * N, e0, e1, N, r0, W, bits, blk, false, bad);
-  if (A.out_relaxed)
-    write_mask_range(A.out_relaxed + (int64_t)b * N * N, e0, e1, N, r0, W, bits, blk, true, bad);
+  uint8_t* mt = A.out_mask ? A.out_mask + (int64_t)b * N * N : nullptr;
+  uint8_t* mr = A.out_relaxed ? A.out_relaxed + (int64_t)b * N * N : nullptr;
+  if ((N & 15) == 0 && (((uintptr_t)mt | (uintptr_t)mr) & 15) == 0) {
+    write_masks_aligned(mt, mr, N, r0, r1, W, bits, blk, bad);
+  } else {
+    if (mt) write_mask_range(mt, e0, e1, N, r0, W, bits, blk, false, bad);
+    if (mr) write_mask_range(mr, e0, e1, N, r0, W, bits, blk, true, bad);
+  }
 }
 
 hipError_t launch_mask(const MaskLaunch& A, hipStream_t stream) {

@@ -122,7 +122,7 @@ struct TreeLaunch {
 };
 
 constexpr int kMaxMaskNodes = 1024;  // tree masks: nodes per tree
-constexpr int64_t kMaskSlabBytes = 64 << 10;  // tree masks: mask bytes per workgroup
+constexpr int64_t kMaskSlabBytes = 16 << 10;  // tree masks: mask bytes per workgroup (measured: 16 KB beat 8, 32 and 64 KB)
 
 struct MaskLaunch {
   const int32_t* parents;  // [B][N]

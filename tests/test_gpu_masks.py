@@ -94,3 +94,25 @@ def test_unaligned_buffers_and_partial_outputs(gpu):
     # bytes around the outputs untouched
     bb, bb2 = big.cpu().numpy(), big2.cpu().numpy()
     assert (bb[:3] == 7).all() and (bb[3 + n:] == 7).all() and (bb2[:13] == 7).all() and (bb2[13 + n:] == 7).all()
+
+
+@pytest.mark.parametrize("N", [16, 48, 64, 208, 512])
+def test_rows_of_whole_vectors(gpu, N):
+    """N a multiple of 16 with 16-byte aligned outputs (both masks from one
+    pass over the slab), with each mask also requested alone and one invalid
+    tree in the batch (its masks all zero)."""
+    g = np.random.default_rng(100 + N)
+    P = _random_parents(g, 4, N, "random")
+    P[2, N // 2] = N // 2 + 1  # forward parent: invalid tree
+    Bl = g.integers(-1, max(2, N // 5), P.shape).astype(np.int32)
+    _check(P, Bl, _run(gpu, P, Bl), f"whole vectors N={N}")
+    Pt, Bt = torch.from_numpy(P).cuda(), torch.from_numpy(Bl).cuda()
+    m_only = gpu.spec_tree_mask(Pt, Bt, want_relaxed=False)
+    r_only = gpu.spec_tree_mask(Pt, Bt, want_mask=False, want_relaxed=True, want_depth=False)
+    torch.cuda.synchronize()
+    assert m_only[1] is None and r_only[0] is None and r_only[2] is None
+    m, d, r = m_only[0].cpu().numpy(), m_only[2].cpu().numpy(), r_only[1].cpu().numpy()
+    for b in range(P.shape[0]):
+        wm, wr, wd = O.tree_masks(P[b], Bl[b])
+        assert np.array_equal(m[b], wm) and np.array_equal(d[b], wd) and np.array_equal(r[b], wr), b
+    assert not m[2].any() and not r[2].any() and (d[2] == -1).all()
