@@ -1,7 +1,8 @@
 """Host-side work decomposition (csrc/sv_plan.hpp, plain integer C++): compiled
 with the host compiler and checked against the rules it documents, re-derived
 here independently: chunk sizes, finish parts, the early-exit grouping, the
-one-pass draft choice and the workspace layout."""
+one-pass draft choice, the workspace layout, and sizes at the largest shapes
+the C ABI accepts (built with the address and undefined-behaviour sanitizers)."""
 import json
 import math
 import os
@@ -40,6 +41,16 @@ int main() {
   int nch, cu;
   split_row(128256, 2, 136 << 10, &nch, &cu);
   std::printf(", \"split\": [%d,%d]", nch, cu);
+  // the largest shapes the C ABI accepts (B 2^24, gamma 64, V 2^30, N 1024):
+  // every size is computed in 64-bit arithmetic without overflow
+  const long long Bm = 1LL << 24, Vm = 1LL << 30;
+  const SampleLayout Lm = sample_layout(Bm, 64, Vm);
+  const TreeLayout Tm = tree_layout(Bm, 1024, Vm);
+  int nchm, cum;
+  split_row(Vm, 4, chunk_bytes_for(Bm * (129LL * Vm * 4)), &nchm, &cum);
+  std::printf(", \"max\": [%lld,%lld,%lld,%d,%d,%d,%d,%lld]", (long long)Lm.total, (long long)Tm.total,
+              (long long)chunk_bytes_for(Bm * (129LL * Vm * 4)), nchm, cum, finish_parts(Bm, draw_steps(Vm)),
+              early_tail_start(Bm, 64, Vm, 4, 4), (long long)draw_steps(Vm));
   std::printf("}\n");
   return 0;
 }
@@ -56,7 +67,10 @@ def plan():
     src, exe = os.path.join(d, "plan.cpp"), os.path.join(d, "plan")
     with open(src, "w") as f:
         f.write(PROGRAM)
-    subprocess.run([gxx, "-std=c++17", "-O1", "-I", os.path.dirname(PLAN), src, "-o", exe], check=True)
+    # host build with the address and undefined-behaviour sanitizers: any
+    # signed overflow or out-of-bounds access in the plan arithmetic aborts
+    subprocess.run([gxx, "-std=c++17", "-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-I", os.path.dirname(PLAN), src, "-o", exe], check=True)
     out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
     shutil.rmtree(d)
     return json.loads(out)
@@ -115,3 +129,17 @@ def test_row_split(plan):
     # a 256 KB row in chunks of at most 136 KB: two chunks of 4 KB-multiple units covering the row
     nch, cu = plan["split"]
     assert nch == 2 and cu % 256 == 0 and nch * cu * 16 >= 128256 * 2 and (nch - 1) * cu * 16 < 128256 * 2
+
+
+def test_largest_shapes(plan):
+    """B = 2^24, gamma = 64, V = 2^30 (fp32), N = 1024: the sizes the C ABI's
+    limits allow are computed without overflow (the sanitized build aborts on
+    signed overflow) and are consistent."""
+    lay_total, tree_total, chunk, nch, cu, parts, tail, steps = plan["max"]
+    B, G, V = 1 << 24, 64, 1 << 30
+    assert steps == V // 2048
+    # partials of (2 gamma + 1) rows of up to V * 4 / 16 KB chunks, plus the step masses
+    assert lay_total >= B * (2 * G + 1) * (V * 4 // (16 << 10)) * 4 * 16 + B * steps * 8
+    assert lay_total < 1 << 62 and tree_total >= B * 1024 * (V * 4 // (16 << 10)) * 16
+    assert (16 << 10) <= chunk <= (256 << 10) and cu % 256 == 0 and nch * cu * 16 >= V * 4
+    assert parts == 1 and 0 <= tail <= G
