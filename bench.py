@@ -520,7 +520,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the verify step shards by sequence "
-                                   "with no exchange (see DESIGN.md), and no multi-GPU figure is produced",
+                                   "with no exchange, and no multi-GPU figure is produced",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.calibrate_copy:
