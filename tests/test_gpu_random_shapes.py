@@ -1,0 +1,67 @@
+"""GPU parity on seeded random shapes: batch, gamma, vocabulary, dtypes,
+row padding and per-sequence temperatures drawn at random (fixed seeds), so
+that the combinations between the hand-picked edge cases are covered too: the
+one-pass call and the early-exit call against the fp64 oracle with the parity
+contract, and against each other; greedy trees of random size, vocabulary and
+dtype bit for bit."""
+import numpy as np
+import pytest
+
+import synth
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+TREE_CASES = 8
+
+
+def _shape(k):
+    g = np.random.default_rng(9000 + k)
+    V = int(np.exp(g.uniform(np.log(2), np.log(300000))))
+    G = int(g.integers(1, 21))
+    B = int(g.integers(1, 41))
+    # keep the oracle's work (all rows of every sequence) to a few seconds
+    while B > 1 and B * (2 * G + 1) * V > 30_000_000:
+        B //= 2
+    tdt, ddt = g.choice(["bf16", "f32"], 2)
+    pad = None if g.random() < 0.5 else int(-(-V // 8) * 8 + 8 * g.integers(0, 4))
+    if pad is None and V % 8:
+        pad = -(-V // 8) * 8  # rows must start on 16-byte boundaries (the C ABI rejects others)
+    T = g.uniform(0.3, 2.0, B).astype(np.float32)
+    return B, G, V, str(tdt), str(ddt), pad, T
+
+
+@pytest.mark.parametrize("k", range(CASES))
+def test_random_shape(gpu, k):
+    B, G, V, tdt, ddt, pad, T = _shape(k)
+    H.log(f"random shape {k}: B={B} gamma={G} V={V} {tdt}/{ddt} pad={pad}")
+    inp = synth.make_custom_sample(B, G, V, tdt, ddt, T=T, noise_sd=0.6, seed=k + 1)
+    tens = H.sample_tensors(inp, pad_to=pad)
+    one = H.run_sample(gpu, tens)
+    ee = H.run_sample(gpu, tens, early_exit=True)
+    for name, out in (("one pass", one), ("early exit", ee)):
+        t = H.check_sample(inp, out)
+        H.log(f"[random {k} {name}] {t.summary()}")
+        assert not t.fail, t.fail[:3]
+        assert t.flagged <= 2
+    differ, bad = H.compare_one_pass(one, ee)
+    assert not bad, bad[:3]
+
+
+@pytest.mark.parametrize("k", range(TREE_CASES))
+def test_random_tree_shape(gpu, k):
+    g = np.random.default_rng(9500 + k)
+    B = int(g.integers(1, 17))
+    N = int(np.exp(g.uniform(0, np.log(120))))  # the draft-tree generator reaches ~120 nodes at depth 6
+    V = int(np.exp(g.uniform(np.log(8), np.log(200000))))
+    while B > 1 and B * N * V > 30_000_000:
+        B //= 2
+    V = -(-V // 8) * 8  # whole 16-byte rows for either dtype
+    dt = str(g.choice(["bf16", "f32"]))
+    H.log(f"random tree shape {k}: B={B} N={N} V={V} {dt}")
+    ti = synth.make_tree_inputs(4, seed=k + 1, B=B, N=N, V=V, dtype=dt)
+    out = H.run_tree(gpu, H.tree_tensors(ti))
+    fails = H.check_tree(ti.logits, ti.dtype, ti.parents, ti.tokens, out)
+    H.log(f"[random tree {k}] trees={B} mismatches={len(fails)}")
+    assert not fails, fails[:3]
