@@ -3,7 +3,8 @@ row padding and per-sequence temperatures drawn at random (fixed seeds), so
 that the combinations between the hand-picked edge cases are covered too: the
 one-pass call and the early-exit call against the fp64 oracle with the parity
 contract, and against each other; greedy trees of random size, vocabulary and
-dtype bit for bit."""
+dtype bit for bit; draft-side sampling of random batches (both of its paths:
+one pass for many or short rows, statistics and draw for few long ones)."""
 import numpy as np
 import pytest
 
@@ -14,6 +15,7 @@ pytestmark = pytest.mark.gpu
 
 CASES = 24
 TREE_CASES = 8
+DRAFT_CASES = 8
 
 
 def _shape(k):
@@ -65,3 +67,20 @@ def test_random_tree_shape(gpu, k):
     fails = H.check_tree(ti.logits, ti.dtype, ti.parents, ti.tokens, out)
     H.log(f"[random tree {k}] trees={B} mismatches={len(fails)}")
     assert not fails, fails[:3]
+
+
+@pytest.mark.parametrize("k", range(DRAFT_CASES))
+def test_random_draft_shape(gpu, k):
+    g = np.random.default_rng(9700 + k)
+    B = int(np.exp(g.uniform(0, np.log(300))))
+    V = int(np.exp(g.uniform(np.log(2), np.log(400000))))
+    while B > 1 and B * V > 30_000_000:
+        B //= 2
+    dt = str(g.choice(["bf16", "f32"]))
+    T = g.uniform(0.3, 2.0, B).astype(np.float32)
+    H.log(f"random draft shape {k}: B={B} V={V} {dt}")
+    d = synth.make_draft_rows(B, V, dt, T=T, seed=k + 1)
+    t = H.check_draft(d, H.run_draft(gpu, H.draft_tensors(d, pad_to=-(-V // 8) * 8 if V % 8 else None)))
+    H.log(f"[random draft {k}] {t.summary()}")
+    assert not t.fail, t.fail[:3]
+    assert t.flagged <= 2
