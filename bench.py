@@ -27,6 +27,8 @@ gamma=4, V=32, fp32), c2 7B-class vocab (B=64, gamma=4, V=32000, bf16), c3
 large vocab (B=256, gamma=8, V=128256, bf16, T=0.7), c4 greedy tree (B=32,
 N=60, V=32000, bf16), c5 stress (B=512, gamma=5, V=256000, bf16 target, fp32
 draft, per-row T in [0.3, 1.5]). The default is c5, the largest single-GPU one.
+b3 and b5 run configurations 3 and 5 at a batch of one sequence; s3 and s5 at
+32 and 64 sequences, one GPU's share of the batch split by sequence over eight.
 
 --calibrate-copy runs a plain 1 GiB device-to-device copy instead (used to
 scale the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 runs). For the
@@ -53,7 +55,12 @@ import synth  # noqa: E402
 
 PEAK_HBM_GBPS = float(os.environ.get("SV_PEAK_HBM_GBPS", "8000"))
 WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "d3": 3, "d5": 5, "m": 0, "t4": 4, "t1024": 4,
-             "b3": 3, "b5": 5}  # b3, b5: configurations 3 and 5 at a batch of one sequence (latency)
+             "b3": 3, "b5": 5, "s3": 3, "s5": 5}
+# Batch sizes other than the configuration's: b3, b5 are configurations 3 and 5
+# at a batch of one sequence (latency); s3, s5 at one eighth of their batch
+# (32 and 64 sequences), the share of one GPU when the batch is split by
+# sequence over eight.
+BATCH = {"b3": 1, "b5": 1, "s3": 32, "s5": 64}
 MARKOV = dict(B=512, V=16384, gamma=5, T=1.0, dtype="bf16", noise_sd=0.8)
 CSRC = os.path.join(ROOT, "lossless_draft_verification_05_amd", "csrc")
 
@@ -540,9 +547,8 @@ def main():
     tree = cid == 4
     log(f"[bench] building inputs for {args.workload} (seed {args.seed})")
     t0 = time.perf_counter()
-    batch1 = args.workload.startswith("b")
     inp = synth.make_tree_inputs(4, seed=args.seed) if tree else \
-        synth.make_sample_inputs(cid, seed=args.seed, B=1 if batch1 else None)
+        synth.make_sample_inputs(cid, seed=args.seed, B=BATCH.get(args.workload))
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
 
     cpu = None
@@ -641,7 +647,8 @@ def main():
         unit = "positions/s"
         s1_bytes, _ = sample_bytes(cfg, B, G, V)
         tdesc = cfg.temperature if not isinstance(cfg.temperature, tuple) else f"U[{cfg.temperature[1]}, {cfg.temperature[2]}] per row"
-        cfg_desc = {"workload": f"{args.workload}: {cfg.name}" + (" at a batch of one" if batch1 else ""),
+        nb = BATCH.get(args.workload)
+        cfg_desc = {"workload": f"{args.workload}: {cfg.name}" + (f" at a batch of {nb}" if nb else ""),
                     "B": B, "gamma": G, "V": V,
                     "target_dtype": cfg.target_dtype, "draft_dtype": cfg.draft_dtype, "temperature": tdesc,
                     "seed": args.seed}
