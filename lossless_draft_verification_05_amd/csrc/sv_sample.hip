@@ -455,9 +455,7 @@ __global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, 
 // ---------------------------------------------------------------------------
 // draw kernel
 // ---------------------------------------------------------------------------
-// Unnormalised mass of the 8 tokens of octet `oct` (token ids 8*oct .. 8*oct+7):
-// residual mode r_v = max(0, e^p_v - kappa e^q_v) = Sp * max(0, p_v - q_v);
-// bonus mode r_v = e^p_v = Sp * p_v. Tokens at or beyond V get 0.
+// Octet `oct` of a row holds token ids 8*oct .. 8*oct+7.
 //
 // Raw words of one octet of a row, loaded with no branch so that the loads of
 // several octets are all in flight before the first is used: an octet at or
@@ -549,7 +547,9 @@ struct OctetRaw<0> {
   }
 };
 
-// Masses of 8 tokens (see SeqPlan for the two forms).
+// Unnormalised masses of 8 tokens (see SeqPlan for the two forms): residual
+// mode r_v = max(0, e^p_v - kappa e^q_v) = Sp * max(0, p_v - q_v); bonus mode
+// r_v = e^p_v = Sp * p_v. Tokens at or beyond V (value -inf) get 0.
 template <int MODE, int FORM>
 __device__ __forceinline__ void mass8(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P, float (&r)[8]) {
 #pragma unroll
