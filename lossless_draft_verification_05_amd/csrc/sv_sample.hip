@@ -869,21 +869,16 @@ __device__ __forceinline__ int wave_find(const double* arr, int len, double t, d
   return last_i;
 }
 
-// Rescan of step ss of the draw row(s) of sequence b by one wave, in token
+// The scan of one step's token masses rr[j] (octet ss * kStepOctets +
+// kWave * j + lane, j < NJ, zero past the row's end) by one wave, in token
 // order (octet j-major, then lane, then slot): the first token whose running
 // mass acc + ... exceeds t (acc: the mass of the steps before ss). If rounding
 // leaves none, the step's last token with positive mass. Every lane returns y.
-template <int TD, int DD, bool kBatch = true>
-__device__ __forceinline__ int rescan_step(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int ss, double t,
-                                           double acc, int lane) {
-  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
-  const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
-  const int64_t noct = ((int64_t)A.V + 7) / 8;
-  float rr[kU2][8];
-  step_octet_masses<TD, DD, kBatch>(trow, drow, ss, noct, A.V, mode, P, lane, rr);
+template <int NJ>
+__device__ __forceinline__ int scan_step(const float (&rr)[NJ][8], int ss, double t, double acc, int lane) {
   int y = -1;
   int last_pos = -1;
-  for (int j = 0; j < kU2 && y < 0; ++j) {
+  for (int j = 0; j < NJ && y < 0; ++j) {
     const int64_t oct = (int64_t)ss * kStepOctets + kWave * j + lane;
     const double os = (double)sum8(rr[j]);
     const double incl = wave_incl_scan(os, lane);
@@ -923,6 +918,19 @@ __device__ __forceinline__ int rescan_step(const SampleLaunch& A, int b, const S
     y = m;
   }
   return y;
+}
+
+// Rescan of step ss of the draw row(s) of sequence b by one wave: its token
+// masses, then the scan above.
+template <int TD, int DD, bool kBatch = true>
+__device__ __forceinline__ int rescan_step(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int ss, double t,
+                                           double acc, int lane) {
+  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
+  const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
+  const int64_t noct = ((int64_t)A.V + 7) / 8;
+  float rr[kU2][8];
+  step_octet_masses<TD, DD, kBatch>(trow, drow, ss, noct, A.V, mode, P, lane, rr);
+  return scan_step<kU2>(rr, ss, t, acc, lane);
 }
 
 // Every output of a valid sequence b once y is drawn: threads t0, t0 + nt, ...
@@ -1633,17 +1641,51 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
   const char* drow = (n < G) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   int mode = P.mode;
-  constexpr bool kB = PL > 4;  // rows of more than kWave octets: batch the step's loads
-  double total = (mode == kModeResidual) ? direct_step_mass<TD, DD, kModeResidual, kB>(trow, drow, 0, noct, A.V, P, lane)
-                                         : direct_step_mass<TD, DD, kModeBonus, kB>(trow, drow, 0, noct, A.V, P, lane);
-  if (!(total > 0.0) && mode == kModeResidual) {
-    // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
-    mode = kModeBonus;
-    total = direct_step_mass<TD, DD, kModeBonus, kB>(trow, drow, 0, noct, A.V, P, lane);
+  const float ug = A.uniforms[(int64_t)b * (G + 1) + G];
+  if constexpr (PL <= 4) {
+    // Rows of at most 32 octets: a lane holds at most one octet of the step.
+    // Its values are loaded once and serve the total, the bonus-mode fallback
+    // and the scan (the same operations, in the same order, as the step mass
+    // and rescan of longer rows).
+    const bool have = lane < noct;
+    float xt[8], xd[8], rr[1][8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xd[k] = 0.0f;
+    if (have) {
+      load_octet<TD>(trow, lane, A.V, xt);
+      if (mode == kModeResidual) load_octet<DD>(drow, lane, A.V, xd);
+    }
+    auto step_total = [&](int m) -> double {
+      double lacc = 0.0;
+      if (have) {
+        mass8_of(xt, xd, m, P, rr[0]);
+        lacc += (double)sum8(rr[0]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rr[0][k] = 0.0f;
+      }
+      return wave_sum(lacc);
+    };
+    double total = step_total(mode);
+    if (!(total > 0.0) && mode == kModeResidual) {
+      // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
+      mode = kModeBonus;
+      total = step_total(mode);
+    }
+    const int y = scan_step<1>(rr, 0, (double)ug * total, 0.0, lane);
+    write_outputs<TD>(A, b, P, mode, y, total, lane, 0, kWave);
+  } else {
+    double total = (mode == kModeResidual) ? direct_step_mass<TD, DD, kModeResidual>(trow, drow, 0, noct, A.V, P, lane)
+                                           : direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
+    if (!(total > 0.0) && mode == kModeResidual) {
+      // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
+      mode = kModeBonus;
+      total = direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
+    }
+    const double t = (double)ug * total;
+    const int y = rescan_step<TD, DD>(A, b, P, mode, 0, t, 0.0, lane);
+    write_outputs<TD>(A, b, P, mode, y, total, lane, 0, kWave);
   }
-  const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
-  const int y = rescan_step<TD, DD, kB>(A, b, P, mode, 0, t, 0.0, lane);
-  write_outputs<TD>(A, b, P, mode, y, total, lane, 0, kWave);
 }
 
 // ---------------------------------------------------------------------------
