@@ -65,6 +65,7 @@ struct SeqPlan {
   float kap_hi;  // kappa = Sp / Sq as a float pair (hi + lo)
   float kap_lo;
   float cp, cq, corr;
+  float ug;       // the draw's uniform
   double sp;      // sum_v exp2((x_v - mp) * kl) over target row n
   double sq;      // same for draft row n
   double fscale;  // F

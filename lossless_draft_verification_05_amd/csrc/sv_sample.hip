@@ -933,15 +933,16 @@ __device__ __forceinline__ int rescan_step(const SampleLaunch& A, int b, const S
   return scan_step<kU2>(rr, ss, t, acc, lane);
 }
 
-// Every output of a valid sequence b once y is drawn: threads t0, t0 + nt, ...
-// write the tokens; thread t0 the scalars.
+// Every output of a valid sequence b once y is drawn, by one wave whose lane
+// k < gamma holds draft token k in xi (so the tokens are not loaded again).
 template <int TD>
 __device__ __forceinline__ void write_outputs(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int y,
-                                              double total, int t, int t0, int nt) {
+                                              double total, int lane, int xi) {
   const int G = A.gamma, n = P.n;
   int32_t* otok = A.out_tok + (int64_t)b * (G + 1);
-  for (int k = t - t0; k <= G; k += nt) otok[k] = (k < n) ? A.tokens[(int64_t)b * G + k] : (k == n ? y : -1);
-  if (t == t0) {
+  if (lane < G) otok[lane] = (lane < n) ? xi : (lane == n ? y : -1);
+  if (lane == 0) {
+    otok[G] = (n == G) ? y : -1;
     if (A.out_n) A.out_n[b] = n;
     if (A.diag_mass) A.diag_mass[b] = (float)(total / (P.sp * P.fscale));
     if (A.out_py) {
@@ -969,27 +970,23 @@ __device__ __forceinline__ void write_invalid(const SampleLaunch& A, int b, int 
 }
 
 // Inverse-CDF draw from the step masses stot[0..ns2) (total mass `total`) of
-// the draw row(s) of sequence b, then every output of the sequence. Wave 0
-// searches; all threads of the workgroup (kFinThreads) write. sh_y: LDS slot.
+// the draw row(s) of sequence b, then every output of the sequence, by wave 0
+// (the other waves return): lane k < gamma of wave 0 holds draft token k in xi.
 template <int TD, int DD>
 __device__ __forceinline__ void draw_and_write(const SampleLaunch& A, int b, const SeqPlan& P, int mode, const double* stot,
-                               double total, int* sh_y) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = A.gamma;
-  // (5) inverse-CDF search (wave 0)
-  if (w == 0) {
-    const double t = (double)A.uniforms[(int64_t)b * (G + 1) + G] * total;
-    double acc = 0.0;
-    // wave_find returns -1 only if every mass is zero, which valid rows rule
-    // out; clamp anyway so that no index can leave the arrays.
-    const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
-    const int y = rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane);
-    if (lane == 0) *sh_y = y;
-  }
-  __syncthreads();
+                                               double total, int xi) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w != 0) return;
+  // (5) inverse-CDF search
+  const double t = (double)P.ug * total;
+  double acc = 0.0;
+  // wave_find returns -1 only if every mass is zero, which valid rows rule
+  // out; clamp anyway so that no index can leave the arrays.
+  const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
+  const int y = rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane);
   // (6) outputs
-  write_outputs<TD>(A, b, P, mode, *sh_y, total, tid, 0, kFinThreads);
+  write_outputs<TD>(A, b, P, mode, y, total, lane, xi);
 }
 
 // The plan of the draw of a sequence whose first stop is n (gamma: every
@@ -1001,6 +998,7 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
   if (n == G) valid = valid && tn.valid;
   SeqPlan Q;
   Q.valid = valid;
+  Q.ug = ug;
   Q.n = n;
   Q.mode = (n == G) ? kModeBonus : kModeResidual;
   Q.kl = kl;
@@ -1049,7 +1047,6 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   __shared__ int rV[kMaxRows];
   __shared__ SeqPlan sP;
   __shared__ double sh_total;
-  __shared__ int sh_y;
   __shared__ int sh_last;
   __shared__ double sh_steps[kLdsSteps];  // step masses when the row has at most kLdsSteps steps
 
@@ -1231,7 +1228,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
   const double total = sh_total;
 
-  draw_and_write<TD, DD>(A, b, P, mode, stot, total, &sh_y);
+  draw_and_write<TD, DD>(A, b, P, mode, stot, total, xi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1435,7 +1432,6 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   __shared__ double stepS[kLdsSteps];
   __shared__ SeqPlan sP;
   __shared__ double sh_total;
-  __shared__ int sh_y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x;
@@ -1474,6 +1470,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       SeqPlan Q;
       Q.valid = tv && u >= 0.0f && u < 1.0f && __builtin_isfinite(total) && total > 0.0 &&
                 __builtin_isfinite(mp);
+      Q.ug = u;
       Q.n = 0;
       Q.mode = kModeBonus;
       Q.form = sub ? 0 : 1;
@@ -1499,7 +1496,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     }
     return;
   }
-  draw_and_write<DT, DT>(A, b, P, kModeBonus, stepS, sh_total, &sh_y);
+  draw_and_write<DT, DT>(A, b, P, kModeBonus, stepS, sh_total, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1641,7 +1638,6 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
   const char* drow = (n < G) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   int mode = P.mode;
-  const float ug = A.uniforms[(int64_t)b * (G + 1) + G];
   if constexpr (PL <= 4) {
     // Rows of at most 32 octets: a lane holds at most one octet of the step.
     // Its values are loaded once and serve the total, the bonus-mode fallback
@@ -1672,8 +1668,8 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
       mode = kModeBonus;
       total = step_total(mode);
     }
-    const int y = scan_step<1>(rr, 0, (double)ug * total, 0.0, lane);
-    write_outputs<TD>(A, b, P, mode, y, total, lane, 0, kWave);
+    const int y = scan_step<1>(rr, 0, (double)P.ug * total, 0.0, lane);
+    write_outputs<TD>(A, b, P, mode, y, total, lane, xi);
   } else {
     double total = (mode == kModeResidual) ? direct_step_mass<TD, DD, kModeResidual>(trow, drow, 0, noct, A.V, P, lane)
                                            : direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
@@ -1682,9 +1678,9 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
       mode = kModeBonus;
       total = direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
     }
-    const double t = (double)ug * total;
+    const double t = (double)P.ug * total;
     const int y = rescan_step<TD, DD>(A, b, P, mode, 0, t, 0.0, lane);
-    write_outputs<TD>(A, b, P, mode, y, total, lane, 0, kWave);
+    write_outputs<TD>(A, b, P, mode, y, total, lane, xi);
   }
 }
 
