@@ -488,9 +488,12 @@ def early_exit_bytes(cfg, B, G, V, n_acc):
 
 # ----------------------------------------------------------------------------
 def traffic_from_profiles(workload: str, sha: str):
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
-    if not os.path.exists(path):
+    # profiles/<dominant kernel>_<workload>_traffic.json
+    import glob
+    found = glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_traffic.json"))
+    if len(found) != 1:
         return None
+    path = found[0]
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_sha") != sha:
