@@ -49,9 +49,11 @@ __device__ __forceinline__ void argmax_units(ArgState& st, const Unit<DT> (&un)[
 }
 
 // The workgroup streams units [c_begin, c_end); thread t takes units
-// c_begin + t + 256 k (one contiguous 4 KB block per load instruction). Each
-// thread still sees its units in increasing order, so strict ">" keeps the
-// first index of a tie within a thread.
+// c_begin + t + 256 k (one contiguous 4 KB block per load instruction), kU1
+// of them per round: every load of a round is issued first (a lane past c_end
+// loads the chunk's last unit and skips it), then the units are compared one
+// at a time in increasing order, so strict ">" keeps the first index of a tie
+// within a thread and only one unit's values are live at once.
 template <int DT>
 __device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int V, int64_t c_begin, int64_t c_end,
                                               ArgState& st) {
@@ -59,26 +61,7 @@ __device__ __forceinline__ void stream_argmax(const char* __restrict__ row, int 
   const int tid = threadIdx.x;
   const int64_t nu_row = ((int64_t)V + E - 1) / E;
   const bool ragged = (V % E) != 0;
-  int64_t full_end = c_end;
-  if (ragged && full_end > nu_row - 1) full_end = nu_row - 1;
-  int64_t base = c_begin;
-  for (; base + (int64_t)kThreads * kU1 <= full_end; base += (int64_t)kThreads * kU1) {
-    uint4 w[kU1];
-    int64_t u[kU1];
-#pragma unroll
-    for (int j = 0; j < kU1; ++j) {
-      u[j] = base + tid + kThreads * j;
-      w[j] = load16(row + u[j] * 16);
-    }
-    Unit<DT> un[kU1];
-#pragma unroll
-    for (int j = 0; j < kU1; ++j) un[j].unpack(w[j]);
-    argmax_units<DT, kU1>(st, un, u);
-  }
-  // The tail: every load first, then the units in order (one memory round
-  // trip, not one per unit); a lane past c_end loads the chunk's last unit and
-  // skips it.
-  if (base < c_end) {
+  for (int64_t base = c_begin; base < c_end; base += (int64_t)kThreads * kU1) {
     uint4 w[kU1];
 #pragma unroll
     for (int j = 0; j < kU1; ++j) {
