@@ -1,0 +1,109 @@
+"""GPU tests of how the calls sit on streams: every entry point enqueued on a
+side stream (default priority) gives the default stream's results, and a
+graph that captures one call of each entry point (the sampling verify with
+its split finish, the early-exit verify, the greedy tree, the draft sampler
+and the tree masks) replays to the eager results every time, with eager work
+on the outputs and synchronisations between the replays. None of the calls
+records a memory set: the workspace needs no clearing and the outputs are
+written by the kernels."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs():
+    # 12 sequences: fewer than the CUs, so the finish splits each sequence's draw
+    inp = synth.make_custom_sample(12, 4, 70001, "bf16", "f32", T=np.linspace(0.4, 1.6, 12, dtype=np.float32),
+                                   noise_sd=0.7, seed=41)
+    tens = H.sample_tensors(inp, pad_to=70008)
+    ti = synth.make_tree_inputs(4, seed=42, B=6, N=40, V=20000)
+    tt = H.tree_tensors(ti)
+    d = synth.make_draft_rows(10, 30000, "bf16", T=np.linspace(0.5, 1.5, 10, dtype=np.float32), seed=43)
+    dt = H.draft_tensors(d)
+    P = torch.from_numpy(ti.parents).cuda()
+    Bl = torch.from_numpy(np.stack([synth.tree_blocks(p) for p in ti.parents])).cuda()
+    return tens, tt, dt, P, Bl
+
+
+def _all_calls(gpu, tens, tt, dt, P, Bl, outs, ws):
+    """One call of every entry point into the fixed output tensors `outs`."""
+    gpu.spec_verify_sample(**tens, out_num_accepted=outs["n"], out_tokens=outs["tok"], workspace=ws["s"])
+    gpu.spec_verify_sample_early_exit(**tens, out_num_accepted=outs["en"], out_tokens=outs["etok"],
+                                      workspace=ws["e"])
+    gpu.spec_verify_greedy_tree(**tt, out_accept_len=outs["len"], out_path=outs["path"], out_bonus=outs["bonus"],
+                                out_argmax=outs["am"], workspace=ws["t"])
+    gpu.spec_draft_sample(**dt, out_tokens=outs["y"], workspace=ws["d"])
+    gpu.spec_tree_mask(P, Bl, want_relaxed=True, out_mask=outs["mask"], out_relaxed=outs["rel"],
+                       out_depth=outs["depth"])
+
+
+def _outputs(tens, tt, dt, P):
+    B, G = tens["draft_tokens"].shape
+    Bt, N = tt["parents"].shape
+    i32 = dict(dtype=torch.int32, device="cuda")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    return {"n": torch.empty(B, **i32), "tok": torch.empty((B, G + 1), **i32),
+            "en": torch.empty(B, **i32), "etok": torch.empty((B, G + 1), **i32),
+            "len": torch.empty(Bt, **i32), "path": torch.empty((Bt, N), **i32), "bonus": torch.empty(Bt, **i32),
+            "am": torch.empty((Bt, N), **i32), "y": torch.empty(dt["logits"].shape[0], **i32),
+            "mask": torch.empty((Bt, N, N), **u8), "rel": torch.empty((Bt, N, N), **u8),
+            "depth": torch.empty((Bt, N), **i32)}
+
+
+def _workspaces(gpu):
+    return {k: gpu.Workspace() for k in ("s", "e", "t", "d")}
+
+
+def _snapshot(outs):
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy().copy() for k, v in outs.items()}
+
+
+def test_side_stream_matches_default_stream(gpu):
+    H.log("every entry point on a side stream vs the default stream")
+    tens, tt, dt, P, Bl = _inputs()
+    ref_outs = _outputs(tens, tt, dt, P)
+    _all_calls(gpu, tens, tt, dt, P, Bl, ref_outs, _workspaces(gpu))
+    ref = _snapshot(ref_outs)
+    outs = _outputs(tens, tt, dt, P)
+    ws = _workspaces(gpu)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _all_calls(gpu, tens, tt, dt, P, Bl, outs, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    got = _snapshot(outs)
+    for k in ref:
+        assert np.array_equal(ref[k], got[k]), k
+    assert (ref["n"] >= 0).all() and (ref["len"] >= 0).all()
+
+
+def test_graph_replays_match_eager(gpu):
+    H.log("one graph capturing every entry point, replayed 5 times against the eager results")
+    tens, tt, dt, P, Bl = _inputs()
+    outs = _outputs(tens, tt, dt, P)
+    ws = _workspaces(gpu)
+    _all_calls(gpu, tens, tt, dt, P, Bl, outs, ws)  # eager: also sizes every workspace before the capture
+    ref = _snapshot(outs)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream, as graph capture expects
+        _all_calls(gpu, tens, tt, dt, P, Bl, outs, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _all_calls(gpu, tens, tt, dt, P, Bl, outs, ws)
+    for r in range(5):
+        for v in outs.values():  # eager work on the outputs between replays
+            v.fill_(-3 if v.dtype == torch.int32 else 7)
+        torch.cuda.synchronize()
+        graph.replay()
+        got = _snapshot(outs)
+        for k in ref:
+            assert np.array_equal(ref[k], got[k]), (r, k)
