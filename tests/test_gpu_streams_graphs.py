@@ -3,9 +3,10 @@ side stream (default priority) gives the default stream's results, and a
 graph that captures one call of each entry point (the sampling verify with
 its split finish, the early-exit verify, the greedy tree, the draft sampler
 and the tree masks) replays to the eager results every time, with eager work
-on the outputs and synchronisations between the replays. None of the calls
-records a memory set: the workspace needs no clearing and the outputs are
-written by the kernels."""
+on the outputs and synchronisations between the replays; two batches on two
+streams at once give their one-at-a-time results. None of the calls records a
+memory set: the workspace needs no clearing and the outputs are written by
+the kernels."""
 import numpy as np
 import pytest
 import torch
@@ -107,3 +108,36 @@ def test_graph_replays_match_eager(gpu):
         got = _snapshot(outs)
         for k in ref:
             assert np.array_equal(ref[k], got[k]), (r, k)
+
+
+def test_concurrent_calls_on_two_streams(gpu):
+    """Two batches verified at the same time on two streams, each with its own
+    workspace, give the results of running them one after the other: the
+    library keeps no state between or across calls."""
+    H.log("two sampling batches and two tree batches interleaved on two streams")
+    ins = [synth.make_custom_sample(40, 5, 50000, "bf16", "bf16", T=0.9, noise_sd=0.7, seed=50 + k) for k in (0, 1)]
+    tens = [H.sample_tensors(x) for x in ins]
+    tis = [synth.make_tree_inputs(4, seed=60 + k, B=8, N=60, V=20000) for k in (0, 1)]
+    tts = [H.tree_tensors(t) for t in tis]
+    ref = [H.run_sample(gpu, t, diag=False) for t in tens]
+    tref = [H.run_tree(gpu, t) for t in tts]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ws = [(gpu.Workspace(), gpu.Workspace()) for _ in (0, 1)]
+    res = [None, None]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for k in (0, 1):
+            with torch.cuda.stream(streams[k]):
+                res[k] = (gpu.spec_verify_sample(**tens[k], workspace=ws[k][0]),
+                          gpu.spec_verify_greedy_tree(**tts[k], workspace=ws[k][1]))
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for k in (0, 1):
+            (n, tok, _), (ln, path, bonus, am) = res[k]
+            assert np.array_equal(n.cpu().numpy(), ref[k]["n"]), (rep, k)
+            assert np.array_equal(tok.cpu().numpy(), ref[k]["tokens"]), (rep, k)
+            assert np.array_equal(ln.cpu().numpy(), tref[k]["len"]), (rep, k)
+            assert np.array_equal(path.cpu().numpy(), tref[k]["path"]), (rep, k)
+            assert np.array_equal(bonus.cpu().numpy(), tref[k]["bonus"]), (rep, k)
