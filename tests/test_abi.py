@@ -196,3 +196,34 @@ def test_tree_mask_argument_errors(lib):
     assert f(A, A + 1, 2, 5, A, A + 0x1000, None, None) == -4         # blocks misaligned
     assert f(A, None, 2, 5, None, None, A + 0x2002, None) == -4       # depth misaligned
     assert f(A, None, 2, 5, None, None, None, None) == 0              # nothing requested: no launch
+
+
+def test_argument_checks_from_many_threads(lib):
+    """The host side keeps no shared mutable state: argument checks called
+    from eight threads at once (ctypes releases the interpreter lock during
+    each call) return the same statuses as one thread."""
+    import threading
+
+    cases = [(dict(target=None), -1), (dict(tdt=2), -3), (dict(B=0), -2), (dict(target=A + 2), -4),
+             (dict(wsb=100), -5), (dict(G=65), -2)]
+    errors = []
+
+    def worker(k):
+        try:
+            for it in range(400):
+                over, want = cases[(k + it) % len(cases)]
+                got = call_sample(lib, **over)
+                if got != want:
+                    errors.append((k, it, over, got, want))
+                if lib.sv_sample_workspace_bytes(64, 4, 32000) != lib.sv_sample_workspace_bytes(64, 4, 32000):
+                    errors.append((k, it, "workspace size"))
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
+    assert lib.sv_last_hip_error() == 0
