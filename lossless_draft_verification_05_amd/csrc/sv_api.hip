@@ -114,8 +114,9 @@ static SampleLaunch plan_sample(const SampleArgs& a, bool early = false) {
   const int64_t G = a.gamma, V = a.V, B = a.B;
   const int64_t total = B * ((G + 1) * V * et + G * V * ed);
   const int64_t cb = early ? early_chunk_bytes() : chunk_bytes_for(total);
-  split_row(V, et, cb, &L.nct, &L.cut);
-  split_row(V, ed, cb, &L.ncd, &L.cud);
+  // chunks start on 16 KB batch boundaries of their rows (see chunk_bytes_for)
+  split_row(V, et, cb, &L.nct, &L.cut, kBatchUnits);
+  split_row(V, ed, cb, &L.ncd, &L.cud, kBatchUnits);
   L.per_seq = (int)((G + 1) * L.nct + G * L.ncd);
   L.ns2 = (int)draw_steps(V);
   L.parts = finish_parts(B, L.ns2);
@@ -123,6 +124,7 @@ static SampleLaunch plan_sample(const SampleArgs& a, bool early = false) {
   char* ws = (char*)a.ws;
   L.part = (RowPartial*)(ws + lay.off_part);
   L.steptot = (double*)(ws + lay.off_step);
+  L.stepq = (double*)(ws + lay.off_stepq);
   L.done = (int32_t*)(ws + lay.off_done);
   return L;
 }

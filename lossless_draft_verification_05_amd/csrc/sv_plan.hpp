@@ -25,14 +25,24 @@ constexpr int64_t kEarlyChunkBytes = 128 << 10;  // early-exit statistics work u
 constexpr double kEarlyAlpha = 0.7;             // acceptance rate assumed when grouping positions
 constexpr double kEarlyLaunchBytes = 64e6;      // bytes moved in about the time one extra launch costs
 constexpr int64_t kFinTargetWGs = 256;          // finish: split sequences over parts up to one workgroup per CU
+constexpr int64_t kBatchUnits = (int64_t)kThreads * kU1;  // 1024 units = 16 KB: one batch of every thread
+constexpr double kExactBelow = 0.125;  // residual mass (share of p's) below which the exact pass runs
 
-enum : int { kModeResidual = 0, kModeBonus = 1 };
+// kModeExact: the residual of the exact pass (after a first pass found its mass
+// below kExactBelow), taken as e_p * (1 - 2^w) with w = log2(q / p) formed from
+// the logit difference, and corrected to first order for the error of the
+// normalisers' ratio (SeqPlan::g).
+enum : int { kModeResidual = 0, kModeBonus = 1, kModeExact = 2 };
 
 // Partial statistics of one wave's share of one chunk of one logits row
-// (stats pass), against a reference logit m (a value of the share, or -inf if
-// every value was -inf):
-//   form 1: s = sum of exp2(x * kl - c), c = fp32(m * kl) rounded once;
-//   form 0: s = sum of exp2((x - m) * kl)  (reference m * kl, exact in fp64).
+// (stats pass):
+//   form 1: s = sum of exp2(x * kl - m), where m is an integer number of log2
+//           units (a float holding an integer, |m| < 2^24, or -inf when every
+//           value was -inf); every term of every batch was taken against an
+//           integer shift at or just above that batch's maximum and moved to m
+//           by an exact power of two;
+//   form 0: s = sum of exp2((x - m) * kl) against a reference logit m (used
+//           when a shift would reach 2^24: tiny temperatures or huge logits).
 struct RowPartial {
   float m;
   int form;
@@ -41,34 +51,47 @@ struct RowPartial {
 
 // The finish kernel's per-sequence plan for the draw (held in LDS).
 //
-// Mass of token v of the drawn distribution, up to one positive factor per
-// sequence:
+// Row statistics: p_v = exp2(x_t,v * kl - ct) / sp over target row n and
+// q_v = exp2(x_d,v * kl - cd) / sq over draft row n (ct, cd in log2 units,
+// fp64). Mass of token v of the drawn distribution, up to one positive factor
+// F * sp per sequence:
 //  form 1 (shifts folded into one FMA each):
 //    e_p = exp2(fma(x_t, kl, -cp)), e_q = exp2(fma(x_d, kl, -cq)),
 //    r = max(0, fma(e_q, corr, e_p - e_q)) after a rejection, r = e_p otherwise.
-//    cp = fp32(mp * kl); cq = fp32(mq * kl - log2(Sp / Sq) - (mp * kl - cp)),
-//    so e_q carries the ratio of the normalisers; corr = (exact cq - cq) * ln 2
-//    removes, to first order, the rounding of cq. r = F * Sp * max(0, p - q)
-//    with F = exp2(mp * kl - cp) (fscale).
+//    cp = fp32(ct) (exact when ct is an integer); cq = fp32(cqx) with
+//    cqx = cd - log2(sp / sq) - (ct - cp), so e_q carries the ratio of the
+//    normalisers; corr = (cqx - cq) * ln 2 removes, to first order, the
+//    rounding of cq. r = F * sp * max(0, p - q) with F = exp2(ct - cp) (fscale).
+//  exact pass (form 1 only, kModeExact): w = fma(x_d - x_t, kl, dt) =
+//    log2(q_v / p_v) with dt = cp - cqx; e = e_p where w <= 0, else e_q taken
+//    as exp2(e_p's exponent + w) (as exp2(fma(x_d, kl, -cq) - cq_lo) where the
+//    target logit is -inf); d = e_p - e_q = -e * expm1_2(-|w|) with the sign of
+//    -w, its magnitude exact to a few ulp however close p and q are;
+//    r = max(0, d) - g * (e_q where d > 0), g the first-order correction of
+//    the normalisers' ratio from the signed sum of d over the row.
 //  form 0 (used when a shift is 2^24 or more in magnitude, where its fp32
 //  rounding would be half a log2 unit or more):
 //    e_p = exp2((x_t - mp) * kl), e_q = exp2((x_d - mq) * kl),
-//    r = max(0, e_p - kappa e_q) with kappa = Sp / Sq as a float pair; F = 1.
+//    r = max(0, e_p - kappa e_q) with kappa as a float pair, F = exp2(ct - mp * kl).
 struct SeqPlan {
   int valid;   // 0: the sequence is invalid (all outputs -1)
   int n;       // accepted drafts
   int mode;    // kModeResidual (row n pair) or kModeBonus (target row n == gamma)
   int form;    // 1: FMA shifts, 0: subtract-multiply
   float kl;    // log2(e) / T, fp32
-  float mp;    // maximum of target row n, logit units
-  float mq;    // maximum of draft row n
-  float kap_hi;  // kappa = Sp / Sq as a float pair (hi + lo)
+  float mp;    // form 0: reference logit of target row n
+  float mq;    // form 0: reference logit of draft row n
+  float kap_hi;  // form 0: kappa (F * sp) / (F_q * sq) as a float pair (hi + lo)
   float kap_lo;
   float cp, cq, corr;
+  float cq_lo;    // cqx - cq
+  float dt;       // fp32(cp - cqx): log2(q_v / p_v) - (x_d - x_t) * kl
   float ug;       // the draw's uniform
-  double sp;      // sum_v exp2((x_v - mp) * kl) over target row n
-  double sq;      // same for draft row n
+  double ct;      // shift of target row n (log2 units)
+  double sp;      // sum_v exp2(x_v * kl - ct) over target row n
+  double sq;      // sum_v exp2(x_v * kl - cd) over draft row n
   double fscale;  // F
+  double g;       // exact pass: first-order correction factor (0 otherwise)
 };
 
 // Partial argmax of one wave's share of one chunk of one row (tree pass).
@@ -103,6 +126,7 @@ struct SampleLaunch {
   // workspace
   RowPartial* part;  // [B][per_seq][kWaves]
   double* steptot;   // [B][ns2]; with parts > 1 it holds -1 (no mass yet) before each finish launch
+  double* stepq;     // [B][ns2]: q-mass of each step's positive residual (exact pass, steps beyond LDS)
   int32_t* reach;    // [B] early exit only (else null): rows 0..reach-1 have statistics
   int32_t* done;     // [B] finish parts done; zeroed by the statistics pass and by the drawing part
 };
@@ -143,9 +167,13 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // Bytes of work per stats/argmax workgroup for a call that streams total_bytes.
+// A multiple of 16 KB (one batch of 4 units of every thread), so that every
+// chunk starts on a batch boundary of its row: the statistics pass then forms
+// the same batches, with the same fp32 arithmetic, whatever the chunking (and
+// so whatever the batch size of the call).
 inline int64_t chunk_bytes_for(int64_t total_bytes) {
   int64_t c = clamp64(total_bytes / kTargetWGs, kMinChunkBytes, kMaxChunkBytes);
-  return round_up(c, (int64_t)kThreads * 16);
+  return round_up(c, kBatchUnits * 16);
 }
 
 // Work unit of the tree's argmax kernel: the same rule with its own lower bound.
@@ -155,12 +183,13 @@ inline int64_t tree_chunk_bytes_for(int64_t total_bytes) {
   return round_up(c, (int64_t)kThreads * 16);
 }
 
-// Split a row of V elements of esz bytes into nch chunks of cu 16-byte units.
-inline void split_row(int64_t V, int esz, int64_t chunk_bytes, int* nch, int* cu) {
+// Split a row of V elements of esz bytes into nch chunks of cu 16-byte units,
+// cu a multiple of `align` units (chunk_bytes is a multiple of align * 16).
+inline void split_row(int64_t V, int esz, int64_t chunk_bytes, int* nch, int* cu, int64_t align = kThreads) {
   int64_t nu = ceil_div(V * esz, 16);
   int64_t per = chunk_bytes / 16;
   int64_t n = ceil_div(nu, per);
-  int64_t c = round_up(ceil_div(nu, n), kThreads);
+  int64_t c = round_up(ceil_div(nu, n), align);
   *nch = (int)ceil_div(nu, c);
   *cu = (int)c;
 }
@@ -171,7 +200,7 @@ inline int64_t max_chunks_per_row(int64_t V) { return ceil_div(V * 4, kMinChunkB
 inline int64_t align256(int64_t x) { return round_up(x, 256); }
 
 struct SampleLayout {
-  int64_t off_part, off_step, off_reach, off_done, total;
+  int64_t off_part, off_step, off_stepq, off_reach, off_done, total;
 };
 
 inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
@@ -248,6 +277,8 @@ inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
   o += align256(B * (2 * gamma + 1) * max_chunks_per_row(V) * kWaves * (int64_t)sizeof(RowPartial));
   L.off_step = o;
   o += align256(B * draw_steps(V) * 8);
+  L.off_stepq = o;
+  o += draw_steps(V) > kLdsSteps ? align256(B * draw_steps(V) * 8) : 0;
   L.off_reach = o;
   o += align256(B * 4);
   L.off_done = o;

@@ -40,21 +40,27 @@ constexpr int kMaxRows = 2 * 64 + 1;
 // ---------------------------------------------------------------------------
 // streaming tempered sum-exp
 // ---------------------------------------------------------------------------
-// Per-lane state of the statistics pass. Terms are taken against a reference
-// logit m that moves up only when a new value would make a term exceed 2^64
-// (about once per lane and row), so the common case computes no maximum:
-//  FMA form: term = exp2(fma(x, kl, -c)) with c = fp32(m * kl) rounded once,
-//   so s sums 2^(x * kl - c) exactly up to the rounding of each term;
-//  subtract form, used when |m * kl| >= 2^24 (c would then round by half a
-//   log2 unit or more): term = exp2((x - m) * kl).
-// m = c = -inf while every value seen was -inf.
+// Per-lane state of the statistics pass (FMA form): s = sum of
+// exp2(x * kl - c) over the lane's values so far, against an integer shift c
+// (log2 units, a float holding an integer; -inf while every value seen was
+// -inf). Each batch -- the lane's kU1 units of one 16 KB block of the row -- is
+// summed in fp32 against its own integer shift at or just above the batch's
+// maximum, so every term is at most ~1, where an fp32 exponent is finest (the
+// only rounding of x * kl - c is that of the FMA's result), and the batch sum
+// depends on the batch alone; it is then folded into s by exact powers of two.
+// With chunks that start on 16 KB boundaries the batches, and so every fp32
+// rounding, are the same however a row is split into chunks: a call's
+// statistics do not depend on its batch size, only fp64 additions do.
+// The subtract form exp2((x - m) * kl) is used when a shift reaches 2^24
+// (tiny temperatures or huge logits), where an fp32 shift no longer holds
+// every integer.
 struct SumExp {
-  float m;
   float c;
   double s;
-  int ovf;  // |m * kl| >= 2^24: the chunk is redone in the subtract form
+  int ovf;  // a batch shift reached 2^24: the chunk is redone in the subtract form
 };
 
+// Sum of exp2(x * kl - c) over the NU units of a batch, in a fixed order.
 template <int DT, int NU>
 __device__ __forceinline__ float terms_fma(const Unit<DT> (&un)[NU], float kl, float c) {
   constexpr int E = Unit<DT>::kEpu;
@@ -79,35 +85,29 @@ __device__ __forceinline__ float terms_fma(const Unit<DT> (&un)[NU], float kl, f
     return u[0];
 }
 
+// Add a batch sum a taken against shift cb (-inf: an empty batch, a = 0) to
+// the lane's sum, moving the lane's shift up to cb if that is larger. Both
+// shifts are integers, so the rescaling is exact; a NaN batch (NaN or +inf in
+// the row) makes the lane's sum NaN.
+__device__ __forceinline__ void fold_batch(SumExp& st, float cb, float a) {
+  const float hi = fmaxf(st.c, cb);
+  const int e1 = (int)fmaxf(st.c - hi, -1100.0f);  // <= 0; -inf or NaN (no shift yet) -> underflow to 0
+  const int e2 = (int)fmaxf(cb - hi, -1100.0f);
+  st.s = ldexp(st.s, e1) + ldexp((double)a, e2);
+  st.c = hi;
+}
+
 template <int DT, int NU>
 __device__ __forceinline__ void sumexp_fma(SumExp& st, const Unit<DT> (&un)[NU], float kl) {
-  // no reference yet (the first batch of every chunk): straight to the batch maximum
-  float a = __builtin_inff();
-  if (st.c != -INFINITY) a = terms_fma<DT, NU>(un, kl, st.c);
-  if (!(a <= 0x1p64f)) {
-    // a value above the reference by more than 64 / kl, the first finite
-    // value, +inf or NaN: move the reference to the batch maximum and redo
-    float gm = unit_max(un[0]);
-    bool nan = false;
+  float gm = unit_max(un[0]);
 #pragma unroll
-    for (int j = 0; j < NU; ++j) {
-      gm = fmaxf(gm, unit_max(un[j]));
-#pragma unroll
-      for (int k = 0; k < Unit<DT>::kEpu; ++k) nan |= un[j].x[k] != un[j].x[k];
-    }
-    if (gm > st.m) {
-      const float cn = __fmul_rn(gm, kl);
-      // c must round by less than half a log2 unit, or the terms near the
-      // maximum leave the fp32 range: |c| < 2^24, else the subtract form
-      if (!(fabsf(cn) < 0x1p24f) && __builtin_isfinite(gm)) st.ovf = 1;
-      if (st.c != -INFINITY) st.s *= exp2((double)st.c - (double)cn);  // else s is 0
-      st.m = gm;
-      st.c = cn;
-    }
-    a = (st.c == -INFINITY) ? 0.0f : terms_fma<DT, NU>(un, kl, st.c);
-    if (nan) a = __builtin_nanf("");
-  }
-  st.s += (double)a;
+  for (int j = 1; j < NU; ++j) gm = fmaxf(gm, unit_max(un[j]));
+  // the ceiling of the rounded product is at most half an ulp (<= 1/2 while
+  // |c| < 2^24) below gm * kl: every term of the batch is below 2^(1/2)
+  const float cb = ceilf(gm * kl);
+  if (!(fabsf(cb) < 0x1p24f) && __builtin_isfinite(gm)) st.ovf = 1;
+  const float a = (cb == -INFINITY) ? 0.0f : terms_fma<DT, NU>(un, kl, cb);
+  fold_batch(st, cb, a);
 }
 
 // Subtract form: reference m_ref starts at -FLT_MAX and moves to the batch
@@ -242,20 +242,19 @@ __device__ __forceinline__ void stats_chunk(const SampleLaunch& A, int b, int r,
   const int w = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const bool tgt = r < (A.gamma + 1) * A.nct;
   RowPartial rp;
-  SumExp st{-INFINITY, -INFINITY, 0.0, 0};
+  SumExp st{-INFINITY, 0.0, 0};
   if (tgt)
     stream_slot<TD>(A, b, r, kl, st);
   else
     stream_slot<DD>(A, b, r, kl, st);
   if (!__syncthreads_or(st.ovf)) {
+    // the wave's lanes at its largest shift, rescaled by exact powers of two
     const float Mc = wave_max(st.c);
-    if (Mc == -INFINITY) {
+    if (Mc == -INFINITY)
       rp.s = wave_sum(st.s);  // every value -inf (s = 0) or NaN seen
-      rp.m = -INFINITY;
-    } else {
-      rp.s = wave_sum(st.s * (double)hw_exp2(st.c - Mc));
-      rp.m = wave_max(st.c == Mc ? st.m : -INFINITY);  // a lane whose reference is Mc
-    }
+    else
+      rp.s = wave_sum(ldexp(st.s, (int)fmaxf(st.c - Mc, -1100.0f)));
+    rp.m = Mc;
     rp.form = 1;
   } else {
     SumExpSub ss{-FLT_MAX, 0.0};
@@ -275,22 +274,31 @@ __device__ __forceinline__ void stats_chunk(const SampleLaunch& A, int b, int r,
 // (every lane gets the result). Used by the finish kernel and by the gate of
 // the early-exit stats kernel, which must reach the same accept decisions bit
 // for bit; contraction is off so that inlining cannot change the rounding.
+// p_v = exp2(x_v * kl - c) / s.
 struct RowStat {
-  float m;   // reference logit: a value of the row, within 64 / kl of its maximum
-  double s;  // sum_v exp2((x_v - m) * kl)
+  double c;  // shift in log2 units: the largest partial shift
+  float m;   // a logit with m * kl near c (the reference of the subtract form)
+  double s;  // sum_v exp2(x_v * kl - c)
   int valid;
 };
-// Reference of a partial in log2 units, exactly as its terms were taken.
+// Shift of a partial in log2 units, exactly as its terms were taken.
 __device__ __forceinline__ double partial_shift(const RowPartial& p, float kl) {
-  return p.form ? (double)__fmul_rn(p.m, kl) : (double)p.m * (double)kl;
+  return p.form ? (double)p.m : (double)p.m * (double)kl;
 }
 
-__device__ __forceinline__ RowStat row_stat(float Mm, double Ms, double S, float kl, bool tv) {
+// 2^d for d <= 0 in fp64: exact (a power of two) when d is an integer, as it
+// is between two FMA-form partials.
+__device__ __forceinline__ double pow2_le0(double d) {
+  return (d == rint(d)) ? ldexp(1.0, (int)fmax(d, -1100.0)) : exp2(d);
+}
+
+__device__ __forceinline__ RowStat row_stat(double Ms, float Mm, double S, float kl, bool tv) {
 #pragma clang fp contract(off)
   RowStat r;
-  r.m = Mm;
-  r.s = S * exp2(Ms - (double)Mm * (double)kl);
-  r.valid = tv && __builtin_isfinite(r.s) && r.s > 0.0 && __builtin_isfinite(Mm);
+  r.c = Ms;
+  r.m = (Mm != -INFINITY) ? Mm : (float)(Ms / (double)kl);
+  r.s = S;
+  r.valid = tv && __builtin_isfinite(S) && S > 0.0 && __builtin_isfinite(Ms);
   return r;
 }
 
@@ -298,43 +306,38 @@ __device__ __forceinline__ RowStat row_stat(float Mm, double Ms, double S, float
 // partial q), taken with the same operations as the general merge below.
 __device__ __forceinline__ RowStat merge_row_one(const RowPartial& q, bool have, float kl, bool tv) {
 #pragma clang fp contract(off)
-  double Ms = -INFINITY;
-  float Mm = -INFINITY;  // the reference logit of a partial at Ms (the largest such)
-  double S = 0.0;
   double sh = -INFINITY;
-  if (have) {
-    sh = partial_shift(q, kl);
-    Ms = fmax(Ms, sh);
-  }
-  Ms = wave_max_f64(Ms);
-  if (have && sh == Ms) Mm = fmaxf(Mm, q.m);
+  if (have) sh = partial_shift(q, kl);
+  const double Ms = wave_max_f64(sh);
+  float Mm = -INFINITY;  // the reference logit of a subtract-form partial at Ms
+  if (have && sh == Ms && q.form == 0) Mm = q.m;
   Mm = wave_max(Mm);
-  if (have) S += q.s * exp2(sh - Ms);
+  double S = 0.0;
+  if (have) S += q.s * pow2_le0(sh - Ms);
   S = wave_sum(S);
-  return row_stat(Mm, Ms, S, kl, tv);
+  return row_stat(Ms, Mm, S, kl, tv);
 }
 
 __device__ __forceinline__ RowStat merge_row(const RowPartial* P, int nrec, float kl, bool tv, int lane) {
 #pragma clang fp contract(off)
-  double Ms = -INFINITY;
-  float Mm = -INFINITY;  // the reference logit of a partial at Ms (the largest such)
-  double S = 0.0;
   if (nrec <= kWave) {
     // at most one partial per lane, loaded once
     const bool have = lane < nrec;
     RowPartial q{};
     if (have) q = P[lane];
     return merge_row_one(q, have, kl, tv);
-  } else {
-    for (int k = lane; k < nrec; k += kWave) Ms = fmax(Ms, partial_shift(P[k], kl));
-    Ms = wave_max_f64(Ms);
-    for (int k = lane; k < nrec; k += kWave)
-      if (partial_shift(P[k], kl) == Ms) Mm = fmaxf(Mm, P[k].m);
-    Mm = wave_max(Mm);
-    for (int k = lane; k < nrec; k += kWave) S += P[k].s * exp2(partial_shift(P[k], kl) - Ms);
   }
+  double Ms = -INFINITY;
+  for (int k = lane; k < nrec; k += kWave) Ms = fmax(Ms, partial_shift(P[k], kl));
+  Ms = wave_max_f64(Ms);
+  float Mm = -INFINITY;
+  for (int k = lane; k < nrec; k += kWave)
+    if (P[k].form == 0 && partial_shift(P[k], kl) == Ms) Mm = fmaxf(Mm, P[k].m);
+  Mm = wave_max(Mm);
+  double S = 0.0;
+  for (int k = lane; k < nrec; k += kWave) S += P[k].s * pow2_le0(partial_shift(P[k], kl) - Ms);
   S = wave_sum(S);
-  return row_stat(Mm, Ms, S, kl, tv);
+  return row_stat(Ms, Mm, S, kl, tv);
 }
 
 // Accept test of one position: rho = p(x) / q(x) in the log2 domain in fp64;
@@ -352,8 +355,8 @@ __device__ __forceinline__ AcceptOut accept_test(float lt, float ld, const RowSt
   o.qx = __builtin_nanf("");
   const bool ok = tv && t.valid && d.valid && tok_ok && u >= 0.0f && u < 1.0f && ld != -INFINITY;
   if (ok) {
-    const double lp2 = ((double)lt - (double)t.m) * (double)kl;
-    const double lq2 = ((double)ld - (double)d.m) * (double)kl;
+    const double lp2 = (double)lt * (double)kl - t.c;  // the product of two floats is exact
+    const double lq2 = (double)ld * (double)kl - d.c;
     const double rho = exp2(lp2 - lq2) * (d.s / t.s);
     o.px = (float)(exp2(lp2) / t.s);
     o.qx = (float)(exp2(lq2) / d.s);
@@ -547,16 +550,70 @@ struct OctetRaw<0> {
   }
 };
 
-// Unnormalised masses of 8 tokens (see SeqPlan for the two forms): residual
-// mode r_v = max(0, e^p_v - kappa e^q_v) = Sp * max(0, p_v - q_v); bonus mode
-// r_v = e^p_v = Sp * p_v. Tokens at or beyond V (value -inf) get 0.
+// 2^x - 1 for x <= 0 (x may be -inf), to a few ulp relative: on [-1/2, 0]
+// the Taylor polynomial of e^(x ln 2) - 1 to degree 7, in Horner form (its
+// terms alternate, so the truncation error is below the first omitted term,
+// (ln 2 / 2)^8 / 8!, under 2^-25 relative); below -1/2 exp2(x) - 1, which is
+// at least 0.29 in magnitude there, so the subtraction costs at most 2 bits.
+__device__ __forceinline__ float expm1_2(float x) {
+  // (ln 2)^k / k!
+  constexpr float c1 = 0.69314718055994531f, c2 = 0.24022650695910071f, c3 = 0.055504108664821576f,
+                  c4 = 0.0096181291076284772f, c5 = 0.0013333558146428443f, c6 = 1.5403530393381606e-4f,
+                  c7 = 1.5252733804059838e-5f;
+  float p = fmaf(c7, x, c6);
+  p = fmaf(p, x, c5);
+  p = fmaf(p, x, c4);
+  p = fmaf(p, x, c3);
+  p = fmaf(p, x, c2);
+  p = fmaf(p, x, c1);
+  const float poly = p * x;
+  const float e = hw_exp2(x) - 1.0f;
+  return (x >= -0.5f) ? poly : e;
+}
+
+// Terms of one token in the exact pass (form 1; see SeqPlan): r = max(0, d),
+// q = e_q where p >= q (else 0), d = e_p - e_q, all up to the plan's factor.
+// w = log2(q_v / p_v) is formed from the logit difference, so 1 - 2^w keeps
+// its relative accuracy however close p_v and q_v are.
+struct ExactTerm {
+  float r, q, d;
+};
+__device__ __forceinline__ ExactTerm exact_term(float xt, float xd, const SeqPlan& P) {
+  const float w = fmaf(xd - xt, P.kl, P.dt);
+  float ea = fmaf(xt, P.kl, -P.cp) + fmaxf(w, 0.0f);  // log2 of max(e_p, e_q); NaN iff x_t = -inf < x_d
+  if (!(ea == ea)) ea = fmaf(xd, P.kl, -P.cq) - P.cq_lo;
+  const float e = hw_exp2(ea);
+  const float em = expm1_2(fminf(-fabsf(w), 0.0f));  // in [-1, 0]; a NaN w (both -inf) gives 0
+  const float mag = -e * em;                          // |e_p - e_q|
+  const bool pos = w <= 0.0f;                         // p_v >= q_v
+  ExactTerm t;
+  t.r = pos ? mag : 0.0f;
+  t.q = pos ? fmaf(e, em, e) : 0.0f;
+  t.d = pos ? mag : -mag;
+  return t;
+}
+
+// Unnormalised masses of 8 tokens (see SeqPlan for the forms): residual
+// mode r_v = max(0, e^p_v - kappa e^q_v) = F Sp * max(0, p_v - q_v); exact
+// mode the same residual from exact_term, less g times e^q_v where p_v >= q_v
+// (the first-order correction of the normalisers' ratio); bonus mode
+// r_v = e^p_v = F Sp * p_v. Tokens at or beyond V (value -inf) get 0.
 template <int MODE, int FORM>
 __device__ __forceinline__ void mass8(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P, float (&r)[8]) {
+  if constexpr (MODE == kModeExact && FORM == 1) {
+    const float gf = (float)P.g;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const ExactTerm t = exact_term(xt[k], xd[k], P);
+      r[k] = fmaxf(fmaf(-gf, t.q, t.r), 0.0f);
+    }
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     if constexpr (FORM == 1) {
       const float ep = hw_exp2(fmaf(xt[k], P.kl, -P.cp));
-      if constexpr (MODE == kModeResidual) {
+      if constexpr (MODE != kModeBonus) {
         const float eq = hw_exp2(fmaf(xd[k], P.kl, -P.cq));
         r[k] = fmaxf(fmaf(eq, P.corr, ep - eq), 0.0f);
       } else {
@@ -564,7 +621,7 @@ __device__ __forceinline__ void mass8(const float (&xt)[8], const float (&xd)[8]
       }
     } else {
       const float ep = hw_exp2((xt[k] - P.mp) * P.kl);
-      if constexpr (MODE == kModeResidual) {
+      if constexpr (MODE != kModeBonus) {
         const float eq = hw_exp2((xd[k] - P.mq) * P.kl);
         float d = fmaf(-eq, P.kap_hi, ep);
         d = fmaf(-eq, P.kap_lo, d);
@@ -610,7 +667,12 @@ __device__ __forceinline__ void load_octet(const char* row, int64_t oct, int V, 
 // Masses of 8 tokens in the draw's mode and the plan's form.
 __device__ __forceinline__ void mass8_of(const float (&xt)[8], const float (&xd)[8], int mode, const SeqPlan& P,
                                          float (&r)[8]) {
-  if (mode == kModeResidual) {
+  if (mode == kModeExact) {
+    if (P.form == 1)
+      mass8<kModeExact, 1>(xt, xd, P, r);
+    else
+      mass8<kModeResidual, 0>(xt, xd, P, r);
+  } else if (mode == kModeResidual) {
     if (P.form == 1)
       mass8<kModeResidual, 1>(xt, xd, P, r);
     else
@@ -639,7 +701,7 @@ __device__ __forceinline__ void step_octet_masses(const char* trow, const char* 
       if (oct < noct) {
         float xt[8], xd[8];
         load_octet<TD>(trow, oct, V, xt);
-        if (mode == kModeResidual) load_octet<DD>(drow, oct, V, xd);
+        if (mode != kModeBonus) load_octet<DD>(drow, oct, V, xd);
         mass8_of(xt, xd, mode, P, rr[j]);
       } else {
 #pragma unroll
@@ -650,7 +712,7 @@ __device__ __forceinline__ void step_octet_masses(const char* trow, const char* 
   }
   OctetIn<TD> t[kU2];
   OctetIn<DD> d[kU2];
-  if (mode == kModeResidual) {
+  if (mode != kModeBonus) {
 #pragma unroll
     for (int j = 0; j < kU2; ++j) {
       const int64_t oct = s * kStepOctets + kWave * j + lane;
@@ -667,7 +729,7 @@ __device__ __forceinline__ void step_octet_masses(const char* trow, const char* 
     if (oct < noct) {
       float xt[8], xd[8];
       t[j].to_float(oct, V, xt);
-      if (mode == kModeResidual) d[j].to_float(oct, V, xd);
+      if (mode != kModeBonus) d[j].to_float(oct, V, xd);
       mass8_of(xt, xd, mode, P, rr[j]);
     } else {
 #pragma unroll
@@ -726,7 +788,7 @@ __device__ __forceinline__ double direct_step_mass(const char* trow, const char*
       if (oct < noct) {
         float xt[8], xd[8], rr[8];
         load_octet<TD>(trow, oct, V, xt);
-        if (MODE == kModeResidual) load_octet<DD>(drow, oct, V, xd);
+        if (MODE != kModeBonus) load_octet<DD>(drow, oct, V, xd);
         mass8_of(xt, xd, MODE, P, rr);
         lacc += (double)sum8(rr);
       }
@@ -832,6 +894,83 @@ __device__ __forceinline__ void gather_steps(const SampleLaunch& A, int b, const
   }
 }
 
+// The exact pass over step s of the draw row pair by one wave (every lane
+// gets the sums): the residual mass, the q-mass of its positive terms and the
+// signed sum of e_p - e_q over the step's tokens (all with the plan's factor
+// F Sp), from exact_term, octet sums in fp32 as in the draw's scan. A rare
+// path: octets are loaded one at a time, which keeps its registers (and so
+// the finish kernel's) within the streaming loop's budget.
+template <int TD, int DD>
+__device__ __forceinline__ void exact_step_sums(const char* trow, const char* drow, int64_t s, int64_t noct, int V,
+                                                const SeqPlan& P, int lane, double& m, double& q, double& d) {
+  double lm = 0.0, lq = 0.0, ld = 0.0;
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float xt[8], xd[8], rm[8], rq[8], rd[8];
+      load_octet<TD>(trow, oct, V, xt);
+      load_octet<DD>(drow, oct, V, xd);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const ExactTerm e = exact_term(xt[k], xd[k], P);
+        rm[k] = e.r;
+        rq[k] = e.q;
+        rd[k] = e.d;
+      }
+      lm += (double)sum8(rm);
+      lq += (double)sum8(rq);
+      ld += (double)sum8(rd);
+    }
+  }
+  m = wave_sum(lm);
+  q = wave_sum(lq);
+  d = wave_sum(ld);
+}
+
+// The exact pass of sequence b by every wave of the workgroup (wave w takes
+// steps w, w + kFinWaves, ...): step residual masses into stot, the q-masses
+// of their positive terms into sq, each wave's signed sum of e_p - e_q into
+// sh_sd[w].
+template <int TD, int DD>
+__device__ __forceinline__ void exact_pass(const SampleLaunch& A, int b, const SeqPlan& P, double* stot, double* sq,
+                                           double* sh_sd) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
+  const char* drow = A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b;
+  const int64_t noct = ((int64_t)A.V + 7) / 8;
+  double sd = 0.0;
+  for (int s = w; s < A.ns2; s += kFinWaves) {
+    double m, q, d;
+    exact_step_sums<TD, DD>(trow, drow, s, noct, A.V, P, lane, m, q, d);
+    if (lane == 0) {
+      stot[s] = m;
+      sq[s] = q;
+    }
+    sd += d;
+  }
+  if (lane == 0) sh_sd[w] = sd;
+}
+
+// First-order correction of the exact pass, by one wave. Sum_v (e_p - e_q)
+// over the row is F Sp (1 - 2^-eta) when the ratio of the normalisers the
+// plan used is off by 2^eta (exactly 0 for exact normalisers); the residual
+// with the corrected ratio is r_v - g e_q,v where p_v >= q_v, g = 2^eta - 1
+// (terms that change sign under the correction are of second order). Corrects
+// the step masses in place and returns g; `total` gets their sum.
+__device__ __forceinline__ double exact_correct(double sd, double ptot, double* stot, const double* sq, int ns2,
+                                                int lane, double& total) {
+  const double g = sd / (ptot - sd);
+  double acc = 0.0;
+  for (int s = lane; s < ns2; s += kWave) {
+    const double m = fmax(stot[s] - g * sq[s], 0.0);
+    stot[s] = m;
+    acc += m;
+  }
+  total = wave_sum(acc);
+  return g;
+}
+
 // Sum of arr[0..len) by one wave, in a fixed order.
 __device__ __forceinline__ double wave_total(const double* arr, int len, int lane) {
   double acc = 0.0;
@@ -926,7 +1065,7 @@ template <int TD, int DD, bool kBatch = true>
 __device__ __forceinline__ int rescan_step(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int ss, double t,
                                            double acc, int lane) {
   const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
-  const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
+  const char* drow = (mode != kModeBonus) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   float rr[kU2][8];
   step_octet_masses<TD, DD, kBatch>(trow, drow, ss, noct, A.V, mode, P, lane, rr);
@@ -950,7 +1089,7 @@ __device__ __forceinline__ void write_outputs(const SampleLaunch& A, int b, cons
       float py = __builtin_nanf("");
       if (mode == kModeBonus) {
         const float x = load_elem<TD>(A.tgt + (int64_t)b * A.t_seq_b + (int64_t)n * A.t_row_b, y);
-        py = (float)(exp2(((double)x - (double)P.mp) * (double)P.kl) / P.sp);
+        py = (float)(exp2((double)x * (double)P.kl - P.ct) / P.sp);
       }
       A.out_py[b] = py;
     }
@@ -984,7 +1123,10 @@ __device__ __forceinline__ void draw_and_write(const SampleLaunch& A, int b, con
   // wave_find returns -1 only if every mass is zero, which valid rows rule
   // out; clamp anyway so that no index can leave the arrays.
   const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
-  const int y = rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane);
+  // the exact pass's terms take more registers: its (rare) rescan loads one
+  // octet at a time
+  const int y = (mode == kModeExact) ? rescan_step<TD, DD, false>(A, b, P, mode, ss, t, acc, lane)
+                                     : rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane);
   // (6) outputs
   write_outputs<TD>(A, b, P, mode, y, total, lane, xi);
 }
@@ -994,6 +1136,7 @@ __device__ __forceinline__ void draw_and_write(const SampleLaunch& A, int b, con
 // target row n and (n < gamma) draft row n. nst: rows with statistics.
 __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, bool tv, float kl, float ug,
                                              const RowStat& tn, const RowStat& dn) {
+#pragma clang fp contract(off)
   bool valid = tv && (n == G || code_n == 0) && ug >= 0.0f && ug < 1.0f && n < nst;
   if (n == G) valid = valid && tn.valid;
   SeqPlan Q;
@@ -1002,35 +1145,43 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
   Q.n = n;
   Q.mode = (n == G) ? kModeBonus : kModeResidual;
   Q.kl = kl;
+  Q.ct = tn.c;
   Q.mp = tn.m;
   Q.sp = tn.s;
+  Q.g = 0.0;
   const double kld = (double)kl;
-  const double cp = (double)Q.mp * kld;  // exact product of two floats
-  Q.cp = (float)cp;
-  const double dp = cp - (double)Q.cp;
+  Q.cp = (float)tn.c;  // exact for the integer shifts of the statistics pass
+  const double dp = tn.c - (double)Q.cp;
   Q.fscale = exp2(dp);
   // the shifts must round by less than half a log2 unit: |c| < 2^24
-  bool fma_ok = fabs(cp) < 0x1p24;
+  bool fma_ok = fabs(tn.c) < 0x1p24;
+  // subtract form: e_p = exp2((x_t - mp) * kl) = p_v * sp * Fp
+  const double Fp = exp2(tn.c - (double)tn.m * kld);
   if (n < G) {
     Q.mq = dn.m;
     Q.sq = dn.s;
-    const double kap = Q.sp / Q.sq;
+    const double cqx = dn.c - log2(Q.sp / Q.sq) - dp;
+    Q.cq = (float)cqx;
+    Q.cq_lo = (float)(cqx - (double)Q.cq);
+    Q.corr = (float)((cqx - (double)Q.cq) * 0.69314718055994530942);
+    Q.dt = (float)((double)Q.cp - cqx);
+    fma_ok = fma_ok && fabs(cqx) < 0x1p24;
+    const double Fq = exp2(dn.c - (double)dn.m * kld);
+    const double kap = (Q.sp * Fp) / (Q.sq * Fq);
     Q.kap_hi = (float)kap;
     Q.kap_lo = (float)(kap - (double)Q.kap_hi);
-    const double cq = (double)Q.mq * kld - log2(kap) - dp;
-    Q.cq = (float)cq;
-    Q.corr = (float)((cq - (double)Q.cq) * 0.69314718055994530942);
-    fma_ok = fma_ok && fabs(cq) < 0x1p24;
   } else {
     Q.mq = 0.0f;
     Q.sq = 1.0;
     Q.kap_hi = 0.0f;
     Q.kap_lo = 0.0f;
     Q.cq = 0.0f;
+    Q.cq_lo = 0.0f;
     Q.corr = 0.0f;
+    Q.dt = 0.0f;
   }
   Q.form = fma_ok ? 1 : 0;
-  if (!fma_ok) Q.fscale = 1.0;
+  if (!fma_ok) Q.fscale = Fp;
   return Q;
 }
 
@@ -1042,13 +1193,17 @@ template <int TD, int DD>
 // At most 128 VGPRs, so that two 8-wave workgroups fit one CU.
 __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))) void sv_finish_kernel(
     SampleLaunch A) {
+  __shared__ double rC[kMaxRows];
   __shared__ float rM[kMaxRows];
   __shared__ double rS[kMaxRows];
   __shared__ int rV[kMaxRows];
   __shared__ SeqPlan sP;
   __shared__ double sh_total;
+  __shared__ double sh_g;
   __shared__ int sh_last;
+  __shared__ double sh_sd[kFinWaves];
   __shared__ double sh_steps[kLdsSteps];  // step masses when the row has at most kLdsSteps steps
+  __shared__ double sh_q[kLdsSteps];      // exact pass: q-mass of each step's positive residual
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loops over steps stay scalar
@@ -1101,9 +1256,10 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       const int t = w + k * kFinWaves;
       if (t >= nrows) break;
       const int pos = t <= G ? t : t - G - 1;
-      RowStat rs{0.0f, 0.0, 0};
+      RowStat rs{0.0, 0.0f, 0.0, 0};
       if (pos < nst) rs = merge_row_one(q[k], have[k], kl, tv);
       if (lane == 0) {
+        rC[t] = rs.c;
         rM[t] = rs.m;
         rS[t] = rs.s;
         rV[t] = rs.valid;
@@ -1123,6 +1279,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       }
       if (pos >= nst) {
         if (lane == 0) {
+          rC[t] = 0.0;
           rM[t] = 0.0f;
           rS[t] = 0.0;
           rV[t] = 0;
@@ -1131,6 +1288,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       }
       const RowStat rs = merge_row(A.part + ((int64_t)b * A.per_seq + base) * kWaves, nrec, kl, tv, lane);
       if (lane == 0) {
+        rC[t] = rs.c;
         rM[t] = rs.m;
         rS[t] = rs.s;
         rV[t] = rs.valid;
@@ -1147,7 +1305,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       const int i = lane;
       float pxo = __builtin_nanf(""), qxo = __builtin_nanf("");
       if (i < nst) {
-        const RowStat ts{rM[i], rS[i], rV[i]}, ds{rM[G + 1 + i], rS[G + 1 + i], rV[G + 1 + i]};
+        const RowStat ts{rC[i], rM[i], rS[i], rV[i]}, ds{rC[G + 1 + i], rM[G + 1 + i], rS[G + 1 + i], rV[G + 1 + i]};
         const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv);
         code = ao.code;
         pxo = ao.px;
@@ -1162,8 +1320,9 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     const int n = stop ? (__ffsll((long long)stop) - 1) : G;
     const int code_n = __builtin_amdgcn_readlane(code, n < G ? n : 0);
     if (lane == 0) {
-      const RowStat tn{rM[n], rS[n], rV[n]};
-      const RowStat dn = (n < G) ? RowStat{rM[G + 1 + n], rS[G + 1 + n], rV[G + 1 + n]} : RowStat{0.0f, 1.0, 0};
+      const RowStat tn{rC[n], rM[n], rS[n], rV[n]};
+      const RowStat dn =
+          (n < G) ? RowStat{rC[G + 1 + n], rM[G + 1 + n], rS[G + 1 + n], rV[G + 1 + n]} : RowStat{0.0, 0.0f, 1.0, 0};
       sP = make_plan(n, code_n, G, nst, tv, kl, A.uniforms[(int64_t)b * (G + 1) + G], tn, dn);
     }
   }
@@ -1212,7 +1371,30 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     if (lane == 0) sh_total = tot;
   }
   __syncthreads();
-  if (!(sh_total > 0.0) && mode == kModeResidual) {
+  SeqPlan Pd = P;
+  if (mode == kModeResidual && P.form == 1 && !(sh_total >= kExactBelow * P.sp * P.fscale)) {
+    // (4b) A small residual: the difference p - q cancels, and an error of
+    // the normalisers' ratio weighs 1 / (residual mass) on it. The exact pass
+    // streams the row pair again, forms each difference from the logit
+    // difference and corrects the ratio from the signed sum of e_p - e_q.
+    double* sq = lds_steps ? sh_q : A.stepq + (int64_t)b * A.ns2;
+    exact_pass<TD, DD>(A, b, P, stot, sq, sh_sd);
+    __syncthreads();
+    if (w == 0) {
+      double sd = 0.0;
+      for (int k = 0; k < kFinWaves; ++k) sd += sh_sd[k];
+      double tot;
+      const double g = exact_correct(sd, P.sp * P.fscale, stot, sq, A.ns2, lane, tot);
+      if (lane == 0) {
+        sh_total = tot;
+        sh_g = g;
+      }
+    }
+    __syncthreads();
+    mode = kModeExact;
+    Pd.g = sh_g;
+  }
+  if (!(sh_total > 0.0) && mode != kModeBonus) {
     // Nothing left after the rejection (p_n == q_n up to rounding): draw from p_n.
     mode = kModeBonus;
     if (lds_steps)
@@ -1228,7 +1410,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
   const double total = sh_total;
 
-  draw_and_write<TD, DD>(A, b, P, mode, stot, total, xi);
+  draw_and_write<TD, DD>(A, b, Pd, mode, stot, total, xi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1478,11 +1660,16 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       Q.mp = mp;
       Q.mq = 0.0f;
       Q.kap_hi = Q.kap_lo = 0.0f;
+      // the step masses are sums of exp2(x * kl - Ms): in the FMA form Ms is a
+      // float (a lane's shift), so e_p = exp2(fma(x, kl, -cp)) with cp = Ms; in
+      // the subtract form Ms = mp * kl
+      Q.ct = Ms;
       Q.cp = sub ? 0.0f : (float)Ms;
-      Q.cq = Q.corr = 0.0f;
-      Q.fscale = sub ? 1.0 : exp2((double)mp * (double)kl - Ms);  // step masses are F * exp2((x - mp) * kl)
-      Q.sp = total / Q.fscale;
+      Q.cq = Q.corr = Q.cq_lo = Q.dt = 0.0f;
+      Q.fscale = 1.0;
+      Q.sp = total;
       Q.sq = 1.0;
+      Q.g = 0.0;
       sP = Q;
       sh_total = total;
     }
@@ -1521,6 +1708,7 @@ __device__ __forceinline__ RowStat small_row_stat(const float (&x)[PL], float kl
   }
   s = wave_sum(s);
   RowStat r;
+  r.c = (double)m * (double)kl;
   r.m = m;
   r.s = s;
   r.valid = tv && __builtin_isfinite(s) && s > 0.0 && __builtin_isfinite(m);
@@ -1601,11 +1789,13 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
     }
   }
   // slot t's statistics: in every lane for a uniform t, from lane j % 64 for a per-lane j
+  // the row's reference is its maximum m: shift m * kl (exact in fp64)
+  auto stat = [&](float m, double s, int v) { return RowStat{(double)m * (double)kl, m, s, v}; };
   auto slot_uniform = [&](int t) {
     const int l = t & (kWave - 1);
-    if (t < kWave) return RowStat{readlane_f32(m0, l), readlane_f64(s0, l), __builtin_amdgcn_readlane(v0, l)};
-    if (t < 2 * kWave) return RowStat{readlane_f32(m1, l), readlane_f64(s1, l), __builtin_amdgcn_readlane(v1, l)};
-    return RowStat{readlane_f32(m2, l), readlane_f64(s2, l), __builtin_amdgcn_readlane(v2, l)};
+    if (t < kWave) return stat(readlane_f32(m0, l), readlane_f64(s0, l), __builtin_amdgcn_readlane(v0, l));
+    if (t < 2 * kWave) return stat(readlane_f32(m1, l), readlane_f64(s1, l), __builtin_amdgcn_readlane(v1, l));
+    return stat(readlane_f32(m2, l), readlane_f64(s2, l), __builtin_amdgcn_readlane(v2, l));
   };
   // accept tests (lane i: position i; target slot i is its own) and the first stop
   const int j = G + 1 + lane;  // this lane's draft slot
@@ -1615,9 +1805,8 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
   const int dv0 = __shfl(v0, jl, kWave), dv1 = __shfl(v1, jl, kWave), dv2 = __shfl(v2, jl, kWave);
   int code = 1;
   if (lane < G) {
-    const RowStat ts{m0, s0, v0};
-    const RowStat ds = (j < kWave) ? RowStat{dm0, ds0, dv0}
-                                   : (j < 2 * kWave ? RowStat{dm1, ds1, dv1} : RowStat{dm2, ds2, dv2});
+    const RowStat ts = stat(m0, s0, v0);
+    const RowStat ds = (j < kWave) ? stat(dm0, ds0, dv0) : (j < 2 * kWave ? stat(dm1, ds1, dv1) : stat(dm2, ds2, dv2));
     const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv);
     code = ao.code;
     if (A.diag_px) A.diag_px[(int64_t)b * G + lane] = ao.px;
@@ -1627,7 +1816,7 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
   const int n = stop ? (__ffsll((long long)stop) - 1) : G;
   const int code_n = __builtin_amdgcn_readlane(code, n < G ? n : 0);
   const RowStat tn = slot_uniform(n);
-  const RowStat dn = (n < G) ? slot_uniform(G + 1 + n) : RowStat{0.0f, 1.0, 0};
+  const RowStat dn = (n < G) ? slot_uniform(G + 1 + n) : RowStat{0.0, 0.0f, 1.0, 0};
   const SeqPlan P = make_plan(n, code_n, G, G + 1, tv, kl, A.uniforms[(int64_t)b * (G + 1) + G], tn, dn);
   if (!P.valid) {
     write_invalid(A, b, lane, 0, kWave);
@@ -1651,10 +1840,10 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
       load_octet<TD>(trow, lane, A.V, xt);
       if (mode == kModeResidual) load_octet<DD>(drow, lane, A.V, xd);
     }
-    auto step_total = [&](int m) -> double {
+    auto step_total = [&](int m, const SeqPlan& Q) -> double {
       double lacc = 0.0;
       if (have) {
-        mass8_of(xt, xd, m, P, rr[0]);
+        mass8_of(xt, xd, m, Q, rr[0]);
         lacc += (double)sum8(rr[0]);
       } else {
 #pragma unroll
@@ -1662,25 +1851,47 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
       }
       return wave_sum(lacc);
     };
-    double total = step_total(mode);
-    if (!(total > 0.0) && mode == kModeResidual) {
+    SeqPlan Pd = P;
+    double total = step_total(mode, Pd);
+    if (mode == kModeResidual && P.form == 1 && !(total >= kExactBelow * P.sp * P.fscale)) {
+      // a small residual: the exact pass (see the finish kernel), here from
+      // the values already in registers
+      float rd[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rd[k] = have ? exact_term(xt[k], xd[k], P).d : 0.0f;
+      const double d = wave_sum((double)sum8(rd));
+      Pd.g = d / (P.sp * P.fscale - d);
+      mode = kModeExact;
+      total = step_total(mode, Pd);  // the corrected terms, the same ones the scan takes
+    }
+    if (!(total > 0.0) && mode != kModeBonus) {
       // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
       mode = kModeBonus;
-      total = step_total(mode);
+      total = step_total(mode, Pd);
     }
     const int y = scan_step<1>(rr, 0, (double)P.ug * total, 0.0, lane);
-    write_outputs<TD>(A, b, P, mode, y, total, lane, xi);
+    write_outputs<TD>(A, b, Pd, mode, y, total, lane, xi);
   } else {
+    SeqPlan Pd = P;
     double total = (mode == kModeResidual) ? direct_step_mass<TD, DD, kModeResidual>(trow, drow, 0, noct, A.V, P, lane)
                                            : direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
-    if (!(total > 0.0) && mode == kModeResidual) {
+    if (mode == kModeResidual && P.form == 1 && !(total >= kExactBelow * P.sp * P.fscale)) {
+      // a small residual: the exact pass (see the finish kernel) over the one step
+      double m, q, d;
+      exact_step_sums<TD, DD>(trow, drow, 0, noct, A.V, P, lane, m, q, d);
+      Pd.g = d / (P.sp * P.fscale - d);
+      mode = kModeExact;
+      // the corrected terms, the same ones the rescan takes
+      total = direct_step_mass<TD, DD, kModeExact>(trow, drow, 0, noct, A.V, Pd, lane);
+    }
+    if (!(total > 0.0) && mode != kModeBonus) {
       // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
       mode = kModeBonus;
       total = direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
     }
     const double t = (double)P.ug * total;
-    const int y = rescan_step<TD, DD>(A, b, P, mode, 0, t, 0.0, lane);
-    write_outputs<TD>(A, b, P, mode, y, total, lane, xi);
+    const int y = rescan_step<TD, DD>(A, b, Pd, mode, 0, t, 0.0, lane);
+    write_outputs<TD>(A, b, Pd, mode, y, total, lane, xi);
   }
 }
 

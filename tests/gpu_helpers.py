@@ -127,6 +127,7 @@ class Tally:
         self.flag_draw = 0
         self.fail = []
         self.max_prob_rel = 0.0
+        self.max_mass_rel = 0.0
 
     @property
     def flagged(self):
@@ -189,17 +190,24 @@ def check_sample_seq(tally: Tally, b: int, Lt, Ld, x, u, T, gpu, lb=None):
         return o
     # probabilities
     if "p_x" in gpu:
+        # a NaN (or inf) diagnostic of a valid sequence fails: _rel is then NaN
+        # or inf, and only a finite value within the tolerance passes
         for i in range(min(n + 1, G)):
             for key, ref in (("p_x", o.p_x[i]), ("q_x", o.q_x[i])):
-                if float(ref) >= 1e-30 or float(gpu[key][b, i]) >= 1e-30:
-                    r = _rel(gpu[key][b, i], ref)
-                    tally.max_prob_rel = max(tally.max_prob_rel, r)
-                    if r > PROB_RTOL:
-                        tally.fail.append((b, key, i, float(gpu[key][b, i]), float(ref)))
-        r = _rel(gpu["resid_mass"][b], o.resid_mass)
-        tally.max_prob_rel = max(tally.max_prob_rel, r)
-        if r > PROB_RTOL and not o.fallback:
-            tally.fail.append((b, "resid_mass", float(gpu["resid_mass"][b]), o.resid_mass))
+                g = float(gpu[key][b, i])
+                if float(ref) >= 1e-30 or not (g < 1e-30):
+                    r = _rel(g, ref)
+                    if np.isfinite(r):
+                        tally.max_prob_rel = max(tally.max_prob_rel, r)
+                    if not (np.isfinite(g) and r <= PROB_RTOL):
+                        tally.fail.append((b, key, i, g, float(ref)))
+        g = float(gpu["resid_mass"][b])
+        r = _rel(g, o.resid_mass)
+        if np.isfinite(r):
+            tally.max_prob_rel = max(tally.max_prob_rel, r)
+            tally.max_mass_rel = max(tally.max_mass_rel, r)
+        if not (np.isfinite(g) and r <= PROB_RTOL) and not o.fallback:
+            tally.fail.append((b, "resid_mass", g, o.resid_mass))
     return o
 
 

@@ -38,18 +38,22 @@ int main() {
   std::printf(", \"layout\": [[%lld,%lld,%lld,%lld,%lld],[%lld],[%lld]]", (long long)L1.off_part, (long long)L1.off_step,
               (long long)L1.off_reach, (long long)L1.off_done, (long long)L1.total, (long long)L2.total,
               (long long)L3.total);
-  int nch, cu;
+  int nch, cu, nch2, cu2;
   split_row(128256, 2, 136 << 10, &nch, &cu);
-  std::printf(", \"split\": [%d,%d]", nch, cu);
+  split_row(128256, 2, chunk_bytes_for(1116358656LL), &nch2, &cu2, kBatchUnits);
+  std::printf(", \"split\": [%d,%d,%d,%d]", nch, cu, nch2, cu2);
+  const SampleLayout L4 = sample_layout(3, 2, 5000000);
+  std::printf(", \"stepq\": [%lld,%lld,%lld,%lld]", (long long)L4.off_step, (long long)L4.off_stepq,
+              (long long)L4.off_reach, (long long)(L1.off_stepq - L1.off_step));
   // the largest shapes the C ABI accepts (B 2^24, gamma 64, V 2^30, N 1024):
   // every size is computed in 64-bit arithmetic without overflow
   const long long Bm = 1LL << 24, Vm = 1LL << 30;
   const SampleLayout Lm = sample_layout(Bm, 64, Vm);
   const TreeLayout Tm = tree_layout(Bm, 1024, Vm);
   int nchm, cum;
-  split_row(Vm, 4, chunk_bytes_for(Bm * (129LL * Vm * 4)), &nchm, &cum);
+  split_row(Vm, 4, chunk_bytes_for((Bm / 2) * (129LL * Vm * 4)), &nchm, &cum, kBatchUnits);
   std::printf(", \"max\": [%lld,%lld,%lld,%d,%d,%d,%d,%lld]", (long long)Lm.total, (long long)Tm.total,
-              (long long)chunk_bytes_for(Bm * (129LL * Vm * 4)), nchm, cum, finish_parts(Bm, draw_steps(Vm)),
+              (long long)chunk_bytes_for((Bm / 2) * (129LL * Vm * 4)), nchm, cum, finish_parts(Bm, draw_steps(Vm)),
               early_tail_start(Bm, 64, Vm, 4, 4), (long long)draw_steps(Vm));
   std::printf("}\n");
   return 0;
@@ -77,10 +81,11 @@ def plan():
 
 
 def test_chunk_bytes(plan):
-    # total / 8192 work units, clamped to [16 KB, 256 KB], rounded up to 4 KB (256 threads x 16 B)
+    # total / 8192 work units, clamped to [16 KB, 256 KB], rounded up to 16 KB
+    # (one batch: 256 threads x 4 units x 16 B), so chunks start on batch boundaries
     for total, got in zip([1 << 20, 36866560, 1116358656, 4194328576, 1 << 40], plan["chunk"]):
         c = min(max(total // 8192, 16 << 10), 256 << 10)
-        assert got == -(-c // 4096) * 4096, (total, got)
+        assert got == -(-c // 16384) * 16384, (total, got)
 
 
 def test_finish_parts(plan):
@@ -127,8 +132,18 @@ def test_workspace_layout(plan):
 
 def test_row_split(plan):
     # a 256 KB row in chunks of at most 136 KB: two chunks of 4 KB-multiple units covering the row
-    nch, cu = plan["split"]
+    nch, cu, nch2, cu2 = plan["split"]
     assert nch == 2 and cu % 256 == 0 and nch * cu * 16 >= 128256 * 2 and (nch - 1) * cu * 16 < 128256 * 2
+    # the statistics pass's split (configuration 3's call): 16 KB-multiple chunks covering the row
+    assert cu2 % 1024 == 0 and nch2 * cu2 * 16 >= 128256 * 2 and (nch2 - 1) * cu2 * 16 < 128256 * 2
+    assert cu2 * 16 <= 144 << 10
+
+
+def test_step_q_masses(plan):
+    # the exact pass's per-step q-masses get workspace only when the steps exceed LDS (V > 2048 * 2048)
+    step, stepq, reach, small = plan["stepq"]
+    steps = -(-5000000 // 2048)
+    assert stepq - step >= 3 * steps * 8 and reach - stepq >= 3 * steps * 8 and small == -(-64 * 16 * 8 // 256) * 256
 
 
 def test_largest_shapes(plan):
@@ -141,5 +156,5 @@ def test_largest_shapes(plan):
     # partials of (2 gamma + 1) rows of up to V * 4 / 16 KB chunks, plus the step masses
     assert lay_total >= B * (2 * G + 1) * (V * 4 // (16 << 10)) * 4 * 16 + B * steps * 8
     assert lay_total < 1 << 62 and tree_total >= B * 1024 * (V * 4 // (16 << 10)) * 16
-    assert (16 << 10) <= chunk <= (256 << 10) and cu % 256 == 0 and nch * cu * 16 >= V * 4
+    assert (16 << 10) <= chunk <= (256 << 10) and cu % 1024 == 0 and nch * cu * 16 >= V * 4
     assert parts == 1 and 0 <= tail <= G
