@@ -124,7 +124,6 @@ static SampleLaunch plan_sample(const SampleArgs& a, bool early = false) {
   char* ws = (char*)a.ws;
   L.part = (RowPartial*)(ws + lay.off_part);
   L.steptot = (double*)(ws + lay.off_step);
-  L.stepq = (double*)(ws + lay.off_stepq);
   L.done = (int32_t*)(ws + lay.off_done);
   return L;
 }

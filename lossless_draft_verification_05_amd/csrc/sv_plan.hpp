@@ -26,13 +26,8 @@ constexpr double kEarlyAlpha = 0.7;             // acceptance rate assumed when 
 constexpr double kEarlyLaunchBytes = 64e6;      // bytes moved in about the time one extra launch costs
 constexpr int64_t kFinTargetWGs = 256;          // finish: split sequences over parts up to one workgroup per CU
 constexpr int64_t kBatchUnits = (int64_t)kThreads * kU1;  // 1024 units = 16 KB: one batch of every thread
-constexpr double kExactBelow = 0.125;  // residual mass (share of p's) below which the exact pass runs
 
-// kModeExact: the residual of the exact pass (after a first pass found its mass
-// below kExactBelow), taken as e_p * (1 - 2^w) with w = log2(q / p) formed from
-// the logit difference, and corrected to first order for the error of the
-// normalisers' ratio (SeqPlan::g).
-enum : int { kModeResidual = 0, kModeBonus = 1, kModeExact = 2 };
+enum : int { kModeResidual = 0, kModeBonus = 1 };
 
 // Partial statistics of one wave's share of one chunk of one logits row
 // (stats pass):
@@ -56,19 +51,16 @@ struct RowPartial {
 // fp64). Mass of token v of the drawn distribution, up to one positive factor
 // F * sp per sequence:
 //  form 1 (shifts folded into one FMA each):
-//    e_p = exp2(fma(x_t, kl, -cp)), e_q = exp2(fma(x_d, kl, -cq)),
-//    r = max(0, fma(e_q, corr, e_p - e_q)) after a rejection, r = e_p otherwise.
-//    cp = fp32(ct) (exact when ct is an integer); cq = fp32(cqx) with
-//    cqx = cd - log2(sp / sq) - (ct - cp), so e_q carries the ratio of the
-//    normalisers; corr = (cqx - cq) * ln 2 removes, to first order, the
-//    rounding of cq. r = F * sp * max(0, p - q) with F = exp2(ct - cp) (fscale).
-//  exact pass (form 1 only, kModeExact): w = fma(x_d - x_t, kl, dt) =
-//    log2(q_v / p_v) with dt = cp - cqx; e = e_p where w <= 0, else e_q taken
-//    as exp2(e_p's exponent + w) (as exp2(fma(x_d, kl, -cq) - cq_lo) where the
-//    target logit is -inf); d = e_p - e_q = -e * expm1_2(-|w|) with the sign of
-//    -w, its magnitude exact to a few ulp however close p and q are;
-//    r = max(0, d) - g * (e_q where d > 0), g the first-order correction of
-//    the normalisers' ratio from the signed sum of d over the row.
+//    e_p = exp2(fma(x_t, kl, -cp)) with cp = fp32(ct) (exact when ct is an
+//    integer), F = exp2(ct - cp) (fscale); r = e_p = F sp p_v for the bonus row.
+//    After a rejection: w = fma(x_d - x_t, kl, dt) = log2(q_v / p_v) with
+//    dt = cp - cqx, cqx = cd - log2(sp / sq) - (ct - cp) (e_q = F sp q_v =
+//    exp2(x_d * kl - cqx)); e = e_p where w <= 0, else e_q, taken as
+//    exp2(e_p's exponent + w) (as exp2(fma(x_d, kl, -cq) - cq_lo), cq + cq_lo
+//    = cqx, where the target logit is -inf); |e_p - e_q| = -e * expm1_2(-|w|),
+//    exact to a few ulp however close p and q are, and r = that where p >= q,
+//    less g * e_q, g the first-order correction of the normalisers' ratio from
+//    the signed sum of e_p - e_q over the row. r = F sp * max(0, p - q).
 //  form 0 (used when a shift is 2^24 or more in magnitude, where its fp32
 //  rounding would be half a log2 unit or more):
 //    e_p = exp2((x_t - mp) * kl), e_q = exp2((x_d - mq) * kl),
@@ -83,7 +75,7 @@ struct SeqPlan {
   float mq;    // form 0: reference logit of draft row n
   float kap_hi;  // form 0: kappa (F * sp) / (F_q * sq) as a float pair (hi + lo)
   float kap_lo;
-  float cp, cq, corr;
+  float cp, cq;
   float cq_lo;    // cqx - cq
   float dt;       // fp32(cp - cqx): log2(q_v / p_v) - (x_d - x_t) * kl
   float ug;       // the draw's uniform
@@ -125,8 +117,8 @@ struct SampleLaunch {
   int parts;  // finish workgroups per sequence, each streaming a share of the draw's steps
   // workspace
   RowPartial* part;  // [B][per_seq][kWaves]
-  double* steptot;   // [B][ns2]; with parts > 1 it holds -1 (no mass yet) before each finish launch
-  double* stepq;     // [B][ns2]: q-mass of each step's positive residual (exact pass, steps beyond LDS)
+  double* steptot;   // [B][3][ns2] step sums (masses, q-masses, signed sums) when they exceed LDS, and the
+                     // finish parts' hand-off (sentinels -1, -1, NaN before each finish launch when parts > 1)
   int32_t* reach;    // [B] early exit only (else null): rows 0..reach-1 have statistics
   int32_t* done;     // [B] finish parts done; zeroed by the statistics pass and by the drawing part
 };
@@ -200,7 +192,7 @@ inline int64_t max_chunks_per_row(int64_t V) { return ceil_div(V * 4, kMinChunkB
 inline int64_t align256(int64_t x) { return round_up(x, 256); }
 
 struct SampleLayout {
-  int64_t off_part, off_step, off_stepq, off_reach, off_done, total;
+  int64_t off_part, off_step, off_reach, off_done, total;
 };
 
 inline int64_t draw_steps(int64_t V) { return ceil_div(V, kStepTokens); }
@@ -276,9 +268,7 @@ inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
   L.off_part = o;
   o += align256(B * (2 * gamma + 1) * max_chunks_per_row(V) * kWaves * (int64_t)sizeof(RowPartial));
   L.off_step = o;
-  o += align256(B * draw_steps(V) * 8);
-  L.off_stepq = o;
-  o += draw_steps(V) > kLdsSteps ? align256(B * draw_steps(V) * 8) : 0;
+  o += align256(B * 3 * draw_steps(V) * 8);
   L.off_reach = o;
   o += align256(B * 4);
   L.off_done = o;

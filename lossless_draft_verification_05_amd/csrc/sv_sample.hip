@@ -369,10 +369,18 @@ __device__ __forceinline__ AcceptOut accept_test(float lt, float ld, const RowSt
 
 // The finish parts' hand-off state of sequence b before a finish launch: no
 // part done, no step mass yet (one workgroup of the sequence calls this).
+// (The step sums of sequence b are [3][ns2] in the workspace: masses and
+// q-masses hold -1 until published, signed sums NaN.)
 __device__ __forceinline__ void reset_handoff(const SampleLaunch& A, int b) {
   if (threadIdx.x == 0) A.done[b] = 0;
-  if (A.parts > 1)
-    for (int s = threadIdx.x; s < A.ns2; s += blockDim.x) A.steptot[(int64_t)b * A.ns2 + s] = -1.0;
+  if (A.parts > 1) {
+    double* g = A.steptot + (int64_t)b * 3 * A.ns2;
+    for (int s = threadIdx.x; s < A.ns2; s += blockDim.x) {
+      g[s] = -1.0;
+      g[A.ns2 + s] = -1.0;
+      g[2 * A.ns2 + s] = __builtin_nan("");
+    }
+  }
 }
 
 // One pass: one workgroup per (sequence, chunk slot) over every row.
@@ -550,75 +558,119 @@ struct OctetRaw<0> {
   }
 };
 
-// 2^x - 1 for x <= 0 (x may be -inf), to a few ulp relative: on [-1/2, 0]
-// the Taylor polynomial of e^(x ln 2) - 1 to degree 7, in Horner form (its
-// terms alternate, so the truncation error is below the first omitted term,
-// (ln 2 / 2)^8 / 8!, under 2^-25 relative); below -1/2 exp2(x) - 1, which is
-// at least 0.29 in magnitude there, so the subtraction costs at most 2 bits.
+// 2^x - 1 for x <= 0 (x may be -inf), to a few ulp relative: on [-1/2, 0] as
+// x * P(x), P of degree 4 fitted for the smallest maximum relative error
+// (Lawson's iteratively reweighted least squares; coefficients from
+// fit_expm1_2.py, 2.3 ulp at most in this fp32 Horner form); below -1/2 as
+// exp2(x) - 1, which is at least 0.29 in magnitude there, so the subtraction
+// keeps it within a few ulp of a faithful exp2.
 __device__ __forceinline__ float expm1_2(float x) {
-  // (ln 2)^k / k!
-  constexpr float c1 = 0.69314718055994531f, c2 = 0.24022650695910071f, c3 = 0.055504108664821576f,
-                  c4 = 0.0096181291076284772f, c5 = 0.0013333558146428443f, c6 = 1.5403530393381606e-4f,
-                  c7 = 1.5252733804059838e-5f;
-  float p = fmaf(c7, x, c6);
-  p = fmaf(p, x, c5);
-  p = fmaf(p, x, c4);
-  p = fmaf(p, x, c3);
+  constexpr float c0 = 6.931471825e-01f, c1 = 2.402256429e-01f, c2 = 5.549040809e-02f, c3 = 9.541280568e-03f,
+                  c4 = 1.154452213e-03f;
+  float p = fmaf(c4, x, c3);
   p = fmaf(p, x, c2);
   p = fmaf(p, x, c1);
+  p = fmaf(p, x, c0);
   const float poly = p * x;
   const float e = hw_exp2(x) - 1.0f;
   return (x >= -0.5f) ? poly : e;
 }
 
-// Terms of one token in the exact pass (form 1; see SeqPlan): r = max(0, d),
-// q = e_q where p >= q (else 0), d = e_p - e_q, all up to the plan's factor.
-// w = log2(q_v / p_v) is formed from the logit difference, so 1 - 2^w keeps
-// its relative accuracy however close p_v and q_v are.
-struct ExactTerm {
-  float r, q, d;
+// One token of the residual in the FMA form (see SeqPlan): e = max(e_p, e_q)
+// and mag = |e_p - e_q| = -e * expm1_2(-|w|), with w = log2(q_v / p_v) formed
+// from the logit difference, so mag keeps its relative accuracy however close
+// p_v and q_v are; pos: p_v >= q_v (the residual is mag there, else 0).
+// Where the target logit is -inf and the draft's is not, e (= e_q) comes out
+// NaN; the caller redoes such octets with resid_fix (a NaN octet sum).
+struct ResidTerm {
+  float e, mag;
+  bool pos;
 };
-__device__ __forceinline__ ExactTerm exact_term(float xt, float xd, const SeqPlan& P) {
+__device__ __forceinline__ ResidTerm resid_term(float xt, float xd, const SeqPlan& P) {
+  ResidTerm t;
   const float w = fmaf(xd - xt, P.kl, P.dt);
-  float ea = fmaf(xt, P.kl, -P.cp) + fmaxf(w, 0.0f);  // log2 of max(e_p, e_q); NaN iff x_t = -inf < x_d
-  if (!(ea == ea)) ea = fmaf(xd, P.kl, -P.cq) - P.cq_lo;
-  const float e = hw_exp2(ea);
-  const float em = expm1_2(fminf(-fabsf(w), 0.0f));  // in [-1, 0]; a NaN w (both -inf) gives 0
-  const float mag = -e * em;                          // |e_p - e_q|
-  const bool pos = w <= 0.0f;                         // p_v >= q_v
-  ExactTerm t;
-  t.r = pos ? mag : 0.0f;
-  t.q = pos ? fmaf(e, em, e) : 0.0f;
-  t.d = pos ? mag : -mag;
+  t.e = hw_exp2(fmaf(xt, P.kl, -P.cp) + fmaxf(w, 0.0f));
+  t.mag = -t.e * expm1_2(fminf(-fabsf(w), 0.0f));  // a NaN w (both logits -inf) gives 0
+  t.pos = w <= 0.0f;
+  return t;
+}
+// The same token when its target logit is -inf (p_v = 0): e = e_q from the
+// draft logit alone.
+__device__ __forceinline__ ResidTerm resid_fix(float xt, float xd, const SeqPlan& P) {
+  ResidTerm t = resid_term(xt, xd, P);
+  if (!(t.e == t.e)) {
+    t.e = hw_exp2(fmaf(xd, P.kl, -P.cq) - P.cq_lo);
+    t.mag = t.e;
+  }
   return t;
 }
 
-// Unnormalised masses of 8 tokens (see SeqPlan for the forms): residual
-// mode r_v = max(0, e^p_v - kappa e^q_v) = F Sp * max(0, p_v - q_v); exact
-// mode the same residual from exact_term, less g times e^q_v where p_v >= q_v
-// (the first-order correction of the normalisers' ratio); bonus mode
-// r_v = e^p_v = F Sp * p_v. Tokens at or beyond V (value -inf) get 0.
+// Sums over the 8 tokens of an octet in the residual's FMA form: r = the
+// residual (mag where p >= q), pe = e_p where p >= q, a = mag everywhere
+// (the step's q-mass of the positive residual is pe - r, its signed sum of
+// e_p - e_q is 2 r - a). Pairwise fp32 sums, as sum8. FIX: take resid_fix
+// (needed only where a target logit of -inf meets a finite draft logit, which
+// leaves a NaN in a).
+struct ResidSums {
+  float r, pe, a;
+};
+template <bool FIX>
+__device__ __forceinline__ ResidSums resid_sums8(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P) {
+  float r[8], pe[8], a[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const ResidTerm t = FIX ? resid_fix(xt[k], xd[k], P) : resid_term(xt[k], xd[k], P);
+    r[k] = t.pos ? t.mag : 0.0f;
+    pe[k] = t.pos ? t.e : 0.0f;
+    a[k] = t.mag;
+  }
+  return ResidSums{((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])),
+                   ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7])),
+                   ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]))};
+}
+
+// resid_sums8 in the streaming loop: the fix is redone only if a NaN shows up
+// in the wave (a wave-uniform branch, so its exponentials are not computed
+// speculatively for every token).
+__device__ __forceinline__ ResidSums resid_sums8_checked(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P) {
+  ResidSums o = resid_sums8<false>(xt, xd, P);
+  const bool bad = !(o.a == o.a);
+  if (__builtin_expect(__ballot(bad) != 0, 0) && bad) o = resid_sums8<true>(xt, xd, P);
+  return o;
+}
+
+// Unnormalised masses of 8 tokens (see SeqPlan for the forms). Residual mode,
+// FMA form: r_v = mag - g (e_p - mag) where p_v >= q_v, clamped at 0, else 0:
+// F Sp * max(0, p_v - q_v) with the normalisers' ratio corrected to first
+// order (g = 0 before the correction is known); subtract form: max(0, e^p_v -
+// kappa e^q_v). Bonus mode: r_v = e^p_v = F Sp * p_v. Tokens at or beyond V
+// (value -inf) get 0.
 template <int MODE, int FORM>
 __device__ __forceinline__ void mass8(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P, float (&r)[8]) {
-  if constexpr (MODE == kModeExact && FORM == 1) {
+  if constexpr (MODE == kModeResidual && FORM == 1) {
     const float gf = (float)P.g;
+    bool bad = false;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const ExactTerm t = exact_term(xt[k], xd[k], P);
-      r[k] = fmaxf(fmaf(-gf, t.q, t.r), 0.0f);
+      const ResidTerm t = resid_term(xt[k], xd[k], P);
+      r[k] = t.pos ? fmaxf(fmaf(-gf, t.e - t.mag, t.mag), 0.0f) : 0.0f;
+      bad |= !(t.mag == t.mag);
+    }
+    // a target logit of -inf next to a finite draft logit (a NaN term):
+    // redo the octet with resid_fix, in a wave-uniform branch
+    if (__builtin_expect(__ballot(bad) != 0, 0) && bad) {
+#pragma nounroll
+      for (int k = 0; k < 8; ++k) {
+        const ResidTerm t = resid_fix(xt[k], xd[k], P);
+        r[k] = t.pos ? fmaxf(fmaf(-gf, t.e - t.mag, t.mag), 0.0f) : 0.0f;
+      }
     }
     return;
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     if constexpr (FORM == 1) {
-      const float ep = hw_exp2(fmaf(xt[k], P.kl, -P.cp));
-      if constexpr (MODE != kModeBonus) {
-        const float eq = hw_exp2(fmaf(xd[k], P.kl, -P.cq));
-        r[k] = fmaxf(fmaf(eq, P.corr, ep - eq), 0.0f);
-      } else {
-        r[k] = ep;
-      }
+      r[k] = hw_exp2(fmaf(xt[k], P.kl, -P.cp));
     } else {
       const float ep = hw_exp2((xt[k] - P.mp) * P.kl);
       if constexpr (MODE != kModeBonus) {
@@ -667,12 +719,7 @@ __device__ __forceinline__ void load_octet(const char* row, int64_t oct, int V, 
 // Masses of 8 tokens in the draw's mode and the plan's form.
 __device__ __forceinline__ void mass8_of(const float (&xt)[8], const float (&xd)[8], int mode, const SeqPlan& P,
                                          float (&r)[8]) {
-  if (mode == kModeExact) {
-    if (P.form == 1)
-      mass8<kModeExact, 1>(xt, xd, P, r);
-    else
-      mass8<kModeResidual, 0>(xt, xd, P, r);
-  } else if (mode == kModeResidual) {
+  if (mode == kModeResidual) {
     if (P.form == 1)
       mass8<kModeResidual, 1>(xt, xd, P, r);
     else
@@ -738,6 +785,28 @@ __device__ __forceinline__ void step_octet_masses(const char* trow, const char* 
   }
 }
 
+// Per-step sums of the drawn distribution: m its mass; for the residual's
+// FMA form also q, the q-mass of its positive part (sum of e_q where
+// p_v >= q_v), and d, the signed sum of e_p - e_q over the step (the
+// first-order correction of the normalisers' ratio takes both; 0 otherwise).
+struct StepSums {
+  double m, q, d;
+};
+// Where the steps' sums go: LDS when the steps fit, else the workspace.
+struct StepOut {
+  double *m, *q, *d;
+};
+
+// The wave's sums of a step from its lanes' shares (r: residual, pe: e_p where
+// p >= q, a: |e_p - e_q|), every lane gets them.
+__device__ __forceinline__ StepSums wave_step_sums(double r, double pe, double a) {
+  StepSums o;
+  o.m = wave_sum(r);
+  o.q = wave_sum(pe) - o.m;
+  o.d = 2.0 * o.m - wave_sum(a);
+  return o;
+}
+
 // Raw loads of half a step (1024 tokens) of the draw row(s) for one wave:
 // kU2 / 2 octets per lane per row. Only used where the step lies inside the row.
 constexpr int kHalfU = kU2 / 2;
@@ -754,63 +823,102 @@ struct HalfStep {
       if constexpr (MODE == kModeResidual) d[j].load(drow, oct);
     }
   }
-  // This lane's share of the half step's mass, added to lacc in octet order.
+  // This lane's share of the half step's sums, added in octet order (only r
+  // outside the residual's FMA form).
   template <int FORM>
-  __device__ __forceinline__ void mass(const SeqPlan& P, double& lacc) const {
+  __device__ __forceinline__ void sums(const SeqPlan& P, double& r, double& pe, double& a) const {
 #pragma unroll
     for (int j = 0; j < kHalfU; ++j) {
-      float xt[8], xd[8], rr[8];
+      float xt[8], xd[8];
       t[j].unpack(xt);
       if constexpr (MODE == kModeResidual) d[j].unpack(xd);
-      mass8<MODE, FORM>(xt, xd, P, rr);
-      lacc += (double)sum8(rr);
+      if constexpr (MODE == kModeResidual && FORM == 1) {
+        const ResidSums o = resid_sums8_checked(xt, xd, P);
+        r += (double)o.r;
+        pe += (double)o.pe;
+        a += (double)o.a;
+      } else {
+        float rr[8];
+        mass8<MODE, FORM>(xt, xd, P, rr);
+        r += (double)sum8(rr);
+      }
     }
   }
 };
 
-// Mass of step s of the draw row(s), octet by octet with bounds checks (every
-// lane gets it). Inside the row these are the same operations in the same
-// order as the pipelined loop below, so both give the same bits for a step.
-template <int TD, int DD, int MODE, bool kBatch = true>
-__device__ __forceinline__ double direct_step_mass(const char* trow, const char* drow, int64_t s, int64_t noct, int V,
-                                                   const SeqPlan& P, int lane) {
-  double lacc = 0.0;
-  if constexpr (kBatch) {
-    float rr[kU2][8];
-    step_octet_masses<TD, DD>(trow, drow, s, noct, V, MODE, P, lane, rr);
+// The sums of step s of the draw row(s), every load of the step issued before
+// the first use, bounds-checked (every lane gets them). Inside the row these
+// are the same operations in the same order as the pipelined loop below, so
+// both give the same bits for a step.
+template <int TD, int DD, int MODE, int FORM>
+__device__ __forceinline__ StepSums direct_step_sums(const char* trow, const char* drow, int64_t s, int64_t noct,
+                                                     int V, const SeqPlan& P, int lane) {
+  OctetIn<TD> t[kU2];
+  OctetIn<DD> d[kU2];
 #pragma unroll
-    for (int j = 0; j < kU2; ++j)
-      if (s * kStepOctets + kWave * j + lane < noct) lacc += (double)sum8(rr[j]);
-  } else {
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    t[j].load(trow, oct, noct, V);
+    if constexpr (MODE == kModeResidual) d[j].load(drow, oct, noct, V);
+  }
+  double r = 0.0, pe = 0.0, a = 0.0;
 #pragma unroll
-    for (int j = 0; j < kU2; ++j) {
-      const int64_t oct = s * kStepOctets + kWave * j + lane;
-      if (oct < noct) {
-        float xt[8], xd[8], rr[8];
-        load_octet<TD>(trow, oct, V, xt);
-        if (MODE != kModeBonus) load_octet<DD>(drow, oct, V, xd);
-        mass8_of(xt, xd, MODE, P, rr);
-        lacc += (double)sum8(rr);
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float xt[8], xd[8];
+      t[j].to_float(oct, V, xt);
+      if constexpr (MODE == kModeResidual) d[j].to_float(oct, V, xd);
+      if constexpr (MODE == kModeResidual && FORM == 1) {
+        // per octet with the fix (a bounds-checked, rarely taken path)
+        ResidSums o = resid_sums8<false>(xt, xd, P);
+        if (!(o.a == o.a)) o = resid_sums8<true>(xt, xd, P);
+        r += (double)o.r;
+        pe += (double)o.pe;
+        a += (double)o.a;
+      } else {
+        float rr[8];
+        mass8<MODE, FORM>(xt, xd, P, rr);
+        r += (double)sum8(rr);
       }
     }
   }
-  return wave_sum(lacc);
+  if constexpr (MODE == kModeResidual && FORM == 1) return wave_step_sums(r, pe, a);
+  return StepSums{wave_sum(r), 0.0, 0.0};
 }
 
-// Masses of the draw row(s) of sequence b over all steps; wave w of nw takes
-// steps w, w + nw, ... and lane 0 writes each step's mass to out[step].
+template <int TD, int DD>
+__device__ __forceinline__ StepSums direct_step_sums_of(const char* trow, const char* drow, int64_t s, int64_t noct,
+                                                        int V, int mode, const SeqPlan& P, int lane) {
+  if (mode == kModeResidual) {
+    if (P.form == 1) return direct_step_sums<TD, DD, kModeResidual, 1>(trow, drow, s, noct, V, P, lane);
+    return direct_step_sums<TD, DD, kModeResidual, 0>(trow, drow, s, noct, V, P, lane);
+  }
+  if (P.form == 1) return direct_step_sums<TD, DD, kModeBonus, 1>(trow, drow, s, noct, V, P, lane);
+  return direct_step_sums<TD, DD, kModeBonus, 0>(trow, drow, s, noct, V, P, lane);
+}
+
+__device__ __forceinline__ void put_step(const StepOut& out, int s, const StepSums& v) {
+  out.m[s] = v.m;
+  out.q[s] = v.q;
+  out.d[s] = v.d;
+}
+
+// Sums of the draw row(s) of sequence b over all steps; wave w of nw takes
+// steps w, w + nw, ... and lane 0 writes each step's sums to out.
 // Whole steps run as a two-buffer software pipeline over half steps: the loads
 // of the next half are in flight while the wave computes the current one, so
 // its memory and arithmetic overlap.
 template <int TD, int DD, int MODE, int FORM>
 __device__ __forceinline__ void step_masses(const SampleLaunch& A, int b, const SeqPlan& P, int w, int nw,
-                                            double* out) {
+                                            const StepOut& out) {
   const int lane = threadIdx.x & (kWave - 1);
   const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
   const char* drow = (MODE == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   const int full_steps = A.V / kStepTokens;  // steps that lie wholly inside the row
   const int nmine = (full_steps > w) ? (full_steps - w + nw - 1) / nw : 0;  // this wave's whole steps
+  constexpr bool kAll = MODE == kModeResidual && FORM == 1;
   if (nmine > 0) {
     // every load is unconditional inside its block, so no buffer is copied
     // (a copy would wait for the loads in flight)
@@ -818,31 +926,31 @@ __device__ __forceinline__ void step_masses(const SampleLaunch& A, int b, const 
     h0.load(trow, drow, w, 0, lane);
     int64_t st = w;
     for (int i = 0; i + 1 < nmine; ++i, st += nw) {
-      double lacc = 0.0;
+      double r = 0.0, pe = 0.0, a = 0.0;
       h1.load(trow, drow, st, 1, lane);
-      h0.template mass<FORM>(P, lacc);
+      h0.template sums<FORM>(P, r, pe, a);
       h0.load(trow, drow, st + nw, 0, lane);
-      h1.template mass<FORM>(P, lacc);
-      const double tot = wave_sum(lacc);
-      if (lane == 0) out[st] = tot;
+      h1.template sums<FORM>(P, r, pe, a);
+      const StepSums v = kAll ? wave_step_sums(r, pe, a) : StepSums{wave_sum(r), 0.0, 0.0};
+      if (lane == 0) put_step(out, (int)st, v);
     }
-    double lacc = 0.0;
+    double r = 0.0, pe = 0.0, a = 0.0;
     h1.load(trow, drow, st, 1, lane);
-    h0.template mass<FORM>(P, lacc);
-    h1.template mass<FORM>(P, lacc);
-    const double tot = wave_sum(lacc);
-    if (lane == 0) out[st] = tot;
+    h0.template sums<FORM>(P, r, pe, a);
+    h1.template sums<FORM>(P, r, pe, a);
+    const StepSums v = kAll ? wave_step_sums(r, pe, a) : StepSums{wave_sum(r), 0.0, 0.0};
+    if (lane == 0) put_step(out, (int)st, v);
   }
   // the ragged last step (if any), octet by octet
   for (int s = w + nmine * nw; s < A.ns2; s += nw) {
-    const double tot = direct_step_mass<TD, DD, MODE>(trow, drow, s, noct, A.V, P, lane);
-    if (lane == 0) out[s] = tot;
+    const StepSums v = direct_step_sums<TD, DD, MODE, FORM>(trow, drow, s, noct, A.V, P, lane);
+    if (lane == 0) put_step(out, s, v);
   }
 }
 
 template <int TD, int DD>
 __device__ __forceinline__ void all_step_masses(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int w,
-                                                int nw, double* out) {
+                                                int nw, const StepOut& out) {
   if (mode == kModeResidual) {
     if (P.form == 1)
       step_masses<TD, DD, kModeResidual, 1>(A, b, P, w, nw, out);
@@ -856,19 +964,31 @@ __device__ __forceinline__ void all_step_masses(const SampleLaunch& A, int b, co
   }
 }
 
-// The drawing part's copy of every step mass of sequence b into LDS (wave w
+// The workspace's step sums of sequence b ([3][ns2]: m, q, d).
+__device__ __forceinline__ StepOut ws_steps(const SampleLaunch& A, int b) {
+  double* g = A.steptot + (int64_t)b * 3 * A.ns2;
+  return StepOut{g, g + A.ns2, g + 2 * A.ns2};
+}
+
+// Sentinels of a step's sums not yet published (m, q >= 0 and d finite for
+// every valid row).
+__device__ __forceinline__ bool step_published(double m, double q, double d) {
+  return m >= 0.0 && q >= 0.0 && d == d;
+}
+
+// The drawing part's copy of every step's sums of sequence b into LDS (wave w
 // of kFinWaves takes 64-step blocks w, w + kFinWaves, ...). Steps of other
-// parts come from the workspace; one whose mass is not visible yet still holds
-// the sentinel (negative: masses are >= 0) and is recomputed here with the
-// same bits, so no result depends on which stores have landed and no part
-// ever waits for another. The slots are then reset to the sentinel.
+// parts come from the workspace; one whose sums are not all visible yet still
+// holds a sentinel and is recomputed here with the same bits, so no result
+// depends on which stores have landed and no part ever waits for another. The
+// slots are then reset to the sentinels.
 template <int TD, int DD>
 __device__ __forceinline__ void gather_steps(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int part,
-                                             double* sh_steps) {
+                                             const StepOut& sh) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gnw = A.parts * kFinWaves;
-  double* g = A.steptot + (int64_t)b * A.ns2;
+  const StepOut g = ws_steps(A, b);
   const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
   const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
@@ -876,95 +996,49 @@ __device__ __forceinline__ void gather_steps(const SampleLaunch& A, int b, const
     const int s = base + lane;
     const bool in = s < A.ns2;
     const bool mine = (s % gnw) / kFinWaves == part;  // computed by this workgroup: already in LDS
-    double v = 0.0;
-    if (in) v = mine ? sh_steps[s] : __hip_atomic_load(g + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned long long miss = __ballot(in && !(v >= 0.0));
+    StepSums v{0.0, 0.0, 0.0};
+    if (in) {
+      if (mine) {
+        v = StepSums{sh.m[s], sh.q[s], sh.d[s]};
+      } else {
+        v.m = __hip_atomic_load(g.m + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.q = __hip_atomic_load(g.q + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.d = __hip_atomic_load(g.d + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    unsigned long long miss = __ballot(in && !step_published(v.m, v.q, v.d));
     while (miss) {
       const int L = __ffsll((long long)miss) - 1;
       miss &= miss - 1;
-      const double m = (mode == kModeResidual)
-                           ? direct_step_mass<TD, DD, kModeResidual>(trow, drow, base + L, noct, A.V, P, lane)
-                           : direct_step_mass<TD, DD, kModeBonus>(trow, drow, base + L, noct, A.V, P, lane);
+      const StepSums m = direct_step_sums_of<TD, DD>(trow, drow, base + L, noct, A.V, mode, P, lane);
       if (lane == L) v = m;
     }
     if (in) {
-      sh_steps[s] = v;
-      __hip_atomic_store(g + s, -1.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      put_step(sh, s, v);
+      __hip_atomic_store(g.m + s, -1.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(g.q + s, -1.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(g.d + s, __builtin_nan(""), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// The exact pass over step s of the draw row pair by one wave (every lane
-// gets the sums): the residual mass, the q-mass of its positive terms and the
-// signed sum of e_p - e_q over the step's tokens (all with the plan's factor
-// F Sp), from exact_term, octet sums in fp32 as in the draw's scan. A rare
-// path: octets are loaded one at a time, which keeps its registers (and so
-// the finish kernel's) within the streaming loop's budget.
-template <int TD, int DD>
-__device__ __forceinline__ void exact_step_sums(const char* trow, const char* drow, int64_t s, int64_t noct, int V,
-                                                const SeqPlan& P, int lane, double& m, double& q, double& d) {
-  double lm = 0.0, lq = 0.0, ld = 0.0;
-  for (int j = 0; j < kU2; ++j) {
-    const int64_t oct = s * kStepOctets + kWave * j + lane;
-    if (oct < noct) {
-      float xt[8], xd[8], rm[8], rq[8], rd[8];
-      load_octet<TD>(trow, oct, V, xt);
-      load_octet<DD>(drow, oct, V, xd);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const ExactTerm e = exact_term(xt[k], xd[k], P);
-        rm[k] = e.r;
-        rq[k] = e.q;
-        rd[k] = e.d;
-      }
-      lm += (double)sum8(rm);
-      lq += (double)sum8(rq);
-      ld += (double)sum8(rd);
-    }
-  }
-  m = wave_sum(lm);
-  q = wave_sum(lq);
-  d = wave_sum(ld);
-}
-
-// The exact pass of sequence b by every wave of the workgroup (wave w takes
-// steps w, w + kFinWaves, ...): step residual masses into stot, the q-masses
-// of their positive terms into sq, each wave's signed sum of e_p - e_q into
-// sh_sd[w].
-template <int TD, int DD>
-__device__ __forceinline__ void exact_pass(const SampleLaunch& A, int b, const SeqPlan& P, double* stot, double* sq,
-                                           double* sh_sd) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
-  const char* drow = A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b;
-  const int64_t noct = ((int64_t)A.V + 7) / 8;
-  double sd = 0.0;
-  for (int s = w; s < A.ns2; s += kFinWaves) {
-    double m, q, d;
-    exact_step_sums<TD, DD>(trow, drow, s, noct, A.V, P, lane, m, q, d);
-    if (lane == 0) {
-      stot[s] = m;
-      sq[s] = q;
-    }
-    sd += d;
-  }
-  if (lane == 0) sh_sd[w] = sd;
-}
-
-// First-order correction of the exact pass, by one wave. Sum_v (e_p - e_q)
-// over the row is F Sp (1 - 2^-eta) when the ratio of the normalisers the
-// plan used is off by 2^eta (exactly 0 for exact normalisers); the residual
-// with the corrected ratio is r_v - g e_q,v where p_v >= q_v, g = 2^eta - 1
-// (terms that change sign under the correction are of second order). Corrects
-// the step masses in place and returns g; `total` gets their sum.
-__device__ __forceinline__ double exact_correct(double sd, double ptot, double* stot, const double* sq, int ns2,
-                                                int lane, double& total) {
-  const double g = sd / (ptot - sd);
+// The first-order correction of the residual, by one wave (FMA form). With the
+// plan's ratio of the normalisers off by a factor 2^eta, the true residual of
+// token v is e_p - 2^eta e_q, and the signed sum of e_p - e_q over the row is
+// F Sp (1 - 2^-eta) (exactly 0 for an exact ratio). So with g = 2^eta - 1 =
+// d / (F Sp - d), d that sum, each step's residual mass becomes m - g q
+// (terms that change sign under the correction are of second order in eta).
+// Corrects the step masses in place (clamped at 0) and returns g; `total` gets
+// their sum in the order of wave_total.
+__device__ __forceinline__ double correct_steps(const StepOut& st, int ns2, double ptot, int lane, double& total) {
+  double dl = 0.0;
+  for (int s = lane; s < ns2; s += kWave) dl += st.d[s];
+  const double d = wave_sum(dl);
+  const double g = d / (ptot - d);
   double acc = 0.0;
   for (int s = lane; s < ns2; s += kWave) {
-    const double m = fmax(stot[s] - g * sq[s], 0.0);
-    stot[s] = m;
+    const double m = fmax(st.m[s] - g * st.q[s], 0.0);
+    st.m[s] = m;
     acc += m;
   }
   total = wave_sum(acc);
@@ -1123,10 +1197,7 @@ __device__ __forceinline__ void draw_and_write(const SampleLaunch& A, int b, con
   // wave_find returns -1 only if every mass is zero, which valid rows rule
   // out; clamp anyway so that no index can leave the arrays.
   const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
-  // the exact pass's terms take more registers: its (rare) rescan loads one
-  // octet at a time
-  const int y = (mode == kModeExact) ? rescan_step<TD, DD, false>(A, b, P, mode, ss, t, acc, lane)
-                                     : rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane);
+  const int y = rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane);
   // (6) outputs
   write_outputs<TD>(A, b, P, mode, y, total, lane, xi);
 }
@@ -1163,7 +1234,6 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
     const double cqx = dn.c - log2(Q.sp / Q.sq) - dp;
     Q.cq = (float)cqx;
     Q.cq_lo = (float)(cqx - (double)Q.cq);
-    Q.corr = (float)((cqx - (double)Q.cq) * 0.69314718055994530942);
     Q.dt = (float)((double)Q.cp - cqx);
     fma_ok = fma_ok && fabs(cqx) < 0x1p24;
     const double Fq = exp2(dn.c - (double)dn.m * kld);
@@ -1177,7 +1247,6 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
     Q.kap_lo = 0.0f;
     Q.cq = 0.0f;
     Q.cq_lo = 0.0f;
-    Q.corr = 0.0f;
     Q.dt = 0.0f;
   }
   Q.form = fma_ok ? 1 : 0;
@@ -1201,9 +1270,9 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   __shared__ double sh_total;
   __shared__ double sh_g;
   __shared__ int sh_last;
-  __shared__ double sh_sd[kFinWaves];
-  __shared__ double sh_steps[kLdsSteps];  // step masses when the row has at most kLdsSteps steps
-  __shared__ double sh_q[kLdsSteps];      // exact pass: q-mass of each step's positive residual
+  // step sums when the row has at most kLdsSteps steps: masses, q-masses of
+  // the positive residual, signed sums of e_p - e_q
+  __shared__ double sh_steps[kLdsSteps], sh_q[kLdsSteps], sh_d[kLdsSteps];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loops over steps stay scalar
@@ -1334,8 +1403,8 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     return;
   }
 
-  // (4) masses of the drawn distribution, every wave on its steps, into LDS
-  // when they fit, else the workspace. (The two calls differ only in the
+  // (4) sums of the drawn distribution's steps, every wave on its steps, into
+  // LDS when they fit, else the workspace. (The two calls differ only in the
   // address space of the output, which keeps the stores of the streaming loop
   // out of the generic path: after a generic store every wait for a load
   // would drain all loads in flight.)
@@ -1344,71 +1413,65 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   // steps fit in LDS).
   int mode = P.mode;
   const bool lds_steps = A.ns2 <= kLdsSteps;
-  double* stot = lds_steps ? sh_steps : A.steptot + (int64_t)b * A.ns2;
+  const StepOut sh_out{sh_steps, sh_q, sh_d};
+  const StepOut st = lds_steps ? sh_out : ws_steps(A, b);
   if (lds_steps)
-    all_step_masses<TD, DD>(A, b, P, mode, part * kFinWaves + w, K * kFinWaves, sh_steps);
+    all_step_masses<TD, DD>(A, b, P, mode, part * kFinWaves + w, K * kFinWaves, sh_out);
   else
-    all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, A.steptot + (int64_t)b * A.ns2);
-  __syncthreads();  // every wave's step masses are visible to the workgroup
+    all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, ws_steps(A, b));
+  __syncthreads();  // every wave's step sums are visible to the workgroup
   if (K > 1) {
-    // Hand-off: each part publishes its step masses (relaxed device-scope
+    // Hand-off: each part publishes its step sums (relaxed device-scope
     // atomic stores, which no cache of this XCD holds back) and counts itself
-    // done; the part that counts last gathers every mass and draws.
-    double* g = A.steptot + (int64_t)b * A.ns2;
+    // done; the part that counts last gathers every step's sums and draws.
+    const StepOut g = ws_steps(A, b);
     for (int s = tid; s < A.ns2; s += kFinThreads)
-      if ((s % (K * kFinWaves)) / kFinWaves == part)
-        __hip_atomic_store(g + s, sh_steps[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((s % (K * kFinWaves)) / kFinWaves == part) {
+        __hip_atomic_store(g.m + s, sh_steps[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(g.q + s, sh_q[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(g.d + s, sh_d[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     __syncthreads();
     if (tid == 0) sh_last = __hip_atomic_fetch_add(A.done + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == K - 1;
     __syncthreads();
     if (!sh_last) return;
     if (tid == 0) A.done[b] = 0;  // ready for the next finish launch on this workspace
-    gather_steps<TD, DD>(A, b, P, mode, part, sh_steps);
+    gather_steps<TD, DD>(A, b, P, mode, part, sh_out);
     __syncthreads();
   }
   if (w == 0) {
-    const double tot = wave_total(stot, A.ns2, lane);
-    if (lane == 0) sh_total = tot;
+    // the residual's first-order correction of the normalisers' ratio (FMA
+    // form; g = 0 otherwise), then the total
+    double tot, g = 0.0;
+    if (mode == kModeResidual && P.form == 1)
+      g = correct_steps(st, A.ns2, P.sp * P.fscale, lane, tot);
+    else
+      tot = wave_total(st.m, A.ns2, lane);
+    if (lane == 0) {
+      sh_total = tot;
+      sh_g = g;
+    }
   }
   __syncthreads();
   SeqPlan Pd = P;
-  if (mode == kModeResidual && P.form == 1 && !(sh_total >= kExactBelow * P.sp * P.fscale)) {
-    // (4b) A small residual: the difference p - q cancels, and an error of
-    // the normalisers' ratio weighs 1 / (residual mass) on it. The exact pass
-    // streams the row pair again, forms each difference from the logit
-    // difference and corrects the ratio from the signed sum of e_p - e_q.
-    double* sq = lds_steps ? sh_q : A.stepq + (int64_t)b * A.ns2;
-    exact_pass<TD, DD>(A, b, P, stot, sq, sh_sd);
-    __syncthreads();
-    if (w == 0) {
-      double sd = 0.0;
-      for (int k = 0; k < kFinWaves; ++k) sd += sh_sd[k];
-      double tot;
-      const double g = exact_correct(sd, P.sp * P.fscale, stot, sq, A.ns2, lane, tot);
-      if (lane == 0) {
-        sh_total = tot;
-        sh_g = g;
-      }
-    }
-    __syncthreads();
-    mode = kModeExact;
-    Pd.g = sh_g;
-  }
-  if (!(sh_total > 0.0) && mode != kModeBonus) {
+  Pd.g = sh_g;
+  if (!(sh_total > 0.0) && mode == kModeResidual) {
     // Nothing left after the rejection (p_n == q_n up to rounding): draw from p_n.
     mode = kModeBonus;
+    Pd.g = 0.0;
     if (lds_steps)
-      all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, sh_steps);
+      all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, sh_out);
     else
-      all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, A.steptot + (int64_t)b * A.ns2);
+      all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, ws_steps(A, b));
     __syncthreads();
     if (w == 0) {
-      const double tot = wave_total(stot, A.ns2, lane);
+      const double tot = wave_total(st.m, A.ns2, lane);
       if (lane == 0) sh_total = tot;
     }
     __syncthreads();
   }
   const double total = sh_total;
+  const double* stot = st.m;
 
   draw_and_write<TD, DD>(A, b, Pd, mode, stot, total, xi);
 }
@@ -1665,7 +1728,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       // the subtract form Ms = mp * kl
       Q.ct = Ms;
       Q.cp = sub ? 0.0f : (float)Ms;
-      Q.cq = Q.corr = Q.cq_lo = Q.dt = 0.0f;
+      Q.cq = Q.cq_lo = Q.dt = 0.0f;
       Q.fscale = 1.0;
       Q.sp = total;
       Q.sq = 1.0;
@@ -1852,42 +1915,42 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
       return wave_sum(lacc);
     };
     SeqPlan Pd = P;
-    double total = step_total(mode, Pd);
-    if (mode == kModeResidual && P.form == 1 && !(total >= kExactBelow * P.sp * P.fscale)) {
-      // a small residual: the exact pass (see the finish kernel), here from
-      // the values already in registers
-      float rd[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) rd[k] = have ? exact_term(xt[k], xd[k], P).d : 0.0f;
-      const double d = wave_sum((double)sum8(rd));
+    if (mode == kModeResidual && P.form == 1) {
+      // the first-order correction of the normalisers' ratio (see correct_steps)
+      double d = 0.0;
+      if (have) {
+        ResidSums o = resid_sums8<false>(xt, xd, P);
+        if (!(o.a == o.a)) o = resid_sums8<true>(xt, xd, P);
+        d = 2.0 * (double)o.r - (double)o.a;
+      }
+      d = wave_sum(d);
       Pd.g = d / (P.sp * P.fscale - d);
-      mode = kModeExact;
-      total = step_total(mode, Pd);  // the corrected terms, the same ones the scan takes
     }
-    if (!(total > 0.0) && mode != kModeBonus) {
+    double total = step_total(mode, Pd);  // the corrected terms, the same ones the scan takes
+    if (!(total > 0.0) && mode == kModeResidual) {
       // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
       mode = kModeBonus;
+      Pd.g = 0.0;
       total = step_total(mode, Pd);
     }
     const int y = scan_step<1>(rr, 0, (double)P.ug * total, 0.0, lane);
     write_outputs<TD>(A, b, Pd, mode, y, total, lane, xi);
   } else {
     SeqPlan Pd = P;
-    double total = (mode == kModeResidual) ? direct_step_mass<TD, DD, kModeResidual>(trow, drow, 0, noct, A.V, P, lane)
-                                           : direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
-    if (mode == kModeResidual && P.form == 1 && !(total >= kExactBelow * P.sp * P.fscale)) {
-      // a small residual: the exact pass (see the finish kernel) over the one step
-      double m, q, d;
-      exact_step_sums<TD, DD>(trow, drow, 0, noct, A.V, P, lane, m, q, d);
-      Pd.g = d / (P.sp * P.fscale - d);
-      mode = kModeExact;
-      // the corrected terms, the same ones the rescan takes
-      total = direct_step_mass<TD, DD, kModeExact>(trow, drow, 0, noct, A.V, Pd, lane);
+    double total;
+    if (mode == kModeResidual && P.form == 1) {
+      // the first-order correction of the normalisers' ratio (see correct_steps)
+      const StepSums v = direct_step_sums<TD, DD, kModeResidual, 1>(trow, drow, 0, noct, A.V, P, lane);
+      Pd.g = v.d / (P.sp * P.fscale - v.d);
+      total = fmax(v.m - Pd.g * v.q, 0.0);
+    } else {
+      total = direct_step_sums_of<TD, DD>(trow, drow, 0, noct, A.V, mode, P, lane).m;
     }
-    if (!(total > 0.0) && mode != kModeBonus) {
+    if (!(total > 0.0) && mode == kModeResidual) {
       // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
       mode = kModeBonus;
-      total = direct_step_mass<TD, DD, kModeBonus>(trow, drow, 0, noct, A.V, P, lane);
+      Pd.g = 0.0;
+      total = direct_step_sums_of<TD, DD>(trow, drow, 0, noct, A.V, mode, P, lane).m;
     }
     const double t = (double)P.ug * total;
     const int y = rescan_step<TD, DD>(A, b, Pd, mode, 0, t, 0.0, lane);

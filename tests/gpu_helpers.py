@@ -211,6 +211,26 @@ def check_sample_seq(tally: Tally, b: int, Lt, Ld, x, u, T, gpu, lb=None):
     return o
 
 
+def check_sample_parallel(inp, gpu, seqs=None, workers=16):
+    """check_sample over threads (numpy releases the GIL in the oracle's array
+    work); the tallies of the threads are merged in sequence order."""
+    from concurrent.futures import ThreadPoolExecutor
+    B = inp.tokens.shape[0]
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    parts = [seqs[i::workers] for i in range(workers)]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        tallies = list(ex.map(lambda part: check_sample(inp, gpu, part), [p for p in parts if p]))
+    out = Tally()
+    for t in tallies:
+        out.checked += t.checked
+        out.flag_accept += t.flag_accept
+        out.flag_draw += t.flag_draw
+        out.fail += t.fail
+        out.max_prob_rel = max(out.max_prob_rel, t.max_prob_rel)
+        out.max_mass_rel = max(out.max_mass_rel, t.max_mass_rel)
+    return out
+
+
 def check_sample(inp, gpu, seqs=None, tally=None):
     tally = tally or Tally()
     cfg = inp.cfg

@@ -43,8 +43,8 @@ int main() {
   split_row(128256, 2, chunk_bytes_for(1116358656LL), &nch2, &cu2, kBatchUnits);
   std::printf(", \"split\": [%d,%d,%d,%d]", nch, cu, nch2, cu2);
   const SampleLayout L4 = sample_layout(3, 2, 5000000);
-  std::printf(", \"stepq\": [%lld,%lld,%lld,%lld]", (long long)L4.off_step, (long long)L4.off_stepq,
-              (long long)L4.off_reach, (long long)(L1.off_stepq - L1.off_step));
+  std::printf(", \"steps3\": [%lld,%lld,%lld]", (long long)L4.off_step, (long long)L4.off_reach,
+              (long long)(L1.off_reach - L1.off_step));
   // the largest shapes the C ABI accepts (B 2^24, gamma 64, V 2^30, N 1024):
   // every size is computed in 64-bit arithmetic without overflow
   const long long Bm = 1LL << 24, Vm = 1LL << 30;
@@ -126,7 +126,7 @@ def test_workspace_layout(plan):
     assert all(x % 256 == 0 for x in (step, reach, done, total))
     # partials: B (2 gamma + 1) rows x ceil(4 V / 16 KB) chunks x 4 waves x 16 B
     assert step >= 64 * 9 * math.ceil(4 * 32000 / (16 << 10)) * 4 * 16
-    assert reach - step >= 64 * math.ceil(32000 / 2048) * 8     # step masses
+    assert reach - step >= 64 * 3 * math.ceil(32000 / 2048) * 8     # step sums
     assert total_v2 > total and total_b2 > total
 
 
@@ -139,11 +139,12 @@ def test_row_split(plan):
     assert cu2 * 16 <= 144 << 10
 
 
-def test_step_q_masses(plan):
-    # the exact pass's per-step q-masses get workspace only when the steps exceed LDS (V > 2048 * 2048)
-    step, stepq, reach, small = plan["stepq"]
-    steps = -(-5000000 // 2048)
-    assert stepq - step >= 3 * steps * 8 and reach - stepq >= 3 * steps * 8 and small == -(-64 * 16 * 8 // 256) * 256
+def test_step_sums(plan):
+    # three fp64 sums per draw step and sequence (mass, q-mass of the positive
+    # residual, signed sum): LDS overflow and the finish parts' hand-off
+    step, reach, small = plan["steps3"]
+    assert reach - step == -(-3 * 3 * -(-5000000 // 2048) * 8 // 256) * 256
+    assert small == -(-64 * 3 * 16 * 8 // 256) * 256
 
 
 def test_largest_shapes(plan):
@@ -154,7 +155,7 @@ def test_largest_shapes(plan):
     B, G, V = 1 << 24, 64, 1 << 30
     assert steps == V // 2048
     # partials of (2 gamma + 1) rows of up to V * 4 / 16 KB chunks, plus the step masses
-    assert lay_total >= B * (2 * G + 1) * (V * 4 // (16 << 10)) * 4 * 16 + B * steps * 8
+    assert lay_total >= B * (2 * G + 1) * (V * 4 // (16 << 10)) * 4 * 16 + B * 3 * steps * 8
     assert lay_total < 1 << 62 and tree_total >= B * 1024 * (V * 4 // (16 << 10)) * 16
     assert (16 << 10) <= chunk <= (256 << 10) and cu % 1024 == 0 and nch * cu * 16 >= V * 4
     assert parts == 1 and 0 <= tail <= G
