@@ -30,7 +30,9 @@
  *    function returns, 256-byte aligned. It needs no initialisation and holds
  *    nothing between calls. Calls that overlap in time must not share one.
  *  - No C++ exception crosses this interface. The library holds no global
- *    mutable state apart from the thread-local last HIP error.
+ *    mutable state apart from the thread-local last HIP error and the
+ *    per-device address of spec_verify_sample_noalloc's static array (set once
+ *    per device, under a lock).
  *  - Results are deterministic: the same inputs give the same bits.
  */
 #ifndef SPEC_VERIFY_H
@@ -54,7 +56,8 @@ typedef enum {
                             4-byte array is not 4-byte aligned; workspace not 256-byte aligned */
   SV_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
   SV_ERR_HIP = -6,       /* a HIP launch failed; sv_last_hip_error() gives the hipError_t */
-  SV_ERR_ARG = -7        /* any other invalid argument (e.g. an unknown stage) */
+  SV_ERR_ARG = -7,       /* any other invalid argument (e.g. an unknown stage) */
+  SV_ERR_SCRATCH = -8    /* spec_verify_sample_noalloc: the call needs more than SV_NOALLOC_SCRATCH_BYTES */
 } sv_status;
 
 /* Limits checked on the host. */
@@ -125,6 +128,31 @@ int spec_verify_sample(const void* target_logits, int target_dtype, int64_t targ
                        const float* uniforms, const float* temperature, int B, int gamma, int V,
                        int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_sample_noalloc -- spec_verify_sample for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, outputs, kernels and
+ * results, without the workspace. The workspace is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends; its
+ * address on the current device is looked up once (hipGetSymbolAddress) at the
+ * first call on that device. The call allocates nothing.
+ *
+ * Calls on one GPU share its array: calls that may overlap in time on the
+ * same GPU (concurrent streams, or threads) race and must not be made; the
+ * array keeps the last call's contents, which no call depends on. The current
+ * HIP device must be the GPU that owns the pointers and the stream.
+ * Errors: as spec_verify_sample, and SV_ERR_SCRATCH when
+ * sv_sample_workspace_bytes(B, gamma, V) exceeds SV_NOALLOC_SCRATCH_BYTES
+ * (found before any HIP call).
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int spec_verify_sample_noalloc(const void* target_logits, int target_dtype, int64_t target_seq_stride,
+                               int64_t target_row_stride, const void* draft_logits, int draft_dtype,
+                               int64_t draft_seq_stride, int64_t draft_row_stride, const int32_t* draft_tokens,
+                               const float* uniforms, const float* temperature, int B, int gamma, int V,
+                               int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
+                               void* stream);
 
 /*
  * spec_verify_sample_early_exit -- spec_verify_sample that reads no row after

@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("SV_LIBRARY") or os.path.join(HERE, "libspec_verify.so
 
 SV_F32, SV_BF16 = 0, 1
 SV_OK = 0
-_ARG_ERRORS = {-1, -2, -3, -4, -5, -7}
+_ARG_ERRORS = {-1, -2, -3, -4, -5, -7, -8}
 
 _lib = None
 
@@ -33,6 +33,8 @@ SIGNATURES = {
                                         _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sample_early_exit": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
                                              _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample_noalloc": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
+                                          _i32, _vp, _vp, _vp, _vp]),
     "spec_verify_sample_early_exit_grouped": (_i32, [_i32, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp,
                                                      _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy_tree": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
@@ -207,12 +209,18 @@ def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_
     nbytes = sv_sample_workspace_bytes(B, G, V)
     if nbytes == 0:
         raise ValueError(f"shape B={B} gamma={G} V={V} out of range")
+    outputs = (out_num_accepted, out_tokens, d)
+    if stage == "noalloc":  # no workspace: the library's static array
+        args = (_ptr(target), _dtype_code(target), ts, tr, _ptr(draft), _dtype_code(draft), ds, dr,
+                _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), B, G, V, _ptr(out_num_accepted),
+                _ptr(out_tokens), ctypes.byref(dptr) if dptr is not None else None, _stream(stream))
+        keep = (target, draft, draft_tokens, uniforms, temperature, d, dptr)
+        return _launch(lib.spec_verify_sample_noalloc, args, "spec_verify_sample_noalloc", outputs, keep, prepare)
     ws = _workspace(workspace, nbytes, dev)
     args = (_ptr(target), _dtype_code(target), ts, tr, _ptr(draft), _dtype_code(draft), ds, dr, _ptr(draft_tokens),
             _ptr(uniforms), _ptr(temperature), B, G, V, _ptr(out_num_accepted), _ptr(out_tokens),
             ctypes.byref(dptr) if dptr is not None else None, _ptr(ws), ws.numel(), _stream(stream))
     keep = (target, draft, draft_tokens, uniforms, temperature, ws, d, dptr)
-    outputs = (out_num_accepted, out_tokens, d)
     if stage is None:
         return _launch(lib.spec_verify_sample, args, "spec_verify_sample", outputs, keep, prepare)
     if stage == "early_exit":
@@ -240,6 +248,15 @@ def spec_verify_sample(target, draft, draft_tokens, uniforms, temperature, *, ou
     """
     return _sample_call(None, target, draft, draft_tokens, uniforms, temperature, out_num_accepted, out_tokens,
                         diag, workspace, stream, prepare)
+
+
+def spec_verify_sample_noalloc(target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
+                               out_tokens=None, diag=False, stream=None, prepare=False):
+    """spec_verify_sample without a workspace: the library uses its static device array
+    (SV_NOALLOC_SCRATCH_BYTES per GPU) and allocates nothing; calls on one GPU must not
+    overlap. Outputs are allocated here unless given (pass them to allocate nothing at all)."""
+    return _sample_call("noalloc", target, draft, draft_tokens, uniforms, temperature, out_num_accepted, out_tokens,
+                        diag, None, stream, prepare)
 
 
 def spec_verify_sample_early_exit(target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "../../include/spec_verify.h"
 #include "sv_plan.hpp"
@@ -192,11 +194,68 @@ static int run_sample_early(const SampleArgs& a, int tail_start, hipStream_t str
   return hip_status(launch_sample_stage(L, a.tdt, a.ddt, 2, stream));
 }
 
+// ---------------------------------------------------------------------------
+// spec_verify_sample_noalloc: the workspace is a static device array
+// ---------------------------------------------------------------------------
+// One copy per GPU, held until the process ends. In host code `scratch` names a
+// host-side stand-in, not a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept here.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The static array's address on the current device (looked up at the first
+// call on that device).
+static int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return SV_ERR_ARG;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      if (!p) return SV_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SV_OK;
+}
+
 }  // namespace sv
 
 using namespace sv;
 
 extern "C" {
+
+int spec_verify_sample_noalloc(const void* target_logits, int target_dtype, int64_t target_seq_stride,
+                               int64_t target_row_stride, const void* draft_logits, int draft_dtype,
+                               int64_t draft_seq_stride, int64_t draft_row_stride, const int32_t* draft_tokens,
+                               const float* uniforms, const float* temperature, int B, int gamma, int V,
+                               int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
+                               void* stream) {
+  // every argument check of spec_verify_sample first (with a stand-in
+  // workspace of the array's size and alignment), then the size, then the
+  // first HIP call
+  SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
+               draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
+               out_num_accepted, out_tokens, diag, (void*)(uintptr_t)256, (size_t)SV_NOALLOC_SCRATCH_BYTES};
+  int st = validate_sample(a);
+  if (st == SV_ERR_WORKSPACE) return SV_ERR_SCRATCH;  // the layout exceeds the array
+  if (st) return st;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st) return st;
+  a.ws = ws;
+  return run_sample(1, 2, a, (hipStream_t)stream);
+}
 
 size_t sv_sample_workspace_bytes(int B, int gamma, int V) {
   if (B < 1 || B > SV_MAX_BATCH || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
@@ -378,6 +437,7 @@ const char* sv_status_string(int status) {
     case SV_ERR_WORKSPACE: return "workspace missing or too small";
     case SV_ERR_HIP: return "HIP launch failed (see sv_last_hip_error)";
     case SV_ERR_ARG: return "invalid argument";
+    case SV_ERR_SCRATCH: return "call too large for spec_verify_sample_noalloc's static scratch (32 MiB)";
     default: return "unknown status";
   }
 }

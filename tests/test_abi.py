@@ -35,8 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert b"spec_verify" in lib.sv_version()
-    for st in range(-7, 1):
-        assert lib.sv_status_string(st)
+    for st in range(-8, 1):
+        assert lib.sv_status_string(st) and lib.sv_status_string(st) != b"unknown status"
     assert lib.sv_status_string(-99) == b"unknown status"
     assert lib.sv_last_hip_error() == 0
 
@@ -94,6 +94,38 @@ def test_sample_argument_errors(lib, over, want):
     assert call_sample(lib, **over) == want
     for stage in (1, 2, "early_exit", "grouped"):
         assert call_sample(lib, stage=stage, **over) == want
+
+
+def call_noalloc(lib, **over):
+    a = sample_args(**over)
+    return lib.spec_verify_sample_noalloc(a["target"], a["tdt"], a["tss"], a["trs"], a["draft"], a["ddt"], a["dss"],
+                                          a["drs"], a["tokens"], a["uniforms"], a["temps"], a["B"], a["G"], a["V"],
+                                          a["out_n"], a["out_tok"], a["diag"], a["stream"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(target=None), -1), (dict(draft=None), -1), (dict(tokens=None), -1), (dict(uniforms=None), -1),
+    (dict(temps=None), -1), (dict(out_n=None), -1), (dict(out_tok=None), -1),
+    (dict(tdt=2), -3), (dict(ddt=-1), -3),
+    (dict(B=0), -2), (dict(G=0), -2), (dict(G=65), -2), (dict(V=0), -2), (dict(V=(1 << 30) + 1), -2),
+    (dict(trs=63), -2), (dict(tss=-8), -2),
+    (dict(target=A + 2), -4), (dict(trs=68), -4), (dict(tokens=A + 2), -4), (dict(out_tok=A + 1), -4),
+])
+def test_noalloc_argument_errors(lib, over, want):
+    """The entry point without a workspace checks the same arguments, before any HIP call."""
+    assert call_noalloc(lib, **over) == want
+
+
+def test_noalloc_size_limit(lib):
+    """Configuration 5's call fits the 32 MiB static array; a call whose
+    workspace would exceed it is refused with SV_ERR_SCRATCH before any HIP call."""
+    assert 0 < lib.sv_sample_workspace_bytes(512, 5, 256000) <= 32 << 20
+    V = 128256
+    big = dict(B=4096, G=8, V=V, tss=9 * V, trs=V, dss=8 * V, drs=V)
+    assert lib.sv_sample_workspace_bytes(4096, 8, V) > 32 << 20
+    assert call_noalloc(lib, **big) == -8
+    assert b"32 MiB" in lib.sv_status_string(-8)
+    assert lib.sv_last_hip_error() == 0
 
 
 def test_grouping_beyond_gamma(lib):
