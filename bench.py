@@ -108,27 +108,70 @@ def _oracle_draft(b):
     return O.draft_sample_row(O.widen(d.logits[b], d.dtype), float(d.temperature[b]), float(d.uniforms[b])).y
 
 
-def cpu_baseline_draft(d, budget_s: float = 10.0):
-    """The oracle's draft sampler over a bounded sample of rows (cycled), in a
-    pool of worker processes forked before the GPU is touched."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+# The oracle's worker pool: at most 16 processes, the CPU share of one GPU on
+# the benchmark host (os.cpu_count() there reports the whole machine).
+MAX_ORACLE_WORKERS = 16
+
+
+def time_oracle(fn, n_items: int, units, unit: str, what: str, budget_s: float = 10.0, cap: int = 2_000_000):
+    """Time the oracle function fn(i) (item i mod n_items of the same inputs)
+    once in this process on about budget_s / 4 seconds of work, and once in a
+    pool of worker processes (forked before the GPU is touched) on about
+    budget_s seconds. units: units of the metric per item, or None when fn
+    returns its item's units. The pool's rate is the baseline's value."""
     import multiprocessing as mp
 
-    global _CPU_DATA
-    _CPU_DATA = d
-    _oracle_draft(0)
+    fn(0)  # warm (imports, first touch)
     t0 = time.perf_counter()
-    _oracle_draft(0)
+    fn(0)
     t_one = max(time.perf_counter() - t0, 1e-5)
-    workers = max(1, min(16, os.cpu_count() or 1))
-    S = int(min(2_000_000, max(workers, budget_s * workers / t_one)))
+
+    def count(results, items):
+        return sum(results) if units is None else units * items
+
+    s1 = int(min(cap, max(1, 0.25 * budget_s / t_one)))
+    t0 = time.perf_counter()
+    r1 = [fn(i % n_items) for i in range(s1)]
+    dt1 = time.perf_counter() - t0
+    workers = max(1, min(MAX_ORACLE_WORKERS, os.cpu_count() or 1))
+    S = int(min(cap, max(workers, budget_s * workers / t_one)))
     with mp.get_context("fork").Pool(workers) as pool:
         t0 = time.perf_counter()
-        pool.map(_oracle_draft, [i % d.B for i in range(S)], chunksize=max(1, S // (4 * workers)))
+        res = pool.map(fn, [i % n_items for i in range(S)], chunksize=max(1, S // (4 * workers)))
         dt = time.perf_counter() - t0
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = None
+    return {"value": count(res, S) / dt, "unit": unit, "cores": workers, "kind": "oracle",
+            "sample": f"{S} {what} (index mod {n_items}) of the same inputs, {workers} worker processes, {dt:.1f} s",
+            "single_process": {"value": count(r1, s1) / dt1, "unit": unit,
+                               "sample": f"{s1} {what}, one process, {dt1:.1f} s"},
+            "cpu_count": os.cpu_count(), "cpus_available": avail, "cpu_model": _cpu_model(),
+            "pool_cap": f"{MAX_ORACLE_WORKERS} worker processes at most: the CPU share of one GPU on the "
+                        f"benchmark host"}
+
+
+def cpu_baseline_draft(d, budget_s: float = 10.0):
+    """The oracle's draft sampler over a bounded sample of rows (cycled)."""
+    global _CPU_DATA
+    _CPU_DATA = d
+    out = time_oracle(_oracle_draft, d.B, 1, "draft tokens/s", "rows (numpy fp64)", budget_s)
     _CPU_DATA = None
-    return {"value": S / dt, "unit": "draft tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"{S} rows (index mod {d.B}) of the same inputs, numpy fp64, {workers} worker processes, "
-                      f"{dt:.1f} s"}
+    return out
 
 
 def bench_draft(args, cid):
@@ -245,26 +288,15 @@ def bench_markov(args):
     tabs = synth.make_markov_tables(V, c["dtype"], seed=args.seed, noise_sd=c["noise_sd"])
     cpu = None
     if not args.no_cpu_baseline:
-        import multiprocessing as mp
-
         global _CPU_DATA
         Lt = synth.decode(tabs.target, c["dtype"]).astype(np.float64)
         Ld = synth.decode(tabs.draft, c["dtype"]).astype(np.float64)
         K = 4
         _CPU_DATA = ((Lt, Ld), T, K, G)
-        t0 = time.perf_counter()
-        _oracle_markov(0)
-        t_one = max(time.perf_counter() - t0, 1e-4)
-        workers = max(1, min(16, os.cpu_count() or 1))
-        S = int(max(workers, min(4 * B, 10.0 * workers / t_one)))
-        with mp.get_context("fork").Pool(workers) as pool:
-            t0 = time.perf_counter()
-            toks = sum(pool.map(_oracle_markov, range(S), chunksize=max(1, S // (4 * workers))))
-            dt = time.perf_counter() - t0
+        cpu = time_oracle(_oracle_markov, 4 * B, None, "emitted tokens/s",
+                          f"chains x {K} iterations of the oracle loop (draft_sample_row + verify_sample_sequence, "
+                          f"numpy fp64)", cap=4 * B)
         _CPU_DATA = None
-        cpu = {"value": toks / dt, "unit": "emitted tokens/s", "cores": workers, "kind": "oracle",
-               "sample": f"{S} chains x {K} iterations of the oracle loop (draft_sample_row + "
-                         f"verify_sample_sequence, numpy fp64), {workers} worker processes, {dt:.1f} s"}
         log(f"[bench] cpu baseline: {cpu}")
     import torch
 
@@ -354,22 +386,10 @@ def bench_masks(args):
     B, N = P.shape
     cpu = None
     if not args.no_cpu_baseline:
-        import multiprocessing as mp
-
         global _CPU_DATA
         _CPU_DATA = (P, Bl)
-        t0 = time.perf_counter()
-        _oracle_masks(0)
-        t_one = max(time.perf_counter() - t0, 1e-5)
-        workers = max(1, min(16, os.cpu_count() or 1))
-        S = int(min(200_000, max(workers, 10.0 * workers / t_one)))
-        with mp.get_context("fork").Pool(workers) as pool:
-            t0 = time.perf_counter()
-            pool.map(_oracle_masks, [i % B for i in range(S)], chunksize=max(1, S // (4 * workers)))
-            dt = time.perf_counter() - t0
+        cpu = time_oracle(_oracle_masks, B, 1, "trees/s", "trees (python loops)", cap=200_000)
         _CPU_DATA = None
-        cpu = {"value": S / dt, "unit": "trees/s", "cores": workers, "kind": "oracle",
-               "sample": f"{S} trees (index mod {B}), python loops, {workers} worker processes, {dt:.1f} s"}
         log(f"[bench] cpu baseline: {cpu}")
     import torch
 
@@ -423,32 +443,18 @@ def bench_masks(args):
 
 
 def cpu_baseline(inp, tree: bool, budget_s: float = 10.0):
-    """Time the oracle over the first S sequences in a pool of worker processes
-    (fork, before the GPU is touched). S is sized from a one-sequence probe so
-    the timed part takes about ``budget_s`` seconds."""
-    import multiprocessing as mp
-
+    """Time the oracle over sequences (trees) of the same inputs, cycled when
+    the batch takes less than the budget (see time_oracle)."""
     global _CPU_DATA
     _CPU_DATA = inp if tree else (inp, inp.cfg.target_dtype, inp.cfg.draft_dtype)
-    fn = _oracle_tree if tree else _oracle_seq
-    B = inp.parents.shape[0] if tree else inp.tokens.shape[0]
-    fn(0)  # warm (imports, first-touch)
-    t0 = time.perf_counter()
-    fn(0)
-    t_one = max(time.perf_counter() - t0, 1e-5)
-    workers = max(1, min(16, os.cpu_count() or 1))
-    # cycle over the batch (b mod B) when the whole batch takes less than the budget
-    S = int(min(2_000_000, max(workers, budget_s * workers / t_one)))
-    ctx = mp.get_context("fork")
-    with ctx.Pool(workers) as pool:
-        t0 = time.perf_counter()
-        pool.map(fn, [i % B for i in range(S)], chunksize=max(1, S // (4 * workers)))
-        dt = time.perf_counter() - t0
-    units = S * ((inp.parents.shape[1] - 1) if tree else inp.tokens.shape[1])
+    if tree:
+        out = time_oracle(_oracle_tree, inp.parents.shape[0], inp.parents.shape[1] - 1, "nodes/s",
+                          "trees (numpy fp64)", budget_s)
+    else:
+        out = time_oracle(_oracle_seq, inp.tokens.shape[0], inp.tokens.shape[1], "positions/s",
+                          "sequences (numpy fp64)", budget_s)
     _CPU_DATA = None
-    return {"value": units / dt, "unit": "nodes/s" if tree else "positions/s", "cores": workers, "kind": "oracle",
-            "sample": f"{S} {'trees' if tree else 'sequences'} (index mod {B}) of the same inputs, numpy fp64, "
-                      f"{workers} worker processes, {dt:.1f} s"}
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -713,13 +719,20 @@ def main():
         ee_ms = (time.perf_counter() - t2) * 1e3 / args.steps
         ee = (ee_ms, ee_n.cpu().numpy(), ee_t.cpu().numpy())
         log(f"[bench] early exit: {ee_ms:.4f} ms/step")
-    stage_ms = [float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
-                for i in range(ns)]
+    per_kernel = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(ns)] for k in range(args.steps)])
+    stage_ms = [float(v) for v in per_kernel.mean(axis=0)]
     log(f"[bench] {ms_per_step:.4f} ms/step; kernel event means (ms): {stage_ms}")
 
-    detail = {"kernels": {n: {"mean_us": round(m * 1e3, 3)} for n, m in zip(kernel_names, stage_ms)},
+    def dist_us(v):
+        return {"median": round(float(np.median(v)) * 1e3, 3), "p10": round(float(np.percentile(v, 10)) * 1e3, 3),
+                "p90": round(float(np.percentile(v, 90)) * 1e3, 3)}
+
+    detail = {"kernels": {n: {"mean_us": round(m * 1e3, 3), **{k + "_us": v for k, v in dist_us(per_kernel[:, i]).items()}}
+                          for i, (n, m) in enumerate(zip(kernel_names, stage_ms))},
+              "step_event_us": {**dist_us(per_kernel.sum(axis=1)), "steps": args.steps},
               "timing": "ms_per_step: wall clock over the timed steps (whole calls, nothing else on the stream); "
-                        "kernel means: HIP events between the kernels in a second pass of as many steps",
+                        "kernel means and median/p10/p90: HIP events between the kernels in a second pass of as "
+                        "many steps (step_event_us: per step, the sum of its kernels' event intervals)",
               "input_copies": R, "kernel_source_sha": sha}
     if tree:
         lens = outs[0].cpu().numpy()

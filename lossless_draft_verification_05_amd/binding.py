@@ -101,6 +101,10 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _stream_obj(stream, device):
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
 def _need(t: torch.Tensor, name: str, dtype, shape):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
@@ -123,29 +127,42 @@ def _logits3(t: torch.Tensor, name: str, rows: int):
 
 
 class Workspace:
-    """Device workspace grown on demand and reused by calls on one stream.
+    """Device workspace grown on demand and reused by calls.
 
     The kernels keep nothing in it between calls and need it uninitialised;
-    calls that may run at the same time need separate Workspace objects.
+    calls that may run at the same time need separate Workspace objects. The
+    buffer is allocated on the stream of the call that grows it; a call on any
+    other stream records that stream on the buffer (record_stream), so the
+    caching allocator never hands the memory out again while such a call may
+    still use it, also after the buffer is replaced by a larger one.
     """
 
     def __init__(self):
         self.buf = None
+        self._alloc_stream = None
 
-    def get(self, nbytes: int, device) -> torch.Tensor:
+    def get(self, nbytes: int, device, stream=None) -> torch.Tensor:
+        s = _stream_obj(stream, device)
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            with torch.cuda.stream(s):
+                self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._alloc_stream = s
+        elif s != self._alloc_stream:
+            self.buf.record_stream(s)
         return self.buf
 
 
+# Default workspaces, one per (device, stream): calls on different streams never
+# share one, so they can overlap.
 _default_ws = {}
 
 
-def _workspace(ws, nbytes, device):
-    """A Workspace object (default: one per device) or a caller-managed uint8 tensor."""
+def _workspace(ws, nbytes, device, stream=None):
+    """A Workspace object (default: one per device and stream) or a caller-managed uint8 tensor."""
     if ws is None:
-        ws = _default_ws.setdefault(device, Workspace())
-    buf = ws.get(nbytes, device) if isinstance(ws, Workspace) else ws
+        s = _stream_obj(stream, device)
+        ws = _default_ws.setdefault((device, s.cuda_stream), Workspace())
+    buf = ws.get(nbytes, device, stream) if isinstance(ws, Workspace) else ws
     if buf.numel() < nbytes:
         raise ValueError(f"workspace has {buf.numel()} bytes, needs {nbytes}")
     return buf
@@ -216,7 +233,7 @@ def _sample_call(stage, target, draft, draft_tokens, uniforms, temperature, out_
                 _ptr(out_tokens), ctypes.byref(dptr) if dptr is not None else None, _stream(stream))
         keep = (target, draft, draft_tokens, uniforms, temperature, d, dptr)
         return _launch(lib.spec_verify_sample_noalloc, args, "spec_verify_sample_noalloc", outputs, keep, prepare)
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     args = (_ptr(target), _dtype_code(target), ts, tr, _ptr(draft), _dtype_code(draft), ds, dr, _ptr(draft_tokens),
             _ptr(uniforms), _ptr(temperature), B, G, V, _ptr(out_num_accepted), _ptr(out_tokens),
             ctypes.byref(dptr) if dptr is not None else None, _ptr(ws), ws.numel(), _stream(stream))
@@ -305,7 +322,7 @@ def spec_draft_sample(logits, uniforms, temperature, *, out_tokens=None, want_pr
     nbytes = int(lib.sv_draft_workspace_bytes(B, V))
     if nbytes == 0:
         raise ValueError(f"shape B={B} V={V} out of range")
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     args = (_ptr(logits), _dtype_code(logits), logits.stride(0), _ptr(uniforms), _ptr(temperature), B, V,
             _ptr(out_tokens), _ptr(prob) if prob is not None else None, _ptr(ws), ws.numel(), _stream(stream))
     keep = (logits, uniforms, temperature, ws)
@@ -334,7 +351,7 @@ def _tree_call(stage, logits, parents, tokens, out_accept_len, out_path, out_bon
     nbytes = sv_tree_workspace_bytes(B, N, V)
     if nbytes == 0:
         raise ValueError(f"shape B={B} N={N} V={V} out of range")
-    ws = _workspace(workspace, nbytes, dev)
+    ws = _workspace(workspace, nbytes, dev, stream)
     args = (_ptr(logits), _dtype_code(logits), s0, s1, _ptr(parents), _ptr(tokens), B, N, V, _ptr(out_accept_len),
             _ptr(out_path), _ptr(out_bonus), _ptr(out_argmax), _ptr(ws), ws.numel(), _stream(stream))
     keep = (logits, parents, tokens, ws)

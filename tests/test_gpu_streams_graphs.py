@@ -141,3 +141,39 @@ def test_concurrent_calls_on_two_streams(gpu):
             assert np.array_equal(ln.cpu().numpy(), tref[k]["len"]), (rep, k)
             assert np.array_equal(path.cpu().numpy(), tref[k]["path"]), (rep, k)
             assert np.array_equal(bonus.cpu().numpy(), tref[k]["bonus"]), (rep, k)
+
+
+def test_default_workspace_on_two_streams(gpu):
+    """The binding's default workspace is one per (device, stream): two
+    batches verified at the same time on two streams with no workspace given
+    give the sequential results, also when the second call on a stream needs
+    a larger workspace than the first (the old buffer is replaced while the
+    other stream's kernels still run)."""
+    H.log("default workspaces on two streams, growing between calls")
+    small = [synth.make_custom_sample(8, 3, 20000, "bf16", "bf16", T=1.0, noise_sd=0.7, seed=70 + k) for k in (0, 1)]
+    large = [synth.make_custom_sample(48, 5, 80000, "bf16", "f32", T=0.8, noise_sd=0.7, seed=80 + k) for k in (0, 1)]
+    ts = [H.sample_tensors(x) for x in small]
+    tl = [H.sample_tensors(x) for x in large]
+    ref_s = [H.run_sample(gpu, t, diag=False, workspace=gpu.Workspace()) for t in ts]
+    ref_l = [H.run_sample(gpu, t, diag=False, workspace=gpu.Workspace()) for t in tl]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        res = [None, None]
+        for k in (0, 1):
+            with torch.cuda.stream(streams[k]):
+                a = gpu.spec_verify_sample(**ts[k])
+                b = gpu.spec_verify_sample(**tl[k])  # grows this stream's default workspace
+                res[k] = (a, b)
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for k in (0, 1):
+            (na, ta, _), (nb, tb, _) = res[k]
+            assert np.array_equal(na.cpu().numpy(), ref_s[k]["n"]) and np.array_equal(ta.cpu().numpy(), ref_s[k]["tokens"]), (rep, k)
+            assert np.array_equal(nb.cpu().numpy(), ref_l[k]["n"]) and np.array_equal(tb.cpu().numpy(), ref_l[k]["tokens"]), (rep, k)
+    # one default workspace per stream was made
+    from lossless_draft_verification_05_amd import binding as Bmod
+    keys = {k for k in Bmod._default_ws if k[1] in (streams[0].cuda_stream, streams[1].cuda_stream)}
+    assert len(keys) == 2

@@ -53,6 +53,26 @@ def test_alpha_near_goal(cid):
     assert abs(np.mean(al) - cfg.alpha_goal) < 0.03, np.mean(al)
 
 
+def test_config5_normal_rows_alpha_near_goal():
+    """Configuration 5's normal rows: mean alpha within 0.03 of the goal 0.7
+    over 12 sequences (60 positions) of the workload's own rows (seed 0, B =
+    512), each at its per-row temperature."""
+    cfg = synth.CONFIGS[5]
+    cls = synth.row_classes(cfg, 0)
+    temps = synth.temperatures(cfg, 0, cfg.B)
+    scale = synth.draft_noise_scale(5)
+    al = []
+    for b in np.flatnonzero(cls == 0)[:12]:
+        t32 = synth.target_rows(cfg, 0, int(b), cfg.gamma + 1)
+        tr = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(t32))
+        d = synth.draft_rows(cfg, 0, int(b), tr, scale, 0, float(temps[b]))
+        T = float(temps[b])
+        for i in range(cfg.gamma):
+            al.append(O.alpha(O.tempered_softmax(tr[i].astype(np.float64), T)[0],
+                              O.tempered_softmax(d[i].astype(np.float64), T)[0]))
+    assert abs(np.mean(al) - cfg.alpha_goal) < 0.03, np.mean(al)
+
+
 def test_config5_row_classes():
     cfg = synth.CONFIGS[5]
     cls = synth.row_classes(cfg, 0)
