@@ -61,6 +61,10 @@ struct RowPartial {
 //    exact to a few ulp however close p and q are, and r = that where p >= q,
 //    less g * e_q, g the first-order correction of the normalisers' ratio from
 //    the signed sum of e_p - e_q over the row. r = F sp * max(0, p - q).
+//    A 2048-token step whose positive residual is not small next to its
+//    q-mass takes the cheap form instead: e_p = exp2(fma(x_t, kl, -cp)) and
+//    e_q = exp2(fma(x_d, kl, -cq) - cq_lo), one exponential each, the side
+//    of each token still from w (see cheap_ok in sv_sample.hip).
 //  form 0 (used when a shift is 2^24 or more in magnitude, where its fp32
 //  rounding would be half a log2 unit or more):
 //    e_p = exp2((x_t - mp) * kl), e_q = exp2((x_d - mq) * kl),
@@ -117,8 +121,9 @@ struct SampleLaunch {
   int parts;  // finish workgroups per sequence, each streaming a share of the draw's steps
   // workspace
   RowPartial* part;  // [B][per_seq][kWaves]
-  double* steptot;   // [B][3][ns2] step sums (masses, q-masses, signed sums) when they exceed LDS, and the
-                     // finish parts' hand-off (sentinels -1, -1, NaN before each finish launch when parts > 1)
+  double* steptot;   // [B][4][ns2] step sums (masses, q-masses, signed sums, form flags) when they exceed
+                     // LDS, and the finish parts' hand-off (sentinels -1, -1, NaN, -1 before each finish
+                     // launch when parts > 1)
   int32_t* reach;    // [B] early exit only (else null): rows 0..reach-1 have statistics
   int32_t* done;     // [B] finish parts done; zeroed by the statistics pass and by the drawing part
 };
@@ -268,7 +273,7 @@ inline SampleLayout sample_layout(int64_t B, int64_t gamma, int64_t V) {
   L.off_part = o;
   o += align256(B * (2 * gamma + 1) * max_chunks_per_row(V) * kWaves * (int64_t)sizeof(RowPartial));
   L.off_step = o;
-  o += align256(B * 3 * draw_steps(V) * 8);
+  o += align256(B * 4 * draw_steps(V) * 8);
   L.off_reach = o;
   o += align256(B * 4);
   L.off_done = o;

@@ -369,16 +369,17 @@ __device__ __forceinline__ AcceptOut accept_test(float lt, float ld, const RowSt
 
 // The finish parts' hand-off state of sequence b before a finish launch: no
 // part done, no step mass yet (one workgroup of the sequence calls this).
-// (The step sums of sequence b are [3][ns2] in the workspace: masses and
-// q-masses hold -1 until published, signed sums NaN.)
+// (The step sums of sequence b are [4][ns2] in the workspace: masses,
+// q-masses and form flags hold -1 until published, signed sums NaN.)
 __device__ __forceinline__ void reset_handoff(const SampleLaunch& A, int b) {
   if (threadIdx.x == 0) A.done[b] = 0;
   if (A.parts > 1) {
-    double* g = A.steptot + (int64_t)b * 3 * A.ns2;
+    double* g = A.steptot + (int64_t)b * 4 * A.ns2;
     for (int s = threadIdx.x; s < A.ns2; s += blockDim.x) {
       g[s] = -1.0;
       g[A.ns2 + s] = -1.0;
       g[2 * A.ns2 + s] = __builtin_nan("");
+      g[3 * A.ns2 + s] = -1.0;
     }
   }
 }
@@ -639,6 +640,51 @@ __device__ __forceinline__ ResidSums resid_sums8_checked(const float (&xt)[8], c
   return o;
 }
 
+// The residual's cheap form (FMA shifts): e_p and e_q from one exponential
+// each (e_q straight from the draft logit, so logits of -inf give 0 and no
+// NaN), the side of each token from w = log2(q_v / p_v) as in the exact form.
+// Each exponential carries its own rounding, so e_p - e_q is off by a few
+// units of fp32 rounding of e_p wherever p and q are close; a step whose
+// positive residual is small next to its q-mass takes the exact form instead
+// (cheap_ok). Where p_v >= q_v the token's residual is max(e_p - e_q, 0).
+struct CheapTerm {
+  float ep, eq;
+  bool pos;
+};
+__device__ __forceinline__ CheapTerm cheap_term(float xt, float xd, const SeqPlan& P) {
+  CheapTerm t;
+  t.pos = fmaf(xd - xt, P.kl, P.dt) <= 0.0f;
+  t.ep = hw_exp2(fmaf(xt, P.kl, -P.cp));
+  t.eq = hw_exp2(fmaf(xd, P.kl, -P.cq) - P.cq_lo);
+  return t;
+}
+
+// Sums over the 8 tokens of an octet in the cheap form: r = the residual, q =
+// e_q where p >= q (the q-mass of the positive residual), d = e_p - e_q over
+// all 8 (the signed sum). Pairwise fp32 sums, as sum8.
+struct CheapSums {
+  float r, q, d;
+};
+__device__ __forceinline__ CheapSums cheap_sums8(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P) {
+  float r[8], q[8], d[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const CheapTerm t = cheap_term(xt[k], xd[k], P);
+    const float df = t.ep - t.eq;
+    r[k] = t.pos ? fmaxf(df, 0.0f) : 0.0f;
+    q[k] = t.pos ? t.eq : 0.0f;
+    d[k] = df;
+  }
+  return CheapSums{sum8(r), sum8(q), sum8(d)};
+}
+
+// Whether a step's cheap sums stand: its positive residual m is at least
+// 1 / kCheapRatio of its q-mass q (then the rounding of the two exponentials,
+// independent and unbiased per token, is well under 1e-6 of m). Steps where
+// p and q are closer, or whose sums are not finite, take the exact form.
+constexpr double kCheapRatio = 7.0;
+__device__ __forceinline__ bool cheap_ok(double m, double q) { return q <= kCheapRatio * m; }
+
 // Unnormalised masses of 8 tokens (see SeqPlan for the forms). Residual mode,
 // FMA form: r_v = mag - g (e_p - mag) where p_v >= q_v, clamped at 0, else 0:
 // F Sp * max(0, p_v - q_v) with the normalisers' ratio corrected to first
@@ -716,11 +762,26 @@ __device__ __forceinline__ void load_octet(const char* row, int64_t oct, int V, 
   }
 }
 
-// Masses of 8 tokens in the draw's mode and the plan's form.
+// Masses of 8 tokens in the residual's cheap form, corrected to first order
+// as in mass8: r_v = max(0, e_p - e_q - g e_q) where p_v >= q_v, else 0.
+__device__ __forceinline__ void mass8_cheap(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P,
+                                            float (&r)[8]) {
+  const float gf = (float)P.g;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const CheapTerm t = cheap_term(xt[k], xd[k], P);
+    r[k] = t.pos ? fmaxf(fmaf(-gf, t.eq, t.ep - t.eq), 0.0f) : 0.0f;
+  }
+}
+
+// Masses of 8 tokens in the draw's mode and the plan's form (cheap: the
+// residual's cheap form, for a step whose sums took it).
 __device__ __forceinline__ void mass8_of(const float (&xt)[8], const float (&xd)[8], int mode, const SeqPlan& P,
-                                         float (&r)[8]) {
+                                         float (&r)[8], bool cheap = false) {
   if (mode == kModeResidual) {
-    if (P.form == 1)
+    if (P.form == 1 && cheap)
+      mass8_cheap(xt, xd, P, r);
+    else if (P.form == 1)
       mass8<kModeResidual, 1>(xt, xd, P, r);
     else
       mass8<kModeResidual, 0>(xt, xd, P, r);
@@ -733,30 +794,14 @@ __device__ __forceinline__ void mass8_of(const float (&xt)[8], const float (&xd)
 }
 
 // Token masses of step s of the draw row(s) for one wave: rr[j] is octet
-// s * kStepOctets + kWave * j + lane, all zero past the row's end. kBatch:
-// every load of the step is issued before the first mass is taken (one memory
-// round trip per step, not one per octet). Otherwise each octet is loaded
-// only where it exists, which needs fewer registers and, for rows of at most
-// kWave octets (only j = 0 exists), the same single round trip.
-template <int TD, int DD, bool kBatch = true>
-__device__ __forceinline__ void step_octet_masses(const char* trow, const char* drow, int64_t s, int64_t noct, int V,
-                                                  int mode, const SeqPlan& P, int lane, float (&rr)[kU2][8]) {
-  if constexpr (!kBatch) {
-#pragma unroll
-    for (int j = 0; j < kU2; ++j) {
-      const int64_t oct = s * kStepOctets + kWave * j + lane;
-      if (oct < noct) {
-        float xt[8], xd[8];
-        load_octet<TD>(trow, oct, V, xt);
-        if (mode != kModeBonus) load_octet<DD>(drow, oct, V, xd);
-        mass8_of(xt, xd, mode, P, rr[j]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
-      }
-    }
-    return;
-  }
+// s * kStepOctets + kWave * j + lane, all zero past the row's end. Every load
+// of the step is issued before the first mass is taken (one memory round
+// trip). cheap: the step's sums took the residual's cheap form (its masses
+// are then taken in that form, the ones its mass was summed from).
+template <int TD, int DD, bool kCheap>
+__device__ __forceinline__ void step_octet_masses_in(const char* trow, const char* drow, int64_t s, int64_t noct,
+                                                     int V, int mode, const SeqPlan& P, int lane,
+                                                     float (&rr)[kU2][8]) {
   OctetIn<TD> t[kU2];
   OctetIn<DD> d[kU2];
   if (mode != kModeBonus) {
@@ -777,7 +822,10 @@ __device__ __forceinline__ void step_octet_masses(const char* trow, const char* 
       float xt[8], xd[8];
       t[j].to_float(oct, V, xt);
       if (mode != kModeBonus) d[j].to_float(oct, V, xd);
-      mass8_of(xt, xd, mode, P, rr[j]);
+      if constexpr (kCheap)
+        mass8_cheap(xt, xd, P, rr[j]);
+      else
+        mass8_of(xt, xd, mode, P, rr[j]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
@@ -785,16 +833,27 @@ __device__ __forceinline__ void step_octet_masses(const char* trow, const char* 
   }
 }
 
+template <int TD, int DD>
+__device__ __forceinline__ void step_octet_masses(const char* trow, const char* drow, int64_t s, int64_t noct, int V,
+                                                  int mode, const SeqPlan& P, int lane, bool cheap,
+                                                  float (&rr)[kU2][8]) {
+  if (mode == kModeResidual && P.form == 1 && cheap)
+    step_octet_masses_in<TD, DD, true>(trow, drow, s, noct, V, mode, P, lane, rr);
+  else
+    step_octet_masses_in<TD, DD, false>(trow, drow, s, noct, V, mode, P, lane, rr);
+}
+
 // Per-step sums of the drawn distribution: m its mass; for the residual's
 // FMA form also q, the q-mass of its positive part (sum of e_q where
 // p_v >= q_v), and d, the signed sum of e_p - e_q over the step (the
-// first-order correction of the normalisers' ratio takes both; 0 otherwise).
+// first-order correction of the normalisers' ratio takes both; 0 otherwise);
+// c = 1 where the step's sums took the residual's cheap form, else 0.
 struct StepSums {
-  double m, q, d;
+  double m, q, d, c;
 };
 // Where the steps' sums go: LDS when the steps fit, else the workspace.
 struct StepOut {
-  double *m, *q, *d;
+  double *m, *q, *d, *c;
 };
 
 // The wave's sums of a step from its lanes' shares (r: residual, pe: e_p where
@@ -804,6 +863,7 @@ __device__ __forceinline__ StepSums wave_step_sums(double r, double pe, double a
   o.m = wave_sum(r);
   o.q = wave_sum(pe) - o.m;
   o.d = 2.0 * o.m - wave_sum(a);
+  o.c = 0.0;
   return o;
 }
 
@@ -823,20 +883,20 @@ struct HalfStep {
       if constexpr (MODE == kModeResidual) d[j].load(drow, oct);
     }
   }
-  // This lane's share of the half step's sums, added in octet order (only r
-  // outside the residual's FMA form).
+  // This lane's share of the half step's sums, added in octet order: in the
+  // residual's FMA form the cheap sums (r, q, d), else the masses r.
   template <int FORM>
-  __device__ __forceinline__ void sums(const SeqPlan& P, double& r, double& pe, double& a) const {
+  __device__ __forceinline__ void sums(const SeqPlan& P, double& r, double& q, double& dd) const {
 #pragma unroll
     for (int j = 0; j < kHalfU; ++j) {
       float xt[8], xd[8];
       t[j].unpack(xt);
       if constexpr (MODE == kModeResidual) d[j].unpack(xd);
       if constexpr (MODE == kModeResidual && FORM == 1) {
-        const ResidSums o = resid_sums8_checked(xt, xd, P);
+        const CheapSums o = cheap_sums8(xt, xd, P);
         r += (double)o.r;
-        pe += (double)o.pe;
-        a += (double)o.a;
+        q += (double)o.q;
+        dd += (double)o.d;
       } else {
         float rr[8];
         mass8<MODE, FORM>(xt, xd, P, rr);
@@ -846,10 +906,57 @@ struct HalfStep {
   }
 };
 
+// The exact-form sums of the octets of step s held in t, d (residual, FMA
+// form; octets at or past noct skipped), the NaN fix per octet.
+template <int TD, int DD>
+__device__ __forceinline__ StepSums exact_step_sums(const OctetIn<TD> (&t)[kU2], const OctetIn<DD> (&d)[kU2], int64_t s,
+                                                    int64_t noct, int V, const SeqPlan& P, int lane) {
+  double r = 0.0, pe = 0.0, a = 0.0;
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float xt[8], xd[8];
+      t[j].to_float(oct, V, xt);
+      d[j].to_float(oct, V, xd);
+      ResidSums o = resid_sums8<false>(xt, xd, P);
+      if (!(o.a == o.a)) o = resid_sums8<true>(xt, xd, P);
+      r += (double)o.r;
+      pe += (double)o.pe;
+      a += (double)o.a;
+    }
+  }
+  return wave_step_sums(r, pe, a);
+}
+
+// The same sums with each octet loaded on its own (the pipelined loop's
+// fallback, where a step's loads have left the registers): the same
+// operations in the same order, so the same bits, with fewer registers live.
+template <int TD, int DD>
+__device__ __forceinline__ StepSums exact_step_sums_reload(const char* trow, const char* drow, int64_t s,
+                                                           int64_t noct, int V, const SeqPlan& P, int lane) {
+  double r = 0.0, pe = 0.0, a = 0.0;
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float xt[8], xd[8];
+      load_octet<TD>(trow, oct, V, xt);
+      load_octet<DD>(drow, oct, V, xd);
+      ResidSums o = resid_sums8<false>(xt, xd, P);
+      if (!(o.a == o.a)) o = resid_sums8<true>(xt, xd, P);
+      r += (double)o.r;
+      pe += (double)o.pe;
+      a += (double)o.a;
+    }
+  }
+  return wave_step_sums(r, pe, a);
+}
+
 // The sums of step s of the draw row(s), every load of the step issued before
 // the first use, bounds-checked (every lane gets them). Inside the row these
 // are the same operations in the same order as the pipelined loop below, so
-// both give the same bits for a step.
+// both give the same bits for a step. In the residual's FMA form: the cheap
+// sums, or the exact ones where cheap_ok rejects them (from the same loads).
 template <int TD, int DD, int MODE, int FORM>
 __device__ __forceinline__ StepSums direct_step_sums(const char* trow, const char* drow, int64_t s, int64_t noct,
                                                      int V, const SeqPlan& P, int lane) {
@@ -861,7 +968,7 @@ __device__ __forceinline__ StepSums direct_step_sums(const char* trow, const cha
     t[j].load(trow, oct, noct, V);
     if constexpr (MODE == kModeResidual) d[j].load(drow, oct, noct, V);
   }
-  double r = 0.0, pe = 0.0, a = 0.0;
+  double r = 0.0, q = 0.0, dd = 0.0;
 #pragma unroll
   for (int j = 0; j < kU2; ++j) {
     const int64_t oct = s * kStepOctets + kWave * j + lane;
@@ -870,12 +977,10 @@ __device__ __forceinline__ StepSums direct_step_sums(const char* trow, const cha
       t[j].to_float(oct, V, xt);
       if constexpr (MODE == kModeResidual) d[j].to_float(oct, V, xd);
       if constexpr (MODE == kModeResidual && FORM == 1) {
-        // per octet with the fix (a bounds-checked, rarely taken path)
-        ResidSums o = resid_sums8<false>(xt, xd, P);
-        if (!(o.a == o.a)) o = resid_sums8<true>(xt, xd, P);
+        const CheapSums o = cheap_sums8(xt, xd, P);
         r += (double)o.r;
-        pe += (double)o.pe;
-        a += (double)o.a;
+        q += (double)o.q;
+        dd += (double)o.d;
       } else {
         float rr[8];
         mass8<MODE, FORM>(xt, xd, P, rr);
@@ -883,8 +988,12 @@ __device__ __forceinline__ StepSums direct_step_sums(const char* trow, const cha
       }
     }
   }
-  if constexpr (MODE == kModeResidual && FORM == 1) return wave_step_sums(r, pe, a);
-  return StepSums{wave_sum(r), 0.0, 0.0};
+  if constexpr (MODE == kModeResidual && FORM == 1) {
+    const StepSums v{wave_sum(r), wave_sum(q), wave_sum(dd), 1.0};
+    if (cheap_ok(v.m, v.q)) return v;
+    return exact_step_sums<TD, DD>(t, d, s, noct, V, P, lane);
+  }
+  return StepSums{wave_sum(r), 0.0, 0.0, 0.0};
 }
 
 template <int TD, int DD>
@@ -898,10 +1007,27 @@ __device__ __forceinline__ StepSums direct_step_sums_of(const char* trow, const 
   return direct_step_sums<TD, DD, kModeBonus, 0>(trow, drow, s, noct, V, P, lane);
 }
 
+// A whole step's sums in the pipelined loop from the lane's shares: in the
+// residual's FMA form the cheap ones, or, where cheap_ok rejects them, the
+// exact ones from the step loaded again (its data has left the registers;
+// a rare detour).
+template <int TD, int DD, int MODE, int FORM>
+__device__ __forceinline__ StepSums pipeline_step_sums(const char* trow, const char* drow, int64_t s, int64_t noct,
+                                                       int V, const SeqPlan& P, int lane, double r, double q,
+                                                       double dd) {
+  if constexpr (MODE == kModeResidual && FORM == 1) {
+    const StepSums v{wave_sum(r), wave_sum(q), wave_sum(dd), 1.0};
+    if (cheap_ok(v.m, v.q)) return v;
+    return exact_step_sums_reload<TD, DD>(trow, drow, s, noct, V, P, lane);
+  }
+  return StepSums{wave_sum(r), 0.0, 0.0, 0.0};
+}
+
 __device__ __forceinline__ void put_step(const StepOut& out, int s, const StepSums& v) {
   out.m[s] = v.m;
   out.q[s] = v.q;
   out.d[s] = v.d;
+  out.c[s] = v.c;
 }
 
 // Sums of the draw row(s) of sequence b over all steps; wave w of nw takes
@@ -918,7 +1044,6 @@ __device__ __forceinline__ void step_masses(const SampleLaunch& A, int b, const 
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   const int full_steps = A.V / kStepTokens;  // steps that lie wholly inside the row
   const int nmine = (full_steps > w) ? (full_steps - w + nw - 1) / nw : 0;  // this wave's whole steps
-  constexpr bool kAll = MODE == kModeResidual && FORM == 1;
   if (nmine > 0) {
     // every load is unconditional inside its block, so no buffer is copied
     // (a copy would wait for the loads in flight)
@@ -926,19 +1051,19 @@ __device__ __forceinline__ void step_masses(const SampleLaunch& A, int b, const 
     h0.load(trow, drow, w, 0, lane);
     int64_t st = w;
     for (int i = 0; i + 1 < nmine; ++i, st += nw) {
-      double r = 0.0, pe = 0.0, a = 0.0;
+      double r = 0.0, q = 0.0, dd = 0.0;
       h1.load(trow, drow, st, 1, lane);
-      h0.template sums<FORM>(P, r, pe, a);
+      h0.template sums<FORM>(P, r, q, dd);
       h0.load(trow, drow, st + nw, 0, lane);
-      h1.template sums<FORM>(P, r, pe, a);
-      const StepSums v = kAll ? wave_step_sums(r, pe, a) : StepSums{wave_sum(r), 0.0, 0.0};
+      h1.template sums<FORM>(P, r, q, dd);
+      const StepSums v = pipeline_step_sums<TD, DD, MODE, FORM>(trow, drow, st, noct, A.V, P, lane, r, q, dd);
       if (lane == 0) put_step(out, (int)st, v);
     }
-    double r = 0.0, pe = 0.0, a = 0.0;
+    double r = 0.0, q = 0.0, dd = 0.0;
     h1.load(trow, drow, st, 1, lane);
-    h0.template sums<FORM>(P, r, pe, a);
-    h1.template sums<FORM>(P, r, pe, a);
-    const StepSums v = kAll ? wave_step_sums(r, pe, a) : StepSums{wave_sum(r), 0.0, 0.0};
+    h0.template sums<FORM>(P, r, q, dd);
+    h1.template sums<FORM>(P, r, q, dd);
+    const StepSums v = pipeline_step_sums<TD, DD, MODE, FORM>(trow, drow, st, noct, A.V, P, lane, r, q, dd);
     if (lane == 0) put_step(out, (int)st, v);
   }
   // the ragged last step (if any), octet by octet
@@ -964,16 +1089,16 @@ __device__ __forceinline__ void all_step_masses(const SampleLaunch& A, int b, co
   }
 }
 
-// The workspace's step sums of sequence b ([3][ns2]: m, q, d).
+// The workspace's step sums of sequence b ([4][ns2]: m, q, d, c).
 __device__ __forceinline__ StepOut ws_steps(const SampleLaunch& A, int b) {
-  double* g = A.steptot + (int64_t)b * 3 * A.ns2;
-  return StepOut{g, g + A.ns2, g + 2 * A.ns2};
+  double* g = A.steptot + (int64_t)b * 4 * A.ns2;
+  return StepOut{g, g + A.ns2, g + 2 * A.ns2, g + 3 * A.ns2};
 }
 
-// Sentinels of a step's sums not yet published (m, q >= 0 and d finite for
-// every valid row).
-__device__ __forceinline__ bool step_published(double m, double q, double d) {
-  return m >= 0.0 && q >= 0.0 && d == d;
+// Sentinels of a step's sums not yet published (m, q, c >= 0 and d finite
+// for every valid row).
+__device__ __forceinline__ bool step_published(const StepSums& v) {
+  return v.m >= 0.0 && v.q >= 0.0 && v.d == v.d && v.c >= 0.0;
 }
 
 // The drawing part's copy of every step's sums of sequence b into LDS (wave w
@@ -996,17 +1121,18 @@ __device__ __forceinline__ void gather_steps(const SampleLaunch& A, int b, const
     const int s = base + lane;
     const bool in = s < A.ns2;
     const bool mine = (s % gnw) / kFinWaves == part;  // computed by this workgroup: already in LDS
-    StepSums v{0.0, 0.0, 0.0};
+    StepSums v{0.0, 0.0, 0.0, 0.0};
     if (in) {
       if (mine) {
-        v = StepSums{sh.m[s], sh.q[s], sh.d[s]};
+        v = StepSums{sh.m[s], sh.q[s], sh.d[s], sh.c[s]};
       } else {
         v.m = __hip_atomic_load(g.m + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         v.q = __hip_atomic_load(g.q + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         v.d = __hip_atomic_load(g.d + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.c = __hip_atomic_load(g.c + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    unsigned long long miss = __ballot(in && !step_published(v.m, v.q, v.d));
+    unsigned long long miss = __ballot(in && !step_published(v));
     while (miss) {
       const int L = __ffsll((long long)miss) - 1;
       miss &= miss - 1;
@@ -1018,6 +1144,7 @@ __device__ __forceinline__ void gather_steps(const SampleLaunch& A, int b, const
       __hip_atomic_store(g.m + s, -1.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(g.q + s, -1.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(g.d + s, __builtin_nan(""), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(g.c + s, -1.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1135,14 +1262,14 @@ __device__ __forceinline__ int scan_step(const float (&rr)[NJ][8], int ss, doubl
 
 // Rescan of step ss of the draw row(s) of sequence b by one wave: its token
 // masses, then the scan above.
-template <int TD, int DD, bool kBatch = true>
+template <int TD, int DD>
 __device__ __forceinline__ int rescan_step(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int ss, double t,
-                                           double acc, int lane) {
+                                           double acc, int lane, bool cheap) {
   const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
   const char* drow = (mode != kModeBonus) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
   float rr[kU2][8];
-  step_octet_masses<TD, DD, kBatch>(trow, drow, ss, noct, A.V, mode, P, lane, rr);
+  step_octet_masses<TD, DD>(trow, drow, ss, noct, A.V, mode, P, lane, cheap, rr);
   return scan_step<kU2>(rr, ss, t, acc, lane);
 }
 
@@ -1185,9 +1312,10 @@ __device__ __forceinline__ void write_invalid(const SampleLaunch& A, int b, int 
 // Inverse-CDF draw from the step masses stot[0..ns2) (total mass `total`) of
 // the draw row(s) of sequence b, then every output of the sequence, by wave 0
 // (the other waves return): lane k < gamma of wave 0 holds draft token k in xi.
+// scheap: the steps' form flags (null: no step took the cheap form).
 template <int TD, int DD>
 __device__ __forceinline__ void draw_and_write(const SampleLaunch& A, int b, const SeqPlan& P, int mode, const double* stot,
-                                               double total, int xi) {
+                                               const double* scheap, double total, int xi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (w != 0) return;
@@ -1197,7 +1325,8 @@ __device__ __forceinline__ void draw_and_write(const SampleLaunch& A, int b, con
   // wave_find returns -1 only if every mass is zero, which valid rows rule
   // out; clamp anyway so that no index can leave the arrays.
   const int ss = max(wave_find(stot, A.ns2, t, acc, lane), 0);
-  const int y = rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane);
+  const bool cheap = mode == kModeResidual && scheap && scheap[ss] > 0.5;
+  const int y = rescan_step<TD, DD>(A, b, P, mode, ss, t, acc, lane, cheap);
   // (6) outputs
   write_outputs<TD>(A, b, P, mode, y, total, lane, xi);
 }
@@ -1254,6 +1383,21 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
   return Q;
 }
 
+// A copy of a plan held in LDS, in scalar registers: the plan is the same for
+// the whole workgroup, and reading it word by word through readfirstlane
+// tells the compiler so (a plan in vector registers would take 24 of them).
+__device__ __forceinline__ SeqPlan uniform_plan(const SeqPlan& src) {
+  static_assert(sizeof(SeqPlan) % 4 == 0, "the plan is a whole number of 32-bit words");
+  constexpr int kWords = (int)(sizeof(SeqPlan) / 4);
+  uint32_t w[kWords];
+  __builtin_memcpy(w, &src, sizeof(SeqPlan));
+#pragma unroll
+  for (int k = 0; k < kWords; ++k) w[k] = __builtin_amdgcn_readfirstlane(w[k]);
+  SeqPlan P;
+  __builtin_memcpy(&P, w, sizeof(SeqPlan));
+  return P;
+}
+
 // ---------------------------------------------------------------------------
 // finish kernel: one 512-thread workgroup per sequence
 // ---------------------------------------------------------------------------
@@ -1272,7 +1416,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   __shared__ int sh_last;
   // step sums when the row has at most kLdsSteps steps: masses, q-masses of
   // the positive residual, signed sums of e_p - e_q
-  __shared__ double sh_steps[kLdsSteps], sh_q[kLdsSteps], sh_d[kLdsSteps];
+  __shared__ double sh_steps[kLdsSteps], sh_q[kLdsSteps], sh_d[kLdsSteps], sh_c[kLdsSteps];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loops over steps stay scalar
@@ -1396,7 +1540,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     }
   }
   __syncthreads();
-  const SeqPlan P = sP;
+  const SeqPlan P = uniform_plan(sP);
   if (!P.valid) {
     // every part reaches the same plan; part 0 writes the outputs
     if (part == 0) write_invalid(A, b, tid, 0, kFinThreads);
@@ -1413,7 +1557,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   // steps fit in LDS).
   int mode = P.mode;
   const bool lds_steps = A.ns2 <= kLdsSteps;
-  const StepOut sh_out{sh_steps, sh_q, sh_d};
+  const StepOut sh_out{sh_steps, sh_q, sh_d, sh_c};
   const StepOut st = lds_steps ? sh_out : ws_steps(A, b);
   if (lds_steps)
     all_step_masses<TD, DD>(A, b, P, mode, part * kFinWaves + w, K * kFinWaves, sh_out);
@@ -1430,6 +1574,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
         __hip_atomic_store(g.m + s, sh_steps[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(g.q + s, sh_q[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(g.d + s, sh_d[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(g.c + s, sh_c[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     __syncthreads();
     if (tid == 0) sh_last = __hip_atomic_fetch_add(A.done + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == K - 1;
@@ -1471,9 +1616,8 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     __syncthreads();
   }
   const double total = sh_total;
-  const double* stot = st.m;
 
-  draw_and_write<TD, DD>(A, b, Pd, mode, stot, total, xi);
+  draw_and_write<TD, DD>(A, b, Pd, mode, st.m, st.c, total, xi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1738,7 +1882,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     }
   }
   __syncthreads();
-  const SeqPlan P = sP;
+  const SeqPlan P = uniform_plan(sP);
   if (!P.valid) {
     if (tid == 0) {
       A.out_tok[b] = -1;
@@ -1746,7 +1890,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     }
     return;
   }
-  draw_and_write<DT, DT>(A, b, P, kModeBonus, stepS, sh_total, 0);
+  draw_and_write<DT, DT>(A, b, P, kModeBonus, stepS, nullptr, sh_total, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1903,10 +2047,11 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
       load_octet<TD>(trow, lane, A.V, xt);
       if (mode == kModeResidual) load_octet<DD>(drow, lane, A.V, xd);
     }
+    bool cheap = false;
     auto step_total = [&](int m, const SeqPlan& Q) -> double {
       double lacc = 0.0;
       if (have) {
-        mass8_of(xt, xd, m, Q, rr[0]);
+        mass8_of(xt, xd, m, Q, rr[0], cheap);
         lacc += (double)sum8(rr[0]);
       } else {
 #pragma unroll
@@ -1916,14 +2061,24 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
     };
     SeqPlan Pd = P;
     if (mode == kModeResidual && P.form == 1) {
-      // the first-order correction of the normalisers' ratio (see correct_steps)
-      double d = 0.0;
-      if (have) {
-        ResidSums o = resid_sums8<false>(xt, xd, P);
-        if (!(o.a == o.a)) o = resid_sums8<true>(xt, xd, P);
-        d = 2.0 * (double)o.r - (double)o.a;
+      // the step's form (see cheap_ok), then the first-order correction of
+      // the normalisers' ratio (see correct_steps) from its signed sum
+      CheapSums c{0.0f, 0.0f, 0.0f};
+      if (have) c = cheap_sums8(xt, xd, P);
+      const double cm = wave_sum((double)c.r), cq = wave_sum((double)c.q);
+      cheap = cheap_ok(cm, cq);
+      double d;
+      if (cheap) {
+        d = wave_sum((double)c.d);
+      } else {
+        d = 0.0;
+        if (have) {
+          ResidSums o = resid_sums8<false>(xt, xd, P);
+          if (!(o.a == o.a)) o = resid_sums8<true>(xt, xd, P);
+          d = 2.0 * (double)o.r - (double)o.a;
+        }
+        d = wave_sum(d);
       }
-      d = wave_sum(d);
       Pd.g = d / (P.sp * P.fscale - d);
     }
     double total = step_total(mode, Pd);  // the corrected terms, the same ones the scan takes
@@ -1931,6 +2086,7 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
       // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
       mode = kModeBonus;
       Pd.g = 0.0;
+      cheap = false;
       total = step_total(mode, Pd);
     }
     const int y = scan_step<1>(rr, 0, (double)P.ug * total, 0.0, lane);
@@ -1938,11 +2094,13 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
   } else {
     SeqPlan Pd = P;
     double total;
+    bool cheap = false;
     if (mode == kModeResidual && P.form == 1) {
       // the first-order correction of the normalisers' ratio (see correct_steps)
       const StepSums v = direct_step_sums<TD, DD, kModeResidual, 1>(trow, drow, 0, noct, A.V, P, lane);
       Pd.g = v.d / (P.sp * P.fscale - v.d);
       total = fmax(v.m - Pd.g * v.q, 0.0);
+      cheap = v.c > 0.5;
     } else {
       total = direct_step_sums_of<TD, DD>(trow, drow, 0, noct, A.V, mode, P, lane).m;
     }
@@ -1951,9 +2109,10 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
       mode = kModeBonus;
       Pd.g = 0.0;
       total = direct_step_sums_of<TD, DD>(trow, drow, 0, noct, A.V, mode, P, lane).m;
+      cheap = false;
     }
     const double t = (double)P.ug * total;
-    const int y = rescan_step<TD, DD>(A, b, Pd, mode, 0, t, 0.0, lane);
+    const int y = rescan_step<TD, DD>(A, b, Pd, mode, 0, t, 0.0, lane, cheap);
     write_outputs<TD>(A, b, Pd, mode, y, total, lane, xi);
   }
 }

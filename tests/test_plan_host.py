@@ -126,7 +126,7 @@ def test_workspace_layout(plan):
     assert all(x % 256 == 0 for x in (step, reach, done, total))
     # partials: B (2 gamma + 1) rows x ceil(4 V / 16 KB) chunks x 4 waves x 16 B
     assert step >= 64 * 9 * math.ceil(4 * 32000 / (16 << 10)) * 4 * 16
-    assert reach - step >= 64 * 3 * math.ceil(32000 / 2048) * 8     # step sums
+    assert reach - step >= 64 * 4 * math.ceil(32000 / 2048) * 8     # step sums
     assert total_v2 > total and total_b2 > total
 
 
@@ -140,11 +140,11 @@ def test_row_split(plan):
 
 
 def test_step_sums(plan):
-    # three fp64 sums per draw step and sequence (mass, q-mass of the positive
-    # residual, signed sum): LDS overflow and the finish parts' hand-off
+    # four fp64 values per draw step and sequence (mass, q-mass of the positive
+    # residual, signed sum, form flag): LDS overflow and the finish parts' hand-off
     step, reach, small = plan["steps3"]
-    assert reach - step == -(-3 * 3 * -(-5000000 // 2048) * 8 // 256) * 256
-    assert small == -(-64 * 3 * 16 * 8 // 256) * 256
+    assert reach - step == -(-3 * 4 * -(-5000000 // 2048) * 8 // 256) * 256
+    assert small == -(-64 * 4 * 16 * 8 // 256) * 256
 
 
 def test_largest_shapes(plan):
@@ -155,7 +155,7 @@ def test_largest_shapes(plan):
     B, G, V = 1 << 24, 64, 1 << 30
     assert steps == V // 2048
     # partials of (2 gamma + 1) rows of up to V * 4 / 16 KB chunks, plus the step masses
-    assert lay_total >= B * (2 * G + 1) * (V * 4 // (16 << 10)) * 4 * 16 + B * 3 * steps * 8
+    assert lay_total >= B * (2 * G + 1) * (V * 4 // (16 << 10)) * 4 * 16 + B * 4 * steps * 8
     assert lay_total < 1 << 62 and tree_total >= B * 1024 * (V * 4 // (16 << 10)) * 16
     assert (16 << 10) <= chunk <= (256 << 10) and cu % 1024 == 0 and nch * cu * 16 >= V * 4
     assert parts == 1 and 0 <= tail <= G
