@@ -162,14 +162,42 @@ __device__ __forceinline__ void stream_sumexp(const char* __restrict__ row, int 
   int64_t full_end = c_end;
   if (ragged && full_end > nu_row - 1) full_end = nu_row - 1;
   int64_t base = c_begin;
-  for (; base + (int64_t)kThreads * kU1 <= full_end; base += (int64_t)kThreads * kU1) {
-    uint4 w[kU1];
+  // Whole batches, two buffers deep: the loads of the next batch are in
+  // flight while the current one is summed (no buffer is copied: a copy
+  // would wait for its loads).
+  constexpr int64_t BU = (int64_t)kThreads * kU1;
+  const int64_t nb = full_end > base ? (full_end - base) / BU : 0;
+  if (nb > 0) {
+    auto load_batch = [&](uint4 (&w)[kU1], int64_t at) {
 #pragma unroll
-    for (int j = 0; j < kU1; ++j) w[j] = load16(row + (base + tid + kThreads * j) * 16);
-    Unit<DT> un[kU1];
+      for (int j = 0; j < kU1; ++j) w[j] = load16(row + (at + tid + kThreads * j) * 16);
+    };
+    auto sum_batch = [&](const uint4 (&w)[kU1]) {
+      Unit<DT> un[kU1];
 #pragma unroll
-    for (int j = 0; j < kU1; ++j) un[j].unpack(w[j]);
-    sumexp<DT, kU1>(st, un, kl);
+      for (int j = 0; j < kU1; ++j) un[j].unpack(w[j]);
+      sumexp<DT, kU1>(st, un, kl);
+      // the batch is summed before the next loads are issued (else the
+      // compiler holds two batches of values in registers at once)
+      __asm__ volatile("" : "+v"(st.s)::"memory");
+    };
+    uint4 a[kU1], b[kU1];
+    load_batch(a, base);
+    int64_t i = 0;
+    for (; i + 2 < nb; i += 2) {
+      load_batch(b, base + (i + 1) * BU);
+      sum_batch(a);
+      load_batch(a, base + (i + 2) * BU);
+      sum_batch(b);
+    }
+    if (i + 1 < nb) {
+      load_batch(b, base + (i + 1) * BU);
+      sum_batch(a);
+      sum_batch(b);
+    } else {
+      sum_batch(a);
+    }
+    base += nb * BU;
   }
   // The tail (fewer than kU1 units per thread left): every load is issued
   // before the first term is taken, so the chunk ends one memory round trip

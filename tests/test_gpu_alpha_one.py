@@ -78,7 +78,7 @@ def _realised_alpha(inp, nseq=3) -> float:
     return float(np.mean(vals))
 
 
-def _check_paths(gpu, inp, name, paths):
+def _check_paths(gpu, inp, name, paths, min_resid_frac=1 / 3):
     tens = H.sample_tensors(inp)
     for path in paths:
         if path == "one_pass":
@@ -97,7 +97,7 @@ def _check_paths(gpu, inp, name, paths):
               f"residual_draws={rejected}/{inp.B}")
         assert not t.fail, t.fail[:5]
         assert t.flagged <= max(2, inp.B // 50)
-        assert rejected >= inp.B // 3, "too few residual draws to exercise the regime"
+        assert rejected >= int(inp.B * min_resid_frac), "too few residual draws to exercise the regime"
 
 
 @pytest.mark.parametrize("goal", [0.95, 0.99, 0.999])
@@ -128,3 +128,47 @@ def test_alpha_near_one_small_vocab(gpu, V, goal):
     inp, sd = aligned_inputs(48, 6, V, "f32", "f32", goal, T=1.0, seed=V + int(goal * 1000))
     H.log(f"alpha~{goal} V={V} noise sd {sd:.4g} realised alpha {_realised_alpha(inp):.5f}")
     _check_paths(gpu, inp, f"alpha~{goal} V={V}", ["one_pass", "staged", "early_gated"])
+
+
+def mixed_form_inputs(B, G, V, tdt, ddt, seed):
+    """Rows whose 2048-token steps alternate: even steps carry most of the
+    mass with the draft within N(0, 0.02) of the target (a residual much
+    smaller than its q-mass: the exact form), odd steps carry the rest with
+    N(0, 1) draft noise (the cheap form). Drafts are drawn from the new q;
+    accept uniforms near 1 send most sequences to the residual."""
+    inp = synth.make_custom_sample(B, G, V, tdt, ddt, T=1.0, noise_sd=1.0, seed=seed, cid=121)
+    g = np.random.default_rng(seed + 11)
+    even = ((np.arange(V) // 2048) % 2) == 0
+    for b in range(B):
+        t = synth.decode(inp.target[b], tdt).astype(np.float32)
+        t[:, even] += np.float32(3.0)
+        tq = synth._to_dtype(t, tdt)
+        inp.target[b] = tq
+        tr = synth.decode(tq, tdt).astype(np.float32)[:G]
+        sd = np.where(even, np.float32(0.02), np.float32(1.0)).astype(np.float32)
+        d = tr + g.standard_normal(tr.shape, dtype=np.float32) * sd
+        dq = synth._to_dtype(d, ddt)
+        inp.draft[b] = dq
+        dr = synth.decode(dq, ddt).astype(np.float64)
+        for i in range(G):
+            inp.tokens[b, i] = int(np.argmax(dr[i] - np.log(-np.log(g.random(V)))))
+    k = g.integers(int(0.999 * (1 << 24)), 1 << 24, size=(B, G))
+    inp.uniforms[:, :G] = (k.astype(np.float64) * 2.0 ** -24).astype(np.float32)
+    return inp
+
+
+@pytest.mark.parametrize("V,tdt,ddt", [(32000, "bf16", "f32"), (128256, "bf16", "bf16")])
+def test_mixed_step_forms(gpu, V, tdt, ddt):
+    """Sequences whose draw rows mix steps in the residual's exact and cheap
+    forms (each 2048-token step takes its own): parity on every path, and
+    draws land in steps of both forms."""
+    inp = mixed_form_inputs(96, 3, V, tdt, ddt, seed=V % 89)
+    _check_paths(gpu, inp, f"mixed forms V={V} {tdt}/{ddt}", ["one_pass", "staged", "early"], min_resid_frac=0.2)
+    out = H.run_sample(gpu, H.sample_tensors(inp))
+    n = out["n"]
+    y = out["tokens"][np.arange(inp.B), np.clip(n, 0, inp.gamma)]
+    resid = (n >= 0) & (n < inp.gamma)
+    steps = (y[resid] // 2048) % 2
+    H.log(f"[mixed forms V={V}] residual draws {resid.sum()}: in even (exact) steps {int((steps == 0).sum())}, "
+          f"odd (cheap) {int((steps == 1).sum())}")
+    assert (steps == 0).sum() >= 3 and (steps == 1).sum() >= 3
