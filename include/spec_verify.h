@@ -33,7 +33,14 @@
  *    mutable state apart from the thread-local last HIP error and the
  *    per-device address of spec_verify_sample_noalloc's static array (set once
  *    per device, under a lock).
- *  - Results are deterministic: the same inputs give the same bits.
+ *  - Results are deterministic: the same inputs give the same bits. A
+ *    sequence's results barely depend on the batch it is verified in (its
+ *    batch size, its place in the batch, the split of its rows into work
+ *    chunks): every fp32 rounding of its statistics is taken over fixed 16 KB
+ *    blocks of its rows, and only fp64 sums of those blocks' results are
+ *    grouped differently. The reported probabilities then differ by fp64
+ *    rounding, and a decision or token differs only where a quantity lies
+ *    within that rounding of its boundary.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -305,7 +312,6 @@ int spec_verify_greedy_tree_stage(int stage, const void* target_logits, int dtyp
                                   int V, int32_t* out_accept_len, int32_t* out_path, int32_t* out_bonus,
                                   int32_t* out_argmax, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Text of a status code (static storage). */
 /*
  * spec_tree_mask -- attention masks and positions of B draft trees.
  *
@@ -330,6 +336,7 @@ int spec_verify_greedy_tree_stage(int stage, const void* target_logits, int dtyp
 int spec_tree_mask(const int32_t* parents, const int32_t* blocks, int B, int N, uint8_t* out_mask,
                    uint8_t* out_relaxed, int32_t* out_depth, void* stream);
 
+/* Text of a status code (static storage). */
 const char* sv_status_string(int status);
 
 /* hipError_t of the last failed HIP call made by this thread inside the library (0 = none). */
