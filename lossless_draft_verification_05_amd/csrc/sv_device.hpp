@@ -142,6 +142,14 @@ __device__ __forceinline__ double wave_sum(double v) {
   v += dpp_f64<kDppRowRor8>(v);
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
+// The same fixed-order reduction in fp32 (every lane gets the sum).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowRor4>(v);
+  v += dpp_f32<kDppRowRor8>(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
 
 // (value desc, index asc) argmax; NaN values never enter (callers flag them).
 __device__ __forceinline__ void arg_combine(float& v, int& i, float v2, int i2) {

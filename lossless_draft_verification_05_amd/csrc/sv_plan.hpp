@@ -63,8 +63,8 @@ struct RowPartial {
 //    the signed sum of e_p - e_q over the row. r = F sp * max(0, p - q).
 //    A 2048-token step whose positive residual is not small next to its
 //    q-mass takes the cheap form instead: e_p = exp2(fma(x_t, kl, -cp)) and
-//    e_q = exp2(fma(x_d, kl, -cq) - cq_lo), one exponential each, the side
-//    of each token still from w (see cheap_ok in sv_sample.hip).
+//    e_q = cq_s * exp2(fma(x_d, kl, -cq)), one exponential each, the token's
+//    residual t = e_p - e_q where t > 0 (see cheap_ok in sv_sample.hip).
 //  form 0 (used when a shift is 2^24 or more in magnitude, where its fp32
 //  rounding would be half a log2 unit or more):
 //    e_p = exp2((x_t - mp) * kl), e_q = exp2((x_d - mq) * kl),
@@ -81,6 +81,7 @@ struct SeqPlan {
   float kap_lo;
   float cp, cq;
   float cq_lo;    // cqx - cq
+  float cq_s;     // 2^(cq - cqx), fp32: the cheap form's factor of e_q
   float dt;       // fp32(cp - cqx): log2(q_v / p_v) - (x_d - x_t) * kl
   float ug;       // the draw's uniform
   double ct;      // shift of target row n (log2 units)

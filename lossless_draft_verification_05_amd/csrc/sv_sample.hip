@@ -670,25 +670,27 @@ __device__ __forceinline__ ResidSums resid_sums8_checked(const float (&xt)[8], c
 
 // The residual's cheap form (FMA shifts): e_p and e_q from one exponential
 // each (e_q straight from the draft logit, so logits of -inf give 0 and no
-// NaN), the side of each token from w = log2(q_v / p_v) as in the exact form.
-// Each exponential carries its own rounding, so e_p - e_q is off by a few
-// units of fp32 rounding of e_p wherever p and q are close; a step whose
-// positive residual is small next to its q-mass takes the exact form instead
-// (cheap_ok). Where p_v >= q_v the token's residual is max(e_p - e_q, 0).
+// NaN). The draft's shift is the fp32 head cq of cqx; the rest of it is the
+// factor cq_s = 2^-(cqx - cq), applied in the difference's FMA: e1 =
+// exp2(fma(x_d, kl, -cq)), e_q = cq_s e1, t = e_p - e_q = fma(-cq_s, e1, e_p).
+// A token lies on the residual's side where t > 0, and its residual is t there.
+// Each exponential carries its own rounding, so t is off by a few units of
+// fp32 rounding of e_p wherever p and q are close; a step whose positive
+// residual is small next to its q-mass takes the exact form instead
+// (cheap_ok).
 struct CheapTerm {
-  float ep, eq;
-  bool pos;
+  float e1, t;
 };
 __device__ __forceinline__ CheapTerm cheap_term(float xt, float xd, const SeqPlan& P) {
-  CheapTerm t;
-  t.pos = fmaf(xd - xt, P.kl, P.dt) <= 0.0f;
-  t.ep = hw_exp2(fmaf(xt, P.kl, -P.cp));
-  t.eq = hw_exp2(fmaf(xd, P.kl, -P.cq) - P.cq_lo);
-  return t;
+  CheapTerm c;
+  const float ep = hw_exp2(fmaf(xt, P.kl, -P.cp));
+  c.e1 = hw_exp2(fmaf(xd, P.kl, -P.cq));
+  c.t = fmaf(-P.cq_s, c.e1, ep);
+  return c;
 }
 
 // Sums over the 8 tokens of an octet in the cheap form: r = the residual, q =
-// e_q where p >= q (the q-mass of the positive residual), d = e_p - e_q over
+// e_q where t > 0 (the q-mass of the positive residual), d = e_p - e_q over
 // all 8 (the signed sum). Pairwise fp32 sums, as sum8.
 struct CheapSums {
   float r, q, d;
@@ -697,13 +699,12 @@ __device__ __forceinline__ CheapSums cheap_sums8(const float (&xt)[8], const flo
   float r[8], q[8], d[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const CheapTerm t = cheap_term(xt[k], xd[k], P);
-    const float df = t.ep - t.eq;
-    r[k] = t.pos ? fmaxf(df, 0.0f) : 0.0f;
-    q[k] = t.pos ? t.eq : 0.0f;
-    d[k] = df;
+    const CheapTerm c = cheap_term(xt[k], xd[k], P);
+    r[k] = fmaxf(c.t, 0.0f);
+    q[k] = c.t > 0.0f ? c.e1 : 0.0f;
+    d[k] = c.t;
   }
-  return CheapSums{sum8(r), sum8(q), sum8(d)};
+  return CheapSums{sum8(r), sum8(q) * P.cq_s, sum8(d)};
 }
 
 // Whether a step's cheap sums stand: its positive residual m is at least
@@ -712,6 +713,19 @@ __device__ __forceinline__ CheapSums cheap_sums8(const float (&xt)[8], const flo
 // p and q are closer, or whose sums are not finite, take the exact form.
 constexpr double kCheapRatio = 7.0;
 __device__ __forceinline__ bool cheap_ok(double m, double q) { return q <= kCheapRatio * m; }
+
+// A lane's cheap sums over a step, added octet by octet in fp32 and reduced
+// over the wave in fp32 (wave_sum_f32): a step's 2048 terms pass about a
+// dozen fp32 roundings, well under 1e-6 of the step's mass, and the cheap
+// form only stands where the residual is not small next to the terms.
+struct CheapAcc {
+  float r = 0.0f, q = 0.0f, d = 0.0f;
+  __device__ __forceinline__ void add(const CheapSums& o) {
+    r += o.r;
+    q += o.q;
+    d += o.d;
+  }
+};
 
 // Unnormalised masses of 8 tokens (see SeqPlan for the forms). Residual mode,
 // FMA form: r_v = mag - g (e_p - mag) where p_v >= q_v, clamped at 0, else 0:
@@ -791,14 +805,14 @@ __device__ __forceinline__ void load_octet(const char* row, int64_t oct, int V, 
 }
 
 // Masses of 8 tokens in the residual's cheap form, corrected to first order
-// as in mass8: r_v = max(0, e_p - e_q - g e_q) where p_v >= q_v, else 0.
+// as in mass8: r_v = max(0, t - g e_q) where t = e_p - e_q > 0, else 0.
 __device__ __forceinline__ void mass8_cheap(const float (&xt)[8], const float (&xd)[8], const SeqPlan& P,
                                             float (&r)[8]) {
-  const float gf = (float)P.g;
+  const float gs = (float)(P.g * (double)P.cq_s);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const CheapTerm t = cheap_term(xt[k], xd[k], P);
-    r[k] = t.pos ? fmaxf(fmaf(-gf, t.eq, t.ep - t.eq), 0.0f) : 0.0f;
+    const CheapTerm c = cheap_term(xt[k], xd[k], P);
+    r[k] = c.t > 0.0f ? fmaxf(fmaf(-gs, c.e1, c.t), 0.0f) : 0.0f;
   }
 }
 
@@ -895,6 +909,11 @@ __device__ __forceinline__ StepSums wave_step_sums(double r, double pe, double a
   return o;
 }
 
+// The wave's cheap sums of a step (c = 1), every lane gets them.
+__device__ __forceinline__ StepSums cheap_step_sums(const CheapAcc& a) {
+  return StepSums{(double)wave_sum_f32(a.r), (double)wave_sum_f32(a.q), (double)wave_sum_f32(a.d), 1.0};
+}
+
 // Raw loads of half a step (1024 tokens) of the draw row(s) for one wave:
 // kU2 / 2 octets per lane per row. Only used where the step lies inside the row.
 constexpr int kHalfU = kU2 / 2;
@@ -911,25 +930,29 @@ struct HalfStep {
       if constexpr (MODE == kModeResidual) d[j].load(drow, oct);
     }
   }
-  // This lane's share of the half step's sums, added in octet order: in the
-  // residual's FMA form the cheap sums (r, q, d), else the masses r.
+  // This lane's share of the half step's masses r, added in octet order
+  // (bonus mode, or the residual's subtract form).
   template <int FORM>
-  __device__ __forceinline__ void sums(const SeqPlan& P, double& r, double& q, double& dd) const {
+  __device__ __forceinline__ void sums(const SeqPlan& P, double& r) const {
 #pragma unroll
     for (int j = 0; j < kHalfU; ++j) {
       float xt[8], xd[8];
       t[j].unpack(xt);
       if constexpr (MODE == kModeResidual) d[j].unpack(xd);
-      if constexpr (MODE == kModeResidual && FORM == 1) {
-        const CheapSums o = cheap_sums8(xt, xd, P);
-        r += (double)o.r;
-        q += (double)o.q;
-        dd += (double)o.d;
-      } else {
-        float rr[8];
-        mass8<MODE, FORM>(xt, xd, P, rr);
-        r += (double)sum8(rr);
-      }
+      float rr[8];
+      mass8<MODE, FORM>(xt, xd, P, rr);
+      r += (double)sum8(rr);
+    }
+  }
+  // This lane's share of the half step's cheap sums (r, q, d; the residual's
+  // FMA form), added in octet order in fp32 (see CheapAcc).
+  __device__ __forceinline__ void cheap_sums(const SeqPlan& P, CheapAcc& a) const {
+#pragma unroll
+    for (int j = 0; j < kHalfU; ++j) {
+      float xt[8], xd[8];
+      t[j].unpack(xt);
+      d[j].unpack(xd);
+      a.add(cheap_sums8(xt, xd, P));
     }
   }
 };
@@ -996,7 +1019,8 @@ __device__ __forceinline__ StepSums direct_step_sums(const char* trow, const cha
     t[j].load(trow, oct, noct, V);
     if constexpr (MODE == kModeResidual) d[j].load(drow, oct, noct, V);
   }
-  double r = 0.0, q = 0.0, dd = 0.0;
+  double r = 0.0;
+  CheapAcc a;
 #pragma unroll
   for (int j = 0; j < kU2; ++j) {
     const int64_t oct = s * kStepOctets + kWave * j + lane;
@@ -1005,10 +1029,7 @@ __device__ __forceinline__ StepSums direct_step_sums(const char* trow, const cha
       t[j].to_float(oct, V, xt);
       if constexpr (MODE == kModeResidual) d[j].to_float(oct, V, xd);
       if constexpr (MODE == kModeResidual && FORM == 1) {
-        const CheapSums o = cheap_sums8(xt, xd, P);
-        r += (double)o.r;
-        q += (double)o.q;
-        dd += (double)o.d;
+        a.add(cheap_sums8(xt, xd, P));
       } else {
         float rr[8];
         mass8<MODE, FORM>(xt, xd, P, rr);
@@ -1017,7 +1038,7 @@ __device__ __forceinline__ StepSums direct_step_sums(const char* trow, const cha
     }
   }
   if constexpr (MODE == kModeResidual && FORM == 1) {
-    const StepSums v{wave_sum(r), wave_sum(q), wave_sum(dd), 1.0};
+    const StepSums v = cheap_step_sums(a);
     if (cheap_ok(v.m, v.q)) return v;
     return exact_step_sums<TD, DD>(t, d, s, noct, V, P, lane);
   }
@@ -1039,16 +1060,13 @@ __device__ __forceinline__ StepSums direct_step_sums_of(const char* trow, const 
 // residual's FMA form the cheap ones, or, where cheap_ok rejects them, the
 // exact ones from the step loaded again (its data has left the registers;
 // a rare detour).
-template <int TD, int DD, int MODE, int FORM>
-__device__ __forceinline__ StepSums pipeline_step_sums(const char* trow, const char* drow, int64_t s, int64_t noct,
-                                                       int V, const SeqPlan& P, int lane, double r, double q,
-                                                       double dd) {
-  if constexpr (MODE == kModeResidual && FORM == 1) {
-    const StepSums v{wave_sum(r), wave_sum(q), wave_sum(dd), 1.0};
-    if (cheap_ok(v.m, v.q)) return v;
-    return exact_step_sums_reload<TD, DD>(trow, drow, s, noct, V, P, lane);
-  }
-  return StepSums{wave_sum(r), 0.0, 0.0, 0.0};
+template <int TD, int DD>
+__device__ __forceinline__ StepSums pipeline_cheap_step_sums(const char* trow, const char* drow, int64_t s,
+                                                             int64_t noct, int V, const SeqPlan& P, int lane,
+                                                             const CheapAcc& a) {
+  const StepSums v = cheap_step_sums(a);
+  if (cheap_ok(v.m, v.q)) return v;
+  return exact_step_sums_reload<TD, DD>(trow, drow, s, noct, V, P, lane);
 }
 
 __device__ __forceinline__ void put_step(const StepOut& out, int s, const StepSums& v) {
@@ -1078,20 +1096,31 @@ __device__ __forceinline__ void step_masses(const SampleLaunch& A, int b, const 
     HalfStep<TD, DD, MODE> h0, h1;
     h0.load(trow, drow, w, 0, lane);
     int64_t st = w;
+    // the sums of one step from the two halves in its buffers (h1 loaded by
+    // the caller just before); NEXT: load the next step's first half into h0
+    // between the halves
+    auto step = [&](int64_t s, bool next) {
+      if constexpr (MODE == kModeResidual && FORM == 1) {
+        CheapAcc a;
+        h0.cheap_sums(P, a);
+        if (next) h0.load(trow, drow, s + nw, 0, lane);
+        h1.cheap_sums(P, a);
+        return pipeline_cheap_step_sums<TD, DD>(trow, drow, s, noct, A.V, P, lane, a);
+      } else {
+        double r = 0.0;
+        h0.template sums<FORM>(P, r);
+        if (next) h0.load(trow, drow, s + nw, 0, lane);
+        h1.template sums<FORM>(P, r);
+        return StepSums{wave_sum(r), 0.0, 0.0, 0.0};
+      }
+    };
     for (int i = 0; i + 1 < nmine; ++i, st += nw) {
-      double r = 0.0, q = 0.0, dd = 0.0;
       h1.load(trow, drow, st, 1, lane);
-      h0.template sums<FORM>(P, r, q, dd);
-      h0.load(trow, drow, st + nw, 0, lane);
-      h1.template sums<FORM>(P, r, q, dd);
-      const StepSums v = pipeline_step_sums<TD, DD, MODE, FORM>(trow, drow, st, noct, A.V, P, lane, r, q, dd);
+      const StepSums v = step(st, true);
       if (lane == 0) put_step(out, (int)st, v);
     }
-    double r = 0.0, q = 0.0, dd = 0.0;
     h1.load(trow, drow, st, 1, lane);
-    h0.template sums<FORM>(P, r, q, dd);
-    h1.template sums<FORM>(P, r, q, dd);
-    const StepSums v = pipeline_step_sums<TD, DD, MODE, FORM>(trow, drow, st, noct, A.V, P, lane, r, q, dd);
+    const StepSums v = step(st, false);
     if (lane == 0) put_step(out, (int)st, v);
   }
   // the ragged last step (if any), octet by octet
@@ -1391,6 +1420,7 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
     const double cqx = dn.c - log2(Q.sp / Q.sq) - dp;
     Q.cq = (float)cqx;
     Q.cq_lo = (float)(cqx - (double)Q.cq);
+    Q.cq_s = (float)exp2((double)Q.cq - cqx);
     Q.dt = (float)((double)Q.cp - cqx);
     fma_ok = fma_ok && fabs(cqx) < 0x1p24;
     const double Fq = exp2(dn.c - (double)dn.m * kld);
@@ -1404,6 +1434,7 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
     Q.kap_lo = 0.0f;
     Q.cq = 0.0f;
     Q.cq_lo = 0.0f;
+    Q.cq_s = 1.0f;
     Q.dt = 0.0f;
   }
   Q.form = fma_ok ? 1 : 0;
@@ -1901,6 +1932,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       Q.ct = Ms;
       Q.cp = sub ? 0.0f : (float)Ms;
       Q.cq = Q.cq_lo = Q.dt = 0.0f;
+      Q.cq_s = 1.0f;
       Q.fscale = 1.0;
       Q.sp = total;
       Q.sq = 1.0;
