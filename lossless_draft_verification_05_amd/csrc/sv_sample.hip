@@ -375,8 +375,9 @@ struct AcceptOut {
   int code;
   float px, qx;
 };
+// want_p: also p(x) and q(x) (else NaN; the decision is the same either way).
 __device__ __forceinline__ AcceptOut accept_test(float lt, float ld, const RowStat& t, const RowStat& d, float kl,
-                                                 float u, bool tok_ok, bool tv) {
+                                                 float u, bool tok_ok, bool tv, bool want_p) {
 #pragma clang fp contract(off)
   AcceptOut o;
   o.px = __builtin_nanf("");
@@ -386,8 +387,10 @@ __device__ __forceinline__ AcceptOut accept_test(float lt, float ld, const RowSt
     const double lp2 = (double)lt * (double)kl - t.c;  // the product of two floats is exact
     const double lq2 = (double)ld * (double)kl - d.c;
     const double rho = exp2(lp2 - lq2) * (d.s / t.s);
-    o.px = (float)(exp2(lp2) / t.s);
-    o.qx = (float)(exp2(lq2) / d.s);
+    if (want_p) {
+      o.px = (float)(exp2(lp2) / t.s);
+      o.qx = (float)(exp2(lq2) / d.s);
+    }
     o.code = ((double)u < rho) ? 1 : 0;
   } else {
     o.code = 2;
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void sv_stats_pos_kernel(SampleLaunch A, 
     if (tid == 0) {
       const int xi = A.tokens[(int64_t)b * G + i];
       const float ui = A.uniforms[(int64_t)b * (G + 1) + i];
-      const AcceptOut ao = accept_test(sh_g[0], sh_g[1], sh_rs[0], sh_rs[1], kl, ui, xi >= 0 && xi < A.V, tv);
+      const AcceptOut ao = accept_test(sh_g[0], sh_g[1], sh_rs[0], sh_rs[1], kl, ui, xi >= 0 && xi < A.V, tv, false);
       sh_go = ao.code == 1;
       if (ao.code == 1) A.reach[b] = p1 + 1;
     }
@@ -1409,11 +1412,10 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
   const double kld = (double)kl;
   Q.cp = (float)tn.c;  // exact for the integer shifts of the statistics pass
   const double dp = tn.c - (double)Q.cp;
-  Q.fscale = exp2(dp);
   // the shifts must round by less than half a log2 unit: |c| < 2^24
   bool fma_ok = fabs(tn.c) < 0x1p24;
-  // subtract form: e_p = exp2((x_t - mp) * kl) = p_v * sp * Fp
-  const double Fp = exp2(tn.c - (double)tn.m * kld);
+  Q.kap_hi = 0.0f;
+  Q.kap_lo = 0.0f;
   if (n < G) {
     Q.mq = dn.m;
     Q.sq = dn.s;
@@ -1423,22 +1425,28 @@ __device__ __forceinline__ SeqPlan make_plan(int n, int code_n, int G, int nst, 
     Q.cq_s = (float)exp2((double)Q.cq - cqx);
     Q.dt = (float)((double)Q.cp - cqx);
     fma_ok = fma_ok && fabs(cqx) < 0x1p24;
-    const double Fq = exp2(dn.c - (double)dn.m * kld);
-    const double kap = (Q.sp * Fp) / (Q.sq * Fq);
-    Q.kap_hi = (float)kap;
-    Q.kap_lo = (float)(kap - (double)Q.kap_hi);
   } else {
     Q.mq = 0.0f;
     Q.sq = 1.0;
-    Q.kap_hi = 0.0f;
-    Q.kap_lo = 0.0f;
     Q.cq = 0.0f;
     Q.cq_lo = 0.0f;
     Q.cq_s = 1.0f;
     Q.dt = 0.0f;
   }
   Q.form = fma_ok ? 1 : 0;
-  if (!fma_ok) Q.fscale = Fp;
+  if (fma_ok) {
+    Q.fscale = (dp == 0.0) ? 1.0 : exp2(dp);  // 1 for the integer shifts of the statistics pass
+  } else {
+    // subtract form: e_p = exp2((x_t - mp) * kl) = p_v * sp * Fp, kappa = (sp Fp) / (sq Fq)
+    const double Fp = exp2(tn.c - (double)tn.m * kld);
+    Q.fscale = Fp;
+    if (n < G) {
+      const double Fq = exp2(dn.c - (double)dn.m * kld);
+      const double kap = (Q.sp * Fp) / (Q.sq * Fq);
+      Q.kap_hi = (float)kap;
+      Q.kap_lo = (float)(kap - (double)Q.kap_hi);
+    }
+  }
   return Q;
 }
 
@@ -1578,7 +1586,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       float pxo = __builtin_nanf(""), qxo = __builtin_nanf("");
       if (i < nst) {
         const RowStat ts{rC[i], rM[i], rS[i], rV[i]}, ds{rC[G + 1 + i], rM[G + 1 + i], rS[G + 1 + i], rV[G + 1 + i]};
-        const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv);
+        const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv, A.diag_px || A.diag_qx);
         code = ao.code;
         pxo = ao.px;
         qxo = ao.qx;
@@ -2074,7 +2082,7 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
   if (lane < G) {
     const RowStat ts = stat(m0, s0, v0);
     const RowStat ds = (j < kWave) ? stat(dm0, ds0, dv0) : (j < 2 * kWave ? stat(dm1, ds1, dv1) : stat(dm2, ds2, dv2));
-    const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv);
+    const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv, A.diag_px || A.diag_qx);
     code = ao.code;
     if (A.diag_px) A.diag_px[(int64_t)b * G + lane] = ao.px;
     if (A.diag_qx) A.diag_qx[(int64_t)b * G + lane] = ao.qx;
