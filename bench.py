@@ -7,7 +7,9 @@ A step is one pass of the whole hot path over one batch: spec_verify_sample
 (row statistics + accept tests + first rejection, then the residual/bonus draw)
 for the sampling workloads, spec_verify_greedy_tree for the tree workload.
 Inputs are seeded synthetic logits already resident in HBM. Prints ONE JSON
-line on stdout; progress goes to stderr.
+line on stdout; progress goes to stderr. Without --steps / --warmup the
+untimed warm-up lasts about 0.3 s of the same work and the timed pass about
+0.2 s (at least 20 steps each); the line reports the counts used.
 
 Workloads d3, d5 time the draft-side sampler (spec_draft_sample) on the draft
 rows of configurations 3 and 5 (256 x 128256 bf16 at T 0.7; 512 x 256000
@@ -67,6 +69,42 @@ CSRC = os.path.join(ROOT, "lossless_draft_verification_05_amd", "csrc")
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# Untimed and timed work when --warmup / --steps are not given: the GPU
+# settles over tens of milliseconds of sustained work (after 3 untimed steps
+# c3's finish kernel still ran 28% slower than after 300), so the warm-up runs
+# for about WARM_S seconds of the same work and the timed pass for about
+# TIMED_S seconds, each at least MIN_STEPS steps.
+WARM_S, TIMED_S, MIN_STEPS = 0.3, 0.2, 20
+
+
+def warm_up(call, args):
+    """Runs the untimed steps call(0), call(1), ...: args.warmup of them. A
+    missing args.warmup or args.steps is set first from the time of up to
+    three untimed calls (counted in the warm-up)."""
+    import torch
+
+    done = 0
+    if args.warmup is None or args.steps is None:
+        n_probe = 3 if args.warmup is None else min(3, args.warmup)
+        if n_probe > 0:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(n_probe):
+                call(k)
+            torch.cuda.synchronize()
+            est = max((time.perf_counter() - t0) / n_probe, 1e-6)
+        else:
+            est = TIMED_S / MIN_STEPS
+        done = n_probe
+        if args.warmup is None:
+            args.warmup = max(MIN_STEPS, int(np.ceil(WARM_S / est)))
+        if args.steps is None:
+            args.steps = max(MIN_STEPS, int(np.ceil(TIMED_S / est)))
+    for k in range(done, args.warmup):
+        call(k)
+    torch.cuda.synchronize()
 
 
 def kernel_source_sha() -> str:
@@ -204,10 +242,10 @@ def bench_draft(args, cid):
     def timed(calls_of):
         """mean ms per step (wall clock over a pass with nothing else on the
         stream) and per-call HIP-event means (ms, from a second pass)"""
-        for k in range(args.warmup):
+        def step(k):
             for f in calls_of(k % R):
                 f()
-        torch.cuda.synchronize()
+        warm_up(step, args)
         t0 = time.perf_counter()
         for k in range(args.steps):
             for f in calls_of(k % R):
@@ -315,6 +353,10 @@ def bench_markov(args):
     loop = MarkovLoop(up(tabs.target), up(tabs.draft), G, torch.full((B,), T, dtype=torch.float32, device=dev))
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed)
+    if args.warmup is None:
+        args.warmup = 50
+    if args.steps is None:
+        args.steps = 20
     n_it = args.warmup + args.steps
     ud = torch.rand((n_it, B, G), generator=gen, device=dev)
     uv = torch.rand((n_it, B, G + 1), generator=gen, device=dev)
@@ -408,9 +450,7 @@ def bench_masks(args):
 
     def call(k):
         prep[k % R]()
-    for k in range(args.warmup):
-        call(k)
-    torch.cuda.synchronize()
+    warm_up(call, args)
     # timed pass with nothing else on the stream, then a pass with HIP events
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -524,10 +564,10 @@ def run_copy_calibration():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    # untimed steps first: the GPU settles over tens of milliseconds of
-    # sustained work (after 3 steps c3's finish kernel still ran 28% slower)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None)
+    # default: about WARM_S seconds of untimed steps and TIMED_S seconds of
+    # timed ones (see warm_up); the counts are reported
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -673,9 +713,7 @@ def main():
             cfg_desc["entry_point"] = "spec_verify_sample_early_exit"
 
     torch.cuda.synchronize()
-    for k in range(args.warmup):
-        whole[k % R]()
-    torch.cuda.synchronize()
+    warm_up(lambda k: whole[k % R](), args)
     log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
     # The timed pass: whole calls, nothing else on the stream (an event
     # recorded between two kernels costs 10-20 us of GPU time per step here).
