@@ -132,11 +132,12 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
   __shared__ int s_ok;
   __shared__ int s_key[kWaves];
   // Resolve arrays, sized by N at launch (tree_lds_bytes):
-  //   s_g[N] int | s_up[(kLog2MaxNodes+1) * N] short | s_D[2 * N] short | s_A[2 * N] uchar
+  //   s_g[N] int | s_tk[N] int | s_up[(kLog2MaxNodes+1) * N] short | s_D[2 * N] short | s_A[2 * N] uchar
   extern __shared__ __align__(16) char s_dyn[];
   const int NN = A.N;
   int* s_g = reinterpret_cast<int*>(s_dyn);
-  short* s_upb = reinterpret_cast<short*>(s_g + NN);
+  int* s_tk = s_g + NN;  // node tokens
+  short* s_upb = reinterpret_cast<short*>(s_tk + NN);
   short* s_Db = s_upb + (kLog2MaxNodes + 1) * NN;
   unsigned char* s_Ab = reinterpret_cast<unsigned char*>(s_Db + 2 * NN);
 #define s_up(k, i) s_upb[(k) * NN + (i)]
@@ -150,6 +151,9 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
   __syncthreads();
   const ArgPartial* P = A.part + (int64_t)b * per_seq;
   for (int jj = tid; jj < N; jj += kThreads) {
+    // the node's parent and token first: their loads do not wait for the partials'
+    const int pj = A.parents[(int64_t)b * N + jj];
+    const int tk = A.tokens[(int64_t)b * N + jj];
     float v = -INFINITY;
     int i = INT_MAX, bad = 0;
     const ArgPartial* q = P + (int64_t)jj * A.nch;
@@ -171,8 +175,7 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
     s_g[jj] = i;
     if (bad) s_ok = 0;
     if (A.out_argmax) A.out_argmax[(int64_t)b * N + jj] = bad ? -1 : i;
-    const int pj = A.parents[(int64_t)b * N + jj];
-    const int tk = A.tokens[(int64_t)b * N + jj];
+    s_tk[jj] = tk;
     const bool node_ok = (jj == 0) ? (pj == -1) : (pj >= 0 && pj < jj && tk >= 0 && tk < A.V);
     if (!node_ok) s_ok = 0;
     s_up(0, jj) = (short)((jj == 0) ? -1 : pj);
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
     return;
   }
   for (int jj = tid; jj < N; jj += kThreads) {
-    const int tk = A.tokens[(int64_t)b * N + jj];
+    const int tk = s_tk[jj];
     s_A(0, jj) = (jj == 0) ? 1 : (unsigned char)(tk == s_g[s_up(0, jj)]);
     s_D(0, jj) = (jj == 0) ? 0 : 1;
   }
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
 }
 
 size_t tree_lds_bytes(int N) {
-  return (size_t)N * 4 + (size_t)(kLog2MaxNodes + 1) * N * 2 + (size_t)2 * N * 2 + (size_t)2 * N + 16;
+  return (size_t)N * 8 + (size_t)(kLog2MaxNodes + 1) * N * 2 + (size_t)2 * N * 2 + (size_t)2 * N + 16;
 }
 
 // stage 1: per-row argmax partials; stage 2: per-tree resolve
