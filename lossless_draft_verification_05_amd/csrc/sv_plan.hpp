@@ -224,6 +224,7 @@ inline int finish_parts(int64_t B, int64_t ns2) {
 // step masses fit its LDS and there are enough rows to fill the GPU (or the
 // rows are short enough that two launches would cost more than the pass).
 constexpr int64_t kOnePassMinRows = 128;
+constexpr int64_t kDraftWideRows = 256;  // one-pass sampler: 16-wave workgroups up to this many rows
 constexpr int64_t kOnePassShortRowBytes = 64 << 10;
 inline bool draft_one_pass(int64_t B, int64_t V, int esz) {
   return draw_steps(V) <= kLdsSteps && (B >= kOnePassMinRows || V * esz <= kOnePassShortRowBytes);

@@ -1799,14 +1799,14 @@ __device__ __forceinline__ void load_step(const char* row, int64_t s, int64_t no
   }
 }
 
-// FMA-form pass: wave w takes steps w, w + kFinWaves, ...; whole steps through
+// FMA-form pass: wave w of NW takes steps w, w + NW, ...; whole steps through
 // the two-buffer pipeline of the draw, the ragged last step octet by octet.
-template <int DT>
+template <int DT, int NW>
 __device__ void draft_pass_fma(const char* row, int V, int ns2, float kl, LaneRef& R, float* stepC, float* stepM,
                                double* stepS) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = kFinWaves;
+  const int nw = NW;
   const int64_t noct = ((int64_t)V + 7) / 8;
   const int full_steps = V / kStepTokens;
   const int nmine = (full_steps > w) ? (full_steps - w + nw - 1) / nw : 0;
@@ -1846,12 +1846,12 @@ __device__ void draft_pass_fma(const char* row, int V, int ns2, float kl, LaneRe
 
 // Subtract-form pass (|m * kl| >= 2^24 somewhere in the row): each step
 // against its own maximum m_s; stepM = m_s, stepS = sum exp2((x - m_s) * kl).
-template <int DT>
+template <int DT, int NW>
 __device__ void draft_pass_sub(const char* row, int V, int ns2, float kl, float* stepM, double* stepS) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t noct = ((int64_t)V + 7) / 8;
-  for (int s = w; s < ns2; s += kFinWaves) {
+  for (int s = w; s < ns2; s += NW) {
     float x[kU2][8];
     float gm = -INFINITY;
     bool nan = false;
@@ -1884,8 +1884,10 @@ __device__ void draft_pass_sub(const char* row, int V, int ns2, float kl, float*
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))) void sv_draft1_kernel(
+// NW waves per workgroup: 16 when there are at most as many rows as CUs (one
+// workgroup per CU then; twice the loads in flight per row), else 8.
+template <int DT, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4))) void sv_draft1_kernel(
     SampleLaunch A) {
   __shared__ float stepC[kLdsSteps], stepM[kLdsSteps];
   __shared__ double stepS[kLdsSteps];
@@ -1901,10 +1903,10 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   const int ns2 = A.ns2;
 
   LaneRef R{-INFINITY, -INFINITY, 0};
-  draft_pass_fma<DT>(row, A.V, ns2, kl, R, stepC, stepM, stepS);
+  draft_pass_fma<DT, NW>(row, A.V, ns2, kl, R, stepC, stepM, stepS);
   const bool sub = __syncthreads_or(R.ovf) != 0;
   if (sub) {
-    draft_pass_sub<DT>(row, A.V, ns2, kl, stepM, stepS);
+    draft_pass_sub<DT, NW>(row, A.V, ns2, kl, stepM, stepS);
     __syncthreads();
   }
   // merge the steps into step masses against the row's reference (wave 0)
@@ -2237,10 +2239,15 @@ hipError_t launch_sample_small(const SampleLaunch& A, int tdt, int ddt, hipStrea
 }
 
 hipError_t launch_draft_one_pass(const SampleLaunch& A, int dt, hipStream_t stream) {
-  if (dt == 1)
-    hipLaunchKernelGGL((sv_draft1_kernel<1>), dim3((unsigned)A.B), dim3(kFinThreads), 0, stream, A);
+  const bool wide = A.B <= kDraftWideRows;
+  if (dt == 1 && wide)
+    hipLaunchKernelGGL((sv_draft1_kernel<1, 16>), dim3((unsigned)A.B), dim3(16 * kWave), 0, stream, A);
+  else if (dt == 1)
+    hipLaunchKernelGGL((sv_draft1_kernel<1, 8>), dim3((unsigned)A.B), dim3(8 * kWave), 0, stream, A);
+  else if (wide)
+    hipLaunchKernelGGL((sv_draft1_kernel<0, 16>), dim3((unsigned)A.B), dim3(16 * kWave), 0, stream, A);
   else
-    hipLaunchKernelGGL((sv_draft1_kernel<0>), dim3((unsigned)A.B), dim3(kFinThreads), 0, stream, A);
+    hipLaunchKernelGGL((sv_draft1_kernel<0, 8>), dim3((unsigned)A.B), dim3(8 * kWave), 0, stream, A);
   return hipGetLastError();
 }
 
