@@ -162,8 +162,8 @@ int spec_verify_sample_noalloc(const void* target_logits, int target_dtype, int6
                                void* stream);
 
 /*
- * spec_verify_sample_early_exit -- spec_verify_sample that reads no row after
- * a sequence's first rejection.
+ * spec_verify_sample_early_exit -- spec_verify_sample ordered by position, so
+ * that the rows after a sequence's first rejection need not be read.
  *
  * Defines: [SD] "The pith" (the longest accepted prefix is kept: nothing after
  * the first rejection can change the output). Same arguments, outputs,
@@ -173,6 +173,9 @@ int spec_verify_sample_noalloc(const void* target_logits, int target_dtype, int6
  * from the sizes: a position gets its own launch while the bytes its gate is
  * expected to save, at an assumed acceptance rate of 0.7, outweigh a launch;
  * small batches get k = 0, one launch with no gate), then the finish kernel.
+ * With k = 0 and V <= 2048 (rows of one draw step) every row is read in any
+ * case, and the call runs spec_verify_sample's one-kernel path instead (a wave
+ * per sequence; the same results as spec_verify_sample, bit for bit).
  * spec_verify_sample_early_exit_grouped takes k from the caller. In every launch
  * after the first, each workgroup re-derives the accept decision of the
  * position before it and streams its rows only if that position was accepted.
@@ -181,7 +184,8 @@ int spec_verify_sample_noalloc(const void* target_logits, int target_dtype, int6
  * Differences from spec_verify_sample: the row statistics are taken in smaller
  * chunks, so results can differ in rounding (an accept decision within ~1e-7
  * of u, p_x and q_x in the last bits); diag p_x, q_x are NaN for positions
- * whose rows were not read; more kernel launches (k + 2 instead of 2).
+ * whose rows were not read; more kernel launches (k + 2 instead of 2), except
+ * on the one-kernel path above.
  */
 int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, int64_t target_seq_stride,
                                   int64_t target_row_stride, const void* draft_logits, int draft_dtype,

@@ -143,3 +143,24 @@ def test_huge_logits(gpu, grouping):
     """Logits around 10^8 (N(0, 2e7)): the statistics pass takes its subtract form."""
     inp = synth.make_custom_sample(6, 3, 3000, "f32", "f32", T=1.0, noise_sd=1e6, target_sd=2e7, seed=13)
     _both(gpu, inp, name="huge logits", grouping=grouping)
+
+
+@pytest.mark.parametrize("tdt,ddt", [("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16")])
+@pytest.mark.parametrize("V", [32, 700, 2048])
+def test_one_step_rows_no_gate_same_bits(gpu, tdt, ddt, V):
+    """Rows of one draw step (V <= 2048) with no gated position: the early exit
+    reads every row in any case and runs the one-kernel path, so its outputs
+    and diagnostics equal the one-pass call's bit for bit (the grouping chosen
+    from the sizes and tail_start = 0 alike), and match the oracle."""
+    H.log(f"early exit, rows of one step, no gate: V={V} {tdt}/{ddt}")
+    inp = synth.make_custom_sample(40, 4, V, tdt, ddt, T=np.linspace(0.5, 1.5, 40, dtype=np.float32),
+                                   noise_sd=0.6, seed=V + 7)
+    tens = H.sample_tensors(inp, pad_to=8)  # rows padded to 16 bytes (V = 700 in bf16)
+    one = H.run_sample(gpu, tens)
+    for ts in (None, 0):
+        ee = H.run_sample(gpu, tens, early_exit=True, tail_start=ts)
+        for k in one:
+            assert np.array_equal(one[k].view(np.uint8), ee[k].view(np.uint8)), (k, ts)
+    t = H.check_sample(inp, one)
+    H.log(f"[early exit one-step rows V={V}] {t.summary()}")
+    assert not t.fail, t.fail[:3]
