@@ -166,7 +166,12 @@ static int run_draft(int first, int last, const void* logits, int dtype, int64_t
   SampleLaunch L = plan_sample(a);
   L.out_py = out_prob;
   if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
-  if (first == 0) return hip_status(launch_draft_one_pass(L, dtype, stream));
+  if (first == 0) {
+    // rows of one draw step: a wave per row (the verify's one-kernel path with
+    // gamma = 0, a bonus-row draw); longer rows: a workgroup per row
+    if (V <= kStepTokens) return hip_status(launch_sample_small(L, dtype, dtype, stream));
+    return hip_status(launch_draft_one_pass(L, dtype, stream));
+  }
   for (int s = first; s <= last; ++s) {
     st = hip_status(launch_sample_stage(L, dtype, dtype, s, stream));
     if (st) return st;
@@ -353,8 +358,9 @@ size_t sv_draft_workspace_bytes(int B, int V) {
 int spec_draft_sample(const void* logits, int dtype, int64_t row_stride, const float* uniforms,
                       const float* temperature, int B, int V, int32_t* out_tokens, float* out_prob, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  // one pass (one workgroup per row) when the rows keep the GPU busy or are
-  // short, and a row's step masses fit the kernel's LDS; else the two kernels
+  // one pass (one workgroup per row, or a wave per row of at most one draw
+  // step) when the rows keep the GPU busy or are short, and a row's step
+  // masses fit the kernel's LDS; else the two kernels
   const bool one_pass = draft_one_pass(B, V, esz_of(dtype));
   return run_draft(one_pass ? 0 : 1, 2, logits, dtype, row_stride, uniforms, temperature, B, V, out_tokens,
                    out_prob, workspace, workspace_bytes, (hipStream_t)stream);

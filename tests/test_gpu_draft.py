@@ -40,26 +40,30 @@ def test_draft_workloads(gpu, cid):
     assert (out["y"] >= 0).all()
 
 
-def test_masks_ties_and_invalid(gpu):
-    d = synth.make_draft_rows(10, 3000, "f32", T=1.0, seed=5)
+@pytest.mark.parametrize("V", [3000, 2000])
+def test_masks_ties_and_invalid(gpu, V):
+    """V = 3000: the workgroup-per-row kernel; V = 2000 (one draw step): the
+    wave-per-row kernel. The two-kernel (staged) path on the same rows too."""
+    d = synth.make_draft_rows(10, V, "f32", T=1.0, seed=5)
     g = np.random.default_rng(5)
     L = d.logits
-    L[0, g.random(3000) < 0.9] = -np.inf       # mostly masked
+    L[0, g.random(V) < 0.9] = -np.inf          # mostly masked
     L[1, :] = 0.25                              # all ties
     L[2, :] = -np.inf
-    L[2, 2999] = 1.0                            # one token, at the end
+    L[2, V - 1] = 1.0                           # one token, at the end
     L[3, 17] = np.nan                           # invalid
     L[4, 5] = np.inf                            # invalid
     L[5, :] = -np.inf                           # invalid: no finite value
     d.temperature[6] = 0.0                      # invalid temperature
     d.uniforms[7] = 1.0                         # invalid uniform
-    L[8, :1500] = -0.0
-    L[8, 1500:] = 0.0                           # signed zeros tie
+    L[8, :V // 2] = -0.0
+    L[8, V // 2:] = 0.0                         # signed zeros tie
     d.uniforms[9] = 0.0                         # u = 0: first token of positive mass
-    out = H.run_draft(gpu, H.draft_tensors(d))
-    _assert(H.check_draft(d, out), "masks/ties/invalid")
-    assert list(out["y"][3:8]) == [-1] * 5 and np.isnan(out["p"][3:8]).all()
-    assert out["y"][2] == 2999 and out["p"][2] == 1.0
+    tens = H.draft_tensors(d)
+    for name, out in (("one pass", H.run_draft(gpu, tens)), ("staged", H.run_draft(gpu, tens, stage=True))):
+        _assert(H.check_draft(d, out), f"masks/ties/invalid V={V} {name}")
+        assert list(out["y"][3:8]) == [-1] * 5 and np.isnan(out["p"][3:8]).all()
+        assert out["y"][2] == V - 1 and out["p"][2] == 1.0
 
 
 def test_strided_rows_and_stages(gpu):
