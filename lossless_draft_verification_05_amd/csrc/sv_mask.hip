@@ -9,11 +9,13 @@
 // block attend to each other.
 //
 // One 256-thread workgroup per (tree, slab of mask rows). The workgroup loads
-// the parent array into LDS and derives each node's 2nd, 3rd and 4th
-// ancestors from it; one thread per row of the slab then walks from its node
-// to the root four ancestors per step (parents[j] < j bounds the walk by j
-// nodes), setting the bits of the row's ancestors in an LDS bitset and
-// counting the depth. The
+// the parent array into LDS and derives from it, by pointer doubling, each
+// node's 2^m-th ancestor for 2^m up to the L threads it gives each row of the
+// slab (L <= 16, as many as fit); thread k of a row starts at the row's k-th
+// ancestor and jumps L ancestors at a time to the root (parents[j] < j bounds
+// the path by j nodes), so the L threads together set the bits of every
+// ancestor of the row in an LDS bitset, and their node counts sum to the
+// depth. The
 // slab (at most 16 KB of mask bytes, so at most 2 KB of bits) is then written
 // with 16-byte stores, each built from at most two bitset words. When N is a
 // multiple of 16 and the outputs are 16-byte aligned, both masks come from one
@@ -156,8 +158,9 @@ __device__ void write_masks_aligned(uint8_t* out_t, uint8_t* out_r, int N, int r
 }
 
 __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
-  // parents and the 2nd, 3rd, 4th ancestors (-1 past the root); N <= 1024 fits a short
-  __shared__ short par[kMaxMaskNodes], anc2[kMaxMaskNodes], anc3[kMaxMaskNodes], anc4[kMaxMaskNodes];
+  // anc[m][j]: the 2^m-th ancestor of node j (-1 past the root); anc[0] holds
+  // the parents. N <= 1024 fits a short.
+  __shared__ short anc[kMaskJumpLevels + 1][kMaxMaskNodes];
   __shared__ __align__(16) int blk[kMaxMaskNodes];
   __shared__ uint32_t bits[kMaskSlabBytes / 32];  // slab rows x W words: ancestors (and the node itself)
   __shared__ int sh_bad;
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
     const int j = tid + k * kThreads;
     if (j < N) {
       const int p = pv[k];
-      par[j] = (short)p;  // used only when every parent is checked valid below
+      anc[0][j] = (short)p;  // used only when every parent is checked valid below
       blk[j] = bv[k];
       if (j == 0 ? p != -1 : (p < 0 || p >= j)) sh_bad = 1;  // same value from every writer
     }
@@ -196,37 +199,36 @@ __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
   __syncthreads();
   const bool bad = sh_bad != 0;
   const int e0 = r0 * N, e1 = r1 * N;  // N <= 1024: a tree's mask has at most 2^20 bytes
+  // L = 2^lg threads per row of the slab
+  const int nrows = r1 - r0;
+  int lg = 0;
+  while (lg < kMaskJumpLevels && (nrows << (lg + 1)) <= kThreads) ++lg;
   if (!bad) {
-    // ancestors 2, 3 and 4 of every node a walk can visit (those below r1):
-    // a walk step then issues four independent LDS reads instead of a chain
-    // of four dependent ones
-    for (int j = tid; j < r1; j += kThreads) {
-      const int p1 = par[j];
-      const int p2 = p1 >= 0 ? par[p1] : -1;
-      const int p3 = p2 >= 0 ? par[p2] : -1;
-      anc2[j] = (short)p2;
-      anc3[j] = (short)p3;
-      anc4[j] = (short)(p3 >= 0 ? par[p3] : -1);
-    }
-  }
-  __syncthreads();  // `bad` is the same in every thread
-  if (!bad) {
-    // one thread per row: the path to the root, four nodes per step, each
-    // node's bit ORed into the row's bitset (cleared above; the row is this
-    // thread's alone)
-    for (int i = r0 + tid; i < r1; i += kThreads) {
-      uint32_t* row = bits + (i - r0) * W;
-      int d = 0;
-      for (int a = i; a >= 0;) {
-        const int p1 = par[a], p2 = anc2[a], p3 = anc3[a], p4 = anc4[a];
-        atomicOr(row + (a >> 5), 1u << (a & 31));
-        if (p1 >= 0) atomicOr(row + (p1 >> 5), 1u << (p1 & 31));
-        if (p2 >= 0) atomicOr(row + (p2 >> 5), 1u << (p2 & 31));
-        if (p3 >= 0) atomicOr(row + (p3 >> 5), 1u << (p3 & 31));
-        d += 1 + (p1 >= 0) + (p2 >= 0) + (p3 >= 0);
-        a = p4;
+    // the 2^m-th ancestors, m = 1..lg, of every node a walk can visit (those
+    // below r1), one doubling per pass
+    for (int m = 1; m <= lg; ++m) {
+      for (int j = tid; j < r1; j += kThreads) {
+        const int h = anc[m - 1][j];
+        anc[m][j] = (short)(h >= 0 ? anc[m - 1][h] : -1);
       }
-      if (A.out_depth) A.out_depth[(int64_t)b * N + i] = d - 1;
+      __syncthreads();  // `bad` and lg are the same in every thread
+    }
+    // thread k of row i: ancestors k, k + L, k + 2L, ... of i, each one's bit
+    // ORed into the row's bitset (cleared above); the L threads of a row are
+    // consecutive lanes of one wave and share the row's trip count
+    const int k = tid & ((1 << lg) - 1);
+    for (int i = r0 + (tid >> lg); i < r1; i += kThreads >> lg) {
+      uint32_t* row = bits + (i - r0) * W;
+      int a = i;
+      for (int m = 0; m < lg; ++m)
+        if (((k >> m) & 1) && a >= 0) a = anc[m][a];
+      int cnt = 0;
+      for (; a >= 0; a = anc[lg][a]) {
+        atomicOr(row + (a >> 5), 1u << (a & 31));
+        ++cnt;
+      }
+      for (int o = 1; o < (1 << lg); o <<= 1) cnt += __shfl_xor(cnt, o, kWave);
+      if (k == 0 && A.out_depth) A.out_depth[(int64_t)b * N + i] = cnt - 1;
     }
   } else if (A.out_depth) {
     for (int i = r0 + tid; i < r1; i += kThreads) A.out_depth[(int64_t)b * N + i] = -1;

@@ -145,6 +145,7 @@ struct TreeLaunch {
 };
 
 constexpr int kMaxMaskNodes = 1024;  // tree masks: nodes per tree
+constexpr int kMaskJumpLevels = 4;   // tree masks: up to 2^4 threads walk each row
 constexpr int64_t kMaskSlabBytes = 16 << 10;  // tree masks: mask bytes per workgroup (measured: 16 KB beat 8, 32 and 64 KB)
 
 struct MaskLaunch {
