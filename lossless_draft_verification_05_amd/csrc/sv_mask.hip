@@ -199,10 +199,14 @@ __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
   __syncthreads();
   const bool bad = sh_bad != 0;
   const int e0 = r0 * N, e1 = r1 * N;  // N <= 1024: a tree's mask has at most 2^20 bytes
-  // L = 2^lg threads per row of the slab
+  // L = 2^lg threads per row of the slab, as many as fit, up to 16, and at
+  // most about sqrt(N) / 2: every doubling pass costs about two walk steps,
+  // which shallow small trees do not recover (measured: a 60-node tree's
+  // masks are faster at L = 2 than at 4)
   const int nrows = r1 - r0;
+  const int lgcap = min(kMaskJumpLevels, max(0, (31 - __builtin_clz((unsigned)N)) - 2) / 2);
   int lg = 0;
-  while (lg < kMaskJumpLevels && (nrows << (lg + 1)) <= kThreads) ++lg;
+  while (lg < lgcap && (nrows << (lg + 1)) <= kThreads) ++lg;
   if (!bad) {
     // the 2^m-th ancestors, m = 1..lg, of every node a walk can visit (those
     // below r1), one doubling per pass
