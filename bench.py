@@ -706,7 +706,8 @@ def main():
         kernel_names = ["sv_stats_kernel", "sv_finish_kernel"]
         small = V <= 2048 and not args.early_exit  # the full call is one kernel, a wave per sequence
         if small:
-            kernel_names = ["sv_small_kernel"]
+            # two sequences per wave when a row fits half a wave and so do the 2 gamma + 1 row slots
+            kernel_names = ["sv_small2_kernel" if V <= 32 and 2 * G + 1 <= 32 else "sv_small_kernel"]
             prep = {c: [whole[c]] for c in range(R)}
         if args.early_exit:
             kernel_names = ["spec_verify_sample_early_exit"]

@@ -2191,6 +2191,235 @@ __global__ __launch_bounds__(kThreads) void sv_small_kernel(SampleLaunch A) {
 }
 
 // ---------------------------------------------------------------------------
+// tiny vocabularies (V <= 32, 2 gamma + 1 <= 32): two sequences per wave
+// ---------------------------------------------------------------------------
+// Half-wave reductions: the wave reductions' DPP butterfly within 16-lane
+// rows, then rows 0 + 1 (lanes 0-31) and rows 2 + 3 (lanes 32-63) combined
+// apart. For a half whose other lanes hold nothing (-inf, 0) these are the
+// wave reductions' results bit for bit.
+__device__ __forceinline__ float half_max(float v, bool upper) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
+  const float lo = fmaxf(readlane_f32(v, 0), readlane_f32(v, 16));
+  const float hi = fmaxf(readlane_f32(v, 32), readlane_f32(v, 48));
+  return upper ? hi : lo;
+}
+__device__ __forceinline__ double half_sum(double v, bool upper) {
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppRowRor4>(v);
+  v += dpp_f64<kDppRowRor8>(v);
+  const double lo = readlane_f64(v, 0) + readlane_f64(v, 16);
+  const double hi = readlane_f64(v, 32) + readlane_f64(v, 48);
+  return upper ? hi : lo;
+}
+// Inclusive prefix sum within each half (the wave scan without its step
+// from lane 31 into the upper half).
+__device__ __forceinline__ double half_incl_scan(double v) {
+  v += dpp_f64_masked<kDppRowShr1, 0xf>(v);
+  v += dpp_f64_masked<kDppRowShr2, 0xf>(v);
+  v += dpp_f64_masked<kDppRowShr4, 0xf>(v);
+  v += dpp_f64_masked<kDppRowShr8, 0xf>(v);
+  v += dpp_f64_masked<kDppRowBcast15, 0xa>(v);
+  return v;
+}
+
+// The whole verify of sequences with V <= 32 and 2 gamma + 1 <= 32 rows, two
+// per wave: lanes 0-31 take sequence 2 k, lanes 32-63 sequence 2 k + 1 (k the
+// wave's index in the grid), half-lane h holding token h of every row and
+// row slot h's statistics. The steps and their order are those of the
+// one-wave kernel (whose rows of at most 32 tokens leave its upper half
+// empty); every wave operation runs with the whole wave active, each half
+// taking its own results, and a half past the batch computes on the last
+// sequence's rows and writes nothing.
+template <int TD, int DD>
+__global__ __launch_bounds__(kThreads) void sv_small2_kernel(SampleLaunch A) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool upper = lane >= 32;
+  const int hl = lane & 31, base = upper ? 32 : 0;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b0 = (blockIdx.x * kWaves + w) * 2;
+  if (b0 >= A.B) return;  // the whole wave; this kernel has no workgroup barrier
+  const int b = b0 + (upper ? 1 : 0);
+  const bool active = b < A.B;
+  const int bl = active ? b : A.B - 1;  // rows read by a half past the batch
+  const float T = A.temps[bl];
+  const bool tv = temp_ok(T);
+  const float kl = tv ? log2e_over(T) : 1.0f;
+  const int G = A.gamma;
+
+  // the draft tokens, their uniforms and logits (position = half-lane)
+  int xi = 0;
+  float ui = 0.0f, lt = 0.0f, ld = 0.0f;
+  bool tok_ok = false;
+  if (hl < G) {
+    xi = A.tokens[(int64_t)bl * G + hl];
+    ui = A.uniforms[(int64_t)bl * (G + 1) + hl];
+    tok_ok = xi >= 0 && xi < A.V;
+    if (tok_ok) {
+      lt = load_elem<TD>(A.tgt + (int64_t)bl * A.t_seq_b + (int64_t)hl * A.t_row_b, xi);
+      ld = load_elem<DD>(A.dft + (int64_t)bl * A.d_seq_b + (int64_t)hl * A.d_row_b, xi);
+    }
+  }
+  // statistics of target rows 0..G (slots 0..G) and draft rows 0..G-1 (slots
+  // G+1..2G <= 30); slot t is kept by half-lane t
+  constexpr int RB = 16;
+  float m0 = 0.0f;
+  double s0 = 0.0;
+  int v0 = 0;
+  for (int t0 = 0; t0 <= 2 * G; t0 += RB) {
+    float x[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int t = t0 + r;
+      const char* row = (t <= G) ? A.tgt + (int64_t)bl * A.t_seq_b + (int64_t)t * A.t_row_b
+                                 : A.dft + (int64_t)bl * A.d_seq_b + (int64_t)(t - G - 1) * A.d_row_b;
+      x[r] = -INFINITY;
+      if (t <= 2 * G && hl < A.V) x[r] = (t <= G) ? load_elem<TD>(row, hl) : load_elem<DD>(row, hl);
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int t = t0 + r;
+      if (t > 2 * G) break;
+      // the one-wave kernel's row statistics (reference: the row's maximum)
+      const float m = half_max(x[r], upper);
+      const bool nan = x[r] != x[r];
+      double e = 0.0;
+      if (nan || x[r] != -INFINITY) e = nan ? (double)x[r] : (double)hw_exp2((x[r] - m) * kl);
+      const double sm = half_sum(e, upper);
+      if (hl == t) {
+        m0 = m;
+        s0 = sm;
+        v0 = tv && __builtin_isfinite(sm) && sm > 0.0 && __builtin_isfinite(m);
+      }
+    }
+  }
+  auto stat_of = [&](int t) {  // slot t of this half's sequence, in every lane of the half
+    const float m = __shfl(m0, base + t, kWave);
+    const double sm = __shfl(s0, base + t, kWave);
+    const int v = __shfl(v0, base + t, kWave);
+    return RowStat{(double)m * (double)kl, m, sm, v};
+  };
+  // accept tests (half-lane i: position i) and the first stop
+  const RowStat ds = stat_of(G + 1 + hl < 32 ? G + 1 + hl : 31);
+  int code = 1;
+  if (hl < G) {
+    const RowStat ts{(double)m0 * (double)kl, m0, s0, v0};
+    const AcceptOut ao = accept_test(lt, ld, ts, ds, kl, ui, tok_ok, tv, A.diag_px || A.diag_qx);
+    code = ao.code;
+    if (active && A.diag_px) A.diag_px[(int64_t)b * G + hl] = ao.px;
+    if (active && A.diag_qx) A.diag_qx[(int64_t)b * G + hl] = ao.qx;
+  }
+  const unsigned long long stopw = __ballot(code != 1);
+  const unsigned stop = upper ? (unsigned)(stopw >> 32) : (unsigned)stopw;
+  const int n = stop ? (__ffs(stop) - 1) : G;
+  const int code_n = __shfl(code, base + (n < G ? n : 0), kWave);
+  const RowStat tn = stat_of(n);
+  const RowStat dq = stat_of(n < G ? G + 1 + n : 0);
+  const RowStat dn = (n < G) ? dq : RowStat{0.0, 0.0f, 1.0, 0};
+  const SeqPlan P = make_plan(n, code_n, G, G + 1, tv, kl, A.uniforms[(int64_t)bl * (G + 1) + G], tn, dn);
+
+  // the draw row(s): at most 4 octets, one per half-lane
+  const char* trow = A.tgt + (int64_t)bl * A.t_seq_b + (int64_t)n * A.t_row_b;
+  const char* drow = (n < G) ? A.dft + (int64_t)bl * A.d_seq_b + (int64_t)n * A.d_row_b : nullptr;
+  const int noct = (A.V + 7) / 8;
+  int mode = P.mode;
+  const bool have = hl < noct;
+  float xt[8], xd[8], rr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) xd[k] = 0.0f;
+  if (have) {
+    load_octet<TD>(trow, hl, A.V, xt);
+    if (mode == kModeResidual) load_octet<DD>(drow, hl, A.V, xd);
+  }
+  bool cheap = false;
+  auto step_total = [&](int m, const SeqPlan& Q) -> double {
+    double lacc = 0.0;
+    if (have) {
+      mass8_of(xt, xd, m, Q, rr, cheap);
+      lacc = (double)sum8(rr);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rr[k] = 0.0f;
+    }
+    return half_sum(lacc, upper);
+  };
+  SeqPlan Pd = P;
+  // the step's form (see cheap_ok), then the first-order correction of the
+  // normalisers' ratio (see correct_steps) from its signed sum
+  const bool rform = mode == kModeResidual && P.form == 1;
+  CheapSums c{0.0f, 0.0f, 0.0f};
+  if (have && rform) c = cheap_sums8(xt, xd, P);
+  const double cm = half_sum((double)c.r, upper), cq = half_sum((double)c.q, upper);
+  const double cd = half_sum((double)c.d, upper);
+  cheap = rform && cheap_ok(cm, cq);
+  const bool exact = rform && !cheap;
+  double d = cd;
+  if (__ballot(exact)) {
+    double de = 0.0;
+    if (have && exact) {
+      ResidSums o = resid_sums8<false>(xt, xd, P);
+      if (!(o.a == o.a)) o = resid_sums8<true>(xt, xd, P);
+      de = 2.0 * (double)o.r - (double)o.a;
+    }
+    de = half_sum(de, upper);
+    if (exact) d = de;
+  }
+  if (rform) Pd.g = d / (P.sp * P.fscale - d);
+  double total = step_total(mode, Pd);  // the corrected terms, the same ones the scan takes
+  const bool fb = !(total > 0.0) && mode == kModeResidual;
+  if (__ballot(fb)) {
+    // nothing left after the rejection (p_n == q_n up to rounding): draw from p_n
+    if (fb) {
+      mode = kModeBonus;
+      Pd.g = 0.0;
+      cheap = false;
+    }
+    const double t2 = step_total(mode, Pd);  // the other half's terms come out unchanged
+    if (fb) total = t2;
+  }
+  // the scan of the step (the one-wave scan within the half)
+  const double t = (double)P.ug * total;
+  const double os = (double)sum8(rr);
+  const double incl = half_incl_scan(os);
+  const double excl = incl - os;
+  int lk = -1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (rr[k] > 0.0f) lk = k;
+  const unsigned long long hitw = __ballot(os > 0.0 && incl > t);
+  const unsigned hit = upper ? (unsigned)(hitw >> 32) : (unsigned)hitw;
+  const int L = hit ? (__ffs(hit) - 1) : 0;
+  int yy = -1;
+  if (hit && hl == L) {
+    double run = excl;
+    for (int k = 0; k < 8; ++k) {
+      if (rr[k] > 0.0f) {
+        run += (double)rr[k];
+        if (run > t) {
+          yy = hl * 8 + k;
+          break;
+        }
+      }
+    }
+    if (yy < 0) yy = hl * 8 + lk;
+  }
+  int y = __shfl(yy, base + L, kWave);
+  // rounding pushed t past the step's mass: its last positive token
+  int lp = lk >= 0 ? hl * 8 + lk : -1;
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o, kWave));
+  if (!hit) y = lp;
+  if (!active) return;
+  if (!P.valid)
+    write_invalid(A, b, hl, 0, 32);
+  else
+    write_outputs<TD>(A, b, Pd, mode, y, total, hl, xi);
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 template <int TD, int DD>
@@ -2222,7 +2451,10 @@ hipError_t launch_sample_stage(const SampleLaunch& A, int tdt, int ddt, int stag
 template <int TD, int DD>
 static hipError_t launch_small_t(const SampleLaunch& A, hipStream_t stream) {
   const dim3 grid((unsigned)(((int64_t)A.B + kWaves - 1) / kWaves));
-  if (A.V <= kWave)
+  if (A.V <= 32 && 2 * A.gamma + 1 <= 32)
+    hipLaunchKernelGGL((sv_small2_kernel<TD, DD>), dim3((unsigned)(((int64_t)A.B + 2 * kWaves - 1) / (2 * kWaves))),
+                       dim3(kThreads), 0, stream, A);
+  else if (A.V <= kWave)
     hipLaunchKernelGGL((sv_small_kernel<TD, DD, 1>), grid, dim3(kThreads), 0, stream, A);
   else if (A.V <= 4 * kWave)
     hipLaunchKernelGGL((sv_small_kernel<TD, DD, 4>), grid, dim3(kThreads), 0, stream, A);
