@@ -127,7 +127,8 @@ typedef struct {
  *
  * Work on `stream`: the statistics kernel then the finish kernel (see
  * spec_verify_sample_stage); with V <= 2048 a single kernel, one wave per
- * sequence. The paths round differently and agree within the parity contract.
+ * sequence (two per wave when V <= 32 and 2 * gamma + 1 <= 32, with the same
+ * results). The paths round differently and agree within the parity contract.
  */
 int spec_verify_sample(const void* target_logits, int target_dtype, int64_t target_seq_stride,
                        int64_t target_row_stride, const void* draft_logits, int draft_dtype,

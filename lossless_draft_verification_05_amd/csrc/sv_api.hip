@@ -434,8 +434,6 @@ int spec_verify_greedy_tree_stage(int stage, const void* target_logits, int dtyp
                   out_accept_len, out_path, out_bonus, out_argmax, workspace, workspace_bytes, stream);
 }
 
-
-
 const char* sv_status_string(int status) {
   switch (status) {
     case SV_OK: return "ok";
