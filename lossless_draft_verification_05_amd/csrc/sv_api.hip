@@ -121,7 +121,7 @@ static SampleLaunch plan_sample(const SampleArgs& a, bool early = false) {
   split_row(V, ed, cb, &L.ncd, &L.cud, kBatchUnits);
   L.per_seq = (int)((G + 1) * L.nct + G * L.ncd);
   L.ns2 = (int)draw_steps(V);
-  L.parts = finish_parts(B, L.ns2);
+  finish_shape(B, L.ns2, &L.parts, &L.fin_waves);
   const SampleLayout lay = sample_layout(B, G, V);
   char* ws = (char*)a.ws;
   L.part = (RowPartial*)(ws + lay.off_part);

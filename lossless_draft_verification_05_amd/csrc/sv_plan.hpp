@@ -120,6 +120,7 @@ struct SampleLaunch {
   int per_seq;   // (gamma + 1) * nct + gamma * ncd
   int ns2;  // 2048-token steps per row (draw)
   int parts;  // finish workgroups per sequence, each streaming a share of the draw's steps
+  int fin_waves;  // waves per finish workgroup: kFinWaves, or 2 * kFinWaves for split sequences
   // workspace
   RowPartial* part;  // [B][per_seq][kWaves]
   double* steptot;   // [B][4][ns2] step sums (masses, q-masses, signed sums, form flags) when they exceed
@@ -219,6 +220,22 @@ inline int finish_parts(int64_t B, int64_t ns2) {
   const int64_t cap = ns2 / kFinWaves;
   if (k > cap) k = cap;
   return (int)(k < 1 ? 1 : k);
+}
+
+// Waves per finish workgroup and parts per sequence. A sequence split into K
+// parts of kFinWaves waves whose waves stream at most two steps each runs as
+// ceil(K / 2) parts of 2 * kFinWaves waves instead: the same waves (or one
+// part's more) with half the repeated merges and accept tests, and no hand-off
+// at all for K = 2; its stream is one or two round trips per wave either way
+// (measured: c2 0.0298 -> 0.0287 ms, a single 128k or 256k sequence 0.0220 ->
+// 0.0209 and 0.0255 -> 0.0248 ms). With longer streams the workgroups' CUs
+// bound the stream, and halving them costs more (64 sequences of 256k: 0.117
+// -> 0.127 ms), so they keep kFinWaves.
+inline void finish_shape(int64_t B, int64_t ns2, int* parts, int* waves) {
+  const int k = finish_parts(B, ns2);
+  const bool wide = k >= 2 && ns2 <= (int64_t)2 * k * kFinWaves;
+  *waves = wide ? 2 * kFinWaves : kFinWaves;
+  *parts = wide ? (k + 1) / 2 : k;
 }
 
 // Draft sampler: the one-pass kernel (one workgroup per row) when the row's

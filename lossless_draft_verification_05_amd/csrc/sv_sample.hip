@@ -1165,25 +1165,25 @@ __device__ __forceinline__ bool step_published(const StepSums& v) {
 }
 
 // The drawing part's copy of every step's sums of sequence b into LDS (wave w
-// of kFinWaves takes 64-step blocks w, w + kFinWaves, ...). Steps of other
+// of the NW takes 64-step blocks w, w + NW, ...). Steps of other
 // parts come from the workspace; one whose sums are not all visible yet still
 // holds a sentinel and is recomputed here with the same bits, so no result
 // depends on which stores have landed and no part ever waits for another. The
 // slots are then reset to the sentinels.
-template <int TD, int DD>
+template <int TD, int DD, int NW>
 __device__ __forceinline__ void gather_steps(const SampleLaunch& A, int b, const SeqPlan& P, int mode, int part,
                                              const StepOut& sh) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gnw = A.parts * kFinWaves;
+  const int gnw = A.parts * NW;
   const StepOut g = ws_steps(A, b);
   const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
   const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
   const int64_t noct = ((int64_t)A.V + 7) / 8;
-  for (int base = w * kWave; base < A.ns2; base += kFinWaves * kWave) {
+  for (int base = w * kWave; base < A.ns2; base += NW * kWave) {
     const int s = base + lane;
     const bool in = s < A.ns2;
-    const bool mine = (s % gnw) / kFinWaves == part;  // computed by this workgroup: already in LDS
+    const bool mine = (s % gnw) / NW == part;  // computed by this workgroup: already in LDS
     StepSums v{0.0, 0.0, 0.0, 0.0};
     if (in) {
       if (mine) {
@@ -1472,10 +1472,12 @@ __device__ __forceinline__ SeqPlan uniform_plan(const SeqPlan& src) {
 // finish kernel: one 512-thread workgroup per sequence
 // ---------------------------------------------------------------------------
 constexpr int kMergeRows = 3;  // rows per wave merged from one batch of loads: 2 * gamma + 1 <= 24
-template <int TD, int DD>
-// At most 128 VGPRs, so that two 8-wave workgroups fit one CU.
-__global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))) void sv_finish_kernel(
+// NW: waves per workgroup (kFinWaves, or twice that for split sequences).
+template <int TD, int DD, int NW>
+// At most 128 VGPRs, so that two 8-wave workgroups (one 16-wave one) fit a CU.
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4))) void sv_finish_kernel(
     SampleLaunch A) {
+  constexpr int NT = NW * kWave;
   __shared__ double rC[kMaxRows];
   __shared__ float rM[kMaxRows];
   __shared__ double rS[kMaxRows];
@@ -1521,12 +1523,12 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   // kMergeRows rows, a wave loads the partials of all its rows before merging
   // any (one memory round trip instead of one per row).
   const int nrows = 2 * G + 1;
-  if (A.nct * kWaves <= kWave && A.ncd * kWaves <= kWave && nrows <= kMergeRows * kFinWaves) {
+  if (A.nct * kWaves <= kWave && A.ncd * kWaves <= kWave && nrows <= kMergeRows * NW) {
     RowPartial q[kMergeRows];
     bool have[kMergeRows];
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
-      const int t = w + k * kFinWaves;
+      const int t = w + k * NW;
       const int pos = t <= G ? t : t - G - 1;
       const int nrec = (t <= G ? A.nct : A.ncd) * kWaves;
       const int base = t <= G ? t * A.nct : tchunks + pos * A.ncd;
@@ -1536,7 +1538,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     }
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
-      const int t = w + k * kFinWaves;
+      const int t = w + k * NW;
       if (t >= nrows) break;
       const int pos = t <= G ? t : t - G - 1;
       RowStat rs{0.0, 0.0f, 0.0, 0};
@@ -1549,7 +1551,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
       }
     }
   } else {
-    for (int t = w; t < nrows; t += kFinWaves) {
+    for (int t = w; t < nrows; t += NW) {
       int nrec, base, pos;
       if (t <= G) {
         nrec = A.nct * kWaves;
@@ -1613,7 +1615,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   const SeqPlan P = uniform_plan(sP);
   if (!P.valid) {
     // every part reaches the same plan; part 0 writes the outputs
-    if (part == 0) write_invalid(A, b, tid, 0, kFinThreads);
+    if (part == 0) write_invalid(A, b, tid, 0, NT);
     return;
   }
 
@@ -1623,24 +1625,24 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
   // out of the generic path: after a generic store every wait for a load
   // would drain all loads in flight.)
   // With K parts the waves of all parts share the steps round-robin: wave w of
-  // part p is wave p * kFinWaves + w of K * kFinWaves (K > 1 only when the
+  // part p is wave p * NW + w of K * NW (K > 1 only when the
   // steps fit in LDS).
   int mode = P.mode;
   const bool lds_steps = A.ns2 <= kLdsSteps;
   const StepOut sh_out{sh_steps, sh_q, sh_d, sh_c};
   const StepOut st = lds_steps ? sh_out : ws_steps(A, b);
   if (lds_steps)
-    all_step_masses<TD, DD>(A, b, P, mode, part * kFinWaves + w, K * kFinWaves, sh_out);
+    all_step_masses<TD, DD>(A, b, P, mode, part * NW + w, K * NW, sh_out);
   else
-    all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, ws_steps(A, b));
+    all_step_masses<TD, DD>(A, b, P, mode, w, NW, ws_steps(A, b));
   __syncthreads();  // every wave's step sums are visible to the workgroup
   if (K > 1) {
     // Hand-off: each part publishes its step sums (relaxed device-scope
     // atomic stores, which no cache of this XCD holds back) and counts itself
     // done; the part that counts last gathers every step's sums and draws.
     const StepOut g = ws_steps(A, b);
-    for (int s = tid; s < A.ns2; s += kFinThreads)
-      if ((s % (K * kFinWaves)) / kFinWaves == part) {
+    for (int s = tid; s < A.ns2; s += NT)
+      if ((s % (K * NW)) / NW == part) {
         __hip_atomic_store(g.m + s, sh_steps[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(g.q + s, sh_q[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(g.d + s, sh_d[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1651,7 +1653,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     __syncthreads();
     if (!sh_last) return;
     if (tid == 0) A.done[b] = 0;  // ready for the next finish launch on this workspace
-    gather_steps<TD, DD>(A, b, P, mode, part, sh_out);
+    gather_steps<TD, DD, NW>(A, b, P, mode, part, sh_out);
     __syncthreads();
   }
   if (w == 0) {
@@ -1675,9 +1677,9 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(4))
     mode = kModeBonus;
     Pd.g = 0.0;
     if (lds_steps)
-      all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, sh_out);
+      all_step_masses<TD, DD>(A, b, P, mode, w, NW, sh_out);
     else
-      all_step_masses<TD, DD>(A, b, P, mode, w, kFinWaves, ws_steps(A, b));
+      all_step_masses<TD, DD>(A, b, P, mode, w, NW, ws_steps(A, b));
     __syncthreads();
     if (w == 0) {
       const double tot = wave_total(st.m, A.ns2, lane);
@@ -2427,9 +2429,12 @@ static hipError_t launch_pair(const SampleLaunch& A, int stage, hipStream_t stre
   if (stage == 1)
     hipLaunchKernelGGL((sv_stats_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.per_seq)), dim3(kThreads), 0,
                        stream, A);
+  else if (A.fin_waves == 2 * kFinWaves)
+    hipLaunchKernelGGL((sv_finish_kernel<TD, DD, 2 * kFinWaves>), dim3((unsigned)((int64_t)A.B * A.parts)),
+                       dim3(2 * kFinThreads), 0, stream, A);
   else
-    hipLaunchKernelGGL((sv_finish_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.parts)), dim3(kFinThreads), 0,
-                       stream, A);
+    hipLaunchKernelGGL((sv_finish_kernel<TD, DD, kFinWaves>), dim3((unsigned)((int64_t)A.B * A.parts)),
+                       dim3(kFinThreads), 0, stream, A);
   return hipGetLastError();
 }
 

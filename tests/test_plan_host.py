@@ -27,6 +27,12 @@ int main() {
   const long long pb[][2] = {{512, 125}, {256, 63}, {64, 16}, {1, 125}, {1, 63}, {3, 147}, {40, 63}, {1, 2051}, {1, 1},
                              {255, 2048}, {100, 7}};
   for (int i = 0; i < 11; ++i) std::printf("%s%d", i ? "," : "", finish_parts(pb[i][0], pb[i][1]));
+  std::printf("], \"shape\": [");
+  for (int i = 0; i < 11; ++i) {
+    int k, nw;
+    finish_shape(pb[i][0], pb[i][1], &k, &nw);
+    std::printf("%s[%d,%d]", i ? "," : "", k, nw);
+  }
   std::printf("], \"tail\": [");
   const long long tb[][5] = {{512, 5, 256000, 2, 4}, {256, 8, 128256, 2, 2}, {64, 4, 32000, 2, 2},
                              {1, 8, 128256, 2, 2}, {4096, 64, 256000, 4, 4}, {1024, 1, 256000, 2, 2}};
@@ -98,6 +104,29 @@ def test_finish_parts(plan):
              (100, 7)]
     assert plan["parts"] == [parts(B, n) for B, n in cases]
     assert plan["parts"][:4] == [1, 1, 2, 15]
+
+
+def test_finish_shape(plan):
+    # a split whose 8-wave parts stream at most two steps per wave runs as
+    # ceil(K / 2) parts of 16 waves; otherwise K parts of 8 waves
+    def parts(B, ns2):
+        if ns2 > 2048:
+            return 1
+        return max(1, min(-(-256 // B), ns2 // 8))
+
+    def shape(B, ns2):
+        k = parts(B, ns2)
+        if k >= 2 and ns2 <= 2 * k * 8:
+            return [(k + 1) // 2, 16]
+        return [k, 8]
+    cases = [(512, 125), (256, 63), (64, 16), (1, 125), (1, 63), (3, 147), (40, 63), (1, 2051), (1, 1), (255, 2048),
+             (100, 7)]
+    assert plan["shape"] == [shape(B, n) for B, n in cases]
+    # config 5 and 3 batches: one 8-wave part; config 2: one 16-wave part (no hand-off);
+    # one sequence of 256k tokens: 8 parts of 16 waves; 64 sequences of 256k: 4 of 8
+    assert plan["shape"][:4] == [[1, 8], [1, 8], [1, 16], [8, 16]]
+    k, nw = shape(64, 125)
+    assert (k, nw) == (4, 8)
 
 
 def test_early_exit_grouping(plan):
