@@ -144,10 +144,13 @@ def test_workspace_reuse_across_shapes_and_stages(gpu):
 
 
 @pytest.mark.parametrize("B,G,V,tdt,ddt", [(24, 3, 70000, "bf16", "f32"), (3, 2, 300000, "f32", "bf16"),
-                                         (40, 2, 128256, "bf16", "bf16"), (1, 4, 256000, "bf16", "f32")])
+                                         (40, 2, 128256, "bf16", "bf16"), (1, 4, 256000, "bf16", "f32"),
+                                         (128, 2, 70000, "bf16", "bf16"), (100, 2, 100000, "bf16", "f32")])
 def test_finish_split_over_parts(gpu, B, G, V, tdt, ddt):
     """Few sequences with long rows: each sequence's draw is split over several
-    finish workgroups (the last to finish gathers the step masses and draws).
+    finish workgroups (the last to finish gathers the step masses and draws):
+    16-wave parts where the parts' streams are short (the first four shapes),
+    8-wave parts where they are long (B = 128 and 100: 2 and 3 parts).
     Results against the oracle; then the finish stage alone, run three times
     after one statistics stage on a garbage-filled workspace, gives the full
     call's outputs every time (the hand-off state is reset by the statistics
