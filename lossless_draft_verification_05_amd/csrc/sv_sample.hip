@@ -17,8 +17,10 @@
 //           instruction, non-temporal) and keeps a per-lane tempered sum-exp
 //           against a lazily moved reference; one partial per wave.
 //  finish : one 512-thread workgroup per sequence (with fewer sequences than
-//           CUs, several per sequence that hand their step masses to the last
-//           one through relaxed device-scope atomics, no fence and no wait).
+//           CUs, several per sequence -- 1024-thread ones where each wave
+//           streams at most two steps -- that hand their step masses to the
+//           last one through relaxed device-scope atomics, no fence and no
+//           wait).
 //           It merges the partials of the sequence's rows (a wave per row),
 //           gathers p(x), q(x), runs the accept tests and the first-rejection
 //           ballot, streams the one row (pair) the draw needs -- max(0, p_n -
@@ -27,8 +29,9 @@
 //           rescanned step -> one octet to the token whose running mass first
 //           exceeds u_gamma * total, and writes the outputs.
 // With V <= 2048 the whole call is one kernel instead (small: one wave per
-// sequence). Also here: the early-exit statistics kernel (stats_pos) and the
-// one-pass draft sampler (draft1).
+// sequence; small2: two per wave when V <= 32 and 2 gamma + 1 <= 32). Also
+// here: the early-exit statistics kernel (stats_pos) and the one-pass draft
+// sampler (draft1).
 #include <type_traits>
 
 #include "sv_device.hpp"
@@ -1469,7 +1472,7 @@ __device__ __forceinline__ SeqPlan uniform_plan(const SeqPlan& src) {
 }
 
 // ---------------------------------------------------------------------------
-// finish kernel: one 512-thread workgroup per sequence
+// finish kernel: one workgroup (512 or 1024 threads) per sequence or part
 // ---------------------------------------------------------------------------
 constexpr int kMergeRows = 3;  // rows per wave merged from one batch of loads: 2 * gamma + 1 <= 24
 // NW: waves per workgroup (kFinWaves, or twice that for split sequences).
@@ -1693,7 +1696,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 }
 
 // ---------------------------------------------------------------------------
-// one-pass draft sampler: one 512-thread workgroup per row (gamma = 0)
+// one-pass draft sampler: one workgroup (512 or 1024 threads) per row (gamma = 0)
 // ---------------------------------------------------------------------------
 // One pass over the row writes the exact mass of every 2048-token step into
 // LDS, each against its own reference: a lane takes its terms against a
