@@ -659,7 +659,8 @@ def main():
         s1_bytes = B * N * V * esz(inp.dtype) + 2 * B * N * 4
         cfg_desc = {"workload": f"{args.workload}: greedy decoding-tree verification", "B": B, "N": N, "V": V,
                     "logits_dtype": inp.dtype, "seed": args.seed}
-        kernel_names = ["sv_argmax_kernel", "sv_tree_kernel"]
+        # trees of at most 64 nodes resolve in one wave (no LDS, no barrier)
+        kernel_names = ["sv_argmax_kernel", "sv_tree64_kernel" if N <= 64 else "sv_tree_kernel"]
     else:
         cfg = inp.cfg
         t0_ = up(inp.target, cfg.target_dtype)

@@ -16,7 +16,8 @@
 //  tree   : a workgroup per tree merges the row partials and resolves the tree
 //           in LDS by pointer jumping over the parent array (log2 N rounds),
 //           which also leaves a binary-lifting table for writing the accepted
-//           path in parallel.
+//           path in parallel; trees of at most 64 nodes take one wave and do
+//           the same in registers (tree64).
 #include "sv_device.hpp"
 
 namespace sv {
@@ -245,6 +246,102 @@ __global__ __launch_bounds__(kThreads) void sv_tree_kernel(TreeLaunch A) {
 #undef s_A
 }
 
+// Trees of at most 64 nodes: one wave per tree, node j in lane j, and the
+// same resolve as sv_tree_kernel by pointer jumping in registers (ds_bpermute
+// reads another lane's value), so no LDS and no barrier: acc, depth and the
+// 2^k-th ancestor of every node after k rounds, the deepest accepted node
+// (lowest id on ties) by a wave maximum of the same key, then each path entry
+// by binary lifting over the saved ancestor registers.
+constexpr int kWaveTreeRounds = 6;  // ceil(log2 64)
+template <int DT>
+__global__ __launch_bounds__(kWave) void sv_tree64_kernel(TreeLaunch A) {
+  const int j = threadIdx.x;  // node
+  const int b = blockIdx.x;
+  const int N = A.N;
+  const bool in = j < N;
+  const int per_seq = A.N * A.nch;
+  int pj = -1, tk = 0;
+  if (in) {
+    // the node's parent and token first: their loads do not wait for the partials'
+    pj = A.parents[(int64_t)b * N + j];
+    tk = A.tokens[(int64_t)b * N + j];
+  }
+  float v = -INFINITY;
+  int i = INT_MAX, bad = 0;
+  if (in) {
+    const ArgPartial* q = A.part + (int64_t)b * per_seq + (int64_t)j * A.nch;
+    // the row's chunk partials, four loads in flight at a time, combined in chunk order
+    for (int c0 = 0; c0 < A.nch; c0 += 4) {
+      ArgPartial r[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c0 + k < A.nch) r[k] = q[c0 + k];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c0 + k < A.nch) {
+          arg_combine(v, i, r[k].best, r[k].idx);
+          bad |= r[k].bad;
+        }
+    }
+    if (v == INFINITY) bad = 1;  // +inf makes the row unusable
+    if (v == -INFINITY) i = 0;   // a row of -inf only: first index
+    if (A.out_argmax) A.out_argmax[(int64_t)b * N + j] = bad ? -1 : i;
+  }
+  const bool node_ok = (j == 0) ? (pj == -1) : (pj >= 0 && pj < j && tk >= 0 && tk < A.V);
+  int32_t* opath = A.out_path + (int64_t)b * N;
+  if (__ballot(in && (bad || !node_ok)) != 0ull) {  // the same in every lane
+    if (in) opath[j] = -1;
+    if (j == 0) {
+      A.out_len[b] = -1;
+      A.out_bonus[b] = -1;
+    }
+    return;
+  }
+  const int g = i;  // argmax of row j
+  int up = (j == 0 || !in) ? -1 : pj;
+  const int gp = __shfl(g, up >= 0 ? up : 0, kWave);
+  int acc = (j == 0) ? 1 : (in && tk == gp ? 1 : 0);
+  int dep = (j == 0 || !in) ? 0 : 1;
+  int rounds = 0;
+  while ((1 << rounds) < N) ++rounds;
+  int ups[kWaveTreeRounds];  // ups[k]: the 2^k-th ancestor (-1 past the root)
+#pragma unroll
+  for (int k = 0; k < kWaveTreeRounds; ++k) {
+    ups[k] = up;
+    if (k < rounds) {
+      const int src = up >= 0 ? up : j;
+      const int a2 = __shfl(acc, src, kWave), d2 = __shfl(dep, src, kWave), u2 = __shfl(up, src, kWave);
+      if (up >= 0) {
+        acc &= a2;
+        dep += d2;
+        up = u2;
+      }
+    }
+  }
+  // deepest accepted node, lowest id on ties: key = depth * 2048 + (2047 - id)
+  int key = (in && acc) ? ((dep << 11) | (2047 - j)) : -1;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, kWave));
+  const int d = 2047 - (key & 2047);
+  const int depth = key >> 11;
+  // path entry t = the (depth - t)-th ancestor of d, for t <= depth
+  const int dist = depth - j;
+  int node = d;
+#pragma unroll
+  for (int k = 0; k < kWaveTreeRounds; ++k) {
+    if (k < rounds) {
+      const int nn = __shfl(ups[k], node, kWave);
+      if (dist >= 0 && ((dist >> k) & 1)) node = nn;
+    }
+  }
+  if (in) opath[j] = dist >= 0 ? node : -1;
+  const int bonus = __shfl(g, d, kWave);
+  if (j == 0) {
+    A.out_len[b] = depth;
+    A.out_bonus[b] = bonus;
+  }
+}
+
 size_t tree_lds_bytes(int N) {
   return (size_t)N * 8 + (size_t)(kLog2MaxNodes + 1) * N * 2 + (size_t)2 * N * 2 + (size_t)2 * N + 16;
 }
@@ -257,6 +354,11 @@ hipError_t launch_tree(const TreeLaunch& A, int dt, int stage, hipStream_t strea
       hipLaunchKernelGGL((sv_argmax_kernel<1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A);
     else
       hipLaunchKernelGGL((sv_argmax_kernel<0>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A);
+  } else if (A.N <= kWave) {
+    if (dt == 1)
+      hipLaunchKernelGGL((sv_tree64_kernel<1>), dim3((unsigned)A.B), dim3(kWave), 0, stream, A);
+    else
+      hipLaunchKernelGGL((sv_tree64_kernel<0>), dim3((unsigned)A.B), dim3(kWave), 0, stream, A);
   } else {
     if (dt == 1)
       hipLaunchKernelGGL((sv_tree_kernel<1>), dim3((unsigned)A.B), dim3(kThreads), tree_lds_bytes(A.N), stream, A);
