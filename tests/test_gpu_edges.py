@@ -261,6 +261,35 @@ def test_tree_invalid(gpu):
     assert out["argmax"][0, 3] == -1 and out["argmax"][1, 8] == -1
 
 
+@pytest.mark.parametrize("N", [63, 64, 65])
+def test_tree_one_wave_boundary(gpu, N):
+    """Trees of up to 64 nodes resolve in one wave (registers), larger ones in
+    LDS: at N = 63, 64 and 65, a full chain whose edges all match, the same
+    chain broken half way, a star, random trees with repeated sibling tokens
+    (ties on depth go to the lowest id), and an invalid tree in the batch, all
+    bit-exact against the oracle."""
+    g = np.random.default_rng(300 + N)
+    V = 40
+    B = 7
+    L = g.integers(-3, 4, size=(B, N, V)).astype(np.float32)  # many exact ties
+    parents = np.empty((B, N), np.int32)
+    parents[0] = parents[1] = [-1] + list(range(N - 1))
+    parents[2] = [-1] + [0] * (N - 1)
+    for b in range(3, B):
+        parents[b] = [-1] + [int(g.integers(max(0, j - 4), j)) for j in range(1, N)]
+    am = np.argmax(L, axis=2)  # lowest index on ties
+    tokens = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for j in range(1, N):
+            p = parents[b, j]
+            tokens[b, j] = am[b, p] if (b < 2 or g.random() < 0.7) else (am[b, p] + 1) % V
+    tokens[1, N // 2] = (am[1, N // 2 - 1] + 1) % V  # the second chain breaks at node N / 2
+    parents[6, 5] = 9  # a forward parent: invalid tree
+    out = _tree_run_check(gpu, L, parents, tokens)
+    assert out["len"][0] == N - 1 and out["len"][1] == N // 2 - 1
+    assert out["len"][2] == 1 and out["len"][6] == -1 and (out["path"][6] == -1).all()
+
+
 def test_tree_single_node_and_max_chain(gpu):
     g = np.random.default_rng(14)
     L = g.normal(size=(3, 1, 64)).astype(np.float32)
