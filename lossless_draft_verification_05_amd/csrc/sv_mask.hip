@@ -248,8 +248,81 @@ __global__ __launch_bounds__(kThreads) void sv_mask_kernel(MaskLaunch A) {
   }
 }
 
+// Trees of at most 64 nodes: one wave per tree, row j in lane j. A row's
+// ancestors (and itself) are one 64-bit set in a register, built by pointer
+// doubling over the parents with __shfl (set |= the ancestor's set, then jump
+// to the ancestor's ancestor; six rounds cover any depth below 64), so no LDS
+// and no barrier; the depth is its population count minus one. The relaxed
+// mask adds, for every node k with the row's block id, bit k (one ballot per
+// node). Each lane writes its own rows, four bytes at a time (bytes where N or
+// the buffer leaves a row unaligned). An invalid tree's masks are all zero and
+// its depths -1, as in the workgroup kernel.
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const unsigned lo = (unsigned)__shfl((int)(unsigned)v, src, kWave);
+  const unsigned hi = (unsigned)__shfl((int)(unsigned)(v >> 32), src, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void write_row64(uint8_t* out, int N, uint64_t m, bool words) {
+  if (words) {
+    uint32_t* o = reinterpret_cast<uint32_t*>(out);
+    for (int w = 0; w < (N >> 2); ++w) o[w] = bits_to_bytes((uint32_t)(m >> (4 * w)) & 0xfu);
+  } else {
+    for (int t = 0; t < N; ++t) out[t] = (uint8_t)((m >> t) & 1u);
+  }
+}
+
+__global__ __launch_bounds__(kWave) void sv_mask64_kernel(MaskLaunch A) {
+  const int j = threadIdx.x, b = blockIdx.x, N = A.N;
+  const bool in = j < N;
+  int p = -1, bl = -1;
+  if (in) {
+    p = A.parents[(int64_t)b * N + j];
+    if (A.blocks) bl = A.blocks[(int64_t)b * N + j];
+  }
+  const bool ok = (j == 0) ? p == -1 : (p >= 0 && p < j);
+  const bool bad = __ballot(in && !ok) != 0ull;  // the same in every lane
+  uint64_t anc = 0, rel = 0;
+  int depth = -1;
+  if (!bad) {
+    int up = in ? p : -1;
+    anc = in ? ((1ull << j) | (up >= 0 ? 1ull << up : 0ull)) : 0ull;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+      const int src = up >= 0 ? up : j;
+      const uint64_t a2 = shfl_u64(anc, src);
+      const int u2 = __shfl(up, src, kWave);
+      if (up >= 0) {
+        anc |= a2;
+        up = u2;
+      }
+    }
+    depth = in ? __popcll(anc) - 1 : -1;
+    rel = anc;
+    if (A.out_relaxed) {
+      for (int k = 0; k < N; ++k) {
+        const int bk = __builtin_amdgcn_readlane(bl, k);
+        if (bk >= 0 && bl == bk) rel |= 1ull << k;
+      }
+    }
+  }
+  if (!in) return;
+  if (A.out_depth) A.out_depth[(int64_t)b * N + j] = depth;
+  const int64_t row = (int64_t)b * N * N + (int64_t)j * N;
+  if (A.out_mask) {
+    uint8_t* o = A.out_mask + row;
+    write_row64(o, N, anc, (N & 3) == 0 && ((uintptr_t)A.out_mask & 3) == 0);
+  }
+  if (A.out_relaxed) {
+    uint8_t* o = A.out_relaxed + row;
+    write_row64(o, N, rel, (N & 3) == 0 && ((uintptr_t)A.out_relaxed & 3) == 0);
+  }
+}
+
 hipError_t launch_mask(const MaskLaunch& A, hipStream_t stream) {
-  hipLaunchKernelGGL(sv_mask_kernel, dim3((unsigned)((int64_t)A.B * A.nslab)), dim3(kThreads), 0, stream, A);
+  if (A.N <= kWave)
+    hipLaunchKernelGGL(sv_mask64_kernel, dim3((unsigned)A.B), dim3(kWave), 0, stream, A);
+  else
+    hipLaunchKernelGGL(sv_mask_kernel, dim3((unsigned)((int64_t)A.B * A.nslab)), dim3(kThreads), 0, stream, A);
   return hipGetLastError();
 }
 
