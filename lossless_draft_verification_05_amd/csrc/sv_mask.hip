@@ -15,11 +15,12 @@
 // ancestor and jumps L ancestors at a time to the root (parents[j] < j bounds
 // the path by j nodes), so the L threads together set the bits of every
 // ancestor of the row in an LDS bitset, and their node counts sum to the
-// depth. The
-// slab (at most 16 KB of mask bytes, so at most 2 KB of bits) is then written
-// with 16-byte stores, each built from at most two bitset words. When N is a
-// multiple of 16 and the outputs are 16-byte aligned, both masks come from one
-// pass over the slab's vectors, each inside one row and one bitset word.
+// depth. The slab (at most 16 KB of mask bytes, so at most 2 KB of bits) is
+// then written with 16-byte stores, each built from at most two bitset words.
+// When N is a multiple of 16 and the outputs are 16-byte aligned, both masks
+// come from one pass over the slab's vectors, each inside one row and one
+// bitset word. Trees of at most 64 nodes take one wave each instead (mask64,
+// below): every row's ancestor set fits a 64-bit register.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
