@@ -221,10 +221,10 @@ int spec_verify_sample_early_exit_grouped(int tail_start, const void* target_log
  * spec_verify_sample; `stage` selects:
  *   1: row statistics: streams every target and draft row once (maximum and
  *      tempered sum-exp per wave and row chunk, into the workspace);
- *   2: finish, one workgroup per sequence: merges the statistics, runs the
- *      accept tests and the first-rejection scan, streams the one row (pair)
- *      the draw needs, draws by inverse CDF at u[b][gamma] and writes every
- *      output (and diag).
+ *   2: finish, one workgroup per sequence (several for small batches of
+ *      long rows): merges the statistics, runs the accept tests and the
+ *      first-rejection scan, streams the one row (pair) the draw needs, draws
+ *      by inverse CDF at u[b][gamma] and writes every output (and diag).
  * Stage 2 must follow stage 1 on the same stream with the same arguments and
  * workspace. spec_verify_sample enqueues both.
  */
