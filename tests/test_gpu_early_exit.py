@@ -164,3 +164,15 @@ def test_one_step_rows_no_gate_same_bits(gpu, tdt, ddt, V):
     t = H.check_sample(inp, one)
     H.log(f"[early exit one-step rows V={V}] {t.summary()}")
     assert not t.fail, t.fail[:3]
+
+
+@pytest.mark.parametrize("grouping", ["first", "all"])
+@pytest.mark.parametrize("V,tdt,ddt", [(32, "f32", "f32"), (20, "bf16", "bf16"), (700, "bf16", "f32")])
+def test_one_step_rows_gated(gpu, V, tdt, ddt, grouping):
+    """Rows of one draw step with gated positions: the statistics launches and
+    the finish kernel (not the one-kernel path), against the oracle and the
+    one-pass call."""
+    H.log(f"early exit, rows of one step, gated ({grouping}): V={V} {tdt}/{ddt}")
+    inp = synth.make_custom_sample(9, 5, V, tdt, ddt, T=np.linspace(0.6, 1.4, 9, dtype=np.float32),
+                                   noise_sd=0.6, seed=V + 17)
+    _both(gpu, inp, pad=8, name=f"one-step rows V={V}", grouping=grouping)
