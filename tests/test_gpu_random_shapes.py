@@ -4,7 +4,9 @@ that the combinations between the hand-picked edge cases are covered too: the
 one-pass call and the early-exit call against the fp64 oracle with the parity
 contract, and against each other; greedy trees of random size, vocabulary and
 dtype bit for bit; draft-side sampling of random batches (both of its paths:
-one pass for many or short rows, statistics and draw for few long ones)."""
+one pass for many or short rows, statistics and draw for few long ones); tree
+masks of random parent arrays and blocks bit for bit; the early exit under a
+random grouping of positions."""
 import numpy as np
 import pytest
 
@@ -84,3 +86,63 @@ def test_random_draft_shape(gpu, k):
     H.log(f"[random draft {k}] {t.summary()}")
     assert not t.fail, t.fail[:3]
     assert t.flagged <= 2
+
+
+MASK_CASES = 8
+
+
+@pytest.mark.parametrize("k", range(MASK_CASES))
+def test_random_mask_shape(gpu, k):
+    """spec_tree_mask on random parent arrays (N from 1 to 300, on both sides
+    of the one-wave kernel's 64 nodes; parents at most w back, w random), random
+    block ids and, now and then, an invalid tree in the batch: bit-exact
+    against the oracle."""
+    import torch
+
+    from oracle import spec_verify_oracle as O
+
+    g = np.random.default_rng(9900 + k)
+    B = int(g.integers(1, 9))
+    N = int(np.exp(g.uniform(0, np.log(300))))
+    P = np.empty((B, N), np.int32)
+    for b in range(B):
+        w = int(g.integers(1, 20))
+        P[b] = [-1] + [int(g.integers(max(0, j - w), j)) for j in range(1, N)]
+    if B > 1 and N > 2 and g.random() < 0.5:
+        P[B - 1, N - 1] = N - 1  # a self parent: invalid tree
+    Bl = g.integers(-1, max(2, N // 3), (B, N)).astype(np.int32)
+    H.log(f"random mask shape {k}: B={B} N={N}")
+    m, r, d = gpu.spec_tree_mask(torch.from_numpy(P).cuda(), torch.from_numpy(Bl).cuda(), want_relaxed=True)
+    torch.cuda.synchronize()
+    m, r, d = m.cpu().numpy(), r.cpu().numpy(), d.cpu().numpy()
+    for b in range(B):
+        wm, wr, wd = O.tree_masks(P[b], Bl[b])
+        assert np.array_equal(m[b], wm) and np.array_equal(r[b], wr) and np.array_equal(d[b], wd), (k, b)
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_random_shape_grouped_early_exit(gpu, k):
+    """The early exit with a random grouping of positions (tail start 0..gamma)
+    on random shapes, against the oracle and the one-pass call."""
+    g = np.random.default_rng(9800 + k)
+    V = int(np.exp(g.uniform(np.log(1), np.log(300000))))
+    G = int(g.integers(1, 20))
+    B = int(g.integers(1, 60))
+    while B > 1 and B * (2 * G + 1) * V > 20_000_000:
+        B //= 2
+    tdt, ddt = [str(x) for x in g.choice(["bf16", "f32"], 2)]
+    pad = -(-V // 8) * 8 if V % 8 else None
+    ts = int(g.integers(0, G + 1))
+    H.log(f"random grouped early exit {k}: B={B} gamma={G} V={V} {tdt}/{ddt} tail_start={ts}")
+    inp = synth.make_custom_sample(B, G, V, tdt, ddt, T=g.uniform(0.3, 2.0, B).astype(np.float32),
+                                   noise_sd=float(g.uniform(0.05, 1.5)), seed=k + 101)
+    tens = H.sample_tensors(inp, pad_to=pad)
+    one = H.run_sample(gpu, tens)
+    ee = H.run_sample(gpu, tens, early_exit=True, tail_start=ts)
+    for name, out in (("one pass", one), ("early exit", ee)):
+        t = H.check_sample(inp, out)
+        H.log(f"[random grouped {k} {name}] {t.summary()}")
+        assert not t.fail, t.fail[:3]
+        assert t.flagged <= max(2, 0.01 * t.checked)
+    differ, bad = H.compare_one_pass(one, ee)
+    assert not bad, bad[:3]
