@@ -227,8 +227,8 @@ inline int finish_parts(int64_t B, int64_t ns2) {
 // ceil(K / 2) parts of 2 * kFinWaves waves instead: the same waves (or one
 // part's more) with half the repeated merges and accept tests, and no hand-off
 // at all for K = 2; its stream is one or two round trips per wave either way
-// (measured: c2 0.0298 -> 0.0287 ms, a single 128k or 256k sequence 0.0220 ->
-// 0.0209 and 0.0255 -> 0.0248 ms). With longer streams the workgroups' CUs
+// (measured: 64 sequences of 32k bf16 tokens, gamma 4: 0.0298 -> 0.0287 ms; a
+// single 128k or 256k sequence 0.0220 -> 0.0209 and 0.0255 -> 0.0248 ms). With longer streams the workgroups' CUs
 // bound the stream, and halving them costs more (64 sequences of 256k: 0.117
 // -> 0.127 ms), so they keep kFinWaves.
 inline void finish_shape(int64_t B, int64_t ns2, int* parts, int* waves) {
