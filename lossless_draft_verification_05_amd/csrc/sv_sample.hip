@@ -1065,6 +1065,106 @@ __device__ __forceinline__ StepSums direct_step_sums_of(const char* trow, const 
   return direct_step_sums<TD, DD, kModeBonus, 0>(trow, drow, s, noct, V, P, lane);
 }
 
+// One step per wave, its loads kept: direct_step_sums (the same operations in
+// the same order, so the same bits) with the step's octets left in t and d,
+// which the draw then rescans from registers instead of loading them again
+// (the rescan's memory round trip is most of the draw's time on short rows).
+template <int TD, int DD, int MODE, int FORM>
+__device__ __forceinline__ StepSums kept_step_sums(const char* trow, const char* drow, int64_t s, int64_t noct,
+                                                   int V, const SeqPlan& P, int lane, OctetIn<TD> (&t)[kU2],
+                                                   OctetIn<DD> (&d)[kU2]) {
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    t[j].load(trow, oct, noct, V);
+    if constexpr (MODE == kModeResidual) d[j].load(drow, oct, noct, V);
+  }
+  double r = 0.0;
+  CheapAcc a;
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float xt[8], xd[8];
+      t[j].to_float(oct, V, xt);
+      if constexpr (MODE == kModeResidual) d[j].to_float(oct, V, xd);
+      if constexpr (MODE == kModeResidual && FORM == 1) {
+        a.add(cheap_sums8(xt, xd, P));
+      } else {
+        float rr[8];
+        mass8<MODE, FORM>(xt, xd, P, rr);
+        r += (double)sum8(rr);
+      }
+    }
+  }
+  if constexpr (MODE == kModeResidual && FORM == 1) {
+    const StepSums v = cheap_step_sums(a);
+    if (cheap_ok(v.m, v.q)) return v;
+    return exact_step_sums<TD, DD>(t, d, s, noct, V, P, lane);
+  }
+  return StepSums{wave_sum(r), 0.0, 0.0, 0.0};
+}
+
+template <int TD, int DD>
+__device__ __forceinline__ StepSums kept_step_sums_of(const char* trow, const char* drow, int64_t s, int64_t noct,
+                                                      int V, int mode, const SeqPlan& P, int lane,
+                                                      OctetIn<TD> (&t)[kU2], OctetIn<DD> (&d)[kU2]) {
+  if (mode == kModeResidual) {
+    if (P.form == 1) return kept_step_sums<TD, DD, kModeResidual, 1>(trow, drow, s, noct, V, P, lane, t, d);
+    return kept_step_sums<TD, DD, kModeResidual, 0>(trow, drow, s, noct, V, P, lane, t, d);
+  }
+  if (P.form == 1) return kept_step_sums<TD, DD, kModeBonus, 1>(trow, drow, s, noct, V, P, lane, t, d);
+  return kept_step_sums<TD, DD, kModeBonus, 0>(trow, drow, s, noct, V, P, lane, t, d);
+}
+
+// The bonus-mode sums of a kept step (the fallback after a residual of zero
+// mass), from the target octets in t.
+template <int TD, int DD>
+__device__ __forceinline__ StepSums kept_bonus_sums(const OctetIn<TD> (&t)[kU2], int64_t s, int64_t noct, int V,
+                                                    const SeqPlan& P, int lane) {
+  double r = 0.0;
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float xt[8], xd[8];
+      t[j].to_float(oct, V, xt);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xd[k] = 0.0f;
+      float rr[8];
+      if (P.form == 1)
+        mass8<kModeBonus, 1>(xt, xd, P, rr);
+      else
+        mass8<kModeBonus, 0>(xt, xd, P, rr);
+      r += (double)sum8(rr);
+    }
+  }
+  return StepSums{wave_sum(r), 0.0, 0.0, 0.0};
+}
+
+// The token masses of a kept step, as step_octet_masses takes them from memory.
+template <int TD, int DD>
+__device__ __forceinline__ void kept_octet_masses(const OctetIn<TD> (&t)[kU2], const OctetIn<DD> (&d)[kU2], int64_t s,
+                                                  int64_t noct, int V, int mode, const SeqPlan& P, int lane,
+                                                  bool cheap, float (&rr)[kU2][8]) {
+#pragma unroll
+  for (int j = 0; j < kU2; ++j) {
+    const int64_t oct = s * kStepOctets + kWave * j + lane;
+    if (oct < noct) {
+      float xt[8], xd[8];
+      t[j].to_float(oct, V, xt);
+      if (mode != kModeBonus) d[j].to_float(oct, V, xd);
+      if (mode == kModeResidual && P.form == 1 && cheap)
+        mass8_cheap(xt, xd, P, rr[j]);
+      else
+        mass8_of(xt, xd, mode, P, rr[j]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rr[j][k] = 0.0f;
+    }
+  }
+}
+
 // A whole step's sums in the pipelined loop from the lane's shares: in the
 // residual's FMA form the cheap ones, or, where cheap_ok rejects them, the
 // exact ones from the step loaded again (its data has left the registers;
@@ -1476,7 +1576,10 @@ __device__ __forceinline__ SeqPlan uniform_plan(const SeqPlan& src) {
 // ---------------------------------------------------------------------------
 constexpr int kMergeRows = 3;  // rows per wave merged from one batch of loads: 2 * gamma + 1 <= 24
 // NW: waves per workgroup (kFinWaves, or twice that for split sequences).
-template <int TD, int DD, int NW>
+// OS: one workgroup per sequence and at most one step per wave: each wave
+// keeps its step's octets in registers and the wave whose step holds the
+// draw rescans it from there (no second load of the draw row at the end).
+template <int TD, int DD, int NW, bool OS>
 // At most 128 VGPRs, so that two 8-wave workgroups (one 16-wave one) fit a CU.
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4))) void sv_finish_kernel(
     SampleLaunch A) {
@@ -1520,6 +1623,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4)))
       ld = load_elem<DD>(A.dft + (int64_t)b * A.d_seq_b + (int64_t)lane * A.d_row_b, xi);
     }
   }
+
+  __shared__ int sh_xi[kWave];  // the draft tokens, for the wave that draws (OS)
+  if (OS && w == 0) sh_xi[lane] = xi;
 
   // (2) merge the partials of every row: one wave per row, lanes over partials.
   // When every row has at most one partial per lane and each wave has at most
@@ -1622,77 +1728,136 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4)))
     return;
   }
 
-  // (4) sums of the drawn distribution's steps, every wave on its steps, into
-  // LDS when they fit, else the workspace. (The two calls differ only in the
-  // address space of the output, which keeps the stores of the streaming loop
-  // out of the generic path: after a generic store every wait for a load
-  // would drain all loads in flight.)
-  // With K parts the waves of all parts share the steps round-robin: wave w of
-  // part p is wave p * NW + w of K * NW (K > 1 only when the
-  // steps fit in LDS).
-  int mode = P.mode;
-  const bool lds_steps = A.ns2 <= kLdsSteps;
-  const StepOut sh_out{sh_steps, sh_q, sh_d, sh_c};
-  const StepOut st = lds_steps ? sh_out : ws_steps(A, b);
-  if (lds_steps)
-    all_step_masses<TD, DD>(A, b, P, mode, part * NW + w, K * NW, sh_out);
-  else
-    all_step_masses<TD, DD>(A, b, P, mode, w, NW, ws_steps(A, b));
-  __syncthreads();  // every wave's step sums are visible to the workgroup
-  if (K > 1) {
-    // Hand-off: each part publishes its step sums (relaxed device-scope
-    // atomic stores, which no cache of this XCD holds back) and counts itself
-    // done; the part that counts last gathers every step's sums and draws.
-    const StepOut g = ws_steps(A, b);
-    for (int s = tid; s < A.ns2; s += NT)
-      if ((s % (K * NW)) / NW == part) {
-        __hip_atomic_store(g.m + s, sh_steps[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(g.q + s, sh_q[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(g.d + s, sh_d[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(g.c + s, sh_c[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    __syncthreads();
-    if (tid == 0) sh_last = __hip_atomic_fetch_add(A.done + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == K - 1;
-    __syncthreads();
-    if (!sh_last) return;
-    if (tid == 0) A.done[b] = 0;  // ready for the next finish launch on this workspace
-    gather_steps<TD, DD, NW>(A, b, P, mode, part, sh_out);
-    __syncthreads();
-  }
-  if (w == 0) {
-    // the residual's first-order correction of the normalisers' ratio (FMA
-    // form; g = 0 otherwise), then the total
-    double tot, g = 0.0;
-    if (mode == kModeResidual && P.form == 1)
-      g = correct_steps(st, A.ns2, P.sp * P.fscale, lane, tot);
-    else
-      tot = wave_total(st.m, A.ns2, lane);
-    if (lane == 0) {
-      sh_total = tot;
-      sh_g = g;
+  if constexpr (OS) {
+    // (4') one step per wave, its octets kept (parts == 1, ns2 <= NW)
+    int mode = P.mode;
+    const StepOut st{sh_steps, sh_q, sh_d, sh_c};
+    const char* trow = A.tgt + (int64_t)b * A.t_seq_b + (int64_t)P.n * A.t_row_b;
+    const char* drow = (mode == kModeResidual) ? A.dft + (int64_t)b * A.d_seq_b + (int64_t)P.n * A.d_row_b : nullptr;
+    const int64_t noct = ((int64_t)A.V + 7) / 8;
+    OctetIn<TD> kt[kU2];
+    OctetIn<DD> kd[kU2];
+    const bool has = w < A.ns2;
+    if (has) {
+      const StepSums v = kept_step_sums_of<TD, DD>(trow, drow, w, noct, A.V, mode, P, lane, kt, kd);
+      if (lane == 0) put_step(st, w, v);
     }
-  }
-  __syncthreads();
-  SeqPlan Pd = P;
-  Pd.g = sh_g;
-  if (!(sh_total > 0.0) && mode == kModeResidual) {
-    // Nothing left after the rejection (p_n == q_n up to rounding): draw from p_n.
-    mode = kModeBonus;
-    Pd.g = 0.0;
-    if (lds_steps)
-      all_step_masses<TD, DD>(A, b, P, mode, w, NW, sh_out);
-    else
-      all_step_masses<TD, DD>(A, b, P, mode, w, NW, ws_steps(A, b));
     __syncthreads();
     if (w == 0) {
-      const double tot = wave_total(st.m, A.ns2, lane);
-      if (lane == 0) sh_total = tot;
+      double tot, g = 0.0;
+      if (mode == kModeResidual && P.form == 1)
+        g = correct_steps(st, A.ns2, P.sp * P.fscale, lane, tot);
+      else
+        tot = wave_total(st.m, A.ns2, lane);
+      if (lane == 0) {
+        sh_total = tot;
+        sh_g = g;
+      }
     }
     __syncthreads();
-  }
-  const double total = sh_total;
+    SeqPlan Pd = P;
+    Pd.g = sh_g;
+    if (!(sh_total > 0.0) && mode == kModeResidual) {
+      // Nothing left after the rejection (p_n == q_n up to rounding): draw from
+      // p_n, from the kept target octets.
+      mode = kModeBonus;
+      Pd.g = 0.0;
+      if (has) {
+        const StepSums v = kept_bonus_sums<TD, DD>(kt, w, noct, A.V, P, lane);
+        if (lane == 0) put_step(st, w, v);
+      }
+      __syncthreads();
+      if (w == 0) {
+        const double tot = wave_total(st.m, A.ns2, lane);
+        if (lane == 0) sh_total = tot;
+      }
+      __syncthreads();
+    }
+    const double total = sh_total;
+    // (5) the step that holds the draw (every wave finds the same one), then
+    // its rescan by the wave that holds it, and (6) the outputs
+    const double t = (double)Pd.ug * total;
+    double acc = 0.0;
+    const int ss = max(wave_find(st.m, A.ns2, t, acc, lane), 0);
+    if (w != ss) return;
+    const bool cheap = mode == kModeResidual && sh_c[ss] > 0.5;
+    float rr[kU2][8];
+    kept_octet_masses<TD, DD>(kt, kd, ss, noct, A.V, mode, Pd, lane, cheap, rr);
+    const int y = scan_step<kU2>(rr, ss, t, acc, lane);
+    write_outputs<TD>(A, b, Pd, mode, y, total, lane, sh_xi[lane]);
+  } else {
+  // (4) sums of the drawn distribution's steps, every wave on its steps, into
+    // LDS when they fit, else the workspace. (The two calls differ only in the
+    // address space of the output, which keeps the stores of the streaming loop
+    // out of the generic path: after a generic store every wait for a load
+    // would drain all loads in flight.)
+    // With K parts the waves of all parts share the steps round-robin: wave w of
+    // part p is wave p * NW + w of K * NW (K > 1 only when the
+    // steps fit in LDS).
+    int mode = P.mode;
+    const bool lds_steps = A.ns2 <= kLdsSteps;
+    const StepOut sh_out{sh_steps, sh_q, sh_d, sh_c};
+    const StepOut st = lds_steps ? sh_out : ws_steps(A, b);
+    if (lds_steps)
+      all_step_masses<TD, DD>(A, b, P, mode, part * NW + w, K * NW, sh_out);
+    else
+      all_step_masses<TD, DD>(A, b, P, mode, w, NW, ws_steps(A, b));
+    __syncthreads();  // every wave's step sums are visible to the workgroup
+    if (K > 1) {
+      // Hand-off: each part publishes its step sums (relaxed device-scope
+      // atomic stores, which no cache of this XCD holds back) and counts itself
+      // done; the part that counts last gathers every step's sums and draws.
+      const StepOut g = ws_steps(A, b);
+      for (int s = tid; s < A.ns2; s += NT)
+        if ((s % (K * NW)) / NW == part) {
+          __hip_atomic_store(g.m + s, sh_steps[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(g.q + s, sh_q[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(g.d + s, sh_d[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(g.c + s, sh_c[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      __syncthreads();
+      if (tid == 0) sh_last = __hip_atomic_fetch_add(A.done + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == K - 1;
+      __syncthreads();
+      if (!sh_last) return;
+      if (tid == 0) A.done[b] = 0;  // ready for the next finish launch on this workspace
+      gather_steps<TD, DD, NW>(A, b, P, mode, part, sh_out);
+      __syncthreads();
+    }
+    if (w == 0) {
+      // the residual's first-order correction of the normalisers' ratio (FMA
+      // form; g = 0 otherwise), then the total
+      double tot, g = 0.0;
+      if (mode == kModeResidual && P.form == 1)
+        g = correct_steps(st, A.ns2, P.sp * P.fscale, lane, tot);
+      else
+        tot = wave_total(st.m, A.ns2, lane);
+      if (lane == 0) {
+        sh_total = tot;
+        sh_g = g;
+      }
+    }
+    __syncthreads();
+    SeqPlan Pd = P;
+    Pd.g = sh_g;
+    if (!(sh_total > 0.0) && mode == kModeResidual) {
+      // Nothing left after the rejection (p_n == q_n up to rounding): draw from p_n.
+      mode = kModeBonus;
+      Pd.g = 0.0;
+      if (lds_steps)
+        all_step_masses<TD, DD>(A, b, P, mode, w, NW, sh_out);
+      else
+        all_step_masses<TD, DD>(A, b, P, mode, w, NW, ws_steps(A, b));
+      __syncthreads();
+      if (w == 0) {
+        const double tot = wave_total(st.m, A.ns2, lane);
+        if (lane == 0) sh_total = tot;
+      }
+      __syncthreads();
+    }
+    const double total = sh_total;
 
-  draw_and_write<TD, DD>(A, b, Pd, mode, st.m, st.c, total, xi);
+    draw_and_write<TD, DD>(A, b, Pd, mode, st.m, st.c, total, xi);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2427,16 +2592,28 @@ __global__ __launch_bounds__(kThreads) void sv_small2_kernel(SampleLaunch A) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+// The finish keeps each wave's step in registers (OS) unless both rows are
+// fp32: their 64 bytes per octet pair would not fit beside the kernel's
+// other registers (measured: 64 VGPRs spilled).
+template <int TD, int DD>
+constexpr bool kKeepSteps = TD == 1 || DD == 1;
+
 template <int TD, int DD>
 static hipError_t launch_pair(const SampleLaunch& A, int stage, hipStream_t stream) {
   if (stage == 1)
     hipLaunchKernelGGL((sv_stats_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.per_seq)), dim3(kThreads), 0,
                        stream, A);
-  else if (A.fin_waves == 2 * kFinWaves)
-    hipLaunchKernelGGL((sv_finish_kernel<TD, DD, 2 * kFinWaves>), dim3((unsigned)((int64_t)A.B * A.parts)),
+  else if (kKeepSteps<TD, DD> && A.fin_waves == 2 * kFinWaves && A.parts == 1 && A.ns2 <= 2 * kFinWaves)
+    hipLaunchKernelGGL((sv_finish_kernel<TD, DD, 2 * kFinWaves, kKeepSteps<TD, DD>>), dim3((unsigned)A.B),
                        dim3(2 * kFinThreads), 0, stream, A);
+  else if (A.fin_waves == 2 * kFinWaves)
+    hipLaunchKernelGGL((sv_finish_kernel<TD, DD, 2 * kFinWaves, false>), dim3((unsigned)((int64_t)A.B * A.parts)),
+                       dim3(2 * kFinThreads), 0, stream, A);
+  else if (kKeepSteps<TD, DD> && A.parts == 1 && A.ns2 <= kFinWaves)
+    hipLaunchKernelGGL((sv_finish_kernel<TD, DD, kFinWaves, kKeepSteps<TD, DD>>), dim3((unsigned)A.B),
+                       dim3(kFinThreads), 0, stream, A);
   else
-    hipLaunchKernelGGL((sv_finish_kernel<TD, DD, kFinWaves>), dim3((unsigned)((int64_t)A.B * A.parts)),
+    hipLaunchKernelGGL((sv_finish_kernel<TD, DD, kFinWaves, false>), dim3((unsigned)((int64_t)A.B * A.parts)),
                        dim3(kFinThreads), 0, stream, A);
   return hipGetLastError();
 }
