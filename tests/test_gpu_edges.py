@@ -407,3 +407,17 @@ def test_full_acceptance_at_large_gamma(gpu, G):
     inp = synth.make_custom_sample(4, G, 696, "bf16", "bf16", T=0.9, noise_sd=0.0, seed=40 + G)
     for out in _full_and_staged(gpu, inp, f"full acceptance gamma={G}"):
         assert (out["n"] == G).all()
+
+
+@pytest.mark.parametrize("tdt,ddt,T", [("bf16", "f32", 1e-7), ("f32", "bf16", 1e-7), ("bf16", "bf16", 1.0)])
+def test_one_step_per_wave_finish(gpu, tdt, ddt, T):
+    """One finish workgroup per sequence with at most one step per wave (V =
+    5000, 3 steps): the waves keep their steps and the drawing wave rescans
+    from registers, in the FMA form and (T = 1e-7: shifts beyond 2^24) the
+    subtract form; against the oracle, and the staged kernels give the same
+    bits."""
+    H.log(f"one step per wave: {tdt}/{ddt} T={T}")
+    inp = synth.make_custom_sample(6, 3, 5000, tdt, ddt, T=T, noise_sd=0.5, seed=61)
+    out, staged = _full_and_staged(gpu, inp, f"one step per wave {tdt}/{ddt} T={T}")
+    for k in out:
+        assert np.array_equal(out[k].view(np.uint8), staged[k].view(np.uint8)), k
