@@ -174,9 +174,9 @@ int spec_verify_sample_noalloc(const void* target_logits, int target_dtype, int6
  * from the sizes: a position gets its own launch while the bytes its gate is
  * expected to save, at an assumed acceptance rate of 0.7, outweigh a launch;
  * small batches get k = 0, one launch with no gate), then the finish kernel.
- * With k = 0 and V <= 2048 (rows of one draw step) every row is read in any
- * case, and the call runs spec_verify_sample's one-kernel path instead (a wave
- * per sequence; the same results as spec_verify_sample, bit for bit).
+ * With k = 0 every row is read in any case, and the call runs
+ * spec_verify_sample instead (its work units, or its one-kernel path for
+ * V <= 2048; the same results as spec_verify_sample, bit for bit).
  * spec_verify_sample_early_exit_grouped takes k from the caller. In every launch
  * after the first, each workgroup re-derives the accept decision of the
  * position before it and streams its rows only if that position was accepted.
@@ -185,8 +185,8 @@ int spec_verify_sample_noalloc(const void* target_logits, int target_dtype, int6
  * Differences from spec_verify_sample: the row statistics are taken in smaller
  * chunks, so results can differ in rounding (an accept decision within ~1e-7
  * of u, p_x and q_x in the last bits); diag p_x, q_x are NaN for positions
- * whose rows were not read; more kernel launches (k + 2 instead of 2), except
- * on the one-kernel path above.
+ * whose rows were not read; more kernel launches (k + 2 instead of 2). With
+ * k = 0 none of these differences apply.
  */
 int spec_verify_sample_early_exit(const void* target_logits, int target_dtype, int64_t target_seq_stride,
                                   int64_t target_row_stride, const void* draft_logits, int draft_dtype,

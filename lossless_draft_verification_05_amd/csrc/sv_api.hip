@@ -190,9 +190,11 @@ static int run_sample_early(const SampleArgs& a, int tail_start, hipStream_t str
   if ((int64_t)L.B * L.per_seq > 0x7fffffffLL) return SV_ERR_SHAPE;
   L.reach = (int32_t*)((char*)a.ws + sample_layout(a.B, a.gamma, a.V).off_reach);
   const int k = tail_start >= 0 ? tail_start : early_tail_start(a.B, a.gamma, a.V, esz_of(a.tdt), esz_of(a.ddt));
-  // No gated position and rows of one draw step: every row is read either
-  // way, and the one-kernel path (a wave per sequence) does it in one launch.
-  if (k == 0 && a.V <= kStepTokens) return hip_status(launch_sample_small(plan_sample(a), a.tdt, a.ddt, stream));
+  // No gated position: every row is read either way, and the one-pass call
+  // does it with its own work units (finer for small calls: a single 128k
+  // sequence 0.0240 -> 0.0205 ms) or, for rows of one draw step, in one
+  // launch (a wave per sequence); its results are the one-pass call's.
+  if (k == 0) return run_sample(1, 2, a, stream);
   for (int p0 = 0; p0 <= a.gamma;) {
     const int p1 = (p0 < k) ? p0 : a.gamma;
     st = hip_status(launch_sample_pos(L, a.tdt, a.ddt, p0, p1, stream));

@@ -146,13 +146,13 @@ def test_huge_logits(gpu, grouping):
 
 
 @pytest.mark.parametrize("tdt,ddt", [("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16")])
-@pytest.mark.parametrize("V", [32, 700, 2048])
+@pytest.mark.parametrize("V", [32, 700, 2048, 5000, 40000])
 def test_one_step_rows_no_gate_same_bits(gpu, tdt, ddt, V):
-    """Rows of one draw step (V <= 2048) with no gated position: the early exit
-    reads every row in any case and runs the one-kernel path, so its outputs
-    and diagnostics equal the one-pass call's bit for bit (the grouping chosen
-    from the sizes and tail_start = 0 alike), and match the oracle."""
-    H.log(f"early exit, rows of one step, no gate: V={V} {tdt}/{ddt}")
+    """No gated position (a small call: the grouping chosen from the sizes, or
+    tail_start = 0): the early exit reads every row in any case and runs the
+    one-pass call (its one-kernel path for V <= 2048), so its outputs and
+    diagnostics equal the one-pass call's bit for bit, and match the oracle."""
+    H.log(f"early exit, no gate: V={V} {tdt}/{ddt}")
     inp = synth.make_custom_sample(40, 4, V, tdt, ddt, T=np.linspace(0.5, 1.5, 40, dtype=np.float32),
                                    noise_sd=0.6, seed=V + 7)
     tens = H.sample_tensors(inp, pad_to=8)  # rows padded to 16 bytes (V = 700 in bf16)
