@@ -762,6 +762,24 @@ def main():
         ee_ms = (time.perf_counter() - t2) * 1e3 / args.steps
         ee = (ee_ms, ee_n.cpu().numpy(), ee_t.cpu().numpy())
         log(f"[bench] early exit: {ee_ms:.4f} ms/step")
+    # the statistics pass's reads alone (stage 3: same grid, chunks and loads,
+    # no arithmetic) on the same inputs: the read rate that pass could reach
+    ro = None
+    if not tree and not args.early_exit and not small:
+        ro_prep = [binding.spec_verify_sample_stage(3, tcopies[c], dcopies[c], tokens, uni, temps,
+                                                    out_num_accepted=out_n, out_tokens=out_t, workspace=ws,
+                                                    prepare=True) for c in range(R)]
+        for k in range(min(args.warmup, 20)):
+            ro_prep[k % R]()
+        ro_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            ro_ev[k][0].record()
+            ro_prep[k % R]()
+            ro_ev[k][1].record()
+        torch.cuda.synchronize()
+        ro = np.array([e[0].elapsed_time(e[1]) for e in ro_ev])
+        log(f"[bench] statistics reads alone: {ro.mean() * 1e3:.1f} us")
     per_kernel = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(ns)] for k in range(args.steps)])
     stage_ms = [float(v) for v in per_kernel.mean(axis=0)]
     log(f"[bench] {ms_per_step:.4f} ms/step; kernel event means (ms): {stage_ms}")
@@ -796,6 +814,14 @@ def main():
         elif small:
             s1_bytes = step_bytes  # one kernel reads the rows once and the draw row(s) again
         else:
+            if ro is not None:
+                detail["stats_reads_alone"] = {
+                    "entry_point": "spec_verify_sample_stage(3)", "mean_us": round(float(ro.mean()) * 1e3, 3),
+                    "median_us": round(float(np.median(ro)) * 1e3, 3),
+                    "gbps": round(s1_bytes / (float(ro.mean()) * 1e-3) / 1e9, 1),
+                    "stats_kernel_over_reads": round(stage_ms[0] / float(ro.mean()), 4),
+                    "note": "the statistics kernel's grid, chunks and loads with its arithmetic replaced by an xor: "
+                            "the rate at which it could read these bytes"}
             detail["kernels"]["sv_finish_kernel"]["alg_bytes"] = int(s2_bytes)
             detail["kernels"]["sv_finish_kernel"]["gbps"] = round(s2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1)
     detail["kernels"][kernel_names[0]]["alg_bytes"] = int(s1_bytes)

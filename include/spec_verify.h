@@ -225,6 +225,11 @@ int spec_verify_sample_early_exit_grouped(int tail_start, const void* target_log
  *      long rows): merges the statistics, runs the accept tests and the
  *      first-rejection scan, streams the one row (pair) the draw needs, draws
  *      by inverse CDF at u[b][gamma] and writes every output (and diag).
+ *   3: the reads of stage 1 alone, for measurement: the same grid, row
+ *      chunks and 16-byte loads, with the arithmetic replaced by an xor of
+ *      the loaded words. It computes nothing of the method and writes no
+ *      output; its time is the rate at which stage 1 could read these bytes.
+ *      It may leave one word of the workspace changed (stage 1 resets it).
  * Stage 2 must follow stage 1 on the same stream with the same arguments and
  * workspace. spec_verify_sample enqueues both.
  */

@@ -296,7 +296,8 @@ def spec_verify_sample_early_exit_grouped(tail_start, target, draft, draft_token
 
 def spec_verify_sample_stage(stage, target, draft, draft_tokens, uniforms, temperature, *, out_num_accepted=None,
                              out_tokens=None, diag=False, workspace=None, stream=None, prepare=False):
-    """One stage of spec_verify_sample: 1 row statistics, 2 accept tests + residual/bonus draw + outputs."""
+    """One stage of spec_verify_sample: 1 row statistics, 2 accept tests + residual/bonus draw + outputs,
+    3 the reads of stage 1 alone (a measurement of its read rate; no outputs)."""
     return _sample_call(int(stage), target, draft, draft_tokens, uniforms, temperature, out_num_accepted,
                         out_tokens, diag, workspace, stream, prepare)
 

@@ -283,7 +283,7 @@ int spec_verify_sample_stage(int stage, const void* target_logits, int target_dt
                              const float* uniforms, const float* temperature, int B, int gamma, int V,
                              int32_t* out_num_accepted, int32_t* out_tokens, const sv_sample_diag* diag,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (stage < 1 || stage > 2) return SV_ERR_ARG;
+  if (stage < 1 || stage > 3) return SV_ERR_ARG;
   SampleArgs a{target_logits, target_dtype, target_seq_stride, target_row_stride, draft_logits, draft_dtype,
                draft_seq_stride, draft_row_stride, draft_tokens, uniforms, temperature, B, gamma, V,
                out_num_accepted, out_tokens, diag, workspace, workspace_bytes};

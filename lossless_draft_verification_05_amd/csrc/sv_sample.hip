@@ -144,12 +144,25 @@ __device__ __forceinline__ void sumexp_sub(SumExpSub& st, const Unit<DT> (&un)[N
   }
 }
 
+// The read-only pass (a measurement of the rate at which the statistics pass
+// can read its own bytes): every 32-bit word of every unit is folded into one
+// xor, so each 16-byte load is kept whole, and nothing else is computed.
+struct ReadXor {
+  uint32_t s;
+};
+
 template <int DT, int NU, class St>
 __device__ __forceinline__ void sumexp(St& st, const Unit<DT> (&un)[NU], float kl) {
-  if constexpr (std::is_same<St, SumExp>::value)
+  if constexpr (std::is_same<St, SumExp>::value) {
     sumexp_fma<DT, NU>(st, un, kl);
-  else
+  } else if constexpr (std::is_same<St, ReadXor>::value) {
+#pragma unroll
+    for (int j = 0; j < NU; ++j)
+#pragma unroll
+      for (int k = 0; k < Unit<DT>::kEpu; ++k) st.s ^= __float_as_uint(un[j].x[k]);
+  } else {
     sumexp_sub<DT, NU>(st, un, kl);
+  }
 }
 
 // The workgroup streams units [c_begin, c_end) of a row with V elements; thread
@@ -430,6 +443,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
   const float kl = temp_ok(T) ? log2e_over(T) : 1.0f;
   if (r == 0) reset_handoff(A, b);
   stats_chunk<TD, DD>(A, b, r, kl);
+}
+
+// The statistics pass's reads alone: the same grid, chunks and loads as
+// sv_stats_kernel, with the arithmetic replaced by an xor of the loaded words.
+// Writes nothing unless the xor of a workgroup's first wave equals one
+// arbitrary constant (then that value to the sequence's finish counter in the
+// workspace, which the statistics pass resets before any finish reads it).
+template <int TD, int DD>
+__global__ __launch_bounds__(kThreads) void sv_read_kernel(SampleLaunch A) {
+  const int64_t wg = blockIdx.x;
+  const int b = (int)(wg / A.per_seq);
+  const int r = (int)(wg % A.per_seq);
+  ReadXor st{0u};
+  if (r < (A.gamma + 1) * A.nct)
+    stream_slot<TD>(A, b, r, 1.0f, st);
+  else
+    stream_slot<DD>(A, b, r, 1.0f, st);
+  if (threadIdx.x == 0 && st.s == 0x9e3779b9u) A.done[b] = (int32_t)st.s;
 }
 
 // Early exit: the statistics of positions p0..p1 (target rows, and draft rows
@@ -2602,6 +2633,9 @@ template <int TD, int DD>
 static hipError_t launch_pair(const SampleLaunch& A, int stage, hipStream_t stream) {
   if (stage == 1)
     hipLaunchKernelGGL((sv_stats_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.per_seq)), dim3(kThreads), 0,
+                       stream, A);
+  else if (stage == 3)
+    hipLaunchKernelGGL((sv_read_kernel<TD, DD>), dim3((unsigned)((int64_t)A.B * A.per_seq)), dim3(kThreads), 0,
                        stream, A);
   else if (kKeepSteps<TD, DD> && A.fin_waves == 2 * kFinWaves && A.parts == 1 && A.ns2 <= 2 * kFinWaves)
     hipLaunchKernelGGL((sv_finish_kernel<TD, DD, 2 * kFinWaves, kKeepSteps<TD, DD>>), dim3((unsigned)A.B),

@@ -92,7 +92,7 @@ def call_sample(lib, stage=None, **over):
 ])
 def test_sample_argument_errors(lib, over, want):
     assert call_sample(lib, **over) == want
-    for stage in (1, 2, "early_exit", "grouped"):
+    for stage in (1, 2, 3, "early_exit", "grouped"):
         assert call_sample(lib, stage=stage, **over) == want
 
 
@@ -140,8 +140,9 @@ def test_grouping_beyond_gamma(lib):
 
 
 def test_unknown_stage(lib):
-    assert call_sample(lib, stage=3) == -7
+    assert call_sample(lib, stage=4) == -7
     assert call_sample(lib, stage=0) == -7
+    assert call_sample(lib, stage=-1) == -7
     assert call_sample(lib, stage=-1) == -7
 
 

@@ -421,3 +421,22 @@ def test_one_step_per_wave_finish(gpu, tdt, ddt, T):
     out, staged = _full_and_staged(gpu, inp, f"one step per wave {tdt}/{ddt} T={T}")
     for k in out:
         assert np.array_equal(out[k].view(np.uint8), staged[k].view(np.uint8)), k
+
+
+@pytest.mark.parametrize("V,tdt,ddt", [(5000, "bf16", "f32"), (128257, "bf16", "bf16"), (1500, "f32", "f32")])
+def test_read_stage_writes_no_output(gpu, V, tdt, ddt):
+    """Stage 3 (the statistics pass's reads alone, a measurement) leaves every
+    output as it was, and the full call on the same workspace afterwards still
+    gives the oracle's results (the statistics pass resets what stage 3 may
+    have left in the workspace)."""
+    H.log(f"read stage V={V} {tdt}/{ddt}")
+    inp = synth.make_custom_sample(6, 4, V, tdt, ddt, T=[0.7, 1.0, 1.3, 0.9, 1.0, 2.0], seed=V + 7)
+    tens = H.sample_tensors(inp, pad_to=8)
+    ws = gpu.Workspace()
+    B, G = inp.tokens.shape
+    n0 = torch.full((B,), -77, dtype=torch.int32, device="cuda")
+    t0 = torch.full((B, G + 1), -77, dtype=torch.int32, device="cuda")
+    gpu.spec_verify_sample_stage(3, **tens, out_num_accepted=n0, out_tokens=t0, workspace=ws)
+    torch.cuda.synchronize()
+    assert (n0.cpu().numpy() == -77).all() and (t0.cpu().numpy() == -77).all()
+    _check(inp, H.run_sample_staged(gpu, tens, workspace=ws), f"after read stage V={V}")
