@@ -447,9 +447,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
 
 // The statistics pass's reads alone: the same grid, chunks and loads as
 // sv_stats_kernel, with the arithmetic replaced by an xor of the loaded words.
-// Writes nothing unless the xor of a workgroup's first wave equals one
+// Writes nothing unless the xor of a workgroup's first thread equals one
 // arbitrary constant (then that value to the sequence's finish counter in the
-// workspace, which the statistics pass resets before any finish reads it).
+// workspace, which the statistics pass resets before any finish reads it);
+// the comparison keeps every thread's loads alive.
 template <int TD, int DD>
 __global__ __launch_bounds__(kThreads) void sv_read_kernel(SampleLaunch A) {
   const int64_t wg = blockIdx.x;
